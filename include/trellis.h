@@ -1,0 +1,157 @@
+/*
+ * trellis.h -- C ABI of the MI355X (gfx950) packed trellis-coded linear layer.
+ *
+ * Every weight of a stored matrix [R, C] (coded along C) is one k-bit symbol
+ * of a uint32 bitstream, in blocks of T symbols.  The weight at block
+ * position t is decoded from its L-bit state, the window that starts at bit
+ * (T-1-t)*k of the block and wraps at the block end; the state goes through
+ * the "1MAD" computed code to a value, which is scaled by the stored row's
+ * fp16 scale.  Source: mlx-bun 0.2.0 -> 0.4.0 diff (page 55),
+ * src/model/trellis-linear.ts, file header comment (format, axis
+ * convention) and the HEADER decode helpers (trellis_y, trellis_val,
+ * trellis_val_rcp, trellis_state).
+ *
+ * Conventions shared by every entry point
+ *   - Buffers are DEVICE memory owned by the caller; the library never
+ *     allocates on these calls and never keeps a pointer after returning.
+ *   - Tensors are row-major and contiguous.  bf16 and fp16 values are passed
+ *     as uint16_t bit patterns.  codes, x, out and workspace must be 16-byte
+ *     aligned; scales 2-byte aligned.
+ *   - Supported geometry: k in {2, 3, 4}, L = 12, T = 256, C % T == 0,
+ *     R >= 1, C >= 1 (others: TRELLIS_EUNSUPPORTED or TRELLIS_EINVAL).
+ *   - `stream` is a hipStream_t (NULL = the device's default stream).  Calls
+ *     are asynchronous on that stream and never synchronise the host.
+ *   - All checks run on the host before any launch.  On any non-zero return
+ *     nothing was launched and nothing was written; trellis_last_error()
+ *     then describes the problem (thread-local, valid until the next call on
+ *     the same thread).
+ *   - Calls that take a workspace use it as scratch that is fully rewritten
+ *     by the call; concurrent calls must not share one workspace.
+ */
+#ifndef TRELLIS_H
+#define TRELLIS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define TRELLIS_OK 0
+#define TRELLIS_EINVAL (-1)        /* bad pointer, size, alignment or argument */
+#define TRELLIS_EUNSUPPORTED (-2)  /* geometry outside k in {2,3,4}, L = 12, T = 256 */
+#define TRELLIS_EWORKSPACE (-3)    /* workspace smaller than the queried size */
+#define TRELLIS_EHIP (-4)          /* a HIP runtime or library call failed */
+
+/* output element types for the plain matvecs */
+#define TRELLIS_OUT_BF16 0
+#define TRELLIS_OUT_F32 1
+
+/* prefill algorithms */
+#define TRELLIS_PREFILL_FUSED 0        /* decode into LDS tiles feeding bf16 MFMA */
+#define TRELLIS_PREFILL_EXPAND_GEMM 1  /* trellis_expand_bf16 into the workspace, then a GEMM */
+
+/* Largest M accepted by the packed matvecs (the pages' matvec/prefill
+ * crossover, trellis-linear.ts MATVEC_MAX_M). */
+#define TRELLIS_MATVEC_MAX_M 4
+
+/*
+ * trellis_matvec_axis1 -- y[m, r] = sum_c w(r, c) * x[m, c]   (axis = 1).
+ * Source: trellis-linear.ts (page 55), REDUCE kernel comment and
+ * TrellisLinear.forward; shared-M form in trellis-shared-m.ts (page 56).
+ *   codes   uint32 [R, C*k/32]  coded along the input dim C
+ *   scales  fp16   [R]          per output row
+ *   x       bf16   [M, C]
+ *   out     [M, R], bf16 (out_dtype = TRELLIS_OUT_BF16) or f32 (TRELLIS_OUT_F32)
+ *   1 <= M <= TRELLIS_MATVEC_MAX_M.
+ * w(r, c) is the f32 product of the code value and scales[r] (no bf16
+ * rounding of weights); sums accumulate in f32.
+ */
+size_t trellis_matvec_axis1_workspace_bytes(int64_t R, int64_t C, int M, int k, int L, int T);
+int trellis_matvec_axis1(const uint32_t* codes, const uint16_t* scales, const uint16_t* x,
+                         void* out, int out_dtype, int64_t R, int64_t C, int M, int k, int L,
+                         int T, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * trellis_gateup_swiglu -- out[m, r] = bf16(silu(bf16 g) * bf16 u), where
+ * g = gate(x), u = up(x) are two axis-1 matvecs of identical geometry over
+ * the same x.  Cast chain: gate and up to bf16, sigmoid of the bf16 gate to
+ * bf16, silu = bf16(gate * sigmoid), out = bf16(silu * up).
+ * Source: trellis-linear.ts (page 55), GATEUP kernel comment and
+ * fusedGateUpSwiglu / fusedGateUpEligible.
+ *   gcodes, ucodes  uint32 [R, C*k/32];  gscales, uscales fp16 [R]
+ *   x               bf16 [M, C];  out bf16 [M, R];  1 <= M <= 4
+ *   gate_f32, up_f32  optional f32 [M, R] copies of the raw sums (NULL = none)
+ */
+size_t trellis_gateup_swiglu_workspace_bytes(int64_t R, int64_t C, int M, int k, int L, int T);
+int trellis_gateup_swiglu(const uint32_t* gcodes, const uint16_t* gscales, const uint32_t* ucodes,
+                          const uint16_t* uscales, const uint16_t* x, uint16_t* out,
+                          float* gate_f32, float* up_f32, int64_t R, int64_t C, int M, int k,
+                          int L, int T, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * trellis_matvec_axis0 -- y[m, c] = sum_r w(r, c) * x[m, r]   (axis = 0).
+ * The stored matrix is W^T [R_in, C_out], coded along C_out; w uses the
+ * stored row's scale.  Split-K over stored rows into f32 partials in the
+ * workspace, then a second pass folds them.
+ * Source: trellis-linear.ts (page 55), SCATTER kernel comment and
+ * TrellisLinear #scatter (partials, then one sum and a cast).
+ *   codes   uint32 [R_in, C_out*k/32];  scales fp16 [R_in]
+ *   x       bf16 [M, R_in];  out [M, C_out] bf16 or f32;  1 <= M <= 4
+ */
+size_t trellis_matvec_axis0_workspace_bytes(int64_t R_in, int64_t C_out, int M, int k, int L, int T);
+int trellis_matvec_axis0(const uint32_t* codes, const uint16_t* scales, const uint16_t* x,
+                         void* out, int out_dtype, int64_t R_in, int64_t C_out, int M, int k,
+                         int L, int T, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * trellis_expand_bf16 -- out[r, c] = bf16(value(r, c) * scales[r]) for the
+ * stored matrix (stored orientation; an axis-0 caller gets W^T).  value is
+ * y/d correctly rounded to f32; the product is rounded to f32, then to bf16
+ * (nearest even).
+ * Source: trellis-linear.ts (page 55), EXPAND kernel and expandTrellis;
+ * trellis-vector-expand.ts (page 56).
+ *   codes uint32 [R, C*k/32];  scales fp16 [R];  out bf16 [R, C]
+ */
+int trellis_expand_bf16(const uint32_t* codes, const uint16_t* scales, uint16_t* out, int64_t R,
+                        int64_t C, int k, int L, int T, void* stream);
+
+/*
+ * trellis_prefill -- out[m, r] = bf16(sum_c wb(r, c) * x[m, c]) for axis 1,
+ * where wb is the expansion weight of trellis_expand_bf16; f32 accumulation.
+ * Source: trellis-tiled-prefill.ts (page 56) and the expand-then-matmul
+ * fallback of TrellisLinear.forward (page 55).
+ *   codes uint32 [R, C*k/32];  scales fp16 [R];  x bf16 [M, C];  out bf16 [M, R]
+ *   M >= 1;  algo = TRELLIS_PREFILL_FUSED or TRELLIS_PREFILL_EXPAND_GEMM.
+ * The EXPAND_GEMM workspace holds the bf16 [R, C] expansion.
+ */
+size_t trellis_prefill_workspace_bytes(int64_t R, int64_t C, int64_t M, int k, int L, int T,
+                                       int algo);
+int trellis_prefill(const uint32_t* codes, const uint16_t* scales, const uint16_t* x,
+                    uint16_t* out, int64_t R, int64_t C, int64_t M, int k, int L, int T, int algo,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * trellis_decode_states -- test export of the decode primitive: for every
+ * weight of the stored [R, C] matrix, its L-bit state, its 1MAD code y and
+ * the f32 code value y/d (correctly rounded).  Any output may be NULL.
+ * Source: trellis-linear.ts (page 55), HEADER (trellis_state, trellis_y,
+ * trellis_val).
+ *   states uint16 [R, C];  y int16 [R, C];  value f32 [R, C]
+ */
+int trellis_decode_states(const uint32_t* codes, int64_t R, int64_t C, int k, int L, int T,
+                          uint16_t* states, int16_t* y, float* value, void* stream);
+
+/* Description of the last non-OK status on this thread ("" if none). */
+const char* trellis_last_error(void);
+
+/* Library version string. */
+const char* trellis_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TRELLIS_H */
