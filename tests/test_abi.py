@@ -1,0 +1,127 @@
+"""Host-side checks of the C-ABI library (no GPU, no launches).
+
+The library must load on a machine without a GPU, export every symbol that
+include/trellis.h declares, and reject every invalid call on the host
+before any launch (status code + message).  Only invalid calls are made
+here, so no pointer is ever dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import trellis_coded_quantized_amd as tq
+from tests import tolerance as tol
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "trellis.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(trellis_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(tq.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = tq.load_library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert "gfx950" in tq.version()
+
+
+FAKE = ctypes.c_void_p(1 << 20)          # aligned, never dereferenced
+MIS = ctypes.c_void_p((1 << 20) + 4)     # misaligned by 4 bytes
+
+
+def call_axis1(codes=FAKE, scales=FAKE, x=FAKE, out=FAKE, od=0, R=512, C=2048, M=1, k=2, L=12, T=256):
+    lib = tq.load_library()
+    return lib.trellis_matvec_axis1(codes, scales, x, out, od, R, C, M, k, L, T, None, 0, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(k=1), tq.EUNSUPPORTED, "k=1"),
+    (dict(k=5), tq.EUNSUPPORTED, "k=5"),
+    (dict(L=16), tq.EUNSUPPORTED, "L=16"),
+    (dict(T=128), tq.EUNSUPPORTED, "T=128"),
+    (dict(C=2000), tq.EINVAL, "multiple of the block"),
+    (dict(R=0), tq.EINVAL, "empty"),
+    (dict(C=0), tq.EINVAL, "empty"),
+    (dict(M=0), tq.EINVAL, "M=0"),
+    (dict(M=5), tq.EINVAL, "M=5"),
+    (dict(od=7), tq.EINVAL, "out_dtype"),
+    (dict(codes=None), tq.EINVAL, "codes is NULL"),
+    (dict(x=MIS), tq.EINVAL, "x not 16-byte aligned"),
+    (dict(out=None), tq.EINVAL, "out is NULL"),
+    (dict(R=1 << 31), tq.EINVAL, "too large"),
+])
+def test_axis1_rejects_on_host(kw, status, needle):
+    assert call_axis1(**kw) == status
+    assert needle in tq.load_library().trellis_last_error().decode()
+
+
+def test_gateup_rejects_on_host():
+    lib = tq.load_library()
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 17408, 5120, 4, 2, 12, 256, None, 0, None]
+    bad = list(args)
+    bad[2] = None
+    assert lib.trellis_gateup_swiglu(*bad) == tq.EINVAL
+    assert "ucodes is NULL" in lib.trellis_last_error().decode()
+    bad = list(args)
+    bad[10] = 5
+    assert lib.trellis_gateup_swiglu(*bad) == tq.EINVAL
+    bad = list(args)
+    bad[6] = ctypes.c_void_p((1 << 20) + 2)
+    assert lib.trellis_gateup_swiglu(*bad) == tq.EINVAL
+    assert "gate_f32" in lib.trellis_last_error().decode()
+
+
+def test_axis0_workspace_is_checked():
+    lib = tq.load_library()
+    need = lib.trellis_matvec_axis0_workspace_bytes(17408, 5120, 4, 3, 12, 256)
+    assert need > 0
+    rc = lib.trellis_matvec_axis0(FAKE, FAKE, FAKE, FAKE, 0, 17408, 5120, 4, 3, 12, 256, FAKE,
+                                  need - 1, None)
+    assert rc == tq.EWORKSPACE
+    assert "workspace" in lib.trellis_last_error().decode()
+    assert lib.trellis_matvec_axis0_workspace_bytes(17408, 5120, 4, 5, 12, 256) == 0
+
+
+def test_prefill_validation_and_workspace():
+    lib = tq.load_library()
+    R, C = 17408, 5120
+    need = lib.trellis_prefill_workspace_bytes(R, C, 512, 2, 12, 256, tq.PREFILL_EXPAND_GEMM)
+    assert need >= R * C * 2
+    rc = lib.trellis_prefill(FAKE, FAKE, FAKE, FAKE, R, C, 512, 2, 12, 256, tq.PREFILL_EXPAND_GEMM,
+                             FAKE, need - 1, None)
+    assert rc == tq.EWORKSPACE
+    assert lib.trellis_prefill(FAKE, FAKE, FAKE, FAKE, R, C, 512, 2, 12, 256, 9, None, 0, None) == tq.EINVAL
+    assert lib.trellis_prefill(FAKE, FAKE, FAKE, FAKE, R, C, 0, 2, 12, 256, 0, None, 0, None) == tq.EINVAL
+
+
+def test_expand_and_decode_reject_on_host():
+    lib = tq.load_library()
+    assert lib.trellis_expand_bf16(FAKE, FAKE, None, 4, 256, 2, 12, 256, None) == tq.EINVAL
+    assert lib.trellis_expand_bf16(FAKE, FAKE, FAKE, 4, 256, 3, 12, 255, None) == tq.EUNSUPPORTED
+    assert lib.trellis_decode_states(MIS, 4, 256, 2, 12, 256, None, None, None, None) == tq.EINVAL
+    assert lib.trellis_last_error().decode().startswith("trellis_decode_states")
+
+
+# ---- the parity criteria themselves ------------------------------------
+
+def test_tolerance_helpers():
+    o = np.array([1.0, -2.5, 3.0e-3, 0.0, 100.0])
+    assert tol.f32_rel_error(o * (1 + 5e-6), o).max() <= 1e-5
+    assert tol.f32_rel_error(o * (1 + 5e-5), o).max() > 1e-5
+    bits = tol.bf16_bits_from_f64(o)
+    assert not tol.bf16_band_violations(bits, o).any()
+    assert not tol.bf16_band_violations(bits + np.uint16(1), o).any()       # one ulp away (positive values)
+    two = bits.copy()
+    two[0] += 2
+    assert tol.bf16_band_violations(two, o)[0]
+    assert tol.bf16_key(np.array([0x8000], np.uint16))[0] == tol.bf16_key(np.array([0], np.uint16))[0]

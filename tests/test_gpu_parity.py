@@ -1,0 +1,262 @@
+"""GPU parity: the HIP library (through the C ABI) against the CPU oracle.
+
+Decoded states, codes, values and bf16 expansions must match bit for bit;
+matvec sums within the floored 1e-5 relative criterion in f32 and the bf16
+band of tests/tolerance.py; the SwiGLU output within the candidate band of
+its cast chain.  Inputs follow trellis_inputs (seeded, synthetic).  Full
+workload sizes are compared in full where the oracle takes seconds, and on
+sampled outputs for the prefill.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import trellis_coded_quantized_amd as tq
+import trellis_inputs as ti
+from tests import tolerance as tol
+
+pytestmark = pytest.mark.gpu
+
+L, T = 12, 256
+DEV = "cuda:0"
+
+
+def d_codes(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int32)).to(DEV)
+
+
+def d_half(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(DEV).view(torch.float16)
+
+
+def d_bf16(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def h_u16(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def rand_matrix(rng, R, C, k):
+    return ti.codes(rng, R, C, k), ti.scales(rng, R)
+
+
+# ------------------------------------------------------------------ decode
+
+def crafted_codes(R, C, k):
+    words = C * k // 32
+    pats = [0x00000000, 0xFFFFFFFF, 0xAAAAAAAA, 0x55555555, 0x80000001, 0x0F0F0F0F]
+    a = np.empty((R, words), np.uint32)
+    for r in range(R):
+        a[r] = pats[r % len(pats)]
+    return a
+
+
+@pytest.mark.parametrize("k", [2, 3, 4])
+@pytest.mark.parametrize("R,C,kind", [(5, 1024, "random"), (6, 256, "crafted"), (1, 256, "random")])
+def test_decode_states_bit_exact(k, R, C, kind):
+    rng = np.random.default_rng(40 + k)
+    codes = ti.codes(rng, R, C, k) if kind == "random" else crafted_codes(R, C, k)
+    st, ys, vals = tq.decode_states(d_codes(codes), k)
+    ost, oys, ovals = oracle.decode(codes, R, C, k, L, T)
+    assert np.array_equal(st.cpu().numpy().view(np.uint16), ost)
+    assert np.array_equal(ys.cpu().numpy(), oys)
+    assert np.array_equal(vals.cpu().numpy().view(np.uint32), ovals.view(np.uint32))
+
+
+@pytest.mark.parametrize("wl,k", [("gateup", 2), ("axis0", 3), ("layer_chain", 4)])
+def test_decode_states_workload_rows(wl, k):
+    w = ti.WORKLOADS[wl]()
+    m = w.mats[0]
+    for rows in (slice(0, 16), slice(m.R - 16, m.R)):
+        sub = np.ascontiguousarray(m.codes[rows])
+        st, ys, vals = tq.decode_states(d_codes(sub), k)
+        ost, oys, ovals = oracle.decode(sub, sub.shape[0], m.C, k, L, T)
+        assert np.array_equal(st.cpu().numpy().view(np.uint16), ost)
+        assert np.array_equal(vals.cpu().numpy().view(np.uint32), ovals.view(np.uint32))
+
+
+# ------------------------------------------------------------------ axis 1
+
+def check_axis1(codes, scales, x, R, C, M, k, what):
+    want = oracle.matvec_axis1(codes, scales, x, M, R, C, k, L, T)
+    dc, ds, dx = d_codes(codes), d_half(scales), d_bf16(x)
+    got32 = tq.matvec_axis1(dc, ds, dx, k, out_dtype=torch.float32).cpu().numpy()
+    tol.assert_f32_close(got32, want, what + " f32")
+    got16 = h_u16(tq.matvec_axis1(dc, ds, dx, k))
+    tol.assert_bf16_close(got16, want, what + " bf16")
+    # metamorphic: negated input gives exactly negated sums
+    neg = tq.matvec_axis1(dc, ds, d_bf16(x ^ np.uint16(0x8000)), k, out_dtype=torch.float32).cpu().numpy()
+    assert np.array_equal(neg, -got32), what + " negation"
+
+
+@pytest.mark.parametrize("k", [2, 3, 4])
+@pytest.mark.parametrize("R,C,M", [(1, 256, 1), (7, 1280, 4), (130, 768, 3), (67, 2304, 2)])
+def test_axis1_small(k, R, C, M):
+    rng = np.random.default_rng(R * 31 + C + M * 7 + k)
+    codes, scales = rand_matrix(rng, R, C, k)
+    x = ti.activations(rng, M, C)
+    check_axis1(codes, scales, x, R, C, M, k, f"axis1 R={R} C={C} M={M} k={k}")
+
+
+def test_axis1_workload_512x2048_k2_m1():
+    w = ti.axis1_m1()
+    m = w.mats[0]
+    check_axis1(m.codes, m.scales, w.x[0], m.R, m.C, 1, m.k, w.name)
+
+
+def test_axis1_zero_input_is_exact_zero():
+    rng = np.random.default_rng(3)
+    codes, scales = rand_matrix(rng, 33, 512, 3)
+    x = np.zeros((2, 512), np.uint16)
+    got = tq.matvec_axis1(d_codes(codes), d_half(scales), d_bf16(x), 3, out_dtype=torch.float32)
+    assert not got.cpu().numpy().any()
+
+
+# ------------------------------------------------------------------ gate/up
+
+def check_gateup(g, u, x, R, C, M, k, what, want=None):
+    if want is None:
+        want = oracle.gateup_swiglu(g.codes, g.scales, u.codes, u.scales, x, M, R, C, k, L, T)
+    og, ou, _ = want
+    dx = d_bf16(x[:M])
+    gf = torch.empty((M, R), dtype=torch.float32, device=DEV)
+    uf = torch.empty((M, R), dtype=torch.float32, device=DEV)
+    out = tq.gateup_swiglu(d_codes(g.codes), d_half(g.scales), d_codes(u.codes), d_half(u.scales),
+                           dx, k, gate_f32=gf, up_f32=uf)
+    tol.assert_f32_close(gf.cpu().numpy(), og[:M], what + " gate")
+    tol.assert_f32_close(uf.cpu().numpy(), ou[:M], what + " up")
+    tol.assert_swiglu_close(h_u16(out), og[:M], ou[:M], what + " swiglu")
+
+
+@pytest.mark.parametrize("k", [2, 3, 4])
+@pytest.mark.parametrize("R,C,M", [(1, 256, 1), (37, 1280, 4), (129, 512, 2)])
+def test_gateup_small(k, R, C, M):
+    rng = np.random.default_rng(R * 13 + C + M + k)
+    g = ti.Matrix(1, R, C, k, *rand_matrix(rng, R, C, k))
+    u = ti.Matrix(1, R, C, k, *rand_matrix(rng, R, C, k))
+    x = ti.activations(rng, M, C)
+    check_gateup(g, u, x, R, C, M, k, f"gateup R={R} C={C} M={M} k={k}")
+
+
+@pytest.fixture(scope="module")
+def gateup_workload():
+    w = ti.gateup()
+    g, u = w.mats
+    want = oracle.gateup_swiglu(g.codes, g.scales, u.codes, u.scales, w.x[0], 4, g.R, g.C, g.k, L, T)
+    return w, want
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
+def test_gateup_workload_17408x5120_k2(gateup_workload, M):
+    w, want = gateup_workload
+    g, u = w.mats
+    check_gateup(g, u, w.x[0], g.R, g.C, M, g.k, f"{w.name} M={M}", want=want)
+
+
+# ------------------------------------------------------------------ axis 0
+
+def check_axis0(codes, scales, x, R, C, M, k, what, want=None):
+    if want is None:
+        want = oracle.matvec_axis0(codes, scales, x, M, R, C, k, L, T)
+    dc, ds, dx = d_codes(codes), d_half(scales), d_bf16(x[:M])
+    got32 = tq.matvec_axis0(dc, ds, dx, k, out_dtype=torch.float32).cpu().numpy()
+    tol.assert_f32_close(got32, want[:M], what + " f32")
+    got16 = h_u16(tq.matvec_axis0(dc, ds, dx, k))
+    tol.assert_bf16_close(got16, want[:M], what + " bf16")
+
+
+@pytest.mark.parametrize("k", [2, 3, 4])
+@pytest.mark.parametrize("R,C,M", [(1, 256, 1), (3, 768, 4), (200, 512, 2), (1000, 1280, 3)])
+def test_axis0_small(k, R, C, M):
+    rng = np.random.default_rng(R * 17 + C + M + k)
+    codes, scales = rand_matrix(rng, R, C, k)
+    x = ti.activations(rng, M, R)
+    check_axis0(codes, scales, x, R, C, M, k, f"axis0 R={R} C={C} M={M} k={k}")
+
+
+@pytest.fixture(scope="module")
+def axis0_workload():
+    w = ti.axis0()
+    m = w.mats[0]
+    return w, oracle.matvec_axis0(m.codes, m.scales, w.x[0], 4, m.R, m.C, m.k, L, T)
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
+def test_axis0_workload_17408x5120_k3(axis0_workload, M):
+    w, want = axis0_workload
+    m = w.mats[0]
+    check_axis0(m.codes, m.scales, w.x[0], m.R, m.C, M, m.k, f"{w.name} M={M}", want=want)
+
+
+# ------------------------------------------------------------------ layer chain
+
+def test_layer_chain_k4_m4():
+    w = ti.layer_chain()
+    outs = []
+    for m, x in zip(w.mats, w.x):       # back to back on one stream
+        fn = tq.matvec_axis1 if m.axis == 1 else tq.matvec_axis0
+        outs.append(fn(d_codes(m.codes), d_half(m.scales), d_bf16(x), m.k, out_dtype=torch.float32))
+    torch.cuda.synchronize()
+    for m, x, o in zip(w.mats, w.x, outs):
+        ref = oracle.matvec_axis1 if m.axis == 1 else oracle.matvec_axis0
+        want = ref(m.codes, m.scales, x, 4, m.R, m.C, m.k, L, T)
+        tol.assert_f32_close(o.cpu().numpy(), want, f"{w.name} axis{m.axis} {m.R}x{m.C}")
+
+
+# ------------------------------------------------------------------ expand
+
+@pytest.mark.parametrize("k", [2, 3, 4])
+@pytest.mark.parametrize("R,C", [(1, 256), (9, 1280)])
+def test_expand_bit_exact(k, R, C):
+    rng = np.random.default_rng(R + C + k)
+    codes, scales = rand_matrix(rng, R, C, k)
+    got = h_u16(tq.expand_bf16(d_codes(codes), d_half(scales), k))
+    assert np.array_equal(got, oracle.expand_bf16(codes, scales, R, C, k, L, T))
+
+
+def test_expand_workload_rows_bit_exact():
+    w = ti.prefill(Ms=(1,))
+    m = w.mats[0]
+    got = tq.expand_bf16(d_codes(m.codes), d_half(m.scales), m.k)
+    for r0 in (0, m.R // 2, m.R - 32):
+        want = oracle.expand_bf16(m.codes, m.scales, m.R, m.C, m.k, L, T, r0=r0, nr=32)
+        assert np.array_equal(h_u16(got[r0:r0 + 32]), want), r0
+
+
+# ------------------------------------------------------------------ prefill
+
+ALGOS = [tq.PREFILL_FUSED, tq.PREFILL_EXPAND_GEMM]
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("k", [2, 3, 4])
+@pytest.mark.parametrize("R,C,M", [(7, 256, 1), (200, 768, 5), (130, 512, 131)])
+def test_prefill_small(algo, k, R, C, M):
+    rng = np.random.default_rng(R + C + M + k)
+    codes, scales = rand_matrix(rng, R, C, k)
+    x = ti.activations(rng, M, C)
+    got = h_u16(tq.prefill(d_codes(codes), d_half(scales), d_bf16(x), k, algo=algo))
+    want = oracle.prefill_sums(codes, scales, x, M, R, C, k, L, T, np.arange(M), np.arange(R))
+    tol.assert_bf16_close(got, want, f"prefill algo={algo} R={R} C={C} M={M} k={k}")
+
+
+@pytest.fixture(scope="module")
+def prefill_workload():
+    return ti.prefill()
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("M", [32, 512, 2048])
+def test_prefill_workload_17408x5120_k2(prefill_workload, algo, M):
+    w = prefill_workload
+    m = w.mats[0]
+    x = w.x[0][:M]
+    got = tq.prefill(d_codes(m.codes), d_half(m.scales), d_bf16(x), m.k, algo=algo)
+    rng = np.random.default_rng(M)
+    ms = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, 6)]))
+    rows = np.unique(np.concatenate([[0, 1, m.R - 1], rng.integers(0, m.R, 61)]))
+    want = oracle.prefill_sums(m.codes, m.scales, x, M, m.R, m.C, m.k, L, T, ms, rows)
+    sub = h_u16(got[torch.as_tensor(ms, device=DEV)][:, torch.as_tensor(rows, device=DEV)])
+    tol.assert_bf16_close(sub, want, f"{w.name} algo={algo} M={M}")

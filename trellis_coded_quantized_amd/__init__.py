@@ -1,0 +1,242 @@
+"""MI355X (gfx950) linear layer over packed trellis-coded weights.
+
+A thin ctypes binding over libtrellis.so (include/trellis.h).  The functions
+keep the C names without the ``trellis_`` prefix and only marshal
+arguments: shapes and dtypes are checked, outputs and workspaces are
+allocated with PyTorch on the input's device, and the call is enqueued on
+the current PyTorch stream.  Every arithmetic step runs in the HIP library;
+if libtrellis.so is missing the functions raise instead of computing
+anything another way.
+
+Tensor conventions (all CUDA/HIP device tensors, contiguous):
+  codes  int32/uint32 [rows, cols*k/32]  packed code words
+  scales float16 [rows]
+  x      bfloat16 [M, in_features]
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtrellis.so")
+
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
+OUT_BF16, OUT_F32 = 0, 1
+PREFILL_FUSED, PREFILL_EXPAND_GEMM = 0, 1
+MATVEC_MAX_M = 4
+
+# every symbol include/trellis.h declares
+EXPORTS = (
+    "trellis_matvec_axis1_workspace_bytes", "trellis_matvec_axis1",
+    "trellis_gateup_swiglu_workspace_bytes", "trellis_gateup_swiglu",
+    "trellis_matvec_axis0_workspace_bytes", "trellis_matvec_axis0",
+    "trellis_expand_bf16", "trellis_prefill_workspace_bytes", "trellis_prefill",
+    "trellis_decode_states", "trellis_last_error", "trellis_version",
+)
+
+
+class TrellisError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"[status {status}] {msg}")
+        self.status = status
+
+
+_lib = None
+_vp, _i64, _int, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+
+
+def load_library():
+    """Load libtrellis.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} not built; run trellis_coded_quantized_amd._build.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    sig = {
+        "trellis_matvec_axis1_workspace_bytes": (_sz, [_i64, _i64, _int, _int, _int, _int]),
+        "trellis_matvec_axis1": (_int, [_vp, _vp, _vp, _vp, _int, _i64, _i64, _int, _int, _int, _int,
+                                        _vp, _sz, _vp]),
+        "trellis_gateup_swiglu_workspace_bytes": (_sz, [_i64, _i64, _int, _int, _int, _int]),
+        "trellis_gateup_swiglu": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _int,
+                                         _int, _int, _int, _vp, _sz, _vp]),
+        "trellis_matvec_axis0_workspace_bytes": (_sz, [_i64, _i64, _int, _int, _int, _int]),
+        "trellis_matvec_axis0": (_int, [_vp, _vp, _vp, _vp, _int, _i64, _i64, _int, _int, _int, _int,
+                                        _vp, _sz, _vp]),
+        "trellis_expand_bf16": (_int, [_vp, _vp, _vp, _i64, _i64, _int, _int, _int, _vp]),
+        "trellis_prefill_workspace_bytes": (_sz, [_i64, _i64, _i64, _int, _int, _int, _int]),
+        "trellis_prefill": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int, _int,
+                                   _vp, _sz, _vp]),
+        "trellis_decode_states": (_int, [_vp, _i64, _i64, _int, _int, _int, _vp, _vp, _vp, _vp]),
+        "trellis_last_error": (ctypes.c_char_p, []),
+        "trellis_version": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def version() -> str:
+    return load_library().trellis_version().decode()
+
+
+def _check(status: int):
+    if status != OK:
+        raise TrellisError(status, load_library().trellis_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, name, dtypes, ndim):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name}: expected {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+
+
+_CODES = (torch.int32, torch.uint32)
+
+
+def _geometry(codes, k):
+    rows, words = codes.shape
+    if (words * 32) % k:
+        raise ValueError(f"{words} words are not a whole number of {k}-bit symbols")
+    return rows, words * 32 // k
+
+
+def _workspace(nbytes, device, workspace):
+    if nbytes == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def matvec_axis1(codes, scales, x, k, L=12, T=256, out_dtype=torch.bfloat16, out=None,
+                 workspace=None):
+    """y[m, r] = sum_c w(r, c) x[m, c]; codes [R, C*k/32] coded along inputs."""
+    _need(codes, "codes", _CODES, 2)
+    _need(scales, "scales", (torch.float16,), 1)
+    _need(x, "x", (torch.bfloat16,), 2)
+    R, C = _geometry(codes, k)
+    M = x.shape[0]
+    if x.shape[1] != C:
+        raise ValueError(f"x has {x.shape[1]} features, codes encode {C}")
+    if out is None:
+        out = torch.empty((M, R), dtype=out_dtype, device=x.device)
+    od = OUT_F32 if out.dtype == torch.float32 else OUT_BF16
+    lib = load_library()
+    ws, wsb = _workspace(lib.trellis_matvec_axis1_workspace_bytes(R, C, M, k, L, T), x.device, workspace)
+    _check(lib.trellis_matvec_axis1(_ptr(codes), _ptr(scales), _ptr(x), _ptr(out), od, R, C, M, k, L,
+                                    T, _ptr(ws), wsb, _stream(x.device)))
+    return out
+
+
+def gateup_swiglu(gcodes, gscales, ucodes, uscales, x, k, L=12, T=256, out=None,
+                  gate_f32=None, up_f32=None, workspace=None):
+    """bf16 silu(gate(x)) * up(x) with the bf16 cast chain; returns out [M, R]."""
+    for t, n in ((gcodes, "gcodes"), (ucodes, "ucodes")):
+        _need(t, n, _CODES, 2)
+    for t, n in ((gscales, "gscales"), (uscales, "uscales")):
+        _need(t, n, (torch.float16,), 1)
+    _need(x, "x", (torch.bfloat16,), 2)
+    if gcodes.shape != ucodes.shape:
+        raise ValueError("gate and up codes differ in shape")
+    R, C = _geometry(gcodes, k)
+    M = x.shape[0]
+    if x.shape[1] != C:
+        raise ValueError(f"x has {x.shape[1]} features, codes encode {C}")
+    if out is None:
+        out = torch.empty((M, R), dtype=torch.bfloat16, device=x.device)
+    lib = load_library()
+    ws, wsb = _workspace(lib.trellis_gateup_swiglu_workspace_bytes(R, C, M, k, L, T), x.device,
+                         workspace)
+    _check(lib.trellis_gateup_swiglu(_ptr(gcodes), _ptr(gscales), _ptr(ucodes), _ptr(uscales),
+                                     _ptr(x), _ptr(out), _ptr(gate_f32), _ptr(up_f32), R, C, M, k, L,
+                                     T, _ptr(ws), wsb, _stream(x.device)))
+    return out
+
+
+def matvec_axis0(codes_t, scales, x, k, L=12, T=256, out_dtype=torch.bfloat16, out=None,
+                 workspace=None):
+    """y[m, c] = sum_r w(r, c) x[m, r]; codes_t is the stored W^T [R_in, C_out*k/32]."""
+    _need(codes_t, "codes", _CODES, 2)
+    _need(scales, "scales", (torch.float16,), 1)
+    _need(x, "x", (torch.bfloat16,), 2)
+    R, C = _geometry(codes_t, k)
+    M = x.shape[0]
+    if x.shape[1] != R:
+        raise ValueError(f"x has {x.shape[1]} features, stored rows are {R}")
+    if out is None:
+        out = torch.empty((M, C), dtype=out_dtype, device=x.device)
+    od = OUT_F32 if out.dtype == torch.float32 else OUT_BF16
+    lib = load_library()
+    ws, wsb = _workspace(lib.trellis_matvec_axis0_workspace_bytes(R, C, M, k, L, T), x.device,
+                         workspace)
+    _check(lib.trellis_matvec_axis0(_ptr(codes_t), _ptr(scales), _ptr(x), _ptr(out), od, R, C, M, k,
+                                    L, T, _ptr(ws), wsb, _stream(x.device)))
+    return out
+
+
+def expand_bf16(codes, scales, k, L=12, T=256, out=None):
+    """bf16 [R, C] decode of the stored matrix (stored orientation)."""
+    _need(codes, "codes", _CODES, 2)
+    _need(scales, "scales", (torch.float16,), 1)
+    R, C = _geometry(codes, k)
+    if out is None:
+        out = torch.empty((R, C), dtype=torch.bfloat16, device=codes.device)
+    _check(load_library().trellis_expand_bf16(_ptr(codes), _ptr(scales), _ptr(out), R, C, k, L, T,
+                                              _stream(codes.device)))
+    return out
+
+
+def prefill(codes, scales, x, k, L=12, T=256, algo=PREFILL_FUSED, out=None, workspace=None):
+    """bf16 [M, R] = x [M, C] times the bf16 expansion of the axis-1 codes."""
+    _need(codes, "codes", _CODES, 2)
+    _need(scales, "scales", (torch.float16,), 1)
+    _need(x, "x", (torch.bfloat16,), 2)
+    R, C = _geometry(codes, k)
+    M = x.shape[0]
+    if x.shape[1] != C:
+        raise ValueError(f"x has {x.shape[1]} features, codes encode {C}")
+    if out is None:
+        out = torch.empty((M, R), dtype=torch.bfloat16, device=x.device)
+    lib = load_library()
+    ws, wsb = _workspace(lib.trellis_prefill_workspace_bytes(R, C, M, k, L, T, algo), x.device,
+                         workspace)
+    _check(lib.trellis_prefill(_ptr(codes), _ptr(scales), _ptr(x), _ptr(out), R, C, M, k, L, T, algo,
+                               _ptr(ws), wsb, _stream(x.device)))
+    return out
+
+
+def prefill_workspace_bytes(R, C, M, k, algo, L=12, T=256) -> int:
+    return int(load_library().trellis_prefill_workspace_bytes(R, C, M, k, L, T, algo))
+
+
+def decode_states(codes, k, L=12, T=256):
+    """(states int16-bits [R, C], y int16 [R, C], value f32 [R, C]) from the GPU decoder."""
+    _need(codes, "codes", _CODES, 2)
+    R, C = _geometry(codes, k)
+    dev = codes.device
+    st = torch.empty((R, C), dtype=torch.int16, device=dev)
+    ys = torch.empty((R, C), dtype=torch.int16, device=dev)
+    vals = torch.empty((R, C), dtype=torch.float32, device=dev)
+    _check(load_library().trellis_decode_states(_ptr(codes), R, C, k, L, T, _ptr(st), _ptr(ys),
+                                                _ptr(vals), _stream(dev)))
+    return st, ys, vals

@@ -1,0 +1,284 @@
+// api.hip -- the C ABI (include/trellis.h): host-side validation, workspace
+// sizing and dispatch onto the caller's stream.  Validation mirrors the
+// pages' geometry checks before any launch (mlx-bun 0.2.0 -> 0.4.0 diff,
+// page 55, trellis-linear.ts trellisGeometry and fusedGateUpEligible; page 56,
+// the prefill eligibility predicates): nothing is launched or written unless
+// every check passes.
+#include <hipblaslt/hipblaslt.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <map>
+#include <mutex>
+#include <tuple>
+
+#include "../../include/trellis.h"
+#include "internal.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return TRELLIS_OK;
+}
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;      // R, C, M each below 2^31
+constexpr int64_t kMaxElems = (int64_t)1 << 40;    // R * C, M * C, M * R
+
+int check_geometry(const char* fn, int64_t R, int64_t C, int k, int L, int T) {
+  if (k != 2 && k != 3 && k != 4) return fail(TRELLIS_EUNSUPPORTED, "%s: k=%d not in {2,3,4}", fn, k);
+  if (L != 12) return fail(TRELLIS_EUNSUPPORTED, "%s: L=%d unsupported (L must be 12)", fn, L);
+  if (T != 256) return fail(TRELLIS_EUNSUPPORTED, "%s: T=%d unsupported (T must be 256)", fn, T);
+  if (R < 1 || C < 1) return fail(TRELLIS_EINVAL, "%s: empty matrix R=%lld C=%lld", fn, (long long)R, (long long)C);
+  if (R >= kMaxDim || C >= kMaxDim || R * C >= kMaxElems)
+    return fail(TRELLIS_EINVAL, "%s: matrix %lld x %lld too large", fn, (long long)R, (long long)C);
+  if (C % T != 0)
+    return fail(TRELLIS_EINVAL, "%s: C=%lld coded columns not a multiple of the block T=%d", fn, (long long)C, T);
+  return TRELLIS_OK;
+}
+
+int check_ptr(const char* fn, const char* name, const void* p, size_t align) {
+  if (!p) return fail(TRELLIS_EINVAL, "%s: %s is NULL", fn, name);
+  if (reinterpret_cast<uintptr_t>(p) % align != 0)
+    return fail(TRELLIS_EINVAL, "%s: %s not %zu-byte aligned", fn, name, align);
+  return TRELLIS_OK;
+}
+
+int check_m(const char* fn, int64_t M, int64_t maxM) {
+  if (M < 1 || M > maxM) return fail(TRELLIS_EINVAL, "%s: M=%lld outside 1..%lld", fn, (long long)M, (long long)maxM);
+  return TRELLIS_OK;
+}
+
+int check_workspace(const char* fn, const void* ws, size_t have, size_t need) {
+  if (need == 0) return TRELLIS_OK;
+  if (have < need) return fail(TRELLIS_EWORKSPACE, "%s: workspace %zu bytes < required %zu", fn, have, need);
+  return check_ptr(fn, "workspace", ws, 256);
+}
+
+int hip_status(const char* fn, hipError_t e) {
+  if (e == hipSuccess) return ok();
+  return fail(TRELLIS_EHIP, "%s: HIP error %d (%s)", fn, (int)e, hipGetErrorString(e));
+}
+
+#define TRY(expr)            \
+  do {                       \
+    int _rc = (expr);        \
+    if (_rc != TRELLIS_OK) return _rc; \
+  } while (0)
+
+// ---- bf16 GEMM of the expand-then-GEMM prefill (hipBLASLt) --------------
+
+constexpr size_t kGemmWorkspace = (size_t)64 << 20;
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+struct GemmPlan {
+  hipblasLtMatmulDesc_t desc = nullptr;
+  hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, lc = nullptr;
+  hipblasLtMatmulAlgo_t algo;
+};
+
+std::mutex g_lt_mu;
+std::map<int, hipblasLtHandle_t> g_lt_handles;
+std::map<std::tuple<int, int64_t, int64_t, int64_t>, GemmPlan> g_lt_plans;
+
+// out[M, R] (row-major) = x[M, C] * W[R, C]^T.  Column-major view:
+// D (R x M, ld R) = op_T(A: C x R, ld C) * op_N(B: C x M, ld C).
+int gemm_bf16_nt(const char* fn, const uint16_t* W, const uint16_t* x, uint16_t* out, int64_t R,
+                 int64_t C, int64_t M, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int dev = 0;
+  hipError_t he = hipGetDevice(&dev);
+  if (he != hipSuccess) return hip_status(fn, he);
+  std::lock_guard<std::mutex> lock(g_lt_mu);
+  auto hit = g_lt_handles.find(dev);
+  if (hit == g_lt_handles.end()) {
+    hipblasLtHandle_t h = nullptr;
+    if (hipblasLtCreate(&h) != HIPBLAS_STATUS_SUCCESS) return fail(TRELLIS_EHIP, "%s: hipblasLtCreate failed", fn);
+    hit = g_lt_handles.emplace(dev, h).first;
+  }
+  hipblasLtHandle_t h = hit->second;
+  auto key = std::make_tuple(dev, R, C, M);
+  auto pit = g_lt_plans.find(key);
+  if (pit == g_lt_plans.end()) {
+    GemmPlan p;
+    hipblasOperation_t ta = HIPBLAS_OP_T, tb = HIPBLAS_OP_N;
+    uint64_t wsb = kGemmWorkspace;
+    hipblasLtMatmulPreference_t pref = nullptr;
+    hipblasLtMatmulHeuristicResult_t heur[1];
+    int returned = 0;
+    bool good = hipblasLtMatmulDescCreate(&p.desc, HIPBLAS_COMPUTE_32F, HIP_R_32F) == HIPBLAS_STATUS_SUCCESS &&
+                hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSA, &ta, sizeof(ta)) == HIPBLAS_STATUS_SUCCESS &&
+                hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSB, &tb, sizeof(tb)) == HIPBLAS_STATUS_SUCCESS &&
+                hipblasLtMatrixLayoutCreate(&p.la, HIP_R_16BF, (uint64_t)C, (uint64_t)R, C) == HIPBLAS_STATUS_SUCCESS &&
+                hipblasLtMatrixLayoutCreate(&p.lb, HIP_R_16BF, (uint64_t)C, (uint64_t)M, C) == HIPBLAS_STATUS_SUCCESS &&
+                hipblasLtMatrixLayoutCreate(&p.lc, HIP_R_16BF, (uint64_t)R, (uint64_t)M, R) == HIPBLAS_STATUS_SUCCESS &&
+                hipblasLtMatmulPreferenceCreate(&pref) == HIPBLAS_STATUS_SUCCESS &&
+                hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &wsb, sizeof(wsb)) == HIPBLAS_STATUS_SUCCESS &&
+                hipblasLtMatmulAlgoGetHeuristic(h, p.desc, p.la, p.lb, p.lc, p.lc, pref, 1, heur, &returned) == HIPBLAS_STATUS_SUCCESS &&
+                returned > 0;
+    if (pref) hipblasLtMatmulPreferenceDestroy(pref);
+    if (!good) {
+      if (p.la) hipblasLtMatrixLayoutDestroy(p.la);
+      if (p.lb) hipblasLtMatrixLayoutDestroy(p.lb);
+      if (p.lc) hipblasLtMatrixLayoutDestroy(p.lc);
+      if (p.desc) hipblasLtMatmulDescDestroy(p.desc);
+      return fail(TRELLIS_EHIP, "%s: no hipBLASLt bf16 GEMM for %lld x %lld x %lld", fn, (long long)M,
+                  (long long)R, (long long)C);
+    }
+    p.algo = heur[0].algo;
+    pit = g_lt_plans.emplace(key, p).first;
+  }
+  const float alpha = 1.0f, beta = 0.0f;
+  const GemmPlan& p = pit->second;
+  hipblasStatus_t st = hipblasLtMatmul(h, p.desc, &alpha, W, p.la, x, p.lb, &beta, out, p.lc, out,
+                                       p.lc, &p.algo, ws, ws_bytes, stream);
+  if (st != HIPBLAS_STATUS_SUCCESS) return fail(TRELLIS_EHIP, "%s: hipblasLtMatmul status %d", fn, (int)st);
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* trellis_last_error(void) { return g_err; }
+
+const char* trellis_version(void) { return "trellis-mi355x 0.1.0 (gfx950)"; }
+
+size_t trellis_matvec_axis1_workspace_bytes(int64_t R, int64_t C, int M, int k, int L, int T) {
+  if (check_geometry("trellis_matvec_axis1_workspace_bytes", R, C, k, L, T) != TRELLIS_OK) return 0;
+  return trellis::axis1_workspace_bytes(R, C, M, k);
+}
+
+int trellis_matvec_axis1(const uint32_t* codes, const uint16_t* scales, const uint16_t* x,
+                         void* out, int out_dtype, int64_t R, int64_t C, int M, int k, int L,
+                         int T, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "trellis_matvec_axis1";
+  TRY(check_geometry(fn, R, C, k, L, T));
+  TRY(check_m(fn, M, TRELLIS_MATVEC_MAX_M));
+  if (out_dtype != TRELLIS_OUT_BF16 && out_dtype != TRELLIS_OUT_F32)
+    return fail(TRELLIS_EINVAL, "%s: out_dtype=%d unknown", fn, out_dtype);
+  TRY(check_ptr(fn, "codes", codes, 16));
+  TRY(check_ptr(fn, "scales", scales, 2));
+  TRY(check_ptr(fn, "x", x, 16));
+  TRY(check_ptr(fn, "out", out, 16));
+  TRY(check_workspace(fn, workspace, workspace_bytes, trellis::axis1_workspace_bytes(R, C, M, k)));
+  return hip_status(fn, trellis::launch_axis1(codes, scales, nullptr, nullptr, x, out,
+                                              out_dtype == TRELLIS_OUT_F32, nullptr, nullptr, R, C,
+                                              M, k, workspace, (hipStream_t)stream));
+}
+
+size_t trellis_gateup_swiglu_workspace_bytes(int64_t R, int64_t C, int M, int k, int L, int T) {
+  if (check_geometry("trellis_gateup_swiglu_workspace_bytes", R, C, k, L, T) != TRELLIS_OK) return 0;
+  return trellis::axis1_workspace_bytes(R, C, M, k);
+}
+
+int trellis_gateup_swiglu(const uint32_t* gcodes, const uint16_t* gscales, const uint32_t* ucodes,
+                          const uint16_t* uscales, const uint16_t* x, uint16_t* out,
+                          float* gate_f32, float* up_f32, int64_t R, int64_t C, int M, int k,
+                          int L, int T, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "trellis_gateup_swiglu";
+  TRY(check_geometry(fn, R, C, k, L, T));
+  TRY(check_m(fn, M, TRELLIS_MATVEC_MAX_M));
+  TRY(check_ptr(fn, "gcodes", gcodes, 16));
+  TRY(check_ptr(fn, "gscales", gscales, 2));
+  TRY(check_ptr(fn, "ucodes", ucodes, 16));
+  TRY(check_ptr(fn, "uscales", uscales, 2));
+  TRY(check_ptr(fn, "x", x, 16));
+  TRY(check_ptr(fn, "out", out, 16));
+  if (gate_f32) TRY(check_ptr(fn, "gate_f32", gate_f32, 4));
+  if (up_f32) TRY(check_ptr(fn, "up_f32", up_f32, 4));
+  TRY(check_workspace(fn, workspace, workspace_bytes, trellis::axis1_workspace_bytes(R, C, M, k)));
+  return hip_status(fn, trellis::launch_axis1(gcodes, gscales, ucodes, uscales, x, out, 0, gate_f32,
+                                              up_f32, R, C, M, k, workspace, (hipStream_t)stream));
+}
+
+size_t trellis_matvec_axis0_workspace_bytes(int64_t R_in, int64_t C_out, int M, int k, int L, int T) {
+  if (check_geometry("trellis_matvec_axis0_workspace_bytes", R_in, C_out, k, L, T) != TRELLIS_OK) return 0;
+  if (M < 1 || M > TRELLIS_MATVEC_MAX_M) return 0;
+  return trellis::axis0_workspace_bytes(R_in, C_out, M, k);
+}
+
+int trellis_matvec_axis0(const uint32_t* codes, const uint16_t* scales, const uint16_t* x,
+                         void* out, int out_dtype, int64_t R_in, int64_t C_out, int M, int k,
+                         int L, int T, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "trellis_matvec_axis0";
+  TRY(check_geometry(fn, R_in, C_out, k, L, T));
+  TRY(check_m(fn, M, TRELLIS_MATVEC_MAX_M));
+  if (out_dtype != TRELLIS_OUT_BF16 && out_dtype != TRELLIS_OUT_F32)
+    return fail(TRELLIS_EINVAL, "%s: out_dtype=%d unknown", fn, out_dtype);
+  TRY(check_ptr(fn, "codes", codes, 16));
+  TRY(check_ptr(fn, "scales", scales, 2));
+  TRY(check_ptr(fn, "x", x, 16));
+  TRY(check_ptr(fn, "out", out, 16));
+  TRY(check_workspace(fn, workspace, workspace_bytes, trellis::axis0_workspace_bytes(R_in, C_out, M, k)));
+  return hip_status(fn, trellis::launch_axis0(codes, scales, x, out, out_dtype == TRELLIS_OUT_F32,
+                                              R_in, C_out, M, k, workspace, (hipStream_t)stream));
+}
+
+int trellis_expand_bf16(const uint32_t* codes, const uint16_t* scales, uint16_t* out, int64_t R,
+                        int64_t C, int k, int L, int T, void* stream) {
+  const char* fn = "trellis_expand_bf16";
+  TRY(check_geometry(fn, R, C, k, L, T));
+  TRY(check_ptr(fn, "codes", codes, 16));
+  TRY(check_ptr(fn, "scales", scales, 2));
+  TRY(check_ptr(fn, "out", out, 16));
+  return hip_status(fn, trellis::launch_expand(codes, scales, out, R, C, k, (hipStream_t)stream));
+}
+
+size_t trellis_prefill_workspace_bytes(int64_t R, int64_t C, int64_t M, int k, int L, int T,
+                                       int algo) {
+  if (check_geometry("trellis_prefill_workspace_bytes", R, C, k, L, T) != TRELLIS_OK) return 0;
+  (void)M;
+  if (algo == TRELLIS_PREFILL_EXPAND_GEMM) return align_up((size_t)R * (size_t)C * 2, 256) + kGemmWorkspace;
+  return 0;
+}
+
+int trellis_prefill(const uint32_t* codes, const uint16_t* scales, const uint16_t* x,
+                    uint16_t* out, int64_t R, int64_t C, int64_t M, int k, int L, int T, int algo,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "trellis_prefill";
+  TRY(check_geometry(fn, R, C, k, L, T));
+  TRY(check_m(fn, M, kMaxDim - 1));
+  if (M * C >= kMaxElems || M * R >= kMaxElems)
+    return fail(TRELLIS_EINVAL, "%s: M=%lld too large", fn, (long long)M);
+  if (M > (int64_t)65535 * 128) return fail(TRELLIS_EINVAL, "%s: M=%lld too large", fn, (long long)M);
+  if (algo != TRELLIS_PREFILL_FUSED && algo != TRELLIS_PREFILL_EXPAND_GEMM)
+    return fail(TRELLIS_EINVAL, "%s: algo=%d unknown", fn, algo);
+  TRY(check_ptr(fn, "codes", codes, 16));
+  TRY(check_ptr(fn, "scales", scales, 2));
+  TRY(check_ptr(fn, "x", x, 16));
+  TRY(check_ptr(fn, "out", out, 16));
+  const size_t need = trellis_prefill_workspace_bytes(R, C, M, k, L, T, algo);
+  TRY(check_workspace(fn, workspace, workspace_bytes, need));
+  hipStream_t s = (hipStream_t)stream;
+  if (algo == TRELLIS_PREFILL_FUSED)
+    return hip_status(fn, trellis::launch_prefill_fused(codes, scales, x, out, R, C, M, k, s));
+  uint16_t* wexp = reinterpret_cast<uint16_t*>(workspace);
+  const size_t wexp_bytes = align_up((size_t)R * (size_t)C * 2, 256);
+  TRY(hip_status(fn, trellis::launch_expand(codes, scales, wexp, R, C, k, s)));
+  return gemm_bf16_nt(fn, wexp, x, out, R, C, M, reinterpret_cast<char*>(workspace) + wexp_bytes,
+                      workspace_bytes - wexp_bytes, s);
+}
+
+int trellis_decode_states(const uint32_t* codes, int64_t R, int64_t C, int k, int L, int T,
+                          uint16_t* states, int16_t* y, float* value, void* stream) {
+  const char* fn = "trellis_decode_states";
+  TRY(check_geometry(fn, R, C, k, L, T));
+  TRY(check_ptr(fn, "codes", codes, 16));
+  if (states) TRY(check_ptr(fn, "states", states, 2));
+  if (y) TRY(check_ptr(fn, "y", y, 2));
+  if (value) TRY(check_ptr(fn, "value", value, 4));
+  return hip_status(fn, trellis::launch_decode_states(codes, R, C, k, states, y, value, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,36 @@
+// internal.hpp -- host-side launchers shared between the C-ABI layer
+// (api.hip) and the kernel translation units.  Every launcher assumes the
+// caller already validated geometry, pointers and workspace size.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace trellis {
+
+// axis 1 (gate/up when codes1 != nullptr)
+size_t axis1_workspace_bytes(int64_t R, int64_t C, int M, int k);
+hipError_t launch_axis1(const uint32_t* codes0, const uint16_t* scales0, const uint32_t* codes1,
+                        const uint16_t* scales1, const uint16_t* x, void* out, int out_f32,
+                        float* gate_f32, float* up_f32, int64_t R, int64_t C, int M, int k,
+                        void* workspace, hipStream_t stream);
+
+// axis 0
+size_t axis0_workspace_bytes(int64_t R, int64_t C, int M, int k);
+hipError_t launch_axis0(const uint32_t* codes, const uint16_t* scales, const uint16_t* x,
+                        void* out, int out_f32, int64_t R, int64_t C, int M, int k,
+                        void* workspace, hipStream_t stream);
+
+// expansion and decode export
+hipError_t launch_expand(const uint32_t* codes, const uint16_t* scales, uint16_t* out, int64_t R,
+                         int64_t C, int k, hipStream_t stream);
+hipError_t launch_decode_states(const uint32_t* codes, int64_t R, int64_t C, int k,
+                                uint16_t* states, int16_t* y, float* value, hipStream_t stream);
+
+// fused prefill
+hipError_t launch_prefill_fused(const uint32_t* codes, const uint16_t* scales, const uint16_t* x,
+                                uint16_t* out, int64_t R, int64_t C, int64_t M, int k,
+                                hipStream_t stream);
+
+}  // namespace trellis
