@@ -200,7 +200,101 @@ def workload_prefill(args, np, torch, dev):
     return step, cpu_baseline, report
 
 
-WORKLOADS = {"gateup": workload_gateup, "prefill": workload_prefill}
+def _matvec_workload(w, Ms, args, np, torch, dev, label):
+    """Chain of matvec calls (axis 0 or 1) per step, codes rotated over
+    >= 1 GiB of replicas; dominant kernel = the whole call."""
+    import oracle
+    import trellis_coded_quantized_amd as tq
+
+    codes, half, bf16 = _dev_tensors(np, torch, dev)
+    code_bytes = sum(m.codes.nbytes for m in w.mats)
+    nrep = max(1, math.ceil(ROTATE_BYTES / code_bytes))
+    reps = [[codes(m.codes) for m in w.mats]]
+    for _ in range(nrep - 1):
+        reps.append([c.clone() for c in reps[0]])
+    scs = [half(m.scales) for m in w.mats]
+    xs = [bf16(x) for x in w.x]
+    outs = {}
+    wss = []
+    for i, m in enumerate(w.mats):
+        n_out = m.R if m.axis == 1 else m.C
+        for M in Ms:
+            outs[(i, M)] = torch.empty((M, n_out), dtype=torch.bfloat16, device=dev)
+        if m.axis == 0:
+            nb = tq.load_library().trellis_matvec_axis0_workspace_bytes(m.R, m.C, max(Ms), m.k, L, T)
+        else:
+            nb = tq.load_library().trellis_matvec_axis1_workspace_bytes(m.R, m.C, max(Ms), m.k, L, T)
+        wss.append(torch.empty(max(nb, 256), dtype=torch.uint8, device=dev))
+    state = {"i": 0}
+    timer = EventTimer(torch)
+
+    def call(M):
+        rep = reps[state["i"] % nrep]
+        state["i"] += 1
+        for i, m in enumerate(w.mats):
+            fn = tq.matvec_axis1 if m.axis == 1 else tq.matvec_axis0
+            fn(rep[i], scs[i], xs[i][:M], m.k, out=outs[(i, M)], workspace=wss[i])
+
+    def step(timed):
+        for M in Ms:
+            if timed:
+                timer(lambda: call(M))
+            else:
+                call(M)
+
+    def cpu_baseline():
+        m, x = w.mats[0], w.x[0]
+        ref = oracle.matvec_axis1 if m.axis == 1 else oracle.matvec_axis0
+        n_all = m.R if m.axis == 1 else m.C
+        def run(n):
+            t0 = time.perf_counter()
+            sel = np.arange(n)
+            if m.axis == 1:
+                ref(m.codes, m.scales, x, max(Ms), m.R, m.C, m.k, L, T, rows=sel)
+            else:
+                ref(m.codes, m.scales, x, max(Ms), m.R, m.C, m.k, L, T, cols=sel)
+            return time.perf_counter() - t0
+        dt = run(16)
+        n = int(min(n_all, max(16, 16 * args.cpu_seconds / max(dt, 1e-6))))
+        dt = run(n)
+        nbytes = m.codes.nbytes * n // n_all
+        return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+                "sample": f"{n} of {n_all} outputs of the first matrix at M={max(Ms)}, {dt:.2f} s"}
+
+    def report(ms_step):
+        launch_ms = timer.mean_ms()
+        achieved = code_bytes / (launch_ms * 1e-3) / 1e9
+        return {
+            "value": len(Ms) * code_bytes / (ms_step * 1e-3) / 1e9, "unit": "GB/s", "dtype": "f32",
+            "config": {"workload": w.name, "M": list(Ms), "k": w.mats[0].k, "L": L, "T": T,
+                       "matrices": [f"axis{m.axis} {m.R}x{m.C}" for m in w.mats],
+                       "code_bytes_per_call": code_bytes, "replicas": nrep},
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": label,
+                         "mean_launch_us": launch_ms * 1e3},
+        }
+
+    return step, cpu_baseline, report
+
+
+def workload_axis0(args, np, torch, dev):
+    import trellis_inputs as ti
+    Ms = (args.m,) if args.m else (1, 2, 3, 4)
+    return _matvec_workload(ti.axis0(), Ms, args, np, torch, dev, "axis0 scatter + fold")
+
+
+def workload_layer_chain(args, np, torch, dev):
+    import trellis_inputs as ti
+    return _matvec_workload(ti.layer_chain(), (4,), args, np, torch, dev, "4-matrix chain")
+
+
+def workload_axis1_m1(args, np, torch, dev):
+    import trellis_inputs as ti
+    return _matvec_workload(ti.axis1_m1(), (1,), args, np, torch, dev, "axis1 reduce")
+
+
+WORKLOADS = {"gateup": workload_gateup, "prefill": workload_prefill, "axis0": workload_axis0,
+             "layer_chain": workload_layer_chain, "axis1_m1": workload_axis1_m1}
 
 
 def main():
