@@ -293,7 +293,38 @@ def workload_axis1_m1(args, np, torch, dev):
     return _matvec_workload(ti.axis1_m1(), (1,), args, np, torch, dev, "axis1 reduce")
 
 
-WORKLOADS = {"gateup": workload_gateup, "prefill": workload_prefill, "axis0": workload_axis0,
+def workload_copy(args, np, torch, dev):
+    """Plain device-to-device copy of 1 GiB: the HBM reference point, and the
+    known-size kernel that calibrates the FETCH_SIZE / WRITE_SIZE counters."""
+    nbytes = ROTATE_BYTES
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    timer = EventTimer(torch)
+
+    def step(timed):
+        if timed:
+            timer(lambda: dst.copy_(src))
+        else:
+            dst.copy_(src)
+
+    def cpu_baseline():
+        return None
+
+    def report(ms_step):
+        launch_ms = timer.mean_ms()
+        achieved = 2 * nbytes / (launch_ms * 1e-3) / 1e9
+        return {
+            "value": 2 * nbytes / (ms_step * 1e-3) / 1e9, "unit": "GB/s", "dtype": "u8",
+            "config": {"workload": "device copy", "bytes_read": nbytes, "bytes_written": nbytes},
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "copy",
+                         "mean_launch_us": launch_ms * 1e3},
+        }
+
+    return step, cpu_baseline, report
+
+
+WORKLOADS = {"copy": workload_copy, "gateup": workload_gateup, "prefill": workload_prefill, "axis0": workload_axis0,
              "layer_chain": workload_layer_chain, "axis1_m1": workload_axis1_m1}
 
 

@@ -65,11 +65,12 @@ int check_workspace(const char* fn, const void* ws, size_t have, size_t need) {
   return check_ptr(fn, "workspace", ws, 256);
 }
 
-// The axis-1 kernels stage an f16 copy of x ([M, C]) and two 16-row code
-// tiles in LDS.
-int check_axis1_lds(const char* fn, int64_t C, int M, int k) {
-  if (trellis::axis1_lds_bytes(C, M, k) > trellis::kAxis1MaxLdsBytes)
-    return fail(TRELLIS_EUNSUPPORTED, "%s: C=%lld (M=%d, k=%d) exceeds the LDS staging limit", fn, (long long)C, M, k);
+// The axis-1 kernel keeps x in registers (C <= 5120) and a ring of 16-row
+// code tiles in LDS; wider rows are not supported.
+int check_axis1_shape(const char* fn, int64_t R, int64_t C, int M, int k, bool gateup) {
+  if (!trellis::axis1_supported(R, C, M, k, gateup))
+    return fail(TRELLIS_EUNSUPPORTED, "%s: C=%lld (M=%d, k=%d) exceeds the register / LDS staging limit (C <= 5120)",
+                fn, (long long)C, M, k);
   return TRELLIS_OK;
 }
 
@@ -180,7 +181,7 @@ int trellis_matvec_axis1(const uint32_t* codes, const uint16_t* scales, const ui
   TRY(check_ptr(fn, "x", x, 16));
   TRY(check_ptr(fn, "out", out, 16));
   TRY(check_workspace(fn, workspace, workspace_bytes, trellis::axis1_workspace_bytes(R, C, M, k)));
-  TRY(check_axis1_lds(fn, C, M, k));
+  TRY(check_axis1_shape(fn, R, C, M, k, false));
   return hip_status(fn, trellis::launch_axis1(codes, scales, nullptr, nullptr, x, out,
                                               out_dtype == TRELLIS_OUT_F32, nullptr, nullptr, R, C,
                                               M, k, workspace, (hipStream_t)stream));
@@ -207,7 +208,7 @@ int trellis_gateup_swiglu(const uint32_t* gcodes, const uint16_t* gscales, const
   if (gate_f32) TRY(check_ptr(fn, "gate_f32", gate_f32, 4));
   if (up_f32) TRY(check_ptr(fn, "up_f32", up_f32, 4));
   TRY(check_workspace(fn, workspace, workspace_bytes, trellis::axis1_workspace_bytes(R, C, M, k)));
-  TRY(check_axis1_lds(fn, C, M, k));
+  TRY(check_axis1_shape(fn, R, C, M, k, true));
   return hip_status(fn, trellis::launch_axis1(gcodes, gscales, ucodes, uscales, x, out, 0, gate_f32,
                                               up_f32, R, C, M, k, workspace, (hipStream_t)stream));
 }

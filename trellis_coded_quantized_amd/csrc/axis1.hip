@@ -6,29 +6,30 @@
 // chain in the epilogue); page 56, trellis-shared-m.ts (decode once, reuse
 // for every vector).
 //
-// The sum is refactored as y = (scale / d) * sum_c code(r, c) * x[m, c] so
-// the inner product runs on v_mfma_f32_16x16x32_f16 with exact operands:
-//   A (16 rows x 32 k): the integer code y = bytesum(1MAD word) - 510, exact
-//     in f16; built two at a time from the byte sums (v_sad_u8 straight into
-//     f16 bits, one packed subtract).
+// The sum is refactored so the inner product runs on v_mfma_f32_16x16x32_f16
+// with exact operands:
+//   A (16 rows x 32 k): the byte sum b = y + 510 of each 1MAD word, taken as
+//     an f16 subnormal bit pattern (value b * 2^-24, exact for b <= 1023);
+//     v_sad_hi_u8 / v_sad_u8 write two of them into one register directly.
 //   B (32 k x 16 n): x'[n, c] = f16(x[n, c] * 2^e_n), e_n chosen per vector so
 //     the largest |x| lands in [2^14, 2^15); every bf16 value down to 2^-17 of
 //     that maximum is exact in f16.
-//   D: f32 accumulators; the epilogue applies scale/d and 2^-e_n.
+//   D: f32.  sum_c y x' = 2^24 D - 510 S_n with S_n = sum_c x'[n, c], so the
+//     epilogue forms (D - 510 S_n 2^-24) * scale / d * 2^(24 - e_n).
 //
-// Persistent schedule: one workgroup of 8 waves per CU.
-//  1. The workgroup finds e_n and stages x' for all vectors and columns in
-//     LDS (no separate pass over x, no workspace).
-//  2. It streams row groups b, b + grid, ... (16 A-rows each: 16 output rows,
-//     or 8 gate + 8 up rows sharing B).  The 8 waves split a row group's runs
-//     of 32 columns; each lane decodes one whole run per step: k words plus
-//     the next one up (wrapping to word 0 at the block end) hold every window
-//     of the run, and k extra funnel shifts make every window a single
-//     v_bfe_u32 at a constant offset.  Code words ride a 4-deep register ring
-//     that runs across row-group boundaries, so the HBM stream never drains;
-//     B comes from LDS.  Partial D tiles meet in LDS (double buffered, one
-//     barrier per row group) and one wave, rotating with the row group,
-//     applies scale / d, 2^-e and the epilogue.
+// Persistent schedule: one workgroup of 8 waves per CU, row groups
+// b, b + grid, ... (16 A-rows each: 16 output rows, or 8 gate + 8 up rows
+// sharing B).  Each wave owns a fixed slice of the columns, so its B operand
+// lives in registers for the whole kernel.  Code tiles of 16 packed rows
+// stream HBM -> LDS with global_load_lds_dwordx4 into a ring of N slots (one
+// 16-byte pad granule per row spreads the LDS banks).  Every vector-memory
+// operation of the steady state is such a copy, waited for with explicit
+// vmcnt counts, so the ring keeps N - 1 tiles in flight: scales come through
+// the scalar cache, x is staged by the same copy engine, and finished rows
+// wait in LDS until the end, so no vector-register load ever queues behind
+// the ring.  Per row group: decode + MFMA, partial D tiles to LDS, one
+// barrier, refill of the freed slot, and one wave (rotating) reduces the
+// eight partial tiles.
 #include "internal.hpp"
 #include "mfma_common.hpp"
 
@@ -36,44 +37,82 @@ namespace trellis {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(4))) const u32x4 ConstV4;   // read through the scalar cache
 
-constexpr int kPWaves = 8;                     // waves per workgroup (two per SIMD)
-constexpr int kXPad = 16;                      // f16 elements of row padding (spreads LDS banks)
-constexpr int kXRegs = 5;                      // 16-byte pieces of x held per thread while staging (M*C <= 20480 in one pass)
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kMaxSlots = 3;           // two tiles in flight: deeper rings only queue copies that stall the issuing wave
+constexpr int kMaxDma = 6;           // tile copies per wave per tile (C <= 5120, k <= 4: 41 per tile)
+constexpr uint32_t kRedBytes = 2 * kWaves * 4 * 16 * 4;   // f32 [2][wave][n][16 rows]
 
-// Dynamic LDS layout of the persistent kernel.
-struct Axis1Lds {
-  int64_t ldx;          // padded x' row (elements)
-  size_t tile_off;      // two code tiles of 16 rows, row stride rs bytes
-  size_t rs;            // padded tile row (bytes): a row's packed words + 16 B
-  size_t tile_bytes;
-  size_t red_off;       // f32x4 [2][kPWaves][64] partial sums (double buffered)
-  size_t exp_off;       // int [4] exponents, then uint32 [kPWaves][4] max staging
-  size_t total;
+// Geometry shared by the host (LDS sizing) and the kernel.
+struct Axis1Geom {
+  int64_t R, C, nrg, row_bytes;
+  int M, G, gs, ipt, nslots, xslots, nmine_max, scales_aligned;
+  uint32_t gs_magic;    // ceil(2^24 / gs): p / gs == (p * gs_magic) >> 24 for p < 4096
+  uint32_t tile_bytes, red_off, obuf_off, total;
 };
 
-__host__ __device__ inline Axis1Lds axis1_lds(int64_t C, int M, int k) {
-  Axis1Lds l;
-  l.ldx = C + kXPad;
-  // x' f16 [M][ldx] followed by 64 zero bytes (B operand of ragged runs)
-  l.tile_off = ((size_t)M * (size_t)l.ldx * 2 + 64 + 255) / 256 * 256;
-  l.rs = (size_t)C * k / 8 + 16;
-  l.tile_bytes = (16 * l.rs + 255) / 256 * 256;
-  l.red_off = l.tile_off + 2 * l.tile_bytes;
-  l.exp_off = l.red_off + 2 * kPWaves * 64 * sizeof(f32x4);
-  l.total = l.exp_off + 4 * sizeof(int) + kPWaves * 4 * sizeof(uint32_t);
-  return l;
+// s_waitcnt vmcnt(n) with expcnt / lgkmcnt left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void waitcnt_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-__device__ __forceinline__ half8 load_half8(const uint16_t* p) {
+__device__ __forceinline__ void wait_vmcnt(int n) {   // n is wave-uniform
+  switch (n) {
+#define TRELLIS_VM(N) \
+  case N: waitcnt_vm<N>(); break;
+    TRELLIS_VM(0) TRELLIS_VM(1) TRELLIS_VM(2) TRELLIS_VM(3) TRELLIS_VM(4) TRELLIS_VM(5) TRELLIS_VM(6)
+    TRELLIS_VM(7) TRELLIS_VM(8) TRELLIS_VM(9) TRELLIS_VM(10) TRELLIS_VM(11) TRELLIS_VM(12) TRELLIS_VM(13)
+    TRELLIS_VM(14) TRELLIS_VM(15) TRELLIS_VM(16) TRELLIS_VM(17) TRELLIS_VM(18) TRELLIS_VM(19) TRELLIS_VM(20)
+    TRELLIS_VM(21) TRELLIS_VM(22) TRELLIS_VM(23) TRELLIS_VM(24) TRELLIS_VM(25) TRELLIS_VM(26) TRELLIS_VM(27)
+    TRELLIS_VM(28) TRELLIS_VM(29) TRELLIS_VM(30) TRELLIS_VM(31) TRELLIS_VM(32) TRELLIS_VM(33) TRELLIS_VM(34)
+    TRELLIS_VM(35) TRELLIS_VM(36) TRELLIS_VM(37) TRELLIS_VM(38) TRELLIS_VM(39) TRELLIS_VM(40) TRELLIS_VM(41)
+    TRELLIS_VM(42) TRELLIS_VM(43) TRELLIS_VM(44) TRELLIS_VM(45) TRELLIS_VM(46) TRELLIS_VM(47) TRELLIS_VM(48)
+    TRELLIS_VM(49) TRELLIS_VM(50) TRELLIS_VM(51) TRELLIS_VM(52) TRELLIS_VM(53) TRELLIS_VM(54) TRELLIS_VM(55)
+    TRELLIS_VM(56) TRELLIS_VM(57) TRELLIS_VM(58) TRELLIS_VM(59) TRELLIS_VM(60) TRELLIS_VM(61) TRELLIS_VM(62)
+#undef TRELLIS_VM
+    default: break;                  // the counter holds at most 63: always satisfied
+  }
+}
+
+// Workgroup barrier that orders LDS only: it does not wait for the copies in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Largest value over the wave (non-negative inputs), through DPP row shifts
+// and row broadcasts: prefix maxima within each row of 16, then across rows.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false));   // row_shr:1
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false));   // row_shr:2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false));   // row_shr:4
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false));   // row_shr:8
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));   // row_bcast:15
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));   // row_bcast:31
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+__device__ __forceinline__ half8 load_half8(const uint8_t* p) {
   return __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(p));
 }
 
-// The 32 codes of one run as four MFMA A operands of 8 exact f16 values
-// (A[u] element e = position 8u + e of the run).
+__device__ __forceinline__ uint32_t max_abs8(const uint4& v) {
+  const uint32_t u4[4] = {v.x, v.y, v.z, v.w};
+  uint32_t r = 0u;
+#pragma unroll
+  for (int h = 0; h < 4; ++h) r = max(r, max(u4[h] & 0x7FFFu, (u4[h] >> 16) & 0x7FFFu));
+  return r;
+}
+
+// The 32 codes of one run as four MFMA A operands of 8 f16 subnormals
+// (A[u] element e = byte sum of position 8u + e of the run, times 2^-24).
 template <int K>
-__device__ __forceinline__ void decode_run_f16(const uint32_t (&w)[K + 1], uint32_t mul,
-                                               uint64_t add64, uint32_t magic, u32x4 (&A)[4]) {
+__device__ __forceinline__ void decode_run_sub(const uint32_t (&w)[K + 1], uint32_t mul, uint64_t add64,
+                                               u32x4 (&A)[4]) {
   uint32_t a[2 * K];                           // a[j] holds bits 16j .. 16j+31 of the run
 #pragma unroll
   for (int m = 0; m < K; ++m) {
@@ -81,7 +120,7 @@ __device__ __forceinline__ void decode_run_f16(const uint32_t (&w)[K + 1], uint3
     a[2 * m + 1] = __builtin_amdgcn_alignbit(w[m + 1], w[m], 16);
   }
   // three phases, so no 1MAD result is consumed right after it is produced:
-  // all 32 windows, all 32 1MAD words, then the 16 f16 pairs
+  // all 32 windows, all 32 1MAD words, then the 16 byte-sum pairs
   uint32_t st[32];
 #pragma unroll
   for (int p = 0; p < 32; ++p) {
@@ -92,256 +131,302 @@ __device__ __forceinline__ void decode_run_f16(const uint32_t (&w)[K + 1], uint3
 #pragma unroll
   for (int p = 0; p < 32; ++p) xw[p] = onemad_word_mad64(st[p], mul, add64);
 #pragma unroll
-  for (int v = 0; v < 16; ++v) A[v >> 2][v & 3] = code_pair_f16(xw[2 * v], xw[2 * v + 1], magic);
+  for (int v = 0; v < 16; ++v)
+    A[v >> 2][v & 3] = __builtin_amdgcn_sad_u8(xw[2 * v], 0u, __builtin_amdgcn_sad_hi_u8(xw[2 * v + 1], 0u, 0u));
 }
 
-template <int K, int M, bool GATEUP>
-__global__ __launch_bounds__(512) void axis1_persistent_kernel(
+template <int K>
+__device__ __forceinline__ void read_words(const uint8_t* trow, int wo, int so, uint32_t (&W)[K + 1]) {
+  const uint32_t* t32 = reinterpret_cast<const uint32_t*>(trow);
+  if constexpr (K == 2) {
+    const uint2 v = *reinterpret_cast<const uint2*>(t32 + wo);
+    W[0] = v.x;
+    W[1] = v.y;
+  } else if constexpr (K == 4) {
+    const uint4 v = *reinterpret_cast<const uint4*>(t32 + wo);
+    W[0] = v.x;
+    W[1] = v.y;
+    W[2] = v.z;
+    W[3] = v.w;
+  } else {
+#pragma unroll
+    for (int m = 0; m < K; ++m) W[m] = t32[wo + m];
+  }
+  W[K] = t32[so];
+}
+
+__device__ __forceinline__ uint32_t pick4(const u32x4& v, int j) {
+  return j == 0 ? v[0] : j == 1 ? v[1] : j == 2 ? v[2] : v[3];
+}
+
+template <int K, bool GATEUP, int NG>
+__global__ __launch_bounds__(kThreads) void axis1_kernel(
     const uint32_t* __restrict__ codes0, const uint16_t* __restrict__ scales0,
     const uint32_t* __restrict__ codes1, const uint16_t* __restrict__ scales1,
     const uint16_t* __restrict__ x, void* __restrict__ out, int out_f32,
-    float* __restrict__ gate_f32, float* __restrict__ up_f32, int64_t R, int64_t C) {
+    float* __restrict__ gate_f32, float* __restrict__ up_f32, const Axis1Geom g) {
   constexpr int WPB = words_per_block(K);
-  constexpr int ROWS = GATEUP ? 8 : 16;
+  constexpr int ROWS = GATEUP ? 8 : 16;        // output rows per row group
+  constexpr int NOUT = GATEUP ? 2 : 1;         // staged values per output
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const Axis1Lds lay = axis1_lds(C, M, K);
-  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
-  uint16_t* zpad = xs + (int64_t)M * lay.ldx;                  // 32 zero elements
-  f32x4* red = reinterpret_cast<f32x4*>(smem + lay.red_off);
-  int* sexp = reinterpret_cast<int*>(smem + lay.exp_off);
-  uint32_t* smax = reinterpret_cast<uint32_t*>(sexp + 4);
-
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar) index
-  const int64_t n8 = C / 8;
-  const int64_t nrg = (R + ROWS - 1) / ROWS;
-  const int64_t nmine = (nrg > (int64_t)blockIdx.x) ? (nrg - 1 - blockIdx.x) / gridDim.x + 1 : 0;
-  const int64_t row_words = (C / kT) * WPB;
-  const int npieces = (int)(row_words / 4);      // 16-byte pieces per packed row
-  uint8_t* tiles = smem + lay.tile_off;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int M = g.M;
+  const int64_t R = g.R, C = g.C;
+  const int nslots = g.nslots;
+  const int nmine = (int)((g.nrg - 1 - (int64_t)blockIdx.x) / gridDim.x + 1);   // grid <= nrg
+  const int nw = g.ipt > wave ? (g.ipt - 1 - wave) / kWaves + 1 : 0;            // tile copies per tile
+  uint8_t* ring = smem;
+  float* red = reinterpret_cast<float*>(smem + g.red_off);
+  float* obuf = reinterpret_cast<float*>(smem + g.obuf_off);
 
-  // HBM -> LDS copy of the 16 packed rows of local row group t into tile buf:
-  // coalesced 16-byte pieces straight into LDS (global_load_lds_dwordx4);
-  // wave w copies tile rows w and w + 8.
-  auto dma_tile = [&](int64_t t, int buf) {
-    const int64_t rg = (int64_t)blockIdx.x + t * gridDim.x;
+  // ---- copy descriptors: tile granule p = 64 v + lane (v = wave + 8 j) is
+  // granule p % gs of tile row p / gs (the last granule of each row is pad).
+  // dd = active bit | tile row << 16 | byte offset of the granule in its row.
+  uint32_t dd[kMaxDma];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int rr = wave + 8 * h;
-      const int64_t row = rg * ROWS + (GATEUP ? (rr & 7) : rr);
-      const uint32_t* src = ((GATEUP && rr >= 8) ? codes1 : codes0) + (row < R ? row : 0) * row_words;
-      uint8_t* dst = tiles + (size_t)buf * lay.tile_bytes + (size_t)rr * lay.rs;
-      for (int p0 = 0; p0 < npieces; p0 += 64) {
-        if (p0 + lane < npieces)
-          __builtin_amdgcn_global_load_lds(src + (int64_t)(p0 + lane) * 4, dst + (size_t)p0 * 16, 16, 0, 0);
+  for (int j = 0; j < kMaxDma; ++j) {
+    const uint32_t p = (uint32_t)((wave + kWaves * j) * 64 + lane);
+    const uint32_t i = (uint32_t)(((uint64_t)p * g.gs_magic) >> 24), jj = p - i * (uint32_t)g.gs;
+    dd[j] = (j < nw && p < 16u * (uint32_t)g.gs && jj < (uint32_t)g.G) ? (1u << 31) | (i << 16) | (jj * 16u) : 0u;
+  }
+  const uint8_t* cb0 = reinterpret_cast<const uint8_t*>(codes0);
+  const uint8_t* cb1 = reinterpret_cast<const uint8_t*>(GATEUP ? codes1 : codes0);
+  const uint32_t row_bytes = (uint32_t)g.row_bytes;
+  auto issue_tile = [&](int t) {
+    const int64_t rg = (int64_t)blockIdx.x + (int64_t)t * gridDim.x;
+    uint8_t* slot = ring + (size_t)(t % nslots) * g.tile_bytes;
+    const bool full = rg * ROWS + ROWS <= R;   // ragged last row group: clamp rows to R - 1
+    const int64_t gbase = rg * ROWS * g.row_bytes;
+#pragma unroll
+    for (int j = 0; j < kMaxDma; ++j) {
+      if (j < nw) {                            // every issued copy has an active lane
+        const uint32_t d = dd[j];
+        if (d >> 31) {
+          const uint32_t i = (d >> 16) & 15u;
+          const uint32_t ri = GATEUP ? (i & 7u) : i;
+          const uint8_t* base = (GATEUP && i >= 8u) ? cb1 : cb0;
+          const uint8_t* src;
+          if (full) {
+            src = base + gbase + (ri * row_bytes + (d & 0xFFFFu));
+          } else {
+            int64_t row = rg * ROWS + ri;
+            row = row < R ? row : R - 1;
+            src = base + row * g.row_bytes + (d & 0xFFFFu);
+          }
+          __builtin_amdgcn_global_load_lds(src, slot + (size_t)(wave + kWaves * j) * 1024, 16, 0, 0);
+        }
       }
     }
   };
 
-  // the first two tiles stream in while x is staged
-  if (nmine > 0) dma_tile(0, 0);
-  if (nmine > 1) dma_tile(1, 1);
-
-
-  // ---- 1. per-vector exponent and the f16 copy of x in LDS.  One pass:
-  // every thread loads its (up to kXRegs) 16-byte pieces of x at once, keeps
-  // them in registers through the max reduction, then converts them.
-  {
-    const int64_t npc = (int64_t)M * n8;         // 16-byte pieces of x
-    uint4 xv[kXRegs];
-    uint32_t mx[M];
-#pragma unroll
-    for (int m = 0; m < M; ++m) mx[m] = 0u;
-#pragma unroll
-    for (int u = 0; u < kXRegs; ++u) {
-      const int64_t j = tid + (int64_t)u * 512;
-      xv[u] = (j < npc) ? reinterpret_cast<const uint4*>(x)[j] : make_uint4(0u, 0u, 0u, 0u);
-    }
-    for (int64_t j = tid + (int64_t)kXRegs * 512; j < npc; j += 512) {   // rows longer than the registers hold
-      const uint4 v = reinterpret_cast<const uint4*>(x)[j];
-      const int m = (int)((uint32_t)j / (uint32_t)n8);
-      const uint32_t u4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int h = 0; h < 4; ++h)
-#pragma unroll
-        for (int mm = 0; mm < M; ++mm)
-          if (mm == m) mx[mm] = max(mx[mm], max(u4[h] & 0x7FFFu, (u4[h] >> 16) & 0x7FFFu));
-    }
-#pragma unroll
-    for (int u = 0; u < kXRegs; ++u) {
-      const int64_t j = tid + (int64_t)u * 512;
-      const int m = (int)((uint32_t)j / (uint32_t)n8);
-      const uint32_t u4[4] = {xv[u].x, xv[u].y, xv[u].z, xv[u].w};
-      uint32_t v = 0u;
-#pragma unroll
-      for (int h = 0; h < 4; ++h) v = max(v, max(u4[h] & 0x7FFFu, (u4[h] >> 16) & 0x7FFFu));
-#pragma unroll
-      for (int mm = 0; mm < M; ++mm)
-        if (mm == m && j < npc) mx[mm] = max(mx[mm], v);
-    }
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) mx[m] = max(mx[m], (uint32_t)__shfl_xor((int)mx[m], o, 64));
-      if (lane == 0) smax[wave * 4 + m] = mx[m];
-    }
-    if (tid < 4) reinterpret_cast<uint4*>(zpad)[tid] = make_uint4(0u, 0u, 0u, 0u);
-    __syncthreads();
-    int e[M];
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-      uint32_t v = 0u;
-#pragma unroll
-      for (int w = 0; w < kPWaves; ++w) v = max(v, smax[w * 4 + m]);
-      e[m] = 0;
-      if (v != 0u && v < 0x7F80u) {             // finite, non-zero maximum
-        int ex;
-        frexpf(bf16_bits_to_f32(v), &ex);        // max in [2^(ex-1), 2^ex)
-        e[m] = 15 - ex;                          // max * 2^e in [2^14, 2^15)
-      }
-      if (tid == 0) sexp[m] = e[m];
-    }
-    auto convert_store = [&](int64_t j, const uint4& v) {
-      const int m = (int)((uint32_t)j / (uint32_t)n8);
-      const int64_t c8 = j - (int64_t)m * n8;
-      int em = e[0];
-#pragma unroll
-      for (int mm = 1; mm < M; ++mm) em = (mm == m) ? e[mm] : em;
-      const uint32_t u4[4] = {v.x, v.y, v.z, v.w};
-      uint32_t o[4];
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const _Float16 lo = (_Float16)ldexpf(bf16_bits_to_f32(u4[h] & 0xFFFFu), em);
-        const _Float16 hi = (_Float16)ldexpf(bf16_bits_to_f32(u4[h] >> 16), em);
-        o[h] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-      }
-      *reinterpret_cast<uint4*>(xs + (int64_t)m * lay.ldx + c8 * 8) = make_uint4(o[0], o[1], o[2], o[3]);
-    };
-#pragma unroll
-    for (int u = 0; u < kXRegs; ++u) {
-      const int64_t j = tid + (int64_t)u * 512;
-      if (j < npc) convert_store(j, xv[u]);
-    }
-    for (int64_t j = tid + (int64_t)kXRegs * 512; j < npc; j += 512)
-      convert_store(j, reinterpret_cast<const uint4*>(x)[j]);
-  }
-  // ---- 2. row groups
+  // ---- 1. this wave's column slice: runs [rb, re) of 32 columns.  Its
+  // slice of x (M vectors) and the first tiles go out on the copy engine.
   const int i = lane & 15, q = lane >> 4;
   const int nruns = (int)(C / 32);
-  const int per = (nruns + kPWaves - 1) / kPWaves;
-  const int rb = min(nruns, wave * per), re = min(nruns, rb + per);
-  const int nfull = (re - rb) >> 2;              // full groups of four runs (one per lane group q)
-  const int ntail = (re - rb) & 3;               // runs of a ragged last group
-  // word and spill-word offsets of this lane's run in groups 0 and 1 (run = rb + q + 4g)
-  auto word_off = [&](int run) { return (run >> 3) * WPB + (7 - (run & 7)) * K; };
-  auto spill_off = [&](int run) {
-    const int w = (7 - (run & 7)) * K + K;      // word after the run, wrapping to word 0 of the block
-    return (run >> 3) * WPB + (w == WPB ? 0 : w);
-  };
-  const int wo0 = word_off(rb + q), so0 = spill_off(rb + q);
-  const int wo1 = word_off(rb + q + 4), so1 = spill_off(rb + q + 4);
-  const uint16_t* xrow = xs + (int64_t)(i < M ? i : 0) * lay.ldx;
-  // B operand of group g: x' columns of run rb + q + 4g (lanes past the M vectors read the zero pad)
-  const uint16_t* bbase = (i < M) ? xrow + (int64_t)(rb + q) * 32 : zpad;
-  const int bstep = (i < M) ? 128 : 0;
-  const uint32_t mul = kMul, magic = kHalfMagic;
-  const uint64_t add64 = kAdd;
+  const int per = nruns / kWaves;              // C is a multiple of 256: every wave gets `per` runs
+  const int rb = wave * per, re = rb + per;
+  const int ngw = (per + 3) >> 2;              // groups of four runs (<= NG)
+  const int gw = per * 4;                      // 16-byte granules of one vector's slice
+  const int nxg = M * gw;                      // granules of this wave's x slice
+  const int nxw = (nxg + 63) / 64;             // its copies
+  uint8_t* xsl = ring + (size_t)(nslots - g.xslots) * g.tile_bytes + (size_t)wave * nxg * 16;   // [n][slice]
+  for (int j = 0; j < nxw; ++j) {              // every issued copy has an active lane
+    const int p = j * 64 + lane;
+    if (p < nxg) {
+      const int n = (p >= gw) + (p >= 2 * gw) + (p >= 3 * gw), jj = p - n * gw;
+      __builtin_amdgcn_global_load_lds(x + (int64_t)n * C + (int64_t)rb * 32 + jj * 8, xsl + (size_t)j * 1024,
+                                       16, 0, 0);
+    }
+  }
+  const int t0 = min(nmine, nslots - g.xslots);
+  for (int t = 0; t < t0; ++t) issue_tile(t);
+  wait_vmcnt(nw * t0);                         // the x slice has landed
 
-  // epilogue: wave (t mod 8) finalises row group t; lane < ROWS * M owns one output
+  // ---- 2. per-wave exponent e_n: the slice's largest |x[n]| * 2^e lands in
+  // [2^14, 2^15); then x' = f16(x 2^e) in place.  Partial sums are scaled
+  // back by 2^-e before the waves add them up.
+  uint32_t mx0 = 0u, mx1 = 0u, mx2 = 0u, mx3 = 0u;
+  for (int p = lane; p < nxg; p += 64) {
+    const uint32_t a = max_abs8(*reinterpret_cast<const uint4*>(xsl + (size_t)p * 16));
+    const int n = (p >= gw) + (p >= 2 * gw) + (p >= 3 * gw);
+    mx0 = n == 0 ? max(mx0, a) : mx0;
+    mx1 = n == 1 ? max(mx1, a) : mx1;
+    mx2 = n == 2 ? max(mx2, a) : mx2;
+    mx3 = n == 3 ? max(mx3, a) : mx3;
+  }
+  mx0 = wave_max_u32(mx0);
+  mx1 = wave_max_u32(mx1);
+  mx2 = wave_max_u32(mx2);
+  mx3 = wave_max_u32(mx3);
+  auto exponent = [](uint32_t v) {
+    int e = 0;
+    if (v != 0u && v < 0x7F80u) {              // finite, non-zero maximum
+      int ex;
+      frexpf(bf16_bits_to_f32(v), &ex);        // max in [2^(ex-1), 2^ex)
+      e = 15 - ex;
+    }
+    return e;
+  };
+  const int e0 = exponent(mx0), e1 = exponent(mx1), e2 = exponent(mx2), e3 = exponent(mx3);
+  for (int p = lane; p < nxg; p += 64) {
+    const int n = (p >= gw) + (p >= 2 * gw) + (p >= 3 * gw);
+    const int en = n == 0 ? e0 : n == 1 ? e1 : n == 2 ? e2 : e3;
+    uint4* ptr = reinterpret_cast<uint4*>(xsl + (size_t)p * 16);
+    const uint4 v = *ptr;
+    const uint32_t u4[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const _Float16 lo = (_Float16)ldexpf(bf16_bits_to_f32(u4[h] & 0xFFFFu), en);
+      const _Float16 hi = (_Float16)ldexpf(bf16_bits_to_f32(u4[h] >> 16), en);
+      o[h] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    }
+    *ptr = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+
+  // ---- 3. B operand in registers: lane (n, q) of group gg holds
+  // x'[n, run * 32 + 8u .. +7] for run = rb + 4 gg + q (zero past the M
+  // vectors or past the slice, whose A lanes then decode run rb).  The bias
+  // 510 * 2^-24 * sum_c x'[n, c] of the slice comes from the same MFMA with a
+  // constant A (all elements the subnormal 510 * 2^-24) and seeds the
+  // accumulator of every row group.
+  half8 B[NG][4];
+  int wo[NG], so[NG];
+  f32x4 bacc[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) bacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const half8 a510 = __builtin_bit_cast(half8, u32x4{0x01FE01FEu, 0x01FE01FEu, 0x01FE01FEu, 0x01FE01FEu});
+#pragma unroll
+  for (int gg = 0; gg < NG; ++gg) {
+    const int run = rb + 4 * gg + q;
+    const bool valid = run < re;
+    const int runc = valid ? run : rb;
+    const int w0 = (7 - (runc & 7)) * K;
+    wo[gg] = (runc >> 3) * WPB + w0;
+    so[gg] = (runc >> 3) * WPB + (w0 + K == WPB ? 0 : w0 + K);   // word after the run, wrapping in the block
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      B[gg][u] = (valid && i < M) ? load_half8(xsl + ((size_t)i * gw * 8 + (size_t)(4 * gg + q) * 32 + 8 * u) * 2)
+                                  : half8{0, 0, 0, 0, 0, 0, 0, 0};
+      if (gg < ngw) bacc[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a510, B[gg][u], bacc[u], 0, 0, 0);
+    }
+  }
+  const f32x4 nbias = -((bacc[0] + bacc[1]) + (bacc[2] + bacc[3]));   // every row of column n: the slice's bias
+  const int my_e = i == 0 ? e0 : i == 1 ? e1 : i == 2 ? e2 : e3;   // partial-sum scale of column n = i
+  // epilogue lanes: wave (t mod 8) finalises row group t; lane < ROWS * M owns one output
   const int on = lane / ROWS, orr = lane % ROWS;
   const bool oown = lane < ROWS * M;
 
-  __builtin_amdgcn_s_waitcnt(0);              // this wave's part of tiles 0 and 1
-  __syncthreads();
+  // ---- 4. tile 0 has landed (every wave's part) and the x slots are free: fill them
+  wait_vmcnt(nw * (t0 - 1));
+  lds_barrier();
+  const int tfill = min(nmine, nslots);
+  for (int t = t0; t < tfill; ++t) issue_tile(t);
+  int last = tfill - 1;                        // newest tile in flight
 
-  for (int64_t t = 0; t < nmine; ++t) {
-    const int buf = (int)(t & 1);
-    const bool owner = (int)(t % kPWaves) == wave;
-    const int64_t orow = ((int64_t)blockIdx.x + t * gridDim.x) * ROWS + orr;
-    float osc0 = 0.f, osc1 = 0.f;
-    if (owner && oown && orow < R) {
-      osc0 = half_bits_to_f32(scales0[orow]);
-      if constexpr (GATEUP) osc1 = half_bits_to_f32(scales1[orow]);
+  const uint32_t mul = kMul;
+  const uint64_t add64 = kAdd;
+  for (int t = 0; t < nmine; ++t) {
+    const int buf = t & 1;
+    const bool owner = (t & (kWaves - 1)) == wave;
+    const int64_t rg = (int64_t)blockIdx.x + (int64_t)t * gridDim.x;
+    const bool fast_sc = g.scales_aligned && rg * ROWS + ROWS <= R;
+    u32x4 sc0 = u32x4{0u, 0u, 0u, 0u}, sc1 = sc0;
+    if (owner && fast_sc) {                    // the owner's scales, through the scalar cache
+      sc0 = ((ConstV4*)(scales0 + rg * ROWS))[0];
+      if constexpr (GATEUP) sc1 = ((ConstV4*)(scales1 + rg * ROWS))[0];
+      else sc1 = ((ConstV4*)(scales0 + rg * ROWS))[1];
     }
-    const uint32_t* trow = reinterpret_cast<const uint32_t*>(tiles + (size_t)buf * lay.tile_bytes + (size_t)i * lay.rs);
-    // four independent accumulators: the MFMAs of a group do not wait on each other
+    const uint8_t* trow = ring + (size_t)(t % nslots) * g.tile_bytes + (size_t)i * g.gs * 16;
     f32x4 acc[4];
+    acc[0] = nbias;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-    uint32_t Wa[K + 1], Wb[K + 1];
-    half8 Ba[4], Bb[4];
-    auto read_group = [&](int g, uint32_t (&W)[K + 1], half8 (&B)[4]) {
-      const int j = g >> 1;                     // offsets repeat every two groups, one block apart
-      const int wo = ((g & 1) ? wo1 : wo0) + j * WPB;
-      const int so = ((g & 1) ? so1 : so0) + j * WPB;
-#pragma unroll
-      for (int m = 0; m < K; ++m) W[m] = trow[wo + m];
-      W[K] = trow[so];
-      const uint16_t* bp = bbase + (int64_t)g * bstep;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) B[u] = load_half8(bp + 8 * u);
-    };
-    auto consume = [&](const uint32_t (&W)[K + 1], const half8 (&B)[4]) {
+    for (int u = 1; u < 4; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto consume = [&](const uint32_t (&W)[K + 1], const half8 (&Bg)[4]) {
       u32x4 A[4];
-      decode_run_f16<K>(W, mul, add64, magic, A);
+      decode_run_sub<K>(W, mul, add64, A);
 #pragma unroll
       for (int u = 0; u < 4; ++u)
-        acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, A[u]), B[u], acc[u], 0, 0, 0);
+        acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, A[u]), Bg[u], acc[u], 0, 0, 0);
     };
-    // full groups: LDS reads run one group ahead of the decode (ping-pong)
-    if (nfull > 0) read_group(0, Wa, Ba);
-    for (int g = 0; g < nfull; g += 2) {
-      if (g + 1 < nfull) read_group(g + 1, Wb, Bb);
-      consume(Wa, Ba);
-      if (g + 2 < nfull) read_group(g + 2, Wa, Ba);
-      if (g + 1 < nfull) consume(Wb, Bb);
-    }
-    if (ntail) {                                // ragged last group: lanes past the range add zeros
-      const int run = rb + 4 * nfull + q;
-      const bool valid = run < re;
-      const int runc = valid ? run : rb;
-      const uint32_t* bw = trow + (runc >> 3) * WPB;
-      const int w0 = (7 - (runc & 7)) * K;
+    // LDS word reads run one group ahead of the decode (ping-pong)
+    uint32_t Wa[K + 1], Wb[K + 1];
+    read_words<K>(trow, wo[0], so[0], Wa);
 #pragma unroll
-      for (int m = 0; m < K; ++m) Wa[m] = bw[w0 + m];
-      Wa[K] = bw[(w0 + K == WPB) ? 0 : w0 + K];
-      const uint16_t* bp = (i < M && valid) ? xrow + (int64_t)run * 32 : zpad;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) Ba[u] = load_half8(bp + 8 * u);
-      consume(Wa, Ba);
-    }
-    // row group complete: the next tile's copy has landed (this wave's part),
-    // partial D tiles go to LDS, one barrier, then the freed tile is refilled
-    // two row groups ahead and one wave runs the epilogue.
-    red[(buf * kPWaves + wave) * 64 + lane] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (t + 2 < nmine) dma_tile(t + 2, buf);
-    if (owner && oown && orow < R) {
-      // D of a 16x16 tile: lane 16*(a/4) + n holds row a, column n in element a % 4
-      const int e = sexp[on];
-      float s0 = 0.f;
-#pragma unroll
-      for (int v = 0; v < kPWaves; ++v) s0 += red[(buf * kPWaves + v) * 64 + 16 * (orr >> 2) + on][orr & 3];
-      const float v0 = ldexpf(s0 * (osc0 * kRcp), -e);
-      const int64_t o = (int64_t)on * R + orow;
-      if constexpr (GATEUP) {
-        const int ju = orr + 8;
-        float s1 = 0.f;
-#pragma unroll
-        for (int v = 0; v < kPWaves; ++v) s1 += red[(buf * kPWaves + v) * 64 + 16 * (ju >> 2) + on][ju & 3];
-        const float v1 = ldexpf(s1 * (osc1 * kRcp), -e);
-        if (gate_f32) gate_f32[o] = v0;
-        if (up_f32) up_f32[o] = v1;
-        const float gT = round_bf16(v0);
-        const float uT = round_bf16(v1);
-        const float sig = round_bf16(1.0f / (1.0f + expf(-gT)));
-        const float silu = round_bf16(gT * sig);
-        reinterpret_cast<uint16_t*>(out)[o] = f32_to_bf16_bits(silu * uT);
-      } else {
-        if (out_f32) reinterpret_cast<float*>(out)[o] = v0;
-        else reinterpret_cast<uint16_t*>(out)[o] = f32_to_bf16_bits(v0);
+    for (int gg = 0; gg < NG; gg += 2) {
+      const int g1 = gg + 1 < NG ? gg + 1 : NG - 1;
+      const int g2 = gg + 2 < NG ? gg + 2 : NG - 1;
+      if (gg < ngw) {
+        if (gg + 1 < NG && gg + 1 < ngw) read_words<K>(trow, wo[g1], so[g1], Wb);
+        consume(Wa, B[gg]);
+        if (gg + 2 < NG && gg + 2 < ngw) read_words<K>(trow, wo[g2], so[g2], Wa);
+        if (gg + 1 < NG && gg + 1 < ngw) consume(Wb, B[g1]);
       }
+    }
+    // partial D tile: lane (n, q) holds rows 4q .. 4q+3 of column n, scaled
+    // back by 2^-e_n (exact) so every wave's part is in the same units
+    const f32x4 sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    f32x4 part;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) part[e] = ldexpf(sum[e], -my_e);
+    if (i < M) *reinterpret_cast<f32x4*>(red + ((buf * kWaves + wave) * 4 + i) * 16 + 4 * q) = part;
+    // tile t + 1 has landed (this wave's copies), then everyone's parts
+    wait_vmcnt(last > t + 1 ? nw * (last - t - 1) : 0);
+    lds_barrier();
+    if (t + nslots < nmine) {                  // refill the slot just freed
+      issue_tile(t + nslots);
+      last = t + nslots;
+    }
+    if (owner && oown) {
+      float s0v, s1v;
+      if (fast_sc) {
+        const uint32_t d0 = (GATEUP || orr < 8) ? pick4(sc0, (orr >> 1) & 3) : pick4(sc1, (orr >> 1) & 3);
+        s0v = half_bits_to_f32((orr & 1) ? d0 >> 16 : d0 & 0xFFFFu);
+        const uint32_t d1 = pick4(sc1, (orr >> 1) & 3);
+        s1v = half_bits_to_f32((orr & 1) ? d1 >> 16 : d1 & 0xFFFFu);
+      } else {                                 // ragged last row group, or scales not 4-byte aligned
+        const int64_t orow = rg * ROWS + orr;
+        s0v = orow < R ? half_bits_to_f32(scales0[orow]) : 0.f;
+        s1v = (GATEUP && orow < R) ? half_bits_to_f32(scales1[orow]) : 0.f;
+      }
+      const float* rp = red + (buf * kWaves * 4 + on) * 16;
+      float d0 = 0.f;
+#pragma unroll
+      for (int v = 0; v < kWaves; ++v) d0 += rp[v * 64 + orr];
+      float* ob = obuf + ((size_t)(t * M + on) * ROWS + orr) * NOUT;
+      ob[0] = ldexpf(d0 * (s0v * kRcp), 24);
+      if constexpr (GATEUP) {
+        float d1 = 0.f;
+#pragma unroll
+        for (int v = 0; v < kWaves; ++v) d1 += rp[v * 64 + orr + 8];
+        ob[1] = ldexpf(d1 * (s1v * kRcp), 24);
+      }
+    }
+  }
+
+  // ---- 6. write the finished rows
+  lds_barrier();
+  const int per_t = M * ROWS;
+  for (int idx = tid; idx < nmine * per_t; idx += kThreads) {
+    const int t = idx / per_t, r = idx - t * per_t;
+    const int m = r / ROWS, row = r - m * ROWS;
+    const int64_t orow = ((int64_t)blockIdx.x + (int64_t)t * gridDim.x) * ROWS + row;
+    if (orow >= R) continue;
+    const int64_t o = (int64_t)m * R + orow;
+    const float v0 = obuf[(size_t)idx * NOUT];
+    if constexpr (GATEUP) {
+      const float v1 = obuf[(size_t)idx * NOUT + 1];
+      if (gate_f32) gate_f32[o] = v0;
+      if (up_f32) up_f32[o] = v1;
+      const float gT = round_bf16(v0);
+      const float uT = round_bf16(v1);
+      const float sig = round_bf16(1.0f / (1.0f + expf(-gT)));
+      const float silu = round_bf16(gT * sig);
+      reinterpret_cast<uint16_t*>(out)[o] = f32_to_bf16_bits(silu * uT);
+    } else {
+      if (out_f32) reinterpret_cast<float*>(out)[o] = v0;
+      else reinterpret_cast<uint16_t*>(out)[o] = f32_to_bf16_bits(v0);
     }
   }
 }
@@ -358,25 +443,77 @@ int device_cus() {
   return cus[dev];
 }
 
-template <int K, int M, bool GU>
-hipError_t axis1_launch_one(const uint32_t* c0, const uint16_t* s0, const uint32_t* c1,
-                            const uint16_t* s1, const uint16_t* x, void* out, int out_f32,
-                            float* gf, float* uf, int64_t R, int64_t C, hipStream_t stream) {
-  const Axis1Lds lay = axis1_lds(C, M, K);
-  static bool lds_attr = false;                 // raise the dynamic LDS limit once per instantiation
-  if (!lds_attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&axis1_persistent_kernel<K, M, GU>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kAxis1MaxLdsBytes);
-    if (e != hipSuccess) return e;
-    lds_attr = true;
-  }
-  const int64_t rows = GU ? 8 : 16;
+// Runs of 32 per wave -> MFMA groups per wave -> the register-resident B
+// capacity instantiated for it (2 or 5 groups: C <= 2048 or C <= 5120); 0 if
+// C is too wide for B to stay in registers.
+int axis1_ng(int64_t C) {
+  const int64_t nruns = C / 32;
+  const int64_t per = (nruns + kWaves - 1) / kWaves;
+  const int64_t ngw = (per + 3) / 4;
+  return ngw <= 2 ? 2 : ngw <= 5 ? 5 : 0;
+}
+
+// Host geometry; returns false if the shape does not fit (LDS or registers).
+bool axis1_geom(int64_t R, int64_t C, int M, int k, bool gateup, int64_t grid, Axis1Geom& g) {
+  const int rows = gateup ? 8 : 16;
+  g.R = R;
+  g.C = C;
+  g.M = M;
+  g.nrg = (R + rows - 1) / rows;
+  g.row_bytes = C * k / 8;
+  g.G = (int)(g.row_bytes / 16);
+  g.gs = g.G + 1;
+  g.ipt = (16 * g.gs + 63) / 64;
+  g.gs_magic = (uint32_t)(((1u << 24) + g.gs - 1) / g.gs);
+  g.nmine_max = (int)((g.nrg + grid - 1) / grid);
+  g.scales_aligned = 1;
+  if (M < 1 || M > 4 || C % 256 != 0 || axis1_ng(C) == 0 || (g.ipt + kWaves - 1) / kWaves > kMaxDma) return false;
+  g.tile_bytes = (uint32_t)((16 * g.gs * 16 + 255) / 256 * 256);
+  const uint64_t obuf = ((uint64_t)g.nmine_max * M * rows * (gateup ? 2 : 1) * 4 + 255) / 256 * 256;
+  const uint64_t fixed = kRedBytes + obuf;
+  if (fixed >= kAxis1MaxLdsBytes) return false;
+  const uint64_t nsl = (kAxis1MaxLdsBytes - fixed) / g.tile_bytes;
+  g.nslots = (int)(nsl < (uint64_t)kMaxSlots ? nsl : kMaxSlots);
+  g.xslots = (int)(((uint64_t)M * C * 2 + g.tile_bytes - 1) / g.tile_bytes);
+  if (g.nslots < 2 || g.nslots < g.xslots + 1) return false;
+  g.red_off = (uint32_t)g.nslots * g.tile_bytes;
+  g.obuf_off = g.red_off + kRedBytes;
+  g.total = (uint32_t)(g.obuf_off + obuf);
+  return g.total <= kAxis1MaxLdsBytes;
+}
+
+int64_t axis1_grid(int64_t R, bool gateup) {
+  const int64_t rows = gateup ? 8 : 16;
   const int64_t nrg = (R + rows - 1) / rows;
   const int64_t cus = device_cus();
-  const unsigned grid = (unsigned)(nrg < cus ? nrg : cus);
-  hipLaunchKernelGGL((axis1_persistent_kernel<K, M, GU>), dim3(grid), dim3(512), lay.total, stream,
-                     c0, s0, c1, s1, x, out, out_f32, gf, uf, R, C);
+  return nrg < cus ? nrg : cus;
+}
+
+template <int K, bool GU, int NG>
+hipError_t axis1_launch_one(const uint32_t* c0, const uint16_t* s0, const uint32_t* c1,
+                            const uint16_t* s1, const uint16_t* x, void* out, int out_f32,
+                            float* gf, float* uf, const Axis1Geom& g, int64_t grid, hipStream_t stream) {
+  static uint64_t lds_attr = 0;                // devices whose dynamic LDS limit is raised
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+  const uint64_t bit = 1ull << (dev & 63);
+  if (!(lds_attr & bit)) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&axis1_kernel<K, GU, NG>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kAxis1MaxLdsBytes);
+    if (e != hipSuccess) return e;
+    lds_attr |= bit;
+  }
+  hipLaunchKernelGGL((axis1_kernel<K, GU, NG>), dim3((unsigned)grid), dim3(kThreads), g.total, stream,
+                     c0, s0, c1, s1, x, out, out_f32, gf, uf, g);
   return hipGetLastError();
+}
+
+template <int K, int NG>
+hipError_t axis1_dispatch_gu(const uint32_t* c0, const uint16_t* s0, const uint32_t* c1,
+                             const uint16_t* s1, const uint16_t* x, void* out, int out_f32, float* gf,
+                             float* uf, const Axis1Geom& g, int64_t grid, hipStream_t stream) {
+  return c1 ? axis1_launch_one<K, true, NG>(c0, s0, c1, s1, x, out, out_f32, gf, uf, g, grid, stream)
+            : axis1_launch_one<K, false, NG>(c0, s0, c1, s1, x, out, out_f32, gf, uf, g, grid, stream);
 }
 
 template <int K>
@@ -384,25 +521,26 @@ hipError_t axis1_main(const uint32_t* c0, const uint16_t* s0, const uint32_t* c1
                       const uint16_t* s1, const uint16_t* x, void* out, int out_f32, float* gf,
                       float* uf, int64_t R, int64_t C, int M, hipStream_t stream) {
   const bool gu = c1 != nullptr;
-#define TRELLIS_AXIS1_CASE(MM)                                                                      \
-  case MM:                                                                                           \
-    return gu ? axis1_launch_one<K, MM, true>(c0, s0, c1, s1, x, out, out_f32, gf, uf, R, C, stream) \
-              : axis1_launch_one<K, MM, false>(c0, s0, c1, s1, x, out, out_f32, gf, uf, R, C, stream);
-  switch (M) {
-    TRELLIS_AXIS1_CASE(1)
-    TRELLIS_AXIS1_CASE(2)
-    TRELLIS_AXIS1_CASE(3)
-    TRELLIS_AXIS1_CASE(4)
+  const int64_t grid = axis1_grid(R, gu);
+  Axis1Geom g;
+  if (!axis1_geom(R, C, M, K, gu, grid, g)) return hipErrorInvalidValue;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(s0), a1 = reinterpret_cast<uintptr_t>(s1);
+  g.scales_aligned = (a0 % 4 == 0) && (!gu || a1 % 4 == 0);
+  switch (axis1_ng(C)) {
+    case 2: return axis1_dispatch_gu<K, 2>(c0, s0, c1, s1, x, out, out_f32, gf, uf, g, grid, stream);
+    case 5: return axis1_dispatch_gu<K, 5>(c0, s0, c1, s1, x, out, out_f32, gf, uf, g, grid, stream);
     default: return hipErrorInvalidValue;
   }
-#undef TRELLIS_AXIS1_CASE
 }
 
 }  // namespace
 
 size_t axis1_workspace_bytes(int64_t, int64_t, int, int) { return 0; }
 
-size_t axis1_lds_bytes(int64_t C, int M, int k) { return axis1_lds(C, M, k).total; }
+bool axis1_supported(int64_t R, int64_t C, int M, int k, bool gateup) {
+  Axis1Geom g;
+  return axis1_geom(R, C, M, k, gateup, axis1_grid(R, gateup), g);
+}
 
 hipError_t launch_axis1(const uint32_t* codes0, const uint16_t* scales0, const uint32_t* codes1,
                         const uint16_t* scales1, const uint16_t* x, void* out, int out_f32,

@@ -9,11 +9,11 @@
 
 namespace trellis {
 
-// axis 1 (gate/up when codes1 != nullptr).  The persistent kernel keeps an
-// f16 copy of x and two 16-row code tiles in LDS; shapes whose layout
-// exceeds kAxis1MaxLdsBytes are rejected on the host.
+// axis 1 (gate/up when codes1 != nullptr).  The persistent kernel keeps a
+// ring of 16-row code tiles in LDS and x in registers; axis1_supported says
+// whether a shape fits (LDS and register budget), checked on the host.
 constexpr size_t kAxis1MaxLdsBytes = 160 * 1024;
-size_t axis1_lds_bytes(int64_t C, int M, int k);
+bool axis1_supported(int64_t R, int64_t C, int M, int k, bool gateup);
 size_t axis1_workspace_bytes(int64_t R, int64_t C, int M, int k);
 hipError_t launch_axis1(const uint32_t* codes0, const uint16_t* scales0, const uint32_t* codes1,
                         const uint16_t* scales1, const uint16_t* x, void* out, int out_f32,
