@@ -11,25 +11,21 @@
 //   A (16 rows x 32 k): the byte sum b = y + 510 of each 1MAD word, taken as
 //     an f16 subnormal bit pattern (value b * 2^-24, exact for b <= 1023);
 //     v_sad_hi_u8 / v_sad_u8 write two of them into one register directly.
-//   B (32 k x 16 n): x'[n, c] = f16(x[n, c] * 2^e_n), e_n chosen per vector so
-//     the largest |x| lands in [2^14, 2^15); every bf16 value down to 2^-17 of
-//     that maximum is exact in f16.
-//   D: f32.  sum_c y x' = 2^24 D - 510 S_n with S_n = sum_c x'[n, c], so the
-//     epilogue forms (D - 510 S_n 2^-24) * scale / d * 2^(24 - e_n).
+//   B (32 k x 16 n): x'[n, c] = f16(x[n, c] * 2^e), e chosen per vector and
+//     per column slice so the slice's largest |x| lands in [2^14, 2^15); every
+//     bf16 value down to 2^-17 of that maximum is exact in f16.
+//   D: f32, seeded with -510 * 2^-24 * sum_c x'[n, c] (the same MFMA against a
+//     constant A), so D = 2^-24 sum_c y x'.  Each slice's D is scaled back by
+//     2^-e; the sum over slices times 2^24 * scale / d is the output.
 //
-// Persistent schedule: one workgroup of 8 waves per CU, row groups
-// b, b + grid, ... (16 A-rows each: 16 output rows, or 8 gate + 8 up rows
-// sharing B).  Each wave owns a fixed slice of the columns, so its B operand
-// lives in registers for the whole kernel.  Code tiles of 16 packed rows
-// stream HBM -> LDS with global_load_lds_dwordx4 into a ring of N slots (one
-// 16-byte pad granule per row spreads the LDS banks).  Every vector-memory
-// operation of the steady state is such a copy, waited for with explicit
-// vmcnt counts, so the ring keeps N - 1 tiles in flight: scales come through
-// the scalar cache, x is staged by the same copy engine, and finished rows
-// wait in LDS until the end, so no vector-register load ever queues behind
-// the ring.  Per row group: decode + MFMA, partial D tiles to LDS, one
-// barrier, refill of the freed slot, and one wave (rotating) reduces the
-// eight partial tiles.
+// Schedule: one workgroup of 8 waves per CU walks row groups b, b + grid, ...
+// (16 A-rows each: 16 output rows, or 8 gate + 8 up rows sharing B).  Wave w
+// owns column slice w (C / 8 columns) for the whole kernel: its B operand
+// lives in registers, and it copies only the code blocks of its slice
+// (HBM -> its own LDS ring, global_load_lds_dwordx4, explicit vmcnt waits).
+// The waves never wait for each other inside the loop: each leaves its
+// partial D tile of every row group in LDS, and after one barrier at the end
+// all threads add the eight partials in a fixed order and run the epilogue.
 #include "internal.hpp"
 #include "mfma_common.hpp"
 
@@ -37,20 +33,24 @@ namespace trellis {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(4))) const u32x4 ConstV4;   // read through the scalar cache
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kMaxSlots = 3;           // two tiles in flight: deeper rings only queue copies that stall the issuing wave
-constexpr int kMaxDma = 6;           // tile copies per wave per tile (C <= 5120, k <= 4: 41 per tile)
-constexpr uint32_t kRedBytes = 2 * kWaves * 4 * 16 * 4;   // f32 [2][wave][n][16 rows]
+constexpr int kMaxSlots = 4;           // tile ring depth per wave
+constexpr int kMaxDma = 7;             // copies per wave per tile (C <= 5120, k <= 4: 16 rows x 25 granules)
+constexpr int kXPer = 5;               // x granules per lane of a wave's slice (M * C <= 4 * 5120)
+constexpr uint32_t kPartBytes = kWaves * 4 * 16 * 4;   // one row group's partial tiles: f32 [wave][n][16 rows]
 
 // Geometry shared by the host (LDS sizing) and the kernel.
 struct Axis1Geom {
   int64_t R, C, nrg, row_bytes;
-  int M, G, gs, ipt, nslots, xslots, nmine_max, scales_aligned;
-  uint32_t gs_magic;    // ceil(2^24 / gs): p / gs == (p * gs_magic) >> 24 for p < 4096
-  uint32_t tile_bytes, red_off, obuf_off, total;
+  int M;
+  int per;              // runs of 32 columns per wave (C / 256)
+  int gsw;              // granules per tile row of a wave's window (its blocks + one pad granule)
+  int nwd;              // copies per wave per tile: ceil(16 gsw / 64)
+  uint32_t gsw_magic;   // ceil(2^24 / gsw): p / gsw == (p * gsw_magic) >> 24 for p < 4096
+  int nslots, xslots, nmine_max;
+  uint32_t slot_bytes, part_off, total;
 };
 
 // s_waitcnt vmcnt(n) with expcnt / lgkmcnt left alone (gfx9 encoding).
@@ -77,7 +77,7 @@ __device__ __forceinline__ void wait_vmcnt(int n) {   // n is wave-uniform
   }
 }
 
-// Workgroup barrier that orders LDS only: it does not wait for the copies in flight.
+// Workgroup barrier that orders LDS only: it does not wait for copies in flight.
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
@@ -155,10 +155,6 @@ __device__ __forceinline__ void read_words(const uint8_t* trow, int wo, int so, 
   W[K] = t32[so];
 }
 
-__device__ __forceinline__ uint32_t pick4(const u32x4& v, int j) {
-  return j == 0 ? v[0] : j == 1 ? v[1] : j == 2 ? v[2] : v[3];
-}
-
 template <int K, bool GATEUP, int NG>
 __global__ __launch_bounds__(kThreads) void axis1_kernel(
     const uint32_t* __restrict__ codes0, const uint16_t* __restrict__ scales0,
@@ -166,90 +162,103 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
     const uint16_t* __restrict__ x, void* __restrict__ out, int out_f32,
     float* __restrict__ gate_f32, float* __restrict__ up_f32, const Axis1Geom g) {
   constexpr int WPB = words_per_block(K);
+  constexpr int BLK = WPB * 4;                 // bytes per packed block
   constexpr int ROWS = GATEUP ? 8 : 16;        // output rows per row group
-  constexpr int NOUT = GATEUP ? 2 : 1;         // staged values per output
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int i = lane & 15, q = lane >> 4;
   const int M = g.M;
   const int64_t R = g.R, C = g.C;
-  const int nslots = g.nslots;
+  const int NS = g.nslots, nwd = g.nwd, gsw = g.gsw;
   const int nmine = (int)((g.nrg - 1 - (int64_t)blockIdx.x) / gridDim.x + 1);   // grid <= nrg
-  const int nw = g.ipt > wave ? (g.ipt - 1 - wave) / kWaves + 1 : 0;            // tile copies per tile
-  uint8_t* ring = smem;
-  float* red = reinterpret_cast<float*>(smem + g.red_off);
-  float* obuf = reinterpret_cast<float*>(smem + g.obuf_off);
+  uint8_t* ring = smem + (size_t)wave * NS * g.slot_bytes;                      // this wave's slots
+  float* part = reinterpret_cast<float*>(smem + g.part_off);
 
-  // ---- copy descriptors: tile granule p = 64 v + lane (v = wave + 8 j) is
-  // granule p % gs of tile row p / gs (the last granule of each row is pad).
+  // ---- this wave's slice: runs [rb, re) of 32 columns, held in packed
+  // blocks [b0, b1]; a tile row of the wave's window is those blocks
+  const int per = g.per;
+  const int rb = wave * per, re = rb + per;
+  const int b0 = rb >> 3, b1 = (re - 1) >> 3;
+  const int gwr = (b1 - b0 + 1) * (BLK / 16);  // granules of the window per row (< gsw)
+
+  // copy descriptors: window granule p = 64 j + lane is granule p % gsw of
+  // tile row p / gsw (granules past the wave's blocks are skipped).
   // dd = active bit | tile row << 16 | byte offset of the granule in its row.
   uint32_t dd[kMaxDma];
 #pragma unroll
   for (int j = 0; j < kMaxDma; ++j) {
-    const uint32_t p = (uint32_t)((wave + kWaves * j) * 64 + lane);
-    const uint32_t i = (uint32_t)(((uint64_t)p * g.gs_magic) >> 24), jj = p - i * (uint32_t)g.gs;
-    dd[j] = (j < nw && p < 16u * (uint32_t)g.gs && jj < (uint32_t)g.G) ? (1u << 31) | (i << 16) | (jj * 16u) : 0u;
+    const uint32_t p = (uint32_t)(j * 64 + lane);
+    const uint32_t r = (uint32_t)(((uint64_t)p * g.gsw_magic) >> 24), jj = p - r * (uint32_t)gsw;
+    dd[j] = (j < nwd && p < 16u * (uint32_t)gsw && jj < (uint32_t)gwr)
+                ? (1u << 31) | (r << 16) | ((uint32_t)b0 * BLK + jj * 16u) : 0u;
   }
   const uint8_t* cb0 = reinterpret_cast<const uint8_t*>(codes0);
   const uint8_t* cb1 = reinterpret_cast<const uint8_t*>(GATEUP ? codes1 : codes0);
   const uint32_t row_bytes = (uint32_t)g.row_bytes;
   auto issue_tile = [&](int t) {
     const int64_t rg = (int64_t)blockIdx.x + (int64_t)t * gridDim.x;
-    uint8_t* slot = ring + (size_t)(t % nslots) * g.tile_bytes;
-    const bool full = rg * ROWS + ROWS <= R;   // ragged last row group: clamp rows to R - 1
+    uint8_t* slot = ring + (size_t)(t % NS) * g.slot_bytes;
+    const bool full = rg * ROWS + ROWS <= R;   // ragged last row group: rows past R read row R - 1
     const int64_t gbase = rg * ROWS * g.row_bytes;
 #pragma unroll
     for (int j = 0; j < kMaxDma; ++j) {
-      if (j < nw) {                            // every issued copy has an active lane
+      if (j < nwd) {                           // every issued copy has an active lane
         const uint32_t d = dd[j];
         if (d >> 31) {
-          const uint32_t i = (d >> 16) & 15u;
-          const uint32_t ri = GATEUP ? (i & 7u) : i;
-          const uint8_t* base = (GATEUP && i >= 8u) ? cb1 : cb0;
+          const uint32_t r = (d >> 16) & 15u;
+          const uint32_t rr = GATEUP ? (r & 7u) : r;
+          const uint8_t* base = (GATEUP && r >= 8u) ? cb1 : cb0;
           const uint8_t* src;
           if (full) {
-            src = base + gbase + (ri * row_bytes + (d & 0xFFFFu));
+            src = base + gbase + (rr * row_bytes + (d & 0xFFFFu));
           } else {
-            int64_t row = rg * ROWS + ri;
+            int64_t row = rg * ROWS + rr;
             row = row < R ? row : R - 1;
             src = base + row * g.row_bytes + (d & 0xFFFFu);
           }
-          __builtin_amdgcn_global_load_lds(src, slot + (size_t)(wave + kWaves * j) * 1024, 16, 0, 0);
+          __builtin_amdgcn_global_load_lds(src, slot + (size_t)j * 1024, 16, 0, 0);
         }
       }
     }
   };
 
-  // ---- 1. this wave's column slice: runs [rb, re) of 32 columns.  Its
-  // slice of x (M vectors) and the first tiles go out on the copy engine.
-  const int i = lane & 15, q = lane >> 4;
-  const int nruns = (int)(C / 32);
-  const int per = nruns / kWaves;              // C is a multiple of 256: every wave gets `per` runs
-  const int rb = wave * per, re = rb + per;
-  const int ngw = (per + 3) >> 2;              // groups of four runs (<= NG)
-  const int gw = per * 4;                      // 16-byte granules of one vector's slice
-  const int nxg = M * gw;                      // granules of this wave's x slice
-  const int nxw = (nxg + 63) / 64;             // its copies
-  uint8_t* xsl = ring + (size_t)(nslots - g.xslots) * g.tile_bytes + (size_t)wave * nxg * 16;   // [n][slice]
+  // ---- 1. the wave's slice of x (M vectors) lands in its last ring slots
+  // while the first tiles go out
+  const int gx = per * 4;                      // 16-byte granules of one vector's slice
+  const int nxg = M * gx;
+  const int nxw = (nxg + 63) / 64;
+  uint8_t* xsl = ring + (size_t)(NS - g.xslots) * g.slot_bytes;                  // [n][slice], then x'
   for (int j = 0; j < nxw; ++j) {              // every issued copy has an active lane
     const int p = j * 64 + lane;
     if (p < nxg) {
-      const int n = (p >= gw) + (p >= 2 * gw) + (p >= 3 * gw), jj = p - n * gw;
+      const int n = (p >= gx) + (p >= 2 * gx) + (p >= 3 * gx), jj = p - n * gx;
       __builtin_amdgcn_global_load_lds(x + (int64_t)n * C + (int64_t)rb * 32 + jj * 8, xsl + (size_t)j * 1024,
                                        16, 0, 0);
     }
   }
-  const int t0 = min(nmine, nslots - g.xslots);
-  for (int t = 0; t < t0; ++t) issue_tile(t);
-  wait_vmcnt(nw * t0);                         // the x slice has landed
+  // the ring fills a little at a time (a burst of copies would stall the
+  // issuing wave): up to two tiles now, in slots the x slice does not use
+  int next = 0;                                // next tile to copy; tiles go out in order
+  const int t0 = min(nmine, min(2, NS - g.xslots));
+  for (; next < t0; ++next) issue_tile(next);
+  wait_vmcnt(nwd * t0);                        // the x slice has landed
 
-  // ---- 2. per-wave exponent e_n: the slice's largest |x[n]| * 2^e lands in
-  // [2^14, 2^15); then x' = f16(x 2^e) in place.  Partial sums are scaled
-  // back by 2^-e before the waves add them up.
+  // ---- 2. exponent of the slice per vector: its largest |x[n]| * 2^e lands
+  // in [2^14, 2^15); then x' = f16(x 2^e) in place
+  // every lane holds at most kXPer granules of the slice (M * C / 8 / 64 <= 5 * 64 granules per wave)
+  uint4 xr[kXPer];
+#pragma unroll
+  for (int u = 0; u < kXPer; ++u) {
+    const int p = lane + 64 * u;
+    xr[u] = p < nxg ? *reinterpret_cast<const uint4*>(xsl + (size_t)p * 16) : make_uint4(0u, 0u, 0u, 0u);
+  }
   uint32_t mx0 = 0u, mx1 = 0u, mx2 = 0u, mx3 = 0u;
-  for (int p = lane; p < nxg; p += 64) {
-    const uint32_t a = max_abs8(*reinterpret_cast<const uint4*>(xsl + (size_t)p * 16));
-    const int n = (p >= gw) + (p >= 2 * gw) + (p >= 3 * gw);
+#pragma unroll
+  for (int u = 0; u < kXPer; ++u) {
+    const int p = lane + 64 * u;
+    const uint32_t a = max_abs8(xr[u]);        // zero past the slice
+    const int n = (p >= gx) + (p >= 2 * gx) + (p >= 3 * gx);
     mx0 = n == 0 ? max(mx0, a) : mx0;
     mx1 = n == 1 ? max(mx1, a) : mx1;
     mx2 = n == 2 ? max(mx2, a) : mx2;
@@ -269,12 +278,12 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
     return e;
   };
   const int e0 = exponent(mx0), e1 = exponent(mx1), e2 = exponent(mx2), e3 = exponent(mx3);
-  for (int p = lane; p < nxg; p += 64) {
-    const int n = (p >= gw) + (p >= 2 * gw) + (p >= 3 * gw);
+#pragma unroll
+  for (int u = 0; u < kXPer; ++u) {
+    const int p = lane + 64 * u;
+    const int n = (p >= gx) + (p >= 2 * gx) + (p >= 3 * gx);
     const int en = n == 0 ? e0 : n == 1 ? e1 : n == 2 ? e2 : e3;
-    uint4* ptr = reinterpret_cast<uint4*>(xsl + (size_t)p * 16);
-    const uint4 v = *ptr;
-    const uint32_t u4[4] = {v.x, v.y, v.z, v.w};
+    const uint32_t u4[4] = {xr[u].x, xr[u].y, xr[u].z, xr[u].w};
     uint32_t o[4];
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
@@ -282,63 +291,54 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
       const _Float16 hi = (_Float16)ldexpf(bf16_bits_to_f32(u4[h] >> 16), en);
       o[h] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
     }
-    *ptr = make_uint4(o[0], o[1], o[2], o[3]);
+    if (p < nxg) *reinterpret_cast<uint4*>(xsl + (size_t)p * 16) = make_uint4(o[0], o[1], o[2], o[3]);
   }
 
   // ---- 3. B operand in registers: lane (n, q) of group gg holds
   // x'[n, run * 32 + 8u .. +7] for run = rb + 4 gg + q (zero past the M
   // vectors or past the slice, whose A lanes then decode run rb).  The bias
-  // 510 * 2^-24 * sum_c x'[n, c] of the slice comes from the same MFMA with a
-  // constant A (all elements the subnormal 510 * 2^-24) and seeds the
-  // accumulator of every row group.
+  // 510 * 2^-24 * sum x'[n, slice] comes from the same MFMA with a constant A
+  // (every element the subnormal 510 * 2^-24) and seeds every accumulator.
   half8 B[NG][4];
   int wo[NG], so[NG];
   f32x4 bacc[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) bacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
   const half8 a510 = __builtin_bit_cast(half8, u32x4{0x01FE01FEu, 0x01FE01FEu, 0x01FE01FEu, 0x01FE01FEu});
+  const int ngw = (per + 3) >> 2;              // groups of four runs (<= NG)
 #pragma unroll
   for (int gg = 0; gg < NG; ++gg) {
     const int run = rb + 4 * gg + q;
     const bool valid = run < re;
     const int runc = valid ? run : rb;
     const int w0 = (7 - (runc & 7)) * K;
-    wo[gg] = (runc >> 3) * WPB + w0;
-    so[gg] = (runc >> 3) * WPB + (w0 + K == WPB ? 0 : w0 + K);   // word after the run, wrapping in the block
+    const int blk = (runc >> 3) - b0;          // block within the window
+    wo[gg] = blk * WPB + w0;
+    so[gg] = blk * WPB + (w0 + K == WPB ? 0 : w0 + K);   // word after the run, wrapping in the block
+    const uint8_t* bp = xsl + ((size_t)(i < M ? i : 0) * gx * 8 + (size_t)(runc - rb) * 32) * 2;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) B[gg][u] = load_half8(bp + 16 * u);   // in-slice address for every lane
+  }
+#pragma unroll
+  for (int gg = 0; gg < NG; ++gg) {
+    const bool keep = (rb + 4 * gg + q < re) && i < M;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      B[gg][u] = (valid && i < M) ? load_half8(xsl + ((size_t)i * gw * 8 + (size_t)(4 * gg + q) * 32 + 8 * u) * 2)
-                                  : half8{0, 0, 0, 0, 0, 0, 0, 0};
+      if (!keep) B[gg][u] = half8{0, 0, 0, 0, 0, 0, 0, 0};
       if (gg < ngw) bacc[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a510, B[gg][u], bacc[u], 0, 0, 0);
     }
   }
-  const f32x4 nbias = -((bacc[0] + bacc[1]) + (bacc[2] + bacc[3]));   // every row of column n: the slice's bias
-  const int my_e = i == 0 ? e0 : i == 1 ? e1 : i == 2 ? e2 : e3;   // partial-sum scale of column n = i
-  // epilogue lanes: wave (t mod 8) finalises row group t; lane < ROWS * M owns one output
-  const int on = lane / ROWS, orr = lane % ROWS;
-  const bool oown = lane < ROWS * M;
+  const f32x4 nbias = -((bacc[0] + bacc[1]) + (bacc[2] + bacc[3]));   // every row of column n: the bias
+  const int my_e = i == 0 ? e0 : i == 1 ? e1 : i == 2 ? e2 : e3;     // scale of column n = i
 
-  // ---- 4. tile 0 has landed (every wave's part) and the x slots are free: fill them
-  wait_vmcnt(nw * (t0 - 1));
-  lds_barrier();
-  const int tfill = min(nmine, nslots);
-  for (int t = t0; t < tfill; ++t) issue_tile(t);
-  int last = tfill - 1;                        // newest tile in flight
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);     // the x' reads above stay before any later copy
+  if (next == 0 && nmine > 0) issue_tile(next++);   // x filled all but one slot
 
   const uint32_t mul = kMul;
   const uint64_t add64 = kAdd;
   for (int t = 0; t < nmine; ++t) {
-    const int buf = t & 1;
-    const bool owner = (t & (kWaves - 1)) == wave;
-    const int64_t rg = (int64_t)blockIdx.x + (int64_t)t * gridDim.x;
-    const bool fast_sc = g.scales_aligned && rg * ROWS + ROWS <= R;
-    u32x4 sc0 = u32x4{0u, 0u, 0u, 0u}, sc1 = sc0;
-    if (owner && fast_sc) {                    // the owner's scales, through the scalar cache
-      sc0 = ((ConstV4*)(scales0 + rg * ROWS))[0];
-      if constexpr (GATEUP) sc1 = ((ConstV4*)(scales1 + rg * ROWS))[0];
-      else sc1 = ((ConstV4*)(scales0 + rg * ROWS))[1];
-    }
-    const uint8_t* trow = ring + (size_t)(t % nslots) * g.tile_bytes + (size_t)i * g.gs * 16;
+    wait_vmcnt(nwd * (next - 1 - t));          // tile t has landed (tiles after it may be in flight)
+    const uint8_t* trow = ring + (size_t)(t % NS) * g.slot_bytes + (size_t)i * gsw * 16;
     f32x4 acc[4];
     acc[0] = nbias;
 #pragma unroll
@@ -364,48 +364,22 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
         if (gg + 1 < NG && gg + 1 < ngw) consume(Wb, B[g1]);
       }
     }
-    // partial D tile: lane (n, q) holds rows 4q .. 4q+3 of column n, scaled
-    // back by 2^-e_n (exact) so every wave's part is in the same units
+    // partial D tile of this slice: lane (n, q) holds rows 4q .. 4q+3 of
+    // column n; scaled back by 2^-e_n (exact) into common units
     const f32x4 sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-    f32x4 part;
+    f32x4 pv;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) part[e] = ldexpf(sum[e], -my_e);
-    if (i < M) *reinterpret_cast<f32x4*>(red + ((buf * kWaves + wave) * 4 + i) * 16 + 4 * q) = part;
-    // tile t + 1 has landed (this wave's copies), then everyone's parts
-    wait_vmcnt(last > t + 1 ? nw * (last - t - 1) : 0);
-    lds_barrier();
-    if (t + nslots < nmine) {                  // refill the slot just freed
-      issue_tile(t + nslots);
-      last = t + nslots;
-    }
-    if (owner && oown) {
-      float s0v, s1v;
-      if (fast_sc) {
-        const uint32_t d0 = (GATEUP || orr < 8) ? pick4(sc0, (orr >> 1) & 3) : pick4(sc1, (orr >> 1) & 3);
-        s0v = half_bits_to_f32((orr & 1) ? d0 >> 16 : d0 & 0xFFFFu);
-        const uint32_t d1 = pick4(sc1, (orr >> 1) & 3);
-        s1v = half_bits_to_f32((orr & 1) ? d1 >> 16 : d1 & 0xFFFFu);
-      } else {                                 // ragged last row group, or scales not 4-byte aligned
-        const int64_t orow = rg * ROWS + orr;
-        s0v = orow < R ? half_bits_to_f32(scales0[orow]) : 0.f;
-        s1v = (GATEUP && orow < R) ? half_bits_to_f32(scales1[orow]) : 0.f;
-      }
-      const float* rp = red + (buf * kWaves * 4 + on) * 16;
-      float d0 = 0.f;
-#pragma unroll
-      for (int v = 0; v < kWaves; ++v) d0 += rp[v * 64 + orr];
-      float* ob = obuf + ((size_t)(t * M + on) * ROWS + orr) * NOUT;
-      ob[0] = ldexpf(d0 * (s0v * kRcp), 24);
-      if constexpr (GATEUP) {
-        float d1 = 0.f;
-#pragma unroll
-        for (int v = 0; v < kWaves; ++v) d1 += rp[v * 64 + orr + 8];
-        ob[1] = ldexpf(d1 * (s1v * kRcp), 24);
-      }
-    }
+    for (int e = 0; e < 4; ++e) pv[e] = ldexpf(sum[e], -my_e);
+    if (i < M) *reinterpret_cast<f32x4*>(part + ((size_t)(t * kWaves + wave) * 4 + i) * 16 + 4 * q) = pv;
+    // refill: tiles up to t + NS may use the ring now (slot t is free, and
+    // after this row group the x slots too), at most two per row group
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    const int upto = min(nmine - 1, min(t + NS, next + 1));
+    for (; next <= upto; ++next) issue_tile(next);
   }
 
-  // ---- 6. write the finished rows
+  // ---- 5. one barrier, then every output: the eight slices' partials in a
+  // fixed order, times 2^24 * scale / d, and the epilogue
   lds_barrier();
   const int per_t = M * ROWS;
   for (int idx = tid; idx < nmine * per_t; idx += kThreads) {
@@ -414,9 +388,16 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
     const int64_t orow = ((int64_t)blockIdx.x + (int64_t)t * gridDim.x) * ROWS + row;
     if (orow >= R) continue;
     const int64_t o = (int64_t)m * R + orow;
-    const float v0 = obuf[(size_t)idx * NOUT];
+    const float* pp = part + ((size_t)t * kWaves * 4 + m) * 16 + row;
+    float d0 = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) d0 += pp[w * 64];
+    const float v0 = ldexpf(d0 * (half_bits_to_f32(scales0[orow]) * kRcp), 24);
     if constexpr (GATEUP) {
-      const float v1 = obuf[(size_t)idx * NOUT + 1];
+      float d1 = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) d1 += pp[w * 64 + 8];
+      const float v1 = ldexpf(d1 * (half_bits_to_f32(scales1[orow]) * kRcp), 24);
       if (gate_f32) gate_f32[o] = v0;
       if (up_f32) up_f32[o] = v1;
       const float gT = round_bf16(v0);
@@ -443,12 +424,11 @@ int device_cus() {
   return cus[dev];
 }
 
-// Runs of 32 per wave -> MFMA groups per wave -> the register-resident B
-// capacity instantiated for it (2 or 5 groups: C <= 2048 or C <= 5120); 0 if
-// C is too wide for B to stay in registers.
+// MFMA groups of four runs per wave -> the register-resident B capacity
+// instantiated for it (2 or 5 groups: C <= 2048 or C <= 5120); 0 if C is too
+// wide for B to stay in registers.
 int axis1_ng(int64_t C) {
-  const int64_t nruns = C / 32;
-  const int64_t per = (nruns + kWaves - 1) / kWaves;
+  const int64_t per = C / 256;                 // runs per wave
   const int64_t ngw = (per + 3) / 4;
   return ngw <= 2 ? 2 : ngw <= 5 ? 5 : 0;
 }
@@ -456,29 +436,46 @@ int axis1_ng(int64_t C) {
 // Host geometry; returns false if the shape does not fit (LDS or registers).
 bool axis1_geom(int64_t R, int64_t C, int M, int k, bool gateup, int64_t grid, Axis1Geom& g) {
   const int rows = gateup ? 8 : 16;
+  if (M < 1 || M > 4 || C % 256 != 0 || axis1_ng(C) == 0) return false;
+  const int blk = 256 * k / 8;                 // bytes per block
   g.R = R;
   g.C = C;
   g.M = M;
   g.nrg = (R + rows - 1) / rows;
   g.row_bytes = C * k / 8;
-  g.G = (int)(g.row_bytes / 16);
-  g.gs = g.G + 1;
-  g.ipt = (16 * g.gs + 63) / 64;
-  g.gs_magic = (uint32_t)(((1u << 24) + g.gs - 1) / g.gs);
+  g.per = (int)(C / 256);
+  int nb = 0;                                  // widest wave window in blocks
+  for (int w = 0; w < kWaves; ++w) {
+    const int rb = w * g.per, re = rb + g.per;
+    const int b = ((re - 1) >> 3) - (rb >> 3) + 1;
+    nb = b > nb ? b : nb;
+  }
+  g.gsw = nb * blk / 16 + 1;
+  g.nwd = (16 * g.gsw + 63) / 64;
+  if (g.nwd > kMaxDma) return false;
+  // the kernel's vmcnt arithmetic counts nwd copies per tile per wave: each
+  // of them must have at least one active lane (a real granule of the window)
+  for (int w = 0; w < kWaves; ++w) {
+    const int rb = w * g.per, re = rb + g.per;
+    const int gwr = (((re - 1) >> 3) - (rb >> 3) + 1) * blk / 16;
+    for (int j = 0; j < g.nwd; ++j) {
+      bool any = false;
+      for (int p = j * 64; p < j * 64 + 64 && p < 16 * g.gsw && !any; ++p) any = p % g.gsw < gwr;
+      if (!any) return false;
+    }
+  }
+  g.gsw_magic = (uint32_t)(((1u << 24) + g.gsw - 1) / g.gsw);
   g.nmine_max = (int)((g.nrg + grid - 1) / grid);
-  g.scales_aligned = 1;
-  if (M < 1 || M > 4 || C % 256 != 0 || axis1_ng(C) == 0 || (g.ipt + kWaves - 1) / kWaves > kMaxDma) return false;
-  g.tile_bytes = (uint32_t)((16 * g.gs * 16 + 255) / 256 * 256);
-  const uint64_t obuf = ((uint64_t)g.nmine_max * M * rows * (gateup ? 2 : 1) * 4 + 255) / 256 * 256;
-  const uint64_t fixed = kRedBytes + obuf;
-  if (fixed >= kAxis1MaxLdsBytes) return false;
-  const uint64_t nsl = (kAxis1MaxLdsBytes - fixed) / g.tile_bytes;
+  g.slot_bytes = (uint32_t)((16 * g.gsw * 16 + 255) / 256 * 256);
+  const uint64_t parts = (uint64_t)g.nmine_max * kPartBytes;
+  if (parts >= kAxis1MaxLdsBytes) return false;
+  const uint64_t nsl = (kAxis1MaxLdsBytes - parts) / ((uint64_t)kWaves * g.slot_bytes);
   g.nslots = (int)(nsl < (uint64_t)kMaxSlots ? nsl : kMaxSlots);
-  g.xslots = (int)(((uint64_t)M * C * 2 + g.tile_bytes - 1) / g.tile_bytes);
+  const uint64_t xbytes = (uint64_t)M * g.per * 64;   // one wave's x slice
+  g.xslots = (int)((xbytes + g.slot_bytes - 1) / g.slot_bytes);
   if (g.nslots < 2 || g.nslots < g.xslots + 1) return false;
-  g.red_off = (uint32_t)g.nslots * g.tile_bytes;
-  g.obuf_off = g.red_off + kRedBytes;
-  g.total = (uint32_t)(g.obuf_off + obuf);
+  g.part_off = (uint32_t)kWaves * g.nslots * g.slot_bytes;
+  g.total = (uint32_t)(g.part_off + parts);
   return g.total <= kAxis1MaxLdsBytes;
 }
 
@@ -524,8 +521,6 @@ hipError_t axis1_main(const uint32_t* c0, const uint16_t* s0, const uint32_t* c1
   const int64_t grid = axis1_grid(R, gu);
   Axis1Geom g;
   if (!axis1_geom(R, C, M, K, gu, grid, g)) return hipErrorInvalidValue;
-  const uintptr_t a0 = reinterpret_cast<uintptr_t>(s0), a1 = reinterpret_cast<uintptr_t>(s1);
-  g.scales_aligned = (a0 % 4 == 0) && (!gu || a1 % 4 == 0);
   switch (axis1_ng(C)) {
     case 2: return axis1_dispatch_gu<K, 2>(c0, s0, c1, s1, x, out, out_f32, gf, uf, g, grid, stream);
     case 5: return axis1_dispatch_gu<K, 5>(c0, s0, c1, s1, x, out, out_f32, gf, uf, g, grid, stream);
