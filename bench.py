@@ -6,19 +6,33 @@ k = 2, L = 12, T = 256; one step = one call at each M in 1, 2, 3, 4.  The
 value is packed-code bytes per second over the whole step (inputs resident
 in HBM; code buffers rotate over >= 1 GiB of replicas so the 256 MB
 Infinity Cache cannot serve repeats).  Other workloads (--workload) print
-the same JSON line for their own metric.
+the same JSON line for their own metric: the 512 x 2048 reduce matvec, the
+17408 x 5120 k = 3 down-projection scatter, the k = 4 decoder-layer chain,
+and the 17408 x 5120 prefill at M in {32, 512, 2048} (fused or expand +
+GEMM), plus a plain device copy used as the HBM reference point.
+
+Steps run as HIP graphs (one graph per replica offset, captured after an
+eager warm-up) so the Python call overhead of the binding stays out of the
+measurement, as it would in a serving loop; --eager times the plain calls.
+The prefill expand + GEMM path always runs eagerly (the library GEMM is not
+captured).
 
 The JSON line carries:
   roofline      the dominant kernel's algorithmic bytes (or flops) per launch
                 over its mean launch time (HIP events on the launch stream,
-                every launch of the timed region), against the MI355X peak;
+                every step of the timed region), against the MI355X peak;
+                traffic = HBM bytes per launch from the committed rocprofv3
+                FETCH_SIZE / WRITE_SIZE summary under profiles/, or null when
+                the kernel sources changed since those counters were taken;
   cpu_baseline  the CPU oracle timed on a bounded sample of the same
                 workload on this host (a baseline, not a target).
 """
 import argparse
+import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -30,6 +44,8 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 L, T = 12, 256
 ROTATE_BYTES = 1 << 30
+CSRC = os.path.join(ROOT, "trellis_coded_quantized_amd", "csrc")
+DATA = "synthetic: seeded uniform uint32 codes, fp16 scales U[0.005, 0.02], bf16 x ~ N(0, 1)"
 
 
 def _ensure_built():
@@ -37,6 +53,29 @@ def _ensure_built():
     if not os.path.exists(LIB_PATH) or not os.path.exists(os.path.join(ROOT, "oracle", "liboracle.so")):
         import __graft_entry__
         __graft_entry__.build()
+
+
+def sources_sha256(files):
+    """Digest of the kernel sources a counter summary was taken with."""
+    h = hashlib.sha256()
+    for f in sorted(files):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def committed_traffic(profile, files):
+    """HBM bytes per launch from profiles/<profile>, if its source digest
+    matches the sources built now; None otherwise."""
+    path = os.path.join(ROOT, "profiles", profile)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    sha = re.search(r"^source_sha256:\s*([0-9a-f]{64})", text, re.M)
+    tb = re.search(r"^traffic_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
+    if not sha or not tb or sha.group(1) != sources_sha256(files):
+        return None
+    return float(tb.group(1))
 
 
 def _dev_tensors(np, torch, dev):
@@ -52,279 +91,230 @@ def _dev_tensors(np, torch, dev):
     return codes, half, bf16
 
 
-class EventTimer:
-    """Per-launch HIP event pairs on the current (launch) stream."""
+class Workload:
+    """One benchmark workload.  step(s) enqueues step s (replicas chosen by s)
+    on the current stream; `period` distinct steps repeat."""
+    name = ""
+    unit = "GB/s"
+    bound = "hbm"
+    dtype = "f32"
+    graph = True
+    period = 1
+    kernels_per_step = 1
+    units_per_step = 0.0          # algorithmic bytes (GB/s) or flops (TFLOP/s)
+    kernel = ""
+    profile = None                # profiles/ summary holding the traffic counters
+    profile_sources = ()
+    config = {}
 
-    def __init__(self, torch):
-        self.torch = torch
-        self.pairs = []
+    def step(self, s):
+        raise NotImplementedError
 
-    def __call__(self, fn):
-        t = self.torch
-        a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
-        a.record()
-        fn()
-        b.record()
-        self.pairs.append((a, b))
-
-    def mean_ms(self):
-        self.torch.cuda.synchronize()
-        if not self.pairs:
-            return float("nan")
-        return sum(a.elapsed_time(b) for a, b in self.pairs) / len(self.pairs)
+    def cpu_baseline(self, seconds):
+        return None
 
 
-# ------------------------------------------------------------- workloads
+def _nrep(bytes_per_copy):
+    return max(1, math.ceil(ROTATE_BYTES / bytes_per_copy))
 
-def workload_gateup(args, np, torch, dev):
-    import oracle
-    import trellis_coded_quantized_amd as tq
-    import trellis_inputs as ti
 
-    w = ti.gateup()
-    g, u = w.mats
-    codes, half, bf16 = _dev_tensors(np, torch, dev)
-    code_bytes = g.codes.nbytes + u.codes.nbytes
-    nrep = max(1, math.ceil(ROTATE_BYTES / code_bytes))
-    gcs = [codes(g.codes)]
-    ucs = [codes(u.codes)]
-    for _ in range(nrep - 1):
-        gcs.append(gcs[0].clone())
-        ucs.append(ucs[0].clone())
-    gs, us, x = half(g.scales), half(u.scales), bf16(w.x[0])
-    Ms = (1, 2, 3, 4)
-    outs = {M: torch.empty((M, g.R), dtype=torch.bfloat16, device=dev) for M in Ms}
-    state = {"i": 0}
-    timer = EventTimer(torch)
-    per_m = {M: EventTimer(torch) for M in Ms}
+AXIS1_SOURCES = ("axis1.hip", "mfma_common.hpp", "trellis_device.hpp")
 
-    def call(M):
-        i = state["i"] % nrep
-        state["i"] += 1
-        tq.gateup_swiglu(gcs[i], gs, ucs[i], us, x[:M], g.k, out=outs[M])
 
-    def step(timed):
-        for M in Ms:
-            if timed:
-                timer(lambda: call(M))
-                per_m[M].pairs.append(timer.pairs[-1])
-            else:
-                call(M)
+class GateUp(Workload):
+    def __init__(self, args, np, torch, dev):
+        import trellis_coded_quantized_amd as tq
+        import trellis_inputs as ti
+        self.np, self.tq = np, tq
+        self.w = w = ti.gateup()
+        self.g, self.u = g, u = w.mats
+        codes, half, bf16 = _dev_tensors(np, torch, dev)
+        self.code_bytes = g.codes.nbytes + u.codes.nbytes
+        self.nrep = _nrep(self.code_bytes)
+        self.gcs = [codes(g.codes)]
+        self.ucs = [codes(u.codes)]
+        for _ in range(self.nrep - 1):
+            self.gcs.append(self.gcs[0].clone())
+            self.ucs.append(self.ucs[0].clone())
+        self.gs, self.us, self.x = half(g.scales), half(u.scales), bf16(w.x[0])
+        self.Ms = (1, 2, 3, 4)
+        self.outs = {M: torch.empty((M, g.R), dtype=torch.bfloat16, device=dev) for M in self.Ms}
+        self.period = self.nrep // math.gcd(self.nrep, len(self.Ms))
+        self.kernels_per_step = len(self.Ms)
+        self.units_per_step = len(self.Ms) * self.code_bytes
+        self.name = w.name
+        self.kernel = "axis1_kernel (gate/up + SwiGLU), one launch per M"
+        self.profile = "axis1_gateup_17408x5120_k2.md"
+        self.profile_sources = AXIS1_SOURCES
+        self.config = {"workload": w.name, "M": list(self.Ms), "R": g.R, "C": g.C, "k": g.k, "L": L, "T": T,
+                       "code_bytes_per_call": self.code_bytes, "replicas": self.nrep}
 
-    def cpu_baseline():
-        def run(n):
-            t0 = time.perf_counter()
-            oracle.gateup_swiglu(g.codes, g.scales, u.codes, u.scales, w.x[0], 4, g.R, g.C, g.k, L, T,
-                                 rows=np.arange(n))
-            return time.perf_counter() - t0
-        probe = 32
-        dt = run(probe)
-        n = int(min(g.R, max(probe, probe * args.cpu_seconds / max(dt, 1e-6))))
-        dt = run(n)
-        nbytes = 2 * n * g.codes.shape[1] * 4
+    def step(self, s):
+        for j, M in enumerate(self.Ms):
+            i = (s * len(self.Ms) + j) % self.nrep
+            self.tq.gateup_swiglu(self.gcs[i], self.gs, self.ucs[i], self.us, self.x[:M], self.g.k,
+                                  out=self.outs[M])
+
+    def cpu_baseline(self, seconds):
+        import oracle
+        g, u, w, np = self.g, self.u, self.w, self.np
+        t0 = time.perf_counter()
+        nbytes, passes = 0, 0
+        while True:                            # whole steps (M = 1, 2, 3, 4 over every row)
+            for M in self.Ms:
+                oracle.gateup_swiglu(g.codes, g.scales, u.codes, u.scales, w.x[0], M, g.R, g.C, g.k, L, T)
+                nbytes += self.code_bytes
+            passes += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        dt = time.perf_counter() - t0
         return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
-                "sample": f"gate+up rows 0..{n - 1} of {g.R} at M=4 (all four vectors per pass), "
+                "sample": f"{passes} whole steps (gate+up, all {g.R} rows, M = 1..4), {nbytes} code bytes "
+                          f"in {dt:.2f} s"}
+
+
+class Matvec(Workload):
+    """Calls of the axis-1 / axis-0 matvec entry points, one per matrix, per M."""
+
+    def __init__(self, w, Ms, label, profile, sources, args, np, torch, dev):
+        import trellis_coded_quantized_amd as tq
+        self.np, self.tq, self.w, self.Ms = np, tq, w, Ms
+        codes, half, bf16 = _dev_tensors(np, torch, dev)
+        self.code_bytes = sum(m.codes.nbytes for m in w.mats)
+        self.nrep = _nrep(self.code_bytes)
+        self.reps = [[codes(m.codes) for m in w.mats]]
+        for _ in range(self.nrep - 1):
+            self.reps.append([c.clone() for c in self.reps[0]])
+        self.scs = [half(m.scales) for m in w.mats]
+        self.xs = [bf16(x) for x in w.x]
+        self.outs, self.wss = {}, []
+        lib = tq.load_library()
+        for i, m in enumerate(w.mats):
+            n_out = m.R if m.axis == 1 else m.C
+            for M in Ms:
+                self.outs[(i, M)] = torch.empty((M, n_out), dtype=torch.bfloat16, device=dev)
+            fn = lib.trellis_matvec_axis0_workspace_bytes if m.axis == 0 else lib.trellis_matvec_axis1_workspace_bytes
+            nb = fn(m.R, m.C, max(Ms), m.k, L, T)
+            self.wss.append(torch.empty(max(nb, 256), dtype=torch.uint8, device=dev))
+        self.period = self.nrep // math.gcd(self.nrep, len(Ms))
+        self.kernels_per_step = len(Ms) * len(w.mats)
+        self.units_per_step = len(Ms) * self.code_bytes
+        self.name, self.kernel = w.name, label
+        self.profile, self.profile_sources = profile, sources
+        self.config = {"workload": w.name, "M": list(Ms), "k": w.mats[0].k, "L": L, "T": T,
+                       "matrices": [f"axis{m.axis} {m.R}x{m.C}" for m in w.mats],
+                       "code_bytes_per_call": self.code_bytes, "replicas": self.nrep}
+
+    def step(self, s):
+        for j, M in enumerate(self.Ms):
+            rep = self.reps[(s * len(self.Ms) + j) % self.nrep]
+            for i, m in enumerate(self.w.mats):
+                fn = self.tq.matvec_axis1 if m.axis == 1 else self.tq.matvec_axis0
+                fn(rep[i], self.scs[i], self.xs[i][:M], m.k, out=self.outs[(i, M)], workspace=self.wss[i])
+
+    def cpu_baseline(self, seconds):
+        import oracle
+        np = self.np
+        t0 = time.perf_counter()
+        nbytes, passes = 0, 0
+        while True:                            # whole steps: every matrix, every M
+            for M in self.Ms:
+                for m, x in zip(self.w.mats, self.w.x):
+                    ref = oracle.matvec_axis1 if m.axis == 1 else oracle.matvec_axis0
+                    ref(m.codes, m.scales, x, M, m.R, m.C, m.k, L, T)
+                    nbytes += m.codes.nbytes
+            passes += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        dt = time.perf_counter() - t0
+        return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+                "sample": f"{passes} whole steps ({len(self.w.mats)} matrices x M in {list(self.Ms)}), "
                           f"{nbytes} code bytes in {dt:.2f} s"}
 
-    def report(ms_step):
-        launch_ms = timer.mean_ms()
-        per_launch_bytes = code_bytes
-        achieved = per_launch_bytes / (launch_ms * 1e-3) / 1e9
-        detail = {f"M{M}": {"us_per_call": per_m[M].mean_ms() * 1e3,
-                            "GBps": per_launch_bytes / (per_m[M].mean_ms() * 1e-3) / 1e9} for M in Ms}
-        return {
-            "value": 4 * code_bytes / (ms_step * 1e-3) / 1e9, "unit": "GB/s",
-            "dtype": "f32",
-            "config": {"workload": w.name, "M": list(Ms), "R": g.R, "C": g.C, "k": g.k, "L": L, "T": T,
-                       "code_bytes_per_call": code_bytes, "replicas": nrep},
-            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                         "kernel": "gateup (all M)", "mean_launch_us": launch_ms * 1e3},
-            "detail": detail,
-        }
 
-    return step, cpu_baseline, report
+class Prefill(Workload):
+    unit, bound, dtype = "TFLOP/s", "mfma", "bf16"
 
+    def __init__(self, args, np, torch, dev):
+        import trellis_coded_quantized_amd as tq
+        import trellis_inputs as ti
+        self.np, self.tq = np, tq
+        M = args.m or 2048
+        self.M = M
+        self.w = w = ti.prefill(Ms=(M,))
+        self.m = m = w.mats[0]
+        codes, half, bf16 = _dev_tensors(np, torch, dev)
+        self.dc, self.ds, self.dx = codes(m.codes), half(m.scales), bf16(w.x[0])
+        self.out = torch.empty((M, m.R), dtype=torch.bfloat16, device=dev)
+        self.algo = tq.PREFILL_EXPAND_GEMM if args.algo == "expand_gemm" else tq.PREFILL_FUSED
+        nbytes = tq.prefill_workspace_bytes(m.R, m.C, M, m.k, self.algo)
+        self.ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+        self.graph = self.algo == tq.PREFILL_FUSED
+        self.kernels_per_step = 1 if self.graph else 2
+        self.units_per_step = 2.0 * M * m.R * m.C
+        self.name = w.name
+        self.kernel = "prefill_fused_kernel" if self.graph else "expand_kernel + hipBLASLt GEMM (per call)"
+        self.profile = None
+        self.config = {"workload": w.name, "M": M, "R": m.R, "C": m.C, "k": m.k, "L": L, "T": T,
+                       "algo": args.algo}
 
-def workload_prefill(args, np, torch, dev):
-    import oracle
-    import trellis_coded_quantized_amd as tq
-    import trellis_inputs as ti
+    def step(self, s):
+        self.tq.prefill(self.dc, self.ds, self.dx, self.m.k, algo=self.algo, out=self.out, workspace=self.ws)
 
-    M = args.m or 2048
-    w = ti.prefill(Ms=(M,))
-    m = w.mats[0]
-    codes, half, bf16 = _dev_tensors(np, torch, dev)
-    dc, ds, dx = codes(m.codes), half(m.scales), bf16(w.x[0])
-    out = torch.empty((M, m.R), dtype=torch.bfloat16, device=dev)
-    algo = tq.PREFILL_EXPAND_GEMM if args.algo == "expand_gemm" else tq.PREFILL_FUSED
-    nbytes = tq.prefill_workspace_bytes(m.R, m.C, M, m.k, algo)
-    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
-    timer = EventTimer(torch)
-    flops = 2.0 * M * m.R * m.C
-
-    def call():
-        tq.prefill(dc, ds, dx, m.k, algo=algo, out=out, workspace=ws)
-
-    def step(timed):
-        if timed:
-            timer(call)
-        else:
-            call()
-
-    def cpu_baseline():
+    def cpu_baseline(self, seconds):
+        import oracle
+        np, m, M, w = self.np, self.m, self.M, self.w
         ms = np.arange(M)
+
         def run(n):
             t0 = time.perf_counter()
             oracle.prefill_sums(m.codes, m.scales, w.x[0], M, m.R, m.C, m.k, L, T, ms, np.arange(n))
             return time.perf_counter() - t0
         dt = run(4)
-        n = int(min(m.R, max(4, 4 * args.cpu_seconds / max(dt, 1e-6))))
+        n = int(min(m.R, max(4, 4 * seconds / max(dt, 1e-6))))
         dt = run(n)
         f = 2.0 * M * n * m.C
         return {"value": f / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
                 "sample": f"{n} of {m.R} weight rows at M={M}: {f:.3e} flop in {dt:.2f} s"}
 
-    def report(ms_step):
-        launch_ms = timer.mean_ms()
-        achieved = flops / (launch_ms * 1e-3) / 1e12
-        return {
-            "value": flops / (ms_step * 1e-3) / 1e12, "unit": "TFLOP/s", "dtype": "bf16",
-            "config": {"workload": w.name, "M": M, "R": m.R, "C": m.C, "k": m.k, "L": L, "T": T,
-                       "algo": args.algo},
-            "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None,
-                         "kernel": f"prefill {args.algo}", "mean_launch_us": launch_ms * 1e3},
-        }
 
-    return step, cpu_baseline, report
+class Copy(Workload):
+    """Plain device-to-device copy of 1 GiB: the HBM reference point, and the
+    known-size kernel that calibrates the FETCH_SIZE / WRITE_SIZE counters."""
+    dtype = "u8"
+    graph = False
 
+    def __init__(self, args, np, torch, dev):
+        self.src = torch.empty(ROTATE_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        self.dst = torch.empty_like(self.src)
+        self.units_per_step = 2.0 * ROTATE_BYTES
+        self.name = "device copy"
+        self.kernel = "copy"
+        self.config = {"workload": "device copy", "bytes_read": ROTATE_BYTES, "bytes_written": ROTATE_BYTES}
 
-def _matvec_workload(w, Ms, args, np, torch, dev, label):
-    """Chain of matvec calls (axis 0 or 1) per step, codes rotated over
-    >= 1 GiB of replicas; dominant kernel = the whole call."""
-    import oracle
-    import trellis_coded_quantized_amd as tq
-
-    codes, half, bf16 = _dev_tensors(np, torch, dev)
-    code_bytes = sum(m.codes.nbytes for m in w.mats)
-    nrep = max(1, math.ceil(ROTATE_BYTES / code_bytes))
-    reps = [[codes(m.codes) for m in w.mats]]
-    for _ in range(nrep - 1):
-        reps.append([c.clone() for c in reps[0]])
-    scs = [half(m.scales) for m in w.mats]
-    xs = [bf16(x) for x in w.x]
-    outs = {}
-    wss = []
-    for i, m in enumerate(w.mats):
-        n_out = m.R if m.axis == 1 else m.C
-        for M in Ms:
-            outs[(i, M)] = torch.empty((M, n_out), dtype=torch.bfloat16, device=dev)
-        if m.axis == 0:
-            nb = tq.load_library().trellis_matvec_axis0_workspace_bytes(m.R, m.C, max(Ms), m.k, L, T)
-        else:
-            nb = tq.load_library().trellis_matvec_axis1_workspace_bytes(m.R, m.C, max(Ms), m.k, L, T)
-        wss.append(torch.empty(max(nb, 256), dtype=torch.uint8, device=dev))
-    state = {"i": 0}
-    timer = EventTimer(torch)
-
-    def call(M):
-        rep = reps[state["i"] % nrep]
-        state["i"] += 1
-        for i, m in enumerate(w.mats):
-            fn = tq.matvec_axis1 if m.axis == 1 else tq.matvec_axis0
-            fn(rep[i], scs[i], xs[i][:M], m.k, out=outs[(i, M)], workspace=wss[i])
-
-    def step(timed):
-        for M in Ms:
-            if timed:
-                timer(lambda: call(M))
-            else:
-                call(M)
-
-    def cpu_baseline():
-        m, x = w.mats[0], w.x[0]
-        ref = oracle.matvec_axis1 if m.axis == 1 else oracle.matvec_axis0
-        n_all = m.R if m.axis == 1 else m.C
-        def run(n):
-            t0 = time.perf_counter()
-            sel = np.arange(n)
-            if m.axis == 1:
-                ref(m.codes, m.scales, x, max(Ms), m.R, m.C, m.k, L, T, rows=sel)
-            else:
-                ref(m.codes, m.scales, x, max(Ms), m.R, m.C, m.k, L, T, cols=sel)
-            return time.perf_counter() - t0
-        dt = run(16)
-        n = int(min(n_all, max(16, 16 * args.cpu_seconds / max(dt, 1e-6))))
-        dt = run(n)
-        nbytes = m.codes.nbytes * n // n_all
-        return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
-                "sample": f"{n} of {n_all} outputs of the first matrix at M={max(Ms)}, {dt:.2f} s"}
-
-    def report(ms_step):
-        launch_ms = timer.mean_ms()
-        achieved = code_bytes / (launch_ms * 1e-3) / 1e9
-        return {
-            "value": len(Ms) * code_bytes / (ms_step * 1e-3) / 1e9, "unit": "GB/s", "dtype": "f32",
-            "config": {"workload": w.name, "M": list(Ms), "k": w.mats[0].k, "L": L, "T": T,
-                       "matrices": [f"axis{m.axis} {m.R}x{m.C}" for m in w.mats],
-                       "code_bytes_per_call": code_bytes, "replicas": nrep},
-            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": label,
-                         "mean_launch_us": launch_ms * 1e3},
-        }
-
-    return step, cpu_baseline, report
+    def step(self, s):
+        self.dst.copy_(self.src)
 
 
 def workload_axis0(args, np, torch, dev):
     import trellis_inputs as ti
     Ms = (args.m,) if args.m else (1, 2, 3, 4)
-    return _matvec_workload(ti.axis0(), Ms, args, np, torch, dev, "axis0 scatter + fold")
+    return Matvec(ti.axis0(), Ms, "axis0 scatter + fold", None, ("axis0.hip", "trellis_device.hpp"),
+                  args, np, torch, dev)
 
 
 def workload_layer_chain(args, np, torch, dev):
     import trellis_inputs as ti
-    return _matvec_workload(ti.layer_chain(), (4,), args, np, torch, dev, "4-matrix chain")
+    return Matvec(ti.layer_chain(), (4,), "4-launch chain (3 x axis1_kernel, axis0 scatter + fold)", None,
+                  AXIS1_SOURCES, args, np, torch, dev)
 
 
 def workload_axis1_m1(args, np, torch, dev):
     import trellis_inputs as ti
-    return _matvec_workload(ti.axis1_m1(), (1,), args, np, torch, dev, "axis1 reduce")
+    return Matvec(ti.axis1_m1(), (1,), "axis1_kernel (reduce)", None, AXIS1_SOURCES, args, np, torch, dev)
 
 
-def workload_copy(args, np, torch, dev):
-    """Plain device-to-device copy of 1 GiB: the HBM reference point, and the
-    known-size kernel that calibrates the FETCH_SIZE / WRITE_SIZE counters."""
-    nbytes = ROTATE_BYTES
-    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
-    dst = torch.empty_like(src)
-    timer = EventTimer(torch)
-
-    def step(timed):
-        if timed:
-            timer(lambda: dst.copy_(src))
-        else:
-            dst.copy_(src)
-
-    def cpu_baseline():
-        return None
-
-    def report(ms_step):
-        launch_ms = timer.mean_ms()
-        achieved = 2 * nbytes / (launch_ms * 1e-3) / 1e9
-        return {
-            "value": 2 * nbytes / (ms_step * 1e-3) / 1e9, "unit": "GB/s", "dtype": "u8",
-            "config": {"workload": "device copy", "bytes_read": nbytes, "bytes_written": nbytes},
-            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "copy",
-                         "mean_launch_us": launch_ms * 1e3},
-        }
-
-    return step, cpu_baseline, report
-
-
-WORKLOADS = {"copy": workload_copy, "gateup": workload_gateup, "prefill": workload_prefill, "axis0": workload_axis0,
+WORKLOADS = {"copy": Copy, "gateup": GateUp, "prefill": Prefill, "axis0": workload_axis0,
              "layer_chain": workload_layer_chain, "axis1_m1": workload_axis1_m1}
 
 
@@ -334,14 +324,15 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gateup", choices=sorted(WORKLOADS))
-    ap.add_argument("--m", type=int, default=0, help="prefill rows (default 2048)")
+    ap.add_argument("--m", type=int, default=0, help="prefill rows (default 2048) / axis0 M")
     ap.add_argument("--algo", default="fused", choices=["fused", "expand_gemm"])
+    ap.add_argument("--eager", action="store_true", help="time plain calls instead of graph replays")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} requested; this build measures one GPU only "
-              f"(the path runs on a single MI355X, see the sharding notes in the design).", file=sys.stderr)
+              f"(the path runs on a single MI355X; sharding is described in the design notes).", file=sys.stderr)
         sys.exit(2)
 
     _ensure_built()
@@ -350,31 +341,59 @@ def main():
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    step, cpu_baseline, report = WORKLOADS[args.workload](args, np, torch, dev)
+    wl = WORKLOADS[args.workload](args, np, torch, dev)
     print(f"[bench] {args.workload}: warmup {args.warmup}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        step(False)
+    for s in range(args.warmup):
+        wl.step(s)
     torch.cuda.synchronize()
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    graphs = None
+    if wl.graph and not args.eager:
+        graphs = []
+        for s in range(wl.period):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                wl.step(s)
+            graphs.append(g)
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
+    mode = "graph" if graphs else "eager"
+    print(f"[bench] timing {args.steps} steps ({mode})", file=sys.stderr, flush=True)
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(True)
+    for s in range(args.steps):
+        a, b = events[s]
+        a.record()
+        if graphs:
+            graphs[s % len(graphs)].replay()
+        else:
+            wl.step(s)
+        b.record()
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t0) * 1e3 / max(args.steps, 1)
-    res = report(ms_step)
+    step_ms = sum(a.elapsed_time(b) for a, b in events) / max(args.steps, 1)
+    launch_ms = step_ms / wl.kernels_per_step
+    scale = 1e9 if wl.unit == "GB/s" else 1e12
+    per_launch_units = wl.units_per_step / wl.kernels_per_step
+    achieved = per_launch_units / (launch_ms * 1e-3) / scale
+    peak = HBM_PEAK_GBS if wl.bound == "hbm" else BF16_PEAK_TFLOPS
+    traffic = committed_traffic(wl.profile, wl.profile_sources) if wl.profile else None
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        cpu = cpu_baseline()
+        cpu = wl.cpu_baseline(args.cpu_seconds)
     line = {
-        "metric": METRIC, "value": res["value"], "unit": res["unit"], "n_gpus": 1,
+        "metric": METRIC, "value": wl.units_per_step / (ms_step * 1e-3) / scale, "unit": wl.unit, "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": res["dtype"],
-        "data": "synthetic: seeded uniform uint32 codes, fp16 scales U[0.005, 0.02], bf16 x ~ N(0, 1)",
-        "config": res["config"], "roofline": res["roofline"], "cpu_baseline": cpu,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
+        "data": DATA, "config": dict(wl.config, mode=mode),
+        "roofline": {"bound": wl.bound, "achieved": achieved, "peak": peak,
+                     "unit": "GB/s" if wl.bound == "hbm" else "TFLOP/s", "frac": achieved / peak,
+                     "traffic": traffic, "kernel": wl.kernel, "mean_launch_us": launch_ms * 1e3},
+        "cpu_baseline": cpu,
     }
-    if "detail" in res:
-        line["detail"] = res["detail"]
     print(json.dumps(line), flush=True)
 
 

@@ -1,0 +1,86 @@
+"""HIP graph replay of the matvec entry points (the form bench.py times).
+
+A graph captured around a C-ABI call must reproduce the eager result on
+every replay, with eager work and synchronisations between the replays
+(nothing in the captured launches may depend on state that only the first
+replay sets up).  The kernels are deterministic, so replays are compared bit
+for bit with the eager output of the same call.
+"""
+import numpy as np
+import pytest
+import torch
+
+import trellis_coded_quantized_amd as tq
+import trellis_inputs as ti
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+REPLAYS = 4
+
+
+def _d(a, dtype):
+    view = {torch.int32: np.int32, torch.float16: np.int16, torch.bfloat16: np.int16}[dtype]
+    t = torch.from_numpy(np.ascontiguousarray(a).view(view)).to(DEV)
+    return t.view(dtype)
+
+
+def _check_replays(call, out, disturb):
+    call()
+    torch.cuda.synchronize()
+    want = out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(REPLAYS):
+        out.zero_()
+        disturb()                              # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        bits = torch.int32 if out.dtype == torch.float32 else torch.int16
+        assert torch.equal(out.view(bits), want.view(bits)), f"replay {rep} differs from the eager result"
+
+
+@pytest.mark.parametrize("M", [1, 4])
+def test_graph_gateup(M):
+    rng = np.random.default_rng(71)
+    R, C, k = 1000, 2560, 2
+    gc, gs = ti.codes(rng, R, C, k), ti.scales(rng, R)
+    uc, us = ti.codes(rng, R, C, k), ti.scales(rng, R)
+    x = ti.activations(rng, M, C)
+    dgc, dgs, duc, dus = _d(gc, torch.int32), _d(gs, torch.float16), _d(uc, torch.int32), _d(us, torch.float16)
+    dx = _d(x, torch.bfloat16)
+    out = torch.empty((M, R), dtype=torch.bfloat16, device=DEV)
+    other = torch.empty((M, R), dtype=torch.bfloat16, device=DEV)
+    _check_replays(lambda: tq.gateup_swiglu(dgc, dgs, duc, dus, dx, k, out=out), out,
+                   lambda: tq.gateup_swiglu(duc, dus, dgc, dgs, dx, k, out=other))
+
+
+@pytest.mark.parametrize("k", [2, 4])
+def test_graph_axis1(k):
+    rng = np.random.default_rng(72)
+    R, C, M = 777, 5120, 3
+    c, s = ti.codes(rng, R, C, k), ti.scales(rng, R)
+    x = ti.activations(rng, M, C)
+    dc, ds, dx = _d(c, torch.int32), _d(s, torch.float16), _d(x, torch.bfloat16)
+    out = torch.empty((M, R), dtype=torch.float32, device=DEV)
+    junk = torch.empty((M, R), dtype=torch.float32, device=DEV)
+    _check_replays(lambda: tq.matvec_axis1(dc, ds, dx, k, out_dtype=torch.float32, out=out), out,
+                   lambda: tq.matvec_axis1(dc, ds, dx.flip(0).contiguous(), k, out_dtype=torch.float32, out=junk))
+
+
+def test_graph_axis0():
+    rng = np.random.default_rng(73)
+    R, C, M, k = 3000, 1280, 4, 3
+    c, s = ti.codes(rng, R, C, k), ti.scales(rng, R)
+    x = ti.activations(rng, M, R)
+    dc, ds, dx = _d(c, torch.int32), _d(s, torch.float16), _d(x, torch.bfloat16)
+    lib = tq.load_library()
+    ws = torch.empty(max(lib.trellis_matvec_axis0_workspace_bytes(R, C, M, k, 12, 256), 256),
+                     dtype=torch.uint8, device=DEV)
+    out = torch.empty((M, C), dtype=torch.bfloat16, device=DEV)
+    junk = torch.empty((M, C), dtype=torch.bfloat16, device=DEV)
+    _check_replays(lambda: tq.matvec_axis0(dc, ds, dx, k, out=out, workspace=ws), out,
+                   lambda: (ws.fill_(0x7F), tq.matvec_axis0(dc, ds, dx.flip(0).contiguous(), k, out=junk,
+                                                            workspace=ws)))
