@@ -118,7 +118,7 @@ def _nrep(bytes_per_copy):
     return max(1, math.ceil(ROTATE_BYTES / bytes_per_copy))
 
 
-AXIS1_SOURCES = ("axis1.hip", "mfma_common.hpp", "trellis_device.hpp")
+AXIS1_SOURCES = ("axis1.hip", "copy_ring.hpp", "mfma_common.hpp", "trellis_device.hpp")
 
 
 class GateUp(Workload):
@@ -299,7 +299,7 @@ class Copy(Workload):
 def workload_axis0(args, np, torch, dev):
     import trellis_inputs as ti
     Ms = (args.m,) if args.m else (1, 2, 3, 4)
-    return Matvec(ti.axis0(), Ms, "axis0 scatter + fold", None, ("axis0.hip", "trellis_device.hpp"),
+    return Matvec(ti.axis0(), Ms, "axis0 scatter + fold", None, ("axis0.hip", "copy_ring.hpp", "mfma_common.hpp", "trellis_device.hpp"),
                   args, np, torch, dev)
 
 

@@ -231,6 +231,9 @@ int trellis_matvec_axis0(const uint32_t* codes, const uint16_t* scales, const ui
   TRY(check_ptr(fn, "scales", scales, 2));
   TRY(check_ptr(fn, "x", x, 16));
   TRY(check_ptr(fn, "out", out, 16));
+  if (!trellis::axis0_supported(R_in, C_out, M, k))
+    return fail(TRELLIS_EUNSUPPORTED, "%s: shape R=%lld C=%lld M=%d k=%d does not fit the kernel's LDS plan", fn,
+                (long long)R_in, (long long)C_out, M, k);
   TRY(check_workspace(fn, workspace, workspace_bytes, trellis::axis0_workspace_bytes(R_in, C_out, M, k)));
   return hip_status(fn, trellis::launch_axis0(codes, scales, x, out, out_dtype == TRELLIS_OUT_F32,
                                               R_in, C_out, M, k, workspace, (hipStream_t)stream));

@@ -1,62 +1,256 @@
 // axis0.hip -- axis-0 (down projection) matvec for M <= 4 on gfx950.
 //
-// The stored matrix is W^T [R_in, C_out], coded along C_out.  A thread owns
-// four adjacent output columns of one block (one 64-bit circular window
-// covers their four states) and a split of the stored rows; per row it scales
-// its four weights by the row's scale and FMAs them against the broadcast
-// x[m, r].  Partials [S, M, C_out] in f32 are folded by a second kernel.
+// The stored matrix is W^T [R_in, C_out], coded along C_out; the output is
+// out[m, c] = sum_r w(r, c) x[m, r] with w(r, c) = value(s(r, c)) * scale[r].
 // Source: mlx-bun 0.2.0 -> 0.4.0 diff (page 55), trellis-linear.ts SCATTER
-// kernel comment and #scatter (split-K partials, one sum, cast); page 56,
-// trellis-vector-expand.ts (four weights from one 64-bit window).
+// kernel and #scatter (split-K over the stored rows, one fold, cast to the
+// activation dtype); page 56, trellis-vector-expand.ts (four weights from one
+// window).
+//
+// The sum runs on v_mfma_f32_16x16x32_f16 with the 32 stored rows of a block
+// as the contraction dimension:
+//   A (16 columns x 32 rows): lane (i, q) decodes output columns 4i .. 4i+3
+//     of a 64-column chunk (one 32-bit funnel window holds their four states)
+//     for stored rows 8q .. 8q+7; the byte sum b = y + 510 of each 1MAD word
+//     becomes an f16 subnormal (b * 2^-24, exact), two rows per register via
+//     v_sad_hi_u8 / v_sad_u8.  Column 4i + j of the chunk is row i of MFMA j.
+//   B (32 rows x 16 n): x~[n, r] = scale[r] * x[n, r] (exact in f32) times a
+//     per-workgroup 2^e_n, split into f16 hi (column n) and lo (column 4 + n)
+//     halves, so hi + lo carries ~22 bits of every product operand.
+//   D: f32; 2^-24 * 510 * sum_r x~' is the byte-sum bias, subtracted once.
+// Work: workgroup (column group g of 256 columns, row split s) with 8 waves;
+// wave w takes the split's 32-row blocks w, w + 8, ... through its own LDS
+// ring (global_load_lds copies, explicit vmcnt waits, no barrier in the
+// loop).  The waves' D tiles meet in LDS at the end; the workgroup writes its
+// f32 partial [s][m][c], scaled back by 2^-e_n; a fold kernel adds the splits.
+#include "copy_ring.hpp"
 #include "internal.hpp"
-#include "trellis_device.hpp"
+#include "mfma_common.hpp"
 
 namespace trellis {
 namespace {
 
-template <int K, int M>
-__global__ __launch_bounds__(256) void axis0_partial_kernel(
-    const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scales,
-    const uint16_t* __restrict__ x, float* __restrict__ partial, int64_t R, int64_t C,
-    int64_t rows_per_split) {
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kCols = 256;                // output columns per workgroup (one block)
+constexpr int kChunks = kCols / 64;       // 64-column chunks: four MFMAs each
+constexpr int kMaxSlots = 3;
+constexpr int kMaxDma = 5;                // copies per wave per 32-row tile (k = 4: 32 rows x 9 granules)
+constexpr int kMaxRowsPerSplit = 2048;
+constexpr size_t kLdsBudget = 160 * 1024;
+
+struct Axis0Geom {
+  int64_t R, C;
+  int M, ncg, S, rps;     // column groups, row splits, rows per split (multiple of 32)
+  int64_t row_bytes;
+  int gsr;                // granules per tile row in LDS (the group's block + one pad granule)
+  int nwd;                // copies per wave per tile
+  int nslots;
+  uint32_t slot_bytes, xt_off, scr_off, wmax_off, total;
+};
+
+template <int K>
+__global__ __launch_bounds__(kThreads) void axis0_kernel(const uint32_t* __restrict__ codes,
+                                                         const uint16_t* __restrict__ scales,
+                                                         const uint16_t* __restrict__ x,
+                                                         float* __restrict__ partial, const Axis0Geom g) {
   constexpr int WPB = words_per_block(K);
-  const int64_t c0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (c0 >= C) return;
-  const int split = blockIdx.y;
-  const int blk = (int)(c0 / kT), t0 = (int)(c0 % kT);
-  const int pos = (kT - 1 - (t0 + 3)) * K;     // window start of the last of the four
-  const int wi = pos >> 5, off = pos & 31;
-  const int wn = (wi + 1 == WPB) ? 0 : wi + 1;
-  const int64_t row_words = (C / kT) * WPB;
-  const uint32_t* base = codes + (int64_t)blk * WPB;
-  const int64_t r0 = split * rows_per_split;
-  const int64_t r1 = (r0 + rows_per_split < R) ? r0 + rows_per_split : R;
+  constexpr int BLK = WPB * 4;                 // bytes of one block of a row
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int i = lane & 15, q = lane >> 4;
+  const int M = g.M;
+  const int64_t R = g.R, C = g.C;
+  const int cgi = (int)(blockIdx.x % g.ncg), s = (int)(blockIdx.x / g.ncg);
+  const int64_t r0 = (int64_t)s * g.rps;
+  const int nr = (int)((R - r0 < g.rps) ? R - r0 : g.rps);   // rows of this split (>= 1)
+  const int nblk = (nr + 31) >> 5;
+  const int NS = g.nslots, nwd = g.nwd, gsr = g.gsr;
+  uint8_t* ring = smem + (size_t)wave * NS * g.slot_bytes;
+  uint16_t* xt = reinterpret_cast<uint16_t*>(smem + g.xt_off);        // f16 [8][rps]: hi n, lo n
+  float* scr = reinterpret_cast<float*>(smem + g.scr_off);            // x~ f32 [M][rps], later D tiles
+  uint32_t* wmax = reinterpret_cast<uint32_t*>(smem + g.wmax_off);    // [wave][4]
 
-  float acc[4][M];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int m = 0; m < M; ++m) acc[i][m] = 0.0f;
-
-  for (int64_t r = r0; r < r1; ++r) {
-    const uint32_t* bw = base + r * row_words;
-    const uint64_t win = ((uint64_t)bw[wn] << 32 | bw[wi]) >> off;
-    const float sc = half_bits_to_f32(scales[r]);
-    float xr[M];
-#pragma unroll
-    for (int m = 0; m < M; ++m) xr[m] = bf16_bits_to_f32(x[(int64_t)m * R + r]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t s = (uint32_t)(win >> ((3 - i) * K)) & kStateMask;
-      const float w = code_value(code_y(s)) * sc;
-#pragma unroll
-      for (int m = 0; m < M; ++m) acc[i][m] = __builtin_fmaf(w, xr[m], acc[i][m]);
-    }
+  // ---- 1. x~[n, r] = scale[r] * x[n, r] (exact in f32) for the split's rows
+  uint32_t mx0 = 0u, mx1 = 0u, mx2 = 0u, mx3 = 0u;
+  for (int idx = tid; idx < M * nr; idx += kThreads) {
+    const int n = idx / nr, r = idx - n * nr;
+    const float v = bf16_bits_to_f32(x[(int64_t)n * R + r0 + r]) * half_bits_to_f32(scales[r0 + r]);
+    scr[n * g.rps + r] = v;
+    const uint32_t a = __float_as_uint(v) & 0x7FFFFFFFu;
+    mx0 = n == 0 ? max(mx0, a) : mx0;
+    mx1 = n == 1 ? max(mx1, a) : mx1;
+    mx2 = n == 2 ? max(mx2, a) : mx2;
+    mx3 = n == 3 ? max(mx3, a) : mx3;
   }
+
+  // ---- 2. copy descriptors: tile granule p = 64 j + lane is granule p % gsr
+  // of tile row p / gsr (the last granule of a row is pad).  Then the first tiles.
+  const int nmy = nblk > wave ? (nblk - 1 - wave) / kWaves + 1 : 0;   // this wave's 32-row blocks
+  uint32_t dd[kMaxDma];
 #pragma unroll
-  for (int m = 0; m < M; ++m) {
-    float4 v = make_float4(acc[0][m], acc[1][m], acc[2][m], acc[3][m]);
-    *reinterpret_cast<float4*>(partial + ((int64_t)split * M + m) * C + c0) = v;
+  for (int j = 0; j < kMaxDma; ++j) {
+    const int p = j * 64 + lane;
+    const int rr = p / gsr, gg = p - rr * gsr;
+    dd[j] = (j < nwd && p < 32 * gsr && gg < gsr - 1) ? (1u << 31) | ((uint32_t)rr << 16) | (uint32_t)(gg * 16) : 0u;
+  }
+  const uint8_t* cb = reinterpret_cast<const uint8_t*>(codes) + (int64_t)cgi * BLK;
+  auto issue_tile = [&](int t) {             // t-th block of this wave
+    const int64_t rowb = r0 + (int64_t)(wave + kWaves * t) * 32;
+    uint8_t* slot = ring + (size_t)(t % NS) * g.slot_bytes;
+#pragma unroll
+    for (int j = 0; j < kMaxDma; ++j) {
+      if (j < nwd) {                           // every issued copy has an active lane
+        const uint32_t d = dd[j];
+        if (d >> 31) {
+          int64_t row = rowb + ((d >> 16) & 31u);
+          row = row < R ? row : R - 1;         // rows past R read row R - 1 (their x~ is zero)
+          __builtin_amdgcn_global_load_lds(cb + row * g.row_bytes + (d & 0xFFFFu), slot + (size_t)j * 1024,
+                                           16, 0, 0);
+        }
+      }
+    }
+  };
+  int next = 0;
+  for (; next < min(nmy, NS); ++next) issue_tile(next);
+
+  // ---- 3. exponent e_n of the workgroup: its largest |x~[n]| * 2^e lands in [2^14, 2^15)
+  mx0 = wave_max_u32(mx0);
+  mx1 = wave_max_u32(mx1);
+  mx2 = wave_max_u32(mx2);
+  mx3 = wave_max_u32(mx3);
+  if (lane == 0) {
+    wmax[wave * 4 + 0] = mx0;
+    wmax[wave * 4 + 1] = mx1;
+    wmax[wave * 4 + 2] = mx2;
+    wmax[wave * 4 + 3] = mx3;
+  }
+  lds_barrier();
+  auto exponent = [&](int n) {
+    uint32_t v = 0u;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) v = max(v, wmax[w * 4 + n]);
+    int e = 0;
+    if (v != 0u && v < 0x7F800000u) {          // finite, non-zero maximum
+      int ex;
+      frexpf(__uint_as_float(v), &ex);         // max in [2^(ex-1), 2^ex)
+      e = 15 - ex;
+    }
+    return e;
+  };
+  const int e0 = exponent(0), e1 = exponent(1), e2 = exponent(2), e3 = exponent(3);
+  // hi = f16(x~ 2^e), lo = f16(x~ 2^e - hi); rows past the split and vectors
+  // past M stay zero
+  for (int idx = tid; idx < 4 * g.rps; idx += kThreads) {
+    const int n = idx / g.rps, r = idx - n * g.rps;
+    const int en = n == 0 ? e0 : n == 1 ? e1 : n == 2 ? e2 : e3;
+    const float v = (n < M && r < nr) ? ldexpf(scr[n * g.rps + r], en) : 0.f;
+    const _Float16 hi = (_Float16)v;
+    const _Float16 lo = (_Float16)(v - (float)hi);
+    xt[n * g.rps + r] = __builtin_bit_cast(uint16_t, hi);
+    xt[(4 + n) * g.rps + r] = __builtin_bit_cast(uint16_t, lo);
+  }
+  lds_barrier();
+
+  // ---- 4. per-lane decode geometry for the four chunks: the 32-bit window
+  // of columns 4i .. 4i+3 starts at bit (252 - t) k of the block (t = the
+  // chunk offset + 4i), in words wi and wn (wrapping within the block)
+  int wia[kChunks], wna[kChunks], offa[kChunks];
+#pragma unroll
+  for (int ch = 0; ch < kChunks; ++ch) {
+    const int t = ch * 64 + 4 * i;
+    const int p0 = (252 - t) * K;
+    wia[ch] = p0 >> 5;
+    wna[ch] = (wia[ch] + 1 == WPB) ? 0 : wia[ch] + 1;
+    offa[ch] = p0 & 31;
+  }
+  // B of a 32-row block: lane (n', q) holds xt[n'][8q .. 8q+7] (n' < 8), zero otherwise
+  auto load_b = [&](int blk) {
+    const int nn = i < 8 ? i : 0;
+    const half8 v = *reinterpret_cast<const half8*>(xt + nn * g.rps + blk * 32 + 8 * q);
+    return i < 8 ? v : half8{0, 0, 0, 0, 0, 0, 0, 0};
+  };
+  // the byte-sum bias over this wave's blocks: 510 * 2^-24 * sum_r B[r][n'] in every row
+  f32x4 bias = f32x4{0.f, 0.f, 0.f, 0.f};
+  const half8 a510 = __builtin_bit_cast(half8, u32x4{0x01FE01FEu, 0x01FE01FEu, 0x01FE01FEu, 0x01FE01FEu});
+  for (int t = 0; t < nmy; ++t) bias = __builtin_amdgcn_mfma_f32_16x16x32_f16(a510, load_b(wave + kWaves * t), bias, 0, 0, 0);
+
+  f32x4 acc[kChunks][4];
+#pragma unroll
+  for (int ch = 0; ch < kChunks; ++ch)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[ch][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const uint32_t mul = kMul;
+  const uint64_t add64 = kAdd;
+  for (int t = 0; t < nmy; ++t) {
+    wait_vmcnt(nwd * (next - 1 - t));          // tile t has landed
+    const int blk = wave + kWaves * t;
+    const half8 Bv = load_b(blk);
+    const uint8_t* tile = ring + (size_t)(t % NS) * g.slot_bytes + (size_t)(8 * q) * gsr * 16;
+#pragma unroll
+    for (int ch = 0; ch < kChunks; ++ch) {
+      // 8 rows x 4 columns: windows, then 1MAD words, then row-paired byte sums
+      uint32_t st[8][4];
+#pragma unroll
+      for (int rr = 0; rr < 8; ++rr) {
+        const uint32_t* rowp = reinterpret_cast<const uint32_t*>(tile + (size_t)rr * gsr * 16);
+        const uint32_t v = __builtin_amdgcn_alignbit(rowp[wna[ch]], rowp[wia[ch]], offa[ch]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) st[rr][j] = __builtin_amdgcn_ubfe(v, (3 - j) * K, kL);
+      }
+      uint32_t xw[8][4];
+#pragma unroll
+      for (int rr = 0; rr < 8; ++rr)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xw[rr][j] = onemad_word_mad64(st[rr][j], mul, add64);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u32x4 A;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          A[e] = __builtin_amdgcn_sad_u8(xw[2 * e][j], 0u, __builtin_amdgcn_sad_hi_u8(xw[2 * e + 1][j], 0u, 0u));
+        acc[ch][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, A), Bv, acc[ch][j], 0, 0, 0);
+      }
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);   // this tile's reads stay before its slot is refilled
+    if (next < nmy && next <= t + NS) issue_tile(next++);
+  }
+
+  // ---- 5. hi + lo, minus the bias, into LDS; the waves' tiles are added in a
+  // fixed order and scaled by 2^24 / d * 2^-e_n into the partial of this split
+  lds_barrier();                               // every wave is done with the x~ scratch
+  float* red = scr;                            // f32 [wave][M][kCols]
+#pragma unroll
+  for (int ch = 0; ch < kChunks; ++ch)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 d = acc[ch][j] - bias;
+      f32x4 tot;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {            // lane n (< 4) adds lane n + 4 (the lo column)
+        const float de = d[e];                 // by value: bit casts of vector-element lvalues read element 0
+        tot[e] = de + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(de), 0x104, 0xF, 0xF, false));
+      }
+      if (i < M) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int col = ch * 64 + 4 * (4 * q + e) + j;   // MFMA row 4q + e of chunk ch, MFMA j
+          red[(wave * M + i) * kCols + col] = tot[e];
+        }
+      }
+    }
+  lds_barrier();
+  for (int idx = tid; idx < M * kCols; idx += kThreads) {
+    const int n = idx / kCols, col = idx - n * kCols;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) v += red[(w * M + n) * kCols + col];
+    const int en = n == 0 ? e0 : n == 1 ? e1 : n == 2 ? e2 : e3;
+    partial[((int64_t)s * M + n) * C + (int64_t)cgi * kCols + col] = ldexpf(v * kRcp, 24 - en);
   }
 }
 
@@ -65,64 +259,109 @@ __global__ __launch_bounds__(256) void axis0_fold_kernel(const float* __restrict
                                                          int M, int64_t C, int S) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;   // over M * C
   if (i >= (int64_t)M * C) return;
-  const int64_t m = i / C, c = i % C;
   float s = 0.0f;
-  for (int j = 0; j < S; ++j) s += partial[((int64_t)j * M + m) * C + c];
+  for (int j = 0; j < S; ++j) s += partial[(int64_t)j * M * C + i];
   if (out_f32) reinterpret_cast<float*>(out)[i] = s;
   else reinterpret_cast<uint16_t*>(out)[i] = f32_to_bf16_bits(s);
 }
 
-int axis0_splits(int64_t R) {
-  int64_t s = R / 64;
-  if (s < 1) s = 1;
-  if (s > 128) s = 128;
-  return (int)s;
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cus[dev] = v;
+  }
+  return cus[dev];
+}
+
+// Host geometry; false if the shape does not fit.
+bool axis0_geom(int64_t R, int64_t C, int M, int k, Axis0Geom& g) {
+  if (M < 1 || M > 4 || C % kCols != 0) return false;
+  const int blk = 256 * k / 8;
+  g.R = R;
+  g.C = C;
+  g.M = M;
+  g.ncg = (int)(C / kCols);
+  int S = device_cus() / g.ncg;
+  if (S < 1) S = 1;
+  int64_t rps = (R + S - 1) / S;
+  rps = (rps + 31) / 32 * 32;
+  if (rps > kMaxRowsPerSplit) rps = kMaxRowsPerSplit;
+  g.rps = (int)rps;
+  g.S = (int)((R + rps - 1) / rps);
+  g.row_bytes = C * k / 8;
+  g.gsr = blk / 16 + 1;
+  g.nwd = (32 * g.gsr + 63) / 64;
+  if (g.nwd > kMaxDma) return false;
+  g.slot_bytes = (uint32_t)((32 * g.gsr * 16 + 255) / 256 * 256);
+  const size_t xt = (size_t)8 * g.rps * 2;
+  size_t scr = (size_t)M * g.rps * 4;
+  const size_t red = (size_t)kWaves * M * kCols * 4;
+  if (red > scr) scr = red;
+  const size_t fixed = ((xt + 255) / 256 + (scr + 255) / 256) * 256 + 256;
+  if (fixed >= kLdsBudget) return false;
+  size_t ns = (kLdsBudget - fixed) / ((size_t)kWaves * g.slot_bytes);
+  if (ns > (size_t)kMaxSlots) ns = kMaxSlots;
+  if (ns < 2) return false;
+  g.nslots = (int)ns;
+  g.xt_off = (uint32_t)kWaves * g.nslots * g.slot_bytes;
+  g.scr_off = g.xt_off + (uint32_t)((xt + 255) / 256 * 256);
+  g.wmax_off = g.scr_off + (uint32_t)((scr + 255) / 256 * 256);
+  g.total = g.wmax_off + 256;
+  return g.total <= kLdsBudget;
 }
 
 template <int K>
-hipError_t axis0_dispatch_m(const uint32_t* codes, const uint16_t* scales, const uint16_t* x,
-                            float* partial, int64_t R, int64_t C, int M, int S,
-                            hipStream_t stream) {
-  const int64_t rows_per_split = (R + S - 1) / S;
-  const dim3 grid((unsigned)((C / 4 + 255) / 256), (unsigned)S), block(256);
-#define TRELLIS_AXIS0_CASE(MM)                                                                 \
-  case MM:                                                                                      \
-    hipLaunchKernelGGL((axis0_partial_kernel<K, MM>), grid, block, 0, stream, codes, scales, x, \
-                       partial, R, C, rows_per_split);                                          \
-    break;
-  switch (M) {
-    TRELLIS_AXIS0_CASE(1)
-    TRELLIS_AXIS0_CASE(2)
-    TRELLIS_AXIS0_CASE(3)
-    TRELLIS_AXIS0_CASE(4)
-    default: return hipErrorInvalidValue;
+hipError_t axis0_launch(const uint32_t* codes, const uint16_t* scales, const uint16_t* x, float* partial,
+                        const Axis0Geom& g, hipStream_t stream) {
+  static uint64_t lds_attr = 0;                // devices whose dynamic LDS limit is raised
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+  const uint64_t bit = 1ull << (dev & 63);
+  if (!(lds_attr & bit)) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&axis0_kernel<K>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBudget);
+    if (e != hipSuccess) return e;
+    lds_attr |= bit;
   }
-#undef TRELLIS_AXIS0_CASE
+  hipLaunchKernelGGL((axis0_kernel<K>), dim3((unsigned)(g.ncg * g.S)), dim3(kThreads), g.total, stream, codes,
+                     scales, x, partial, g);
   return hipGetLastError();
 }
 
 }  // namespace
 
-size_t axis0_workspace_bytes(int64_t R, int64_t C, int M, int) {
-  return (size_t)axis0_splits(R) * (size_t)M * (size_t)C * sizeof(float);
+bool axis0_supported(int64_t R, int64_t C, int M, int k) {
+  Axis0Geom g;
+  return axis0_geom(R, C, M, k, g);
+}
+
+size_t axis0_workspace_bytes(int64_t R, int64_t C, int M, int k) {
+  Axis0Geom g;
+  if (!axis0_geom(R, C, M, k, g)) return 0;
+  return (size_t)g.S * (size_t)M * (size_t)C * sizeof(float);
 }
 
 hipError_t launch_axis0(const uint32_t* codes, const uint16_t* scales, const uint16_t* x,
                         void* out, int out_f32, int64_t R, int64_t C, int M, int k,
                         void* workspace, hipStream_t stream) {
-  const int S = axis0_splits(R);
+  Axis0Geom g;
+  if (!axis0_geom(R, C, M, k, g)) return hipErrorInvalidValue;
   float* partial = reinterpret_cast<float*>(workspace);
   hipError_t e;
   switch (k) {
-    case 2: e = axis0_dispatch_m<2>(codes, scales, x, partial, R, C, M, S, stream); break;
-    case 3: e = axis0_dispatch_m<3>(codes, scales, x, partial, R, C, M, S, stream); break;
-    case 4: e = axis0_dispatch_m<4>(codes, scales, x, partial, R, C, M, S, stream); break;
+    case 2: e = axis0_launch<2>(codes, scales, x, partial, g, stream); break;
+    case 3: e = axis0_launch<3>(codes, scales, x, partial, g, stream); break;
+    case 4: e = axis0_launch<4>(codes, scales, x, partial, g, stream); break;
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
   const int64_t n = (int64_t)M * C;
   hipLaunchKernelGGL(axis0_fold_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
-                     partial, out, out_f32, M, C, S);
+                     partial, out, out_f32, M, C, g.S);
   return hipGetLastError();
 }
 

@@ -20,7 +20,8 @@ hipError_t launch_axis1(const uint32_t* codes0, const uint16_t* scales0, const u
                         float* gate_f32, float* up_f32, int64_t R, int64_t C, int M, int k,
                         void* workspace, hipStream_t stream);
 
-// axis 0
+// axis 0 (split-K over stored rows, MFMA on 32-row blocks, then a fold)
+bool axis0_supported(int64_t R, int64_t C, int M, int k);
 size_t axis0_workspace_bytes(int64_t R, int64_t C, int M, int k);
 hipError_t launch_axis0(const uint32_t* codes, const uint16_t* scales, const uint16_t* x,
                         void* out, int out_f32, int64_t R, int64_t C, int M, int k,
