@@ -48,7 +48,9 @@ struct Axis0Geom {
   int gsr;                // granules per tile row in LDS (the group's block + one pad granule)
   int nwd;                // copies per wave per tile
   int nslots;
-  uint32_t slot_bytes, xt_off, scr_off, wmax_off, total;
+  int scales16;           // scales 16-byte aligned: 16-byte loads in the prologue
+  int x16;                // every row of x 16-byte aligned (x aligned, R % 8 == 0)
+  uint32_t slot_bytes, xt_off, scr_off, total;
 };
 
 template <int K>
@@ -71,21 +73,7 @@ __global__ __launch_bounds__(kThreads) void axis0_kernel(const uint32_t* __restr
   const int NS = g.nslots, nwd = g.nwd, gsr = g.gsr;
   uint8_t* ring = smem + (size_t)wave * NS * g.slot_bytes;
   uint16_t* xt = reinterpret_cast<uint16_t*>(smem + g.xt_off);        // f16 [8][rps]: hi n, lo n
-  float* scr = reinterpret_cast<float*>(smem + g.scr_off);            // x~ f32 [M][rps], later D tiles
-  uint32_t* wmax = reinterpret_cast<uint32_t*>(smem + g.wmax_off);    // [wave][4]
-
-  // ---- 1. x~[n, r] = scale[r] * x[n, r] (exact in f32) for the split's rows
-  uint32_t mx0 = 0u, mx1 = 0u, mx2 = 0u, mx3 = 0u;
-  for (int idx = tid; idx < M * nr; idx += kThreads) {
-    const int n = idx / nr, r = idx - n * nr;
-    const float v = bf16_bits_to_f32(x[(int64_t)n * R + r0 + r]) * half_bits_to_f32(scales[r0 + r]);
-    scr[n * g.rps + r] = v;
-    const uint32_t a = __float_as_uint(v) & 0x7FFFFFFFu;
-    mx0 = n == 0 ? max(mx0, a) : mx0;
-    mx1 = n == 1 ? max(mx1, a) : mx1;
-    mx2 = n == 2 ? max(mx2, a) : mx2;
-    mx3 = n == 3 ? max(mx3, a) : mx3;
-  }
+  float* scr = reinterpret_cast<float*>(smem + g.scr_off);            // the waves' D tiles at the end
 
   // ---- 2. copy descriptors: tile granule p = 64 j + lane is granule p % gsr
   // of tile row p / gsr (the last granule of a row is pad).  Then the first tiles.
@@ -117,22 +105,63 @@ __global__ __launch_bounds__(kThreads) void axis0_kernel(const uint32_t* __restr
   int next = 0;
   for (; next < min(nmy, NS); ++next) issue_tile(next);
 
-  // ---- 3. exponent e_n of the workgroup: its largest |x~[n]| * 2^e lands in [2^14, 2^15)
+  // ---- 3. x~[n, r] = scale[r] * x[n, r] (exact in f32) for this wave's rows:
+  // lane (t, g) of the wave holds rows 8g .. 8g+7 of its t-th block, loaded
+  // 16 bytes at a time.  The wave's largest |x~[n]| * 2^e lands in
+  // [2^14, 2^15); x~ 2^e is split into f16 hi and lo halves in xt, and the
+  // wave's partial sums are scaled back by 2^-e at the end.
+  const int tb = lane >> 2, g8 = lane & 3;
+  const bool hold = tb < nmy;
+  const int rl = (wave + kWaves * tb) * 32 + 8 * g8;   // first row of the lane's eight, in the split
+  float xv[4][8];
+  uint32_t mx0 = 0u, mx1 = 0u, mx2 = 0u, mx3 = 0u;
+  {
+    uint4 xb[4];
+    uint16_t sb[8];
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+      xb[n] = (g.x16 && hold && n < M && rl + 8 <= nr)
+                  ? *reinterpret_cast<const uint4*>(x + (int64_t)n * R + r0 + rl)
+                  : make_uint4(0u, 0u, 0u, 0u);
+    if (g.scales16 && hold && rl + 8 <= nr) {
+      const uint4 v = *reinterpret_cast<const uint4*>(scales + r0 + rl);
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int h = 0; h < 8; ++h) sb[h] = (uint16_t)(w4[h >> 1] >> (16 * (h & 1)));
+    } else {
+#pragma unroll
+      for (int h = 0; h < 8; ++h) sb[h] = (hold && rl + h < nr) ? scales[r0 + rl + h] : (uint16_t)0;
+    }
+    if (hold && (!g.x16 || rl + 8 > nr)) {     // rows not 16-byte aligned, or the split's ragged last eight
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        uint32_t w4[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int h = 0; h < 8; ++h)
+          if (n < M && rl + h < nr) w4[h >> 1] |= (uint32_t)x[(int64_t)n * R + r0 + rl + h] << (16 * (h & 1));
+        xb[n] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+      }
+    }
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const uint32_t w4[4] = {xb[n].x, xb[n].y, xb[n].z, xb[n].w};
+      uint32_t m = 0u;
+#pragma unroll
+      for (int h = 0; h < 8; ++h) {
+        xv[n][h] = bf16_bits_to_f32((w4[h >> 1] >> (16 * (h & 1))) & 0xFFFFu) * half_bits_to_f32(sb[h]);
+        m = max(m, __float_as_uint(xv[n][h]) & 0x7FFFFFFFu);
+      }
+      if (n == 0) mx0 = m;
+      if (n == 1) mx1 = m;
+      if (n == 2) mx2 = m;
+      if (n == 3) mx3 = m;
+    }
+  }
   mx0 = wave_max_u32(mx0);
   mx1 = wave_max_u32(mx1);
   mx2 = wave_max_u32(mx2);
   mx3 = wave_max_u32(mx3);
-  if (lane == 0) {
-    wmax[wave * 4 + 0] = mx0;
-    wmax[wave * 4 + 1] = mx1;
-    wmax[wave * 4 + 2] = mx2;
-    wmax[wave * 4 + 3] = mx3;
-  }
-  lds_barrier();
-  auto exponent = [&](int n) {
-    uint32_t v = 0u;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) v = max(v, wmax[w * 4 + n]);
+  auto exponent = [](uint32_t v) {
     int e = 0;
     if (v != 0u && v < 0x7F800000u) {          // finite, non-zero maximum
       int ex;
@@ -141,19 +170,24 @@ __global__ __launch_bounds__(kThreads) void axis0_kernel(const uint32_t* __restr
     }
     return e;
   };
-  const int e0 = exponent(0), e1 = exponent(1), e2 = exponent(2), e3 = exponent(3);
-  // hi = f16(x~ 2^e), lo = f16(x~ 2^e - hi); rows past the split and vectors
-  // past M stay zero
-  for (int idx = tid; idx < 4 * g.rps; idx += kThreads) {
-    const int n = idx / g.rps, r = idx - n * g.rps;
-    const int en = n == 0 ? e0 : n == 1 ? e1 : n == 2 ? e2 : e3;
-    const float v = (n < M && r < nr) ? ldexpf(scr[n * g.rps + r], en) : 0.f;
-    const _Float16 hi = (_Float16)v;
-    const _Float16 lo = (_Float16)(v - (float)hi);
-    xt[n * g.rps + r] = __builtin_bit_cast(uint16_t, hi);
-    xt[(4 + n) * g.rps + r] = __builtin_bit_cast(uint16_t, lo);
+  const int e0 = exponent(mx0), e1 = exponent(mx1), e2 = exponent(mx2), e3 = exponent(mx3);
+  if (hold) {
+    const int ev[4] = {e0, e1, e2, e3};
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int h = 0; h < 8; h += 2) {
+        const float v0 = ldexpf(xv[n][h], ev[n]), v1 = ldexpf(xv[n][h + 1], ev[n]);
+        const _Float16 h0 = (_Float16)v0, h1 = (_Float16)v1;
+        const _Float16 l0 = (_Float16)(v0 - (float)h0), l1 = (_Float16)(v1 - (float)h1);
+        hw[h >> 1] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+        lw[h >> 1] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+      }
+      *reinterpret_cast<uint4*>(xt + n * g.rps + rl) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      *reinterpret_cast<uint4*>(xt + (4 + n) * g.rps + rl) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    }
   }
-  lds_barrier();
 
   // ---- 4. per-lane decode geometry for the four chunks: the 32-bit window
   // of columns 4i .. 4i+3 starts at bit (252 - t) k of the block (t = the
@@ -178,6 +212,7 @@ __global__ __launch_bounds__(kThreads) void axis0_kernel(const uint32_t* __restr
   const half8 a510 = __builtin_bit_cast(half8, u32x4{0x01FE01FEu, 0x01FE01FEu, 0x01FE01FEu, 0x01FE01FEu});
   for (int t = 0; t < nmy; ++t) bias = __builtin_amdgcn_mfma_f32_16x16x32_f16(a510, load_b(wave + kWaves * t), bias, 0, 0, 0);
 
+  const int my_e = i == 0 ? e0 : i == 1 ? e1 : i == 2 ? e2 : e3;   // partial-sum scale of column n = i
   f32x4 acc[kChunks][4];
 #pragma unroll
   for (int ch = 0; ch < kChunks; ++ch)
@@ -191,14 +226,21 @@ __global__ __launch_bounds__(kThreads) void axis0_kernel(const uint32_t* __restr
     const int blk = wave + kWaves * t;
     const half8 Bv = load_b(blk);
     const uint8_t* tile = ring + (size_t)(t % NS) * g.slot_bytes + (size_t)(8 * q) * gsr * 16;
-#pragma unroll
-    for (int ch = 0; ch < kChunks; ++ch) {
-      // 8 rows x 4 columns: windows, then 1MAD words, then row-paired byte sums
-      uint32_t st[8][4];
+    // the words of chunk ch for rows 8q .. 8q+7 (read one chunk ahead of the decode)
+    auto load_chunk = [&](int ch, uint32_t (&W)[8][2]) {
 #pragma unroll
       for (int rr = 0; rr < 8; ++rr) {
         const uint32_t* rowp = reinterpret_cast<const uint32_t*>(tile + (size_t)rr * gsr * 16);
-        const uint32_t v = __builtin_amdgcn_alignbit(rowp[wna[ch]], rowp[wia[ch]], offa[ch]);
+        W[rr][0] = rowp[wia[ch]];
+        W[rr][1] = rowp[wna[ch]];
+      }
+    };
+    // 8 rows x 4 columns: windows, then 1MAD words, then row-paired byte sums
+    auto decode_chunk = [&](int ch, const uint32_t (&W)[8][2]) {
+      uint32_t st[8][4];
+#pragma unroll
+      for (int rr = 0; rr < 8; ++rr) {
+        const uint32_t v = __builtin_amdgcn_alignbit(W[rr][1], W[rr][0], offa[ch]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) st[rr][j] = __builtin_amdgcn_ubfe(v, (3 - j) * K, kL);
       }
@@ -215,6 +257,15 @@ __global__ __launch_bounds__(kThreads) void axis0_kernel(const uint32_t* __restr
           A[e] = __builtin_amdgcn_sad_u8(xw[2 * e][j], 0u, __builtin_amdgcn_sad_hi_u8(xw[2 * e + 1][j], 0u, 0u));
         acc[ch][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, A), Bv, acc[ch][j], 0, 0, 0);
       }
+    };
+    uint32_t Wa[8][2], Wb[8][2];
+    load_chunk(0, Wa);
+#pragma unroll
+    for (int ch = 0; ch < kChunks; ch += 2) {
+      load_chunk(ch + 1, Wb);
+      decode_chunk(ch, Wa);
+      if (ch + 2 < kChunks) load_chunk(ch + 2, Wa);
+      decode_chunk(ch + 1, Wb);
     }
     __atomic_signal_fence(__ATOMIC_SEQ_CST);   // this tile's reads stay before its slot is refilled
     if (next < nmy && next <= t + NS) issue_tile(next++);
@@ -222,7 +273,6 @@ __global__ __launch_bounds__(kThreads) void axis0_kernel(const uint32_t* __restr
 
   // ---- 5. hi + lo, minus the bias, into LDS; the waves' tiles are added in a
   // fixed order and scaled by 2^24 / d * 2^-e_n into the partial of this split
-  lds_barrier();                               // every wave is done with the x~ scratch
   float* red = scr;                            // f32 [wave][M][kCols]
 #pragma unroll
   for (int ch = 0; ch < kChunks; ++ch)
@@ -239,7 +289,7 @@ __global__ __launch_bounds__(kThreads) void axis0_kernel(const uint32_t* __restr
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int col = ch * 64 + 4 * (4 * q + e) + j;   // MFMA row 4q + e of chunk ch, MFMA j
-          red[(wave * M + i) * kCols + col] = tot[e];
+          red[(wave * M + i) * kCols + col] = ldexpf(tot[e], -my_e);   // exact: common units
         }
       }
     }
@@ -249,20 +299,38 @@ __global__ __launch_bounds__(kThreads) void axis0_kernel(const uint32_t* __restr
     float v = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) v += red[(w * M + n) * kCols + col];
-    const int en = n == 0 ? e0 : n == 1 ? e1 : n == 2 ? e2 : e3;
-    partial[((int64_t)s * M + n) * C + (int64_t)cgi * kCols + col] = ldexpf(v * kRcp, 24 - en);
+    partial[((int64_t)s * M + n) * C + (int64_t)cgi * kCols + col] = ldexpf(v * kRcp, 24);
   }
 }
 
 __global__ __launch_bounds__(256) void axis0_fold_kernel(const float* __restrict__ partial,
                                                          void* __restrict__ out, int out_f32,
                                                          int M, int64_t C, int S) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;   // over M * C
-  if (i >= (int64_t)M * C) return;
-  float s = 0.0f;
-  for (int j = 0; j < S; ++j) s += partial[(int64_t)j * M * C + i];
-  if (out_f32) reinterpret_cast<float*>(out)[i] = s;
-  else reinterpret_cast<uint16_t*>(out)[i] = f32_to_bf16_bits(s);
+  const int64_t i4 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;   // four outputs of [M, C]
+  if (i4 >= (int64_t)M * C) return;
+  const int64_t stride = (int64_t)M * C;
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j0 = 0; j0 < S; j0 += 16) {         // up to sixteen splits' loads in flight at once
+    float4 v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      v[u] = (j0 + u < S) ? *reinterpret_cast<const float4*>(partial + (j0 + u) * stride + i4)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {             // in split order
+      a.x += v[u].x;
+      a.y += v[u].y;
+      a.z += v[u].z;
+      a.w += v[u].w;
+    }
+  }
+  if (out_f32) {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + i4) = a;
+  } else {
+    const uint32_t lo = (uint32_t)f32_to_bf16_bits(a.x) | ((uint32_t)f32_to_bf16_bits(a.y) << 16);
+    const uint32_t hi = (uint32_t)f32_to_bf16_bits(a.z) | ((uint32_t)f32_to_bf16_bits(a.w) << 16);
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + i4) = make_uint2(lo, hi);
+  }
 }
 
 int device_cus() {
@@ -298,10 +366,8 @@ bool axis0_geom(int64_t R, int64_t C, int M, int k, Axis0Geom& g) {
   if (g.nwd > kMaxDma) return false;
   g.slot_bytes = (uint32_t)((32 * g.gsr * 16 + 255) / 256 * 256);
   const size_t xt = (size_t)8 * g.rps * 2;
-  size_t scr = (size_t)M * g.rps * 4;
-  const size_t red = (size_t)kWaves * M * kCols * 4;
-  if (red > scr) scr = red;
-  const size_t fixed = ((xt + 255) / 256 + (scr + 255) / 256) * 256 + 256;
+  const size_t scr = (size_t)kWaves * M * kCols * 4;
+  const size_t fixed = ((xt + 255) / 256 + (scr + 255) / 256) * 256;
   if (fixed >= kLdsBudget) return false;
   size_t ns = (kLdsBudget - fixed) / ((size_t)kWaves * g.slot_bytes);
   if (ns > (size_t)kMaxSlots) ns = kMaxSlots;
@@ -309,8 +375,9 @@ bool axis0_geom(int64_t R, int64_t C, int M, int k, Axis0Geom& g) {
   g.nslots = (int)ns;
   g.xt_off = (uint32_t)kWaves * g.nslots * g.slot_bytes;
   g.scr_off = g.xt_off + (uint32_t)((xt + 255) / 256 * 256);
-  g.wmax_off = g.scr_off + (uint32_t)((scr + 255) / 256 * 256);
-  g.total = g.wmax_off + 256;
+  g.total = g.scr_off + (uint32_t)((scr + 255) / 256 * 256);
+  g.scales16 = 0;
+  g.x16 = 0;
   return g.total <= kLdsBudget;
 }
 
@@ -350,6 +417,8 @@ hipError_t launch_axis0(const uint32_t* codes, const uint16_t* scales, const uin
                         void* workspace, hipStream_t stream) {
   Axis0Geom g;
   if (!axis0_geom(R, C, M, k, g)) return hipErrorInvalidValue;
+  g.scales16 = reinterpret_cast<uintptr_t>(scales) % 16 == 0;
+  g.x16 = reinterpret_cast<uintptr_t>(x) % 16 == 0 && R % 8 == 0;
   float* partial = reinterpret_cast<float*>(workspace);
   hipError_t e;
   switch (k) {
@@ -359,8 +428,8 @@ hipError_t launch_axis0(const uint32_t* codes, const uint16_t* scales, const uin
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
-  const int64_t n = (int64_t)M * C;
-  hipLaunchKernelGGL(axis0_fold_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+  const int64_t n4 = (int64_t)M * C / 4;        // C is a multiple of 256
+  hipLaunchKernelGGL(axis0_fold_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream,
                      partial, out, out_f32, M, C, g.S);
   return hipGetLastError();
 }
