@@ -60,6 +60,7 @@ __global__ __launch_bounds__(kThreads) void axis0_kernel(const uint32_t* __restr
                                                          float* __restrict__ partial, const Axis0Geom g) {
   constexpr int WPB = words_per_block(K);
   constexpr int BLK = WPB * 4;                 // bytes of one block of a row
+  constexpr int GSR = BLK / 16 + 1;            // granules per tile row in LDS (one pad granule)
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -70,7 +71,8 @@ __global__ __launch_bounds__(kThreads) void axis0_kernel(const uint32_t* __restr
   const int64_t r0 = (int64_t)s * g.rps;
   const int nr = (int)((R - r0 < g.rps) ? R - r0 : g.rps);   // rows of this split (>= 1)
   const int nblk = (nr + 31) >> 5;
-  const int NS = g.nslots, nwd = g.nwd, gsr = g.gsr;
+  const int NS = g.nslots, nwd = g.nwd;
+  constexpr int gsr = GSR;
   uint8_t* ring = smem + (size_t)wave * NS * g.slot_bytes;
   uint16_t* xt = reinterpret_cast<uint16_t*>(smem + g.xt_off);        // f16 [8][rps]: hi n, lo n
   float* scr = reinterpret_cast<float*>(smem + g.scr_off);            // the waves' D tiles at the end
@@ -102,8 +104,6 @@ __global__ __launch_bounds__(kThreads) void axis0_kernel(const uint32_t* __restr
       }
     }
   };
-  int next = 0;
-  for (; next < min(nmy, NS); ++next) issue_tile(next);
 
   // ---- 3. x~[n, r] = scale[r] * x[n, r] (exact in f32) for this wave's rows:
   // lane (t, g) of the wave holds rows 8g .. 8g+7 of its t-th block, loaded
@@ -116,31 +116,45 @@ __global__ __launch_bounds__(kThreads) void axis0_kernel(const uint32_t* __restr
   float xv[4][8];
   uint32_t mx0 = 0u, mx1 = 0u, mx2 = 0u, mx3 = 0u;
   {
+    // when x and scales are 16-byte aligned and the wave's rows are whole, the
+    // copy engine brings its x and scale granules into ring slots 1-2 ahead of
+    // tile 0, so only they are waited for; otherwise plain loads (which then
+    // wait behind tile 0)
+    const bool fast = g.x16 && g.scales16 && NS >= 3 && nmy > 0 && (wave + kWaves * (nmy - 1)) * 32 + 32 <= nr;
+    uint8_t* stg = ring + g.slot_bytes;        // 5 x 1 KB: x[0..3], scales
+    if (fast) {
+#pragma unroll
+      for (int c = 0; c < 5; ++c) {
+        if (c < M || c == 4) {                 // lane 0 holds rows of the wave's first block: active
+          const uint16_t* src = c < 4 ? x + (int64_t)c * R + r0 + rl : scales + r0 + rl;
+          if (hold) __builtin_amdgcn_global_load_lds(src, stg + c * 1024, 16, 0, 0);
+        }
+      }
+    }
+    int next0 = 0;
+    if (nmy > 0) issue_tile(next0++);          // tile 0 streams while x is prepared
     uint4 xb[4];
     uint16_t sb[8];
+    if (fast) {
+      wait_vmcnt(nwd * next0);                 // the x and scale copies have landed
 #pragma unroll
-    for (int n = 0; n < 4; ++n)
-      xb[n] = (g.x16 && hold && n < M && rl + 8 <= nr)
-                  ? *reinterpret_cast<const uint4*>(x + (int64_t)n * R + r0 + rl)
-                  : make_uint4(0u, 0u, 0u, 0u);
-    if (g.scales16 && hold && rl + 8 <= nr) {
-      const uint4 v = *reinterpret_cast<const uint4*>(scales + r0 + rl);
+      for (int n = 0; n < 4; ++n)
+        xb[n] = (hold && n < M) ? *reinterpret_cast<const uint4*>(stg + n * 1024 + lane * 16) : make_uint4(0u, 0u, 0u, 0u);
+      const uint4 v = hold ? *reinterpret_cast<const uint4*>(stg + 4 * 1024 + lane * 16) : make_uint4(0u, 0u, 0u, 0u);
       const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int h = 0; h < 8; ++h) sb[h] = (uint16_t)(w4[h >> 1] >> (16 * (h & 1)));
     } else {
 #pragma unroll
-      for (int h = 0; h < 8; ++h) sb[h] = (hold && rl + h < nr) ? scales[r0 + rl + h] : (uint16_t)0;
-    }
-    if (hold && (!g.x16 || rl + 8 > nr)) {     // rows not 16-byte aligned, or the split's ragged last eight
-#pragma unroll
       for (int n = 0; n < 4; ++n) {
         uint32_t w4[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int h = 0; h < 8; ++h)
-          if (n < M && rl + h < nr) w4[h >> 1] |= (uint32_t)x[(int64_t)n * R + r0 + rl + h] << (16 * (h & 1));
+          if (hold && n < M && rl + h < nr) w4[h >> 1] |= (uint32_t)x[(int64_t)n * R + r0 + rl + h] << (16 * (h & 1));
         xb[n] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
       }
+#pragma unroll
+      for (int h = 0; h < 8; ++h) sb[h] = (hold && rl + h < nr) ? scales[r0 + rl + h] : (uint16_t)0;
     }
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
@@ -188,6 +202,10 @@ __global__ __launch_bounds__(kThreads) void axis0_kernel(const uint32_t* __restr
       *reinterpret_cast<uint4*>(xt + (4 + n) * g.rps + rl) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
     }
   }
+
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);     // the staging reads above stay before slots 1-2 refill
+  int next = nmy > 0 ? 1 : 0;
+  for (; next < min(nmy, NS); ++next) issue_tile(next);
 
   // ---- 4. per-lane decode geometry for the four chunks: the 32-bit window
   // of columns 4i .. 4i+3 starts at bit (252 - t) k of the block (t = the
