@@ -275,6 +275,9 @@ int trellis_prefill(const uint32_t* codes, const uint16_t* scales, const uint16_
   const size_t need = trellis_prefill_workspace_bytes(R, C, M, k, L, T, algo);
   TRY(check_workspace(fn, workspace, workspace_bytes, need));
   hipStream_t s = (hipStream_t)stream;
+  if (algo == TRELLIS_PREFILL_FUSED && !trellis::prefill_fused_supported(R, C, M, k))
+    return fail(TRELLIS_EUNSUPPORTED, "%s: fused kernel needs x and codes below 2 GiB (M=%lld R=%lld C=%lld)",
+                fn, (long long)M, (long long)R, (long long)C);
   if (algo == TRELLIS_PREFILL_FUSED)
     return hip_status(fn, trellis::launch_prefill_fused(codes, scales, x, out, R, C, M, k, s));
   uint16_t* wexp = reinterpret_cast<uint16_t*>(workspace);

@@ -7,132 +7,377 @@
 // (x tile and reconstructed bf16 weight tile in threadgroup memory, matrix
 // multiply-accumulate in f32; precise value before the bf16 weight rounding).
 //
-// Tiling: workgroup of 4 waves computes a 128 (m) x 128 (r) output tile with
-// K steps of 64 columns; each wave owns a 64 x 64 quadrant made of 4 x 4
-// v_mfma_f32_16x16x32_bf16 tiles.  Per K step every thread decodes one run
-// of 32 positions of one weight row (k + 1 words, constant shifts).
+// Tiling.  A workgroup of 4 waves (one per SIMD) owns 512 rows of x and 128
+// weight rows; each wave computes a 128 (x rows) x 128 (weight rows) block
+// as 4 x 4 v_mfma_f32_32x32x16_bf16 tiles with 256 f32 accumulators per
+// lane (the 32 x 32 form keeps each accumulator in place across the loop).
+// Every decoded weight therefore serves 512 rows of x, which keeps the VALU
+// decode (about nine operations per weight) under the MFMA time of a step.
+//
+// x path.  Each wave's 128 rows of x are its own.  They arrive in chunks of
+// 64 columns (one 128-byte line per row) with loads that read 8 whole lines
+// per instruction, go through registers into a double-buffered, XOR-swizzled
+// LDS area of that wave, and are read back in the MFMA operand layout.  (An
+// operand-layout load spans 32 rows per instruction and reaches well under
+// half the L2 bandwidth; LDS DMA would save the registers, but the compiler
+// cannot tell its two buffers apart and waits for the prefetch.)
+//
+// Per step of 32 columns:
+//   * each thread decodes 16 consecutive positions of one weight row for the
+//     next step, between this step's MFMAs, into the other half of a
+//     double-buffered LDS weight tile; its code words are loaded three
+//     steps ahead;
+//   * the loads of an x chunk are issued two steps before they are written
+//     to LDS, and the chunk is read one step after that;
+//   * one workgroup barrier per step (for the weight tile), straddled by the
+//     MFMAs: the interval between two barriers runs the second half of the
+//     previous step from registers and then the first half of this step, so
+//     the matrix core has work while the new step's operands leave LDS.
+// Workgroups are mapped so that the 32 CUs of one XCD work on the same 512
+// rows of x at the same time, which keeps that slice of x in the XCD's L2.
+#include <type_traits>
+
 #include "internal.hpp"
+#include "mfma_common.hpp"
 #include "trellis_device.hpp"
 
 namespace trellis {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBM = 128, kBN = 128, kBK = 64;
-constexpr int kLds = kBK + 8;   // padded LDS row (elements): spreads 16-byte reads over banks
+constexpr int kWaves = 4;
+constexpr int kBM = 512;                 // x rows per workgroup
+constexpr int kBN = 128;                 // weight rows per workgroup
+constexpr int kBK = 32;                  // columns per step
+constexpr int kWM = kBM / kWaves;        // x rows per wave
+constexpr int kFM = kWM / 32;            // MFMA tiles along x rows
+constexpr int kFN = kBN / 32;            // MFMA tiles along weight rows
+constexpr int kRow = kBK + 8;            // padded LDS row (bf16): 80 bytes spread the 16-byte reads
+constexpr int kChunkLines = 8;          // 16-byte blocks per x row in one chunk (64 columns)
+constexpr int kXLoads = kWM / 8;         // x chunk loads per wave (8 rows x 128 bytes each)
+constexpr int kXcds = 8;
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format
+
+// Words holding the windows of 16 consecutive positions once the run is
+// aligned to bit 0; odd k starts half the runs 16 bits into a word, so one
+// more word is loaded and the run is shifted down.
+template <int K>
+struct Run16 {
+  static constexpr int kAligned = (15 * K + kL + 31) / 32;
+  static constexpr int kLoad = kAligned + (K & 1);
+};
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two round-to-nearest-even bf16 conversions in one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+}
+
+// Decode positions q0 + 8 H .. q0 + 8 H + 7 of a run of 16 consecutive
+// positions q0 .. q0 + 15 of one row (half H of the run).  Position q0 + i
+// has its window at bit (15 - i) * K of the aligned run (the block stores
+// position t at bit (T - 1 - t) * K, so later positions sit lower).
+template <int K, int H>
+__device__ __forceinline__ void decode_run8(const uint32_t (&w)[Run16<K>::kLoad], bool shift16,
+                                           float sc, uint32_t mul, uint64_t add64,
+                                           uint32_t (&pk)[4]) {
+  constexpr int NA = Run16<K>::kAligned;
+  uint32_t a[NA];
+#pragma unroll
+  for (int j = 0; j < NA; ++j) {
+    if constexpr (K & 1)
+      a[j] = shift16 ? __builtin_amdgcn_alignbit(w[j + 1], w[j], 16) : w[j];
+    else
+      a[j] = w[j];
+  }
+  float f[8];
+#pragma unroll
+  for (int ii = 0; ii < 8; ++ii) {
+    const int rel = (15 - (8 * H + ii)) * K;
+    const int wi = rel >> 5, ro = rel & 31;
+    uint32_t s;
+    if (ro + kL <= 32)
+      s = (a[wi] >> ro) & kStateMask;
+    else
+      s = window(a[wi], a[wi + 1], (uint32_t)ro);
+    // y = byte sum - 510: v_sad_u8 accumulates onto -510 (mod 2^32)
+    const int y = (int)__builtin_amdgcn_sad_u8(onemad_word_mad64(s, mul, add64), 0u, (uint32_t)-kYOffset);
+    f[ii] = code_value(y) * sc;
+  }
+#pragma unroll
+  for (int p = 0; p < 4; ++p) pk[p] = pack_bf16x2(f[2 * p], f[2 * p + 1]);
+}
 
 template <int K>
-__global__ __launch_bounds__(256) void prefill_fused_kernel(const uint32_t* __restrict__ codes,
-                                                            const uint16_t* __restrict__ scales,
-                                                            const uint16_t* __restrict__ x,
-                                                            uint16_t* __restrict__ out, int64_t R,
-                                                            int64_t C, int64_t M) {
+__global__ __launch_bounds__(256, 1) void prefill_fused_kernel(
+    const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scales,
+    const uint16_t* __restrict__ x, uint16_t* __restrict__ out, int R, int C, int M, int nn,
+    int ntiles, int per_xcd) {
   constexpr int WPB = words_per_block(K);
-  __shared__ __attribute__((aligned(16))) uint16_t As[kBM * kLds];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[kBN * kLds];
+  constexpr int NL = Run16<K>::kLoad;
+  // Separate LDS objects for every buffer, so the compiler knows a step's
+  // writes (next weight tile, next x chunk) never alias its reads and can
+  // move the decode in between the MFMAs.
+  __shared__ __attribute__((aligned(16))) uint16_t Bs0[kBN * kRow];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs1[kBN * kRow];
+  __shared__ __attribute__((aligned(16))) u32x4 Xs0[kWaves][kWM * kChunkLines];
+  __shared__ __attribute__((aligned(16))) u32x4 Xs1[kWaves][kWM * kChunkLines];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int64_t m0 = (int64_t)blockIdx.y * kBM, n0 = (int64_t)blockIdx.x * kBN;
+  // XCD-aware tile order: workgroup b runs on XCD b % 8; that XCD takes a
+  // contiguous range of tiles, which share their 512 x rows.
+  const int bid = blockIdx.x;
+  const int tile = (bid % kXcds) * per_xcd + bid / kXcds;
+  if (tile >= ntiles) return;
+  const int mb = tile / nn, nb = tile - mb * nn;
 
-  f32x4 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: offsets stay in SGPRs
+  const int m_wave = mb * kBM + wave * kWM;
+  const int n0 = nb * kBN;
+  const int nsteps = C / kBK;
+  const int nchunks = nsteps / 2;
 
-  const int drow = tid >> 1, dhalf = tid & 1;   // decode: one 32-position run per thread
-  const int64_t grow = n0 + drow;
-  const bool rvalid = grow < R;
-  const uint32_t* crow = codes + (rvalid ? grow : 0) * (C / kT) * WPB;
-  const float sc = rvalid ? half_bits_to_f32(scales[grow]) : 0.0f;
-
-  for (int64_t kb = 0; kb < C; kb += kBK) {
-    // x tile [128 m][64 k] -> As
+  // x chunk loads: instruction q reads rows 8 q .. 8 q + 7 of the wave, lane
+  // l the 16 bytes at column block l % 8 of row 8 q + l / 8 (rows past M are
+  // clamped to M - 1: their results are never stored).  LDS keeps row r's
+  // block c in slot c ^ ((r / 2) % 8): the operand reads (16 consecutive rows
+  // at one block) then cover all 64 banks once.
+  const __amdgpu_buffer_rsrc_t xr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, M * C * 2, kRsrcWord3);
+  uint32_t xo[kXLoads];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int idx = tid + 256 * j;
-      const int r = idx >> 3, cv = idx & 7;
-      const int64_t gm = m0 + r;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (gm < M) v = *reinterpret_cast<const uint4*>(x + gm * C + kb + 8 * cv);
-      *reinterpret_cast<uint4*>(&As[r * kLds + 8 * cv]) = v;
-    }
-    // weight tile [128 r][64 k] -> Bs, decoded in registers
-    {
-      uint32_t packed[16];
-      if (rvalid) {
-        const int64_t c0 = kb + 32 * dhalf;
-        const int blk = (int)(c0 / kT), q = (int)((c0 % kT) / 32);
-        const uint32_t* bw = crow + (int64_t)blk * WPB;
-        const int w0 = (7 - q) * K;
-        uint32_t w[K + 1];
-#pragma unroll
-        for (int i = 0; i < K; ++i) w[i] = bw[w0 + i];
-        w[K] = bw[(w0 + K == WPB) ? 0 : w0 + K];
-#pragma unroll
-        for (int i = 0; i < 32; i += 2) {
-          const int pa = (31 - i) * K, pb = (30 - i) * K;
-          const uint32_t sa = window(w[pa >> 5], w[(pa >> 5) + 1], pa & 31);
-          const uint32_t sb = window(w[pb >> 5], w[(pb >> 5) + 1], pb & 31);
-          const uint32_t ha = f32_to_bf16_bits(code_value(code_y(sa)) * sc);
-          const uint32_t hb = f32_to_bf16_bits(code_value(code_y(sb)) * sc);
-          packed[i >> 1] = ha | (hb << 16);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) packed[i] = 0u;
-      }
-      uint4* dst = reinterpret_cast<uint4*>(&Bs[drow * kLds + 32 * dhalf]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        dst[j] = make_uint4(packed[4 * j], packed[4 * j + 1], packed[4 * j + 2], packed[4 * j + 3]);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < kBK; kk += 32) {
-      bf16x8 a[4], b[4];
-      const int kofs = kk + 8 * (lane >> 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        a[i] = *reinterpret_cast<const bf16x8*>(&As[(wm * 64 + 16 * i + (lane & 15)) * kLds + kofs]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        b[j] = *reinterpret_cast<const bf16x8*>(&Bs[(wn * 64 + 16 * j + (lane & 15)) * kLds + kofs]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
-    __syncthreads();
+  for (int q = 0; q < kXLoads; ++q) {
+    const int row = min(m_wave + 8 * q + (lane >> 3), M - 1);
+    xo[q] = (uint32_t)row * (uint32_t)C * 2u + (uint32_t)(lane & 7) * 16u;
   }
+  // slot of lane l in instruction q: row 8 q + l / 8, swizzle 4 (q % 2) + l / 16
+  const int xw_even = (lane >> 3) * 8 + ((lane & 7) ^ (lane >> 4));
+  const int xw_odd = (lane >> 3) * 8 + ((lane & 7) ^ (4 + (lane >> 4)));
+  // Operand reads: for half h of a step, lane l supplies columns
+  // 16 (l / 32) + 8 h .. + 7 of the step (any assignment shared by both
+  // operands is a valid split of the contraction); row 32 i + l % 32.
+  const int xr_row = lane & 31, xr_swz = (xr_row >> 1) & 7;
+  const u32x4* const xrd0 = &Xs0[wave][xr_row * kChunkLines];  // + 32 i rows
+  const u32x4* const xrd1 = &Xs1[wave][xr_row * kChunkLines];
 
-  // D of a 16x16 tile: lane holds rows 4*(lane/16) + e, column lane % 16.
+  // Decode assignment: weight row n0 + dr (clamped), positions 16 dh .. + 15
+  // of every step; dh is uniform over a wave.
+  const int dr = lane + 64 * (wave >> 1), dh = wave & 1;
+  const int grow = min(n0 + dr, R - 1);
+  const int row_bytes = (C / kT) * WPB * 4;
+  const __amdgpu_buffer_rsrc_t cr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)codes, (short)0, R * row_bytes, kRsrcWord3);
+  const int cvo = grow * row_bytes;
+  const float sc = half_bits_to_f32(scales[grow]);
+  const uint32_t mul = kMul;
+  const uint64_t add64 = kAdd;
+
+  f32x16 acc[kFM][kFN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kFM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < kFN; ++j) acc[i][j] = f32x16{};
+
+  u32x4 xs[kXLoads];        // x chunk in flight (registers, two steps)
+  uint32_t cw[4][NL];       // code words of steps t + 1 .. t + 3
+
+  // Loads past the end re-read the last chunk / step (in bounds, unused), so
+  // the loop body has no branches.
+  auto load_chunk = [&](int c) {
+    const int soff = min(c, nchunks - 1) * 2 * kBK * 2;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t gm = m0 + wm * 64 + 16 * i + 4 * (lane >> 4) + e;
-        const int64_t gn = n0 + wn * 64 + 16 * j + (lane & 15);
-        if (gm < M && gn < R) out[gm * R + gn] = f32_to_bf16_bits(acc[i][j][e]);
+    for (int q = 0; q < kXLoads; ++q) xs[q] = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)xo[q], soff, 0);
+  };
+  auto store_chunk = [&](u32x4 (*dst)[kWM * kChunkLines]) {
+#pragma unroll
+    for (int q = 0; q < kXLoads; ++q) dst[wave][q * 64 + ((q & 1) ? xw_odd : xw_even)] = xs[q];
+  };
+  // Run of step t: block t / 8, first position q0 = 32 (t % 8) + 16 dh,
+  // lowest window bit (240 - q0) K; words wrap within the block.
+  auto run_bits = [&](int t) { return (kT - 16 - (kBK * (t & 7) + 16 * dh)) * K; };
+  auto load_w = [&](uint32_t (&dst)[NL], int t) {
+    t = min(t, nsteps - 1);
+    const int w0 = run_bits(t) >> 5;
+    const int base = (t >> 3) * WPB * 4;
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      const int wj = (w0 + j >= WPB) ? w0 + j - WPB : w0 + j;
+      dst[j] = __builtin_amdgcn_raw_buffer_load_b32(cr, cvo, base + wj * 4, 0);
+    }
+  };
+  // Half H of the weights of step t (16 bytes per thread) into an LDS
+  // buffer (past the last step: a buffer nobody reads again).
+  auto decode_half = [&](const uint32_t (&w)[NL], int t, uint32_t (&pk)[4], auto half) {
+    decode_run8<K, decltype(half)::value>(w, (run_bits(t) & 31) != 0, sc, mul, add64, pk);
+  };
+  auto store_half = [&](const uint32_t (&pk)[4], uint16_t* buf, int half) {
+    *reinterpret_cast<u32x4*>(&buf[dr * kRow + 16 * dh + 8 * half]) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+  };
+  using H0 = std::integral_constant<int, 0>;
+  using H1 = std::integral_constant<int, 1>;
+
+  // prologue: words of steps 0..2, x chunk 0 into LDS and chunk 1 into
+  // registers, weights of step 0
+  load_w(cw[0], 0);
+  load_w(cw[1], 1);
+  load_w(cw[2], 2);
+  load_chunk(0);
+  store_chunk(Xs0);
+  load_chunk(1);
+  {
+    uint32_t pk[4];
+    decode_half(cw[0], 0, pk, H0{});
+    store_half(pk, Bs0, 0);
+    decode_half(cw[0], 0, pk, H1{});
+    store_half(pk, Bs0, 1);
+  }
+  __syncthreads();
+
+  // MFMA operands of one half h of a step: weights b[j] (rows 32 j + l % 32)
+  // and x a[i] (rows 32 i + l % 32), columns 16 (l / 32) + 8 h .. + 7.
+  const int bofs = (lane & 31) * kRow + 16 * (lane >> 5);
+  auto read_half = [&](int t, int h, const uint16_t* bbuf, const u32x4* xrd, bf16x8 (&b)[kFN],
+                       bf16x8 (&a)[kFM]) {
+#pragma unroll
+    for (int j = 0; j < kFN; ++j) b[j] = *reinterpret_cast<const bf16x8*>(bbuf + bofs + 32 * j * kRow + 8 * h);
+    const int blk = 4 * (t & 1) + 2 * (lane >> 5) + h;      // 16-byte block of the chunk row
+#pragma unroll
+    for (int i = 0; i < kFM; ++i)
+      a[i] = __builtin_bit_cast(bf16x8, xrd[32 * i * kChunkLines + (blk ^ xr_swz)]);
+  };
+  auto mfma_half = [&](const bf16x8 (&b)[kFN], const bf16x8 (&a)[kFM]) {
+#pragma unroll
+    for (int i = 0; i < kFM; ++i)
+#pragma unroll
+      for (int j = 0; j < kFN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+  };
+
+  // Software pipeline across the per-step barrier.  Interval t (between the
+  // barriers of steps t - 1 and t) runs the second half of step t - 1 from
+  // registers, then the first half of step t, while it reads the operands of
+  // step t from LDS and decodes step t + 1.  After each barrier the wave has
+  // MFMA work whose operands are already in registers, so the matrix core
+  // does not wait for the LDS reads of the new step.
+  bf16x8 bp[kFN], ap[kFM];     // second half of the previous step
+  bf16x8 bc[kFN], ac[kFM];     // first half of the current step
+#pragma unroll
+  for (int j = 0; j < kFN; ++j) bp[j] = bf16x8{};
+#pragma unroll
+  for (int i = 0; i < kFM; ++i) ap[i] = bf16x8{};
+
+  // Four steps (two x chunks) per iteration: the step count is a multiple
+  // of 8, every buffer index below is a compile-time constant.  Chunk j of
+  // x is loaded at the start of step 2 j - 3 and written to LDS at the end of
+  // step 2 j - 2 (two steps for the loads to land; every wait below then
+  // covers loads issued at least two steps earlier).
+  for (int t0 = 0; t0 < nsteps; t0 += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = t0 + u;
+      const bool odd = (u & 1) != 0;
+      const uint16_t* bcur = (u & 1) ? Bs1 : Bs0;
+      uint16_t* bnext = (u & 1) ? Bs0 : Bs1;
+      const u32x4* xcur = (u & 2) ? xrd1 : xrd0;
+      uint32_t pk0[4], pk1[4];
+
+      // first region: loads, operands of step t (half 0), MFMAs of step
+      // t - 1 (half 1), decode of step t + 1 (half 0)
+      if (odd) load_chunk((t + 3) / 2);
+      load_w(cw[(u + 3) & 3], t + 3);
+      read_half(t, 0, bcur, xcur, bc, ac);
+      mfma_half(bp, ap);
+      decode_half(cw[(u + 1) & 3], t + 1, pk0, H0{});
+      if (odd)
+        __builtin_amdgcn_sched_group_barrier(0x020, kXLoads + NL, 0);              // VMEM reads
+      else
+        __builtin_amdgcn_sched_group_barrier(0x020, NL, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, kFN + kFM, 0);                  // DS reads
+#pragma unroll
+      for (int g = 0; g < kFM * kFN; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                         // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);                         // VALU
       }
+      __builtin_amdgcn_sched_barrier(0);
+
+      // second region: operands of step t (half 1), MFMAs of step t (half
+      // 0), decode of step t + 1 (half 1), LDS writes
+      read_half(t, 1, bcur, xcur, bp, ap);
+      mfma_half(bc, ac);
+      decode_half(cw[(u + 1) & 3], t + 1, pk1, H1{});
+      store_half(pk0, bnext, 0);
+      store_half(pk1, bnext, 1);
+      if (!odd) store_chunk((u & 2) ? Xs0 : Xs1);     // chunk t / 2 + 1 into the other x buffer
+      __builtin_amdgcn_sched_group_barrier(0x100, kFN + kFM, 0);                  // DS reads
+#pragma unroll
+      for (int g = 0; g < kFM * kFN; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                         // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);                         // VALU
+      }
+      if (odd)
+        __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);                         // DS writes
+      else
+        __builtin_amdgcn_sched_group_barrier(0x200, 2 + kXLoads, 0);
+      __syncthreads();
+      // MFMAs touch no memory, so without a fence the scheduler would move
+      // them across the barrier.
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  mfma_half(bp, ap);           // second half of the last step
+
+  // D of tile (i, j) (weights as the row operand): lane holds x row
+  // m_wave + 32 i + lane % 32 and, for register group g, weight rows
+  // n0 + 32 j + 8 g + 4 (lane / 32) + e, e = 0..3.
+  if (m_wave >= M) return;
+  const bool vec = (R & 3) == 0;
+#pragma unroll
+  for (int i = 0; i < kFM; ++i) {
+    const int m = m_wave + 32 * i + (lane & 31);
+    if (m >= M) continue;
+    uint16_t* orow = out + (size_t)m * (size_t)R;
+#pragma unroll
+    for (int j = 0; j < kFN; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + 32 * j + 8 * g + 4 * (lane >> 5);
+        const f32x16 v = acc[i][j];
+        if (vec && n + 3 < R) {
+          *reinterpret_cast<uint2*>(orow + n) =
+              make_uint2(pack_bf16x2(v[4 * g], v[4 * g + 1]), pack_bf16x2(v[4 * g + 2], v[4 * g + 3]));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n + e < R) orow[n + e] = f32_to_bf16_bits(v[4 * g + e]);
+        }
+      }
+  }
 }
 
 }  // namespace
 
+bool prefill_fused_supported(int64_t R, int64_t C, int64_t M, int k) {
+  // 32-bit buffer offsets: x and one weight matrix's codes below 2 GiB
+  return k >= 2 && k <= 4 && C % (4 * kBK) == 0 && M * C * 2 < ((int64_t)1 << 31) &&
+         R * C * k / 8 < ((int64_t)1 << 31);
+}
+
 hipError_t launch_prefill_fused(const uint32_t* codes, const uint16_t* scales, const uint16_t* x,
                                 uint16_t* out, int64_t R, int64_t C, int64_t M, int k,
                                 hipStream_t stream) {
-  const dim3 grid((unsigned)((R + kBN - 1) / kBN), (unsigned)((M + kBM - 1) / kBM)), block(256);
+  const int nm = (int)((M + kBM - 1) / kBM), nn = (int)((R + kBN - 1) / kBN);
+  const int ntiles = nm * nn, per = (ntiles + kXcds - 1) / kXcds;
+  const dim3 grid((unsigned)(per * kXcds)), block(256);
+  const int r = (int)R, c = (int)C, m = (int)M;
   switch (k) {
-    case 2: hipLaunchKernelGGL(prefill_fused_kernel<2>, grid, block, 0, stream, codes, scales, x, out, R, C, M); break;
-    case 3: hipLaunchKernelGGL(prefill_fused_kernel<3>, grid, block, 0, stream, codes, scales, x, out, R, C, M); break;
-    case 4: hipLaunchKernelGGL(prefill_fused_kernel<4>, grid, block, 0, stream, codes, scales, x, out, R, C, M); break;
+    case 2: hipLaunchKernelGGL(prefill_fused_kernel<2>, grid, block, 0, stream, codes, scales, x, out, r, c, m, nn, ntiles, per); break;
+    case 3: hipLaunchKernelGGL(prefill_fused_kernel<3>, grid, block, 0, stream, codes, scales, x, out, r, c, m, nn, ntiles, per); break;
+    case 4: hipLaunchKernelGGL(prefill_fused_kernel<4>, grid, block, 0, stream, codes, scales, x, out, r, c, m, nn, ntiles, per); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -47,13 +47,15 @@ __device__ __forceinline__ int code_y(uint32_t s) {
   return (int)__builtin_amdgcn_sad_u8(onemad_word(s), 0u, 0u) - kYOffset;
 }
 
-// Code value y / d rounded to nearest binary32: reciprocal product refined
-// by one residual step (exact for every |y| <= 510).
+// Code value y / d rounded to nearest binary32, in two operations: the
+// reciprocal split as kRcp + kRcpLo (kRcpLo = 1/d - kRcp rounded to binary32)
+// and y * kRcp + RN(y * kRcpLo) under one fused rounding.  Checked exactly,
+// with rational arithmetic, to be correctly rounded for every |y| <= 510.
+constexpr float kRcpLo = -0x1.e90d7cp-33f;
+
 __device__ __forceinline__ float code_value(int y) {
   const float yf = (float)y;
-  const float q = yf * kRcp;
-  const float e = __builtin_fmaf(-q, kDiv, yf);
-  return __builtin_fmaf(e, kRcp, q);
+  return __builtin_fmaf(yf, kRcp, yf * kRcpLo);
 }
 
 __device__ __forceinline__ float half_bits_to_f32(uint16_t h) {
