@@ -15,6 +15,23 @@
 #include "../../include/trellis.h"
 #include "internal.hpp"
 
+namespace trellis {
+
+// Compute units of the current device, queried once per device.
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cus[dev] = v;
+  }
+  return cus[dev];
+}
+
+}  // namespace trellis
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -252,9 +269,9 @@ int trellis_expand_bf16(const uint32_t* codes, const uint16_t* scales, uint16_t*
 size_t trellis_prefill_workspace_bytes(int64_t R, int64_t C, int64_t M, int k, int L, int T,
                                        int algo) {
   if (check_geometry("trellis_prefill_workspace_bytes", R, C, k, L, T) != TRELLIS_OK) return 0;
-  (void)M;
   if (algo == TRELLIS_PREFILL_EXPAND_GEMM) return align_up((size_t)R * (size_t)C * 2, 256) + kGemmWorkspace;
-  return 0;
+  if (M < 1 || !trellis::prefill_fused_supported(R, C, M, k)) return 0;
+  return trellis::prefill_fused_workspace_bytes(R, C, M);
 }
 
 int trellis_prefill(const uint32_t* codes, const uint16_t* scales, const uint16_t* x,
@@ -279,7 +296,7 @@ int trellis_prefill(const uint32_t* codes, const uint16_t* scales, const uint16_
     return fail(TRELLIS_EUNSUPPORTED, "%s: fused kernel needs x and codes below 2 GiB (M=%lld R=%lld C=%lld)",
                 fn, (long long)M, (long long)R, (long long)C);
   if (algo == TRELLIS_PREFILL_FUSED)
-    return hip_status(fn, trellis::launch_prefill_fused(codes, scales, x, out, R, C, M, k, s));
+    return hip_status(fn, trellis::launch_prefill_fused(codes, scales, x, out, R, C, M, k, workspace, s));
   uint16_t* wexp = reinterpret_cast<uint16_t*>(workspace);
   const size_t wexp_bytes = align_up((size_t)R * (size_t)C * 2, 256);
   TRY(hip_status(fn, trellis::launch_expand(codes, scales, wexp, R, C, k, s)));

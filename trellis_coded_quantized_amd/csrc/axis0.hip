@@ -351,17 +351,6 @@ __global__ __launch_bounds__(256) void axis0_fold_kernel(const float* __restrict
   }
 }
 
-int device_cus() {
-  static int cus[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
-    cus[dev] = v;
-  }
-  return cus[dev];
-}
 
 // Host geometry; false if the shape does not fit.
 bool axis0_geom(int64_t R, int64_t C, int M, int k, Axis0Geom& g) {

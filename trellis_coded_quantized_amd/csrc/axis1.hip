@@ -370,17 +370,6 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
   }
 }
 
-int device_cus() {
-  static int cus[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
-    cus[dev] = v;
-  }
-  return cus[dev];
-}
 
 // MFMA groups of four runs per wave -> the register-resident B capacity
 // instantiated for it (2 or 5 groups: C <= 2048 or C <= 5120); 0 if C is too

@@ -33,10 +33,15 @@ hipError_t launch_expand(const uint32_t* codes, const uint16_t* scales, uint16_t
 hipError_t launch_decode_states(const uint32_t* codes, int64_t R, int64_t C, int k,
                                 uint16_t* states, int16_t* y, float* value, hipStream_t stream);
 
-// fused prefill (32-bit buffer offsets: x and the codes each below 2 GiB)
+// compute units of the current device (cached per device)
+int device_cus();
+
+// fused prefill (32-bit buffer offsets: x and the codes each below 2 GiB);
+// the workspace holds the f32 partial tiles of the tiles split along K
 bool prefill_fused_supported(int64_t R, int64_t C, int64_t M, int k);
+size_t prefill_fused_workspace_bytes(int64_t R, int64_t C, int64_t M);
 hipError_t launch_prefill_fused(const uint32_t* codes, const uint16_t* scales, const uint16_t* x,
                                 uint16_t* out, int64_t R, int64_t C, int64_t M, int k,
-                                hipStream_t stream);
+                                void* workspace, hipStream_t stream);
 
 }  // namespace trellis

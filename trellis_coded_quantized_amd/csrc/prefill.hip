@@ -113,11 +113,25 @@ __device__ __forceinline__ void decode_run8(const uint32_t (&w)[Run16<K>::kLoad]
   for (int p = 0; p < 4; ++p) pk[p] = pack_bf16x2(f[2 * p], f[2 * p + 1]);
 }
 
+// Work plan.  The first nfull tiles run whole, in the XCD-aware order below.
+// When the tiles left after the full rounds would fill at most half of the
+// CUs, each of those nsplit tiles is cut instead into S segments of seg steps
+// (a multiple of 4), one workgroup each, which leave f32 partial tiles in
+// the workspace; prefill_fold_kernel adds them up.
+struct PrefillPlan {
+  int nn;            // tiles along the weight rows
+  int ntiles;
+  int nfull, per;    // whole tiles; per XCD
+  int nsplit, S, seg;
+};
+
+constexpr int kPartFloats = kBM * kBN;   // one partial tile: 256 floats per thread, float4-interleaved
+
 template <int K>
 __global__ __launch_bounds__(256, 1) void prefill_fused_kernel(
     const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scales,
-    const uint16_t* __restrict__ x, uint16_t* __restrict__ out, int R, int C, int M, int nn,
-    int ntiles, int per_xcd) {
+    const uint16_t* __restrict__ x, uint16_t* __restrict__ out, float* __restrict__ part, int R,
+    int C, int M, PrefillPlan plan) {
   constexpr int WPB = words_per_block(K);
   constexpr int NL = Run16<K>::kLoad;
   // Separate LDS objects for every buffer, so the compiler knows a step's
@@ -129,17 +143,26 @@ __global__ __launch_bounds__(256, 1) void prefill_fused_kernel(
   __shared__ __attribute__((aligned(16))) u32x4 Xs1[kWaves][kWM * kChunkLines];
 
   // XCD-aware tile order: workgroup b runs on XCD b % 8; that XCD takes a
-  // contiguous range of tiles, which share their 512 x rows.
+  // contiguous range of tiles, which share their 512 x rows.  Split
+  // segments come after all whole tiles.
+  const int nsteps = C / kBK;
   const int bid = blockIdx.x;
-  const int tile = (bid % kXcds) * per_xcd + bid / kXcds;
-  if (tile >= ntiles) return;
-  const int mb = tile / nn, nb = tile - mb * nn;
+  int tile, unit = -1, t_begin = 0, t_end = nsteps;
+  if (bid < kXcds * plan.per) {
+    tile = (bid % kXcds) * plan.per + bid / kXcds;
+    if (tile >= plan.nfull) return;
+  } else {
+    unit = bid - kXcds * plan.per;                 // split unit: tile nfull + unit / S, segment unit % S
+    tile = plan.nfull + unit / plan.S;
+    t_begin = (unit % plan.S) * plan.seg;
+    t_end = min(nsteps, t_begin + plan.seg);
+  }
+  const int mb = tile / plan.nn, nb = tile - mb * plan.nn;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: offsets stay in SGPRs
   const int m_wave = mb * kBM + wave * kWM;
   const int n0 = nb * kBN;
-  const int nsteps = C / kBK;
   const int nchunks = nsteps / 2;
 
   // x chunk loads: instruction q reads rows 8 q .. 8 q + 7 of the wave, lane
@@ -221,19 +244,20 @@ __global__ __launch_bounds__(256, 1) void prefill_fused_kernel(
   using H0 = std::integral_constant<int, 0>;
   using H1 = std::integral_constant<int, 1>;
 
-  // prologue: words of steps 0..2, x chunk 0 into LDS and chunk 1 into
-  // registers, weights of step 0
-  load_w(cw[0], 0);
-  load_w(cw[1], 1);
-  load_w(cw[2], 2);
-  load_chunk(0);
+  // prologue (t_begin is a multiple of 4): words of the first three steps,
+  // the first x chunk into LDS and the second into registers, weights of
+  // the first step
+  load_w(cw[0], t_begin);
+  load_w(cw[1], t_begin + 1);
+  load_w(cw[2], t_begin + 2);
+  load_chunk(t_begin / 2);
   store_chunk(Xs0);
-  load_chunk(1);
+  load_chunk(t_begin / 2 + 1);
   {
     uint32_t pk[4];
-    decode_half(cw[0], 0, pk, H0{});
+    decode_half(cw[0], t_begin, pk, H0{});
     store_half(pk, Bs0, 0);
-    decode_half(cw[0], 0, pk, H1{});
+    decode_half(cw[0], t_begin, pk, H1{});
     store_half(pk, Bs0, 1);
   }
   __syncthreads();
@@ -276,7 +300,7 @@ __global__ __launch_bounds__(256, 1) void prefill_fused_kernel(
   // x is loaded at the start of step 2 j - 3 and written to LDS at the end of
   // step 2 j - 2 (two steps for the loads to land; every wait below then
   // covers loads issued at least two steps earlier).
-  for (int t0 = 0; t0 < nsteps; t0 += 4) {
+  for (int t0 = t_begin; t0 < t_end; t0 += 4) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int t = t0 + u;
@@ -331,6 +355,22 @@ __global__ __launch_bounds__(256, 1) void prefill_fused_kernel(
   }
   mfma_half(bp, ap);           // second half of the last step
 
+  if (unit >= 0) {
+    // Split segment: the accumulators go to partial tile `unit`, float4 g4
+    // (16 per MFMA tile (i, j)) of thread tid at float4 index g4 * 256 + tid.
+    float4* dst = reinterpret_cast<float4*>(part) + (size_t)unit * (kPartFloats / 4);
+#pragma unroll
+    for (int i = 0; i < kFM; ++i)
+#pragma unroll
+      for (int j = 0; j < kFN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x16 v = acc[i][j];
+          dst[((i * kFN + j) * 4 + g) * 256 + tid] = make_float4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
+        }
+    return;
+  }
+
   // D of tile (i, j) (weights as the row operand): lane holds x row
   // m_wave + 32 i + lane % 32 and, for register group g, weight rows
   // n0 + 32 j + 8 g + 4 (lane / 32) + e, e = 0..3.
@@ -359,6 +399,62 @@ __global__ __launch_bounds__(256, 1) void prefill_fused_kernel(
   }
 }
 
+// Sum the S partial tiles of every split tile and store bf16: workgroup
+// (split tile, float4 group g4), thread tid; the element mapping is the one
+// of the main kernel's epilogue.
+__global__ __launch_bounds__(256) void prefill_fold_kernel(const float* __restrict__ part,
+                                                           uint16_t* __restrict__ out, int R, int M,
+                                                           PrefillPlan plan) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ts = blockIdx.x / 64, g4 = blockIdx.x % 64;
+  const int tile = plan.nfull + ts;
+  const int mb = tile / plan.nn, nb = tile - mb * plan.nn;
+  const int i = g4 / (kFN * 4), j = (g4 / 4) % kFN, g = g4 % 4;
+  const int m = mb * kBM + wave * kWM + 32 * i + (lane & 31);
+  const int n = nb * kBN + 32 * j + 8 * g + 4 * (lane >> 5);
+  const float4* src = reinterpret_cast<const float4*>(part) + (size_t)ts * plan.S * (kPartFloats / 4) + g4 * 256 + tid;
+  float4 v = src[0];
+  for (int s = 1; s < plan.S; ++s) {
+    const float4 w = src[(size_t)s * (kPartFloats / 4)];
+    v.x += w.x;
+    v.y += w.y;
+    v.z += w.z;
+    v.w += w.w;
+  }
+  if (m >= M) return;
+  uint16_t* orow = out + (size_t)m * (size_t)R;
+  if ((R & 3) == 0 && n + 3 < R) {
+    *reinterpret_cast<uint2*>(orow + n) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+  } else {
+    const float e[4] = {v.x, v.y, v.z, v.w};
+    for (int q = 0; q < 4; ++q)
+      if (n + q < R) orow[n + q] = f32_to_bf16_bits(e[q]);
+  }
+}
+
+PrefillPlan make_plan(int64_t R, int64_t C, int64_t M) {
+  PrefillPlan p{};
+  const int nm = (int)((M + kBM - 1) / kBM);
+  p.nn = (int)((R + kBN - 1) / kBN);
+  p.ntiles = nm * p.nn;
+  const int cus = device_cus();
+  const int nsteps = (int)(C / kBK), quads = nsteps / 4;
+  const int rem = p.ntiles % cus;
+  p.nfull = p.ntiles;
+  p.nsplit = 0;
+  p.S = 1;
+  p.seg = nsteps;
+  if (rem > 0 && 2 * rem <= cus && quads >= 2) {
+    const int S0 = min(cus / rem, quads);
+    p.seg = 4 * ((quads + S0 - 1) / S0);
+    p.S = (nsteps + p.seg - 1) / p.seg;
+    p.nsplit = rem;
+    p.nfull = p.ntiles - rem;
+  }
+  p.per = (p.nfull + kXcds - 1) / kXcds;
+  return p;
+}
+
 }  // namespace
 
 bool prefill_fused_supported(int64_t R, int64_t C, int64_t M, int k) {
@@ -367,19 +463,27 @@ bool prefill_fused_supported(int64_t R, int64_t C, int64_t M, int k) {
          R * C * k / 8 < ((int64_t)1 << 31);
 }
 
+size_t prefill_fused_workspace_bytes(int64_t R, int64_t C, int64_t M) {
+  const PrefillPlan p = make_plan(R, C, M);
+  return (size_t)p.nsplit * (size_t)p.S * kPartFloats * sizeof(float);
+}
+
 hipError_t launch_prefill_fused(const uint32_t* codes, const uint16_t* scales, const uint16_t* x,
                                 uint16_t* out, int64_t R, int64_t C, int64_t M, int k,
-                                hipStream_t stream) {
-  const int nm = (int)((M + kBM - 1) / kBM), nn = (int)((R + kBN - 1) / kBN);
-  const int ntiles = nm * nn, per = (ntiles + kXcds - 1) / kXcds;
-  const dim3 grid((unsigned)(per * kXcds)), block(256);
+                                void* workspace, hipStream_t stream) {
+  const PrefillPlan p = make_plan(R, C, M);
+  float* part = reinterpret_cast<float*>(workspace);
+  const dim3 grid((unsigned)(kXcds * p.per + p.nsplit * p.S)), block(256);
   const int r = (int)R, c = (int)C, m = (int)M;
   switch (k) {
-    case 2: hipLaunchKernelGGL(prefill_fused_kernel<2>, grid, block, 0, stream, codes, scales, x, out, r, c, m, nn, ntiles, per); break;
-    case 3: hipLaunchKernelGGL(prefill_fused_kernel<3>, grid, block, 0, stream, codes, scales, x, out, r, c, m, nn, ntiles, per); break;
-    case 4: hipLaunchKernelGGL(prefill_fused_kernel<4>, grid, block, 0, stream, codes, scales, x, out, r, c, m, nn, ntiles, per); break;
+    case 2: hipLaunchKernelGGL(prefill_fused_kernel<2>, grid, block, 0, stream, codes, scales, x, out, part, r, c, m, p); break;
+    case 3: hipLaunchKernelGGL(prefill_fused_kernel<3>, grid, block, 0, stream, codes, scales, x, out, part, r, c, m, p); break;
+    case 4: hipLaunchKernelGGL(prefill_fused_kernel<4>, grid, block, 0, stream, codes, scales, x, out, part, r, c, m, p); break;
     default: return hipErrorInvalidValue;
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.nsplit == 0) return e;
+  hipLaunchKernelGGL(prefill_fold_kernel, dim3((unsigned)(p.nsplit * 64)), dim3(256), 0, stream, part, out, r, m, p);
   return hipGetLastError();
 }
 
