@@ -119,6 +119,8 @@ def _nrep(bytes_per_copy):
 
 
 AXIS1_SOURCES = ("axis1.hip", "copy_ring.hpp", "mfma_common.hpp", "trellis_device.hpp")
+AXIS0_SOURCES = ("axis0.hip", "copy_ring.hpp", "mfma_common.hpp", "trellis_device.hpp")
+PREFILL_SOURCES = ("prefill.hip", "mfma_common.hpp", "trellis_device.hpp")
 
 
 class GateUp(Workload):
@@ -253,8 +255,10 @@ class Prefill(Workload):
         self.kernels_per_step = 1 if self.graph else 2
         self.units_per_step = 2.0 * M * m.R * m.C
         self.name = w.name
-        self.kernel = "prefill_fused_kernel" if self.graph else "expand_kernel + hipBLASLt GEMM (per call)"
-        self.profile = None
+        self.kernel = ("prefill_fused_kernel (+ prefill_fold_kernel for split tiles), one step" if self.graph
+                       else "expand_kernel + hipBLASLt GEMM (per call)")
+        self.profile = "prefill_17408x5120_k2_m2048.md" if (self.graph and M == 2048) else None
+        self.profile_sources = PREFILL_SOURCES
         self.config = {"workload": w.name, "M": M, "R": m.R, "C": m.C, "k": m.k, "L": L, "T": T,
                        "algo": args.algo}
 
@@ -299,7 +303,7 @@ class Copy(Workload):
 def workload_axis0(args, np, torch, dev):
     import trellis_inputs as ti
     Ms = (args.m,) if args.m else (1, 2, 3, 4)
-    return Matvec(ti.axis0(), Ms, "axis0 scatter + fold", None, ("axis0.hip", "copy_ring.hpp", "mfma_common.hpp", "trellis_device.hpp"),
+    return Matvec(ti.axis0(), Ms, "axis0 scatter + fold", "axis0_scatter_17408x5120_k3.md", AXIS0_SOURCES,
                   args, np, torch, dev)
 
 

@@ -35,6 +35,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kCols = 256;                // output columns per workgroup (one block)
+constexpr int kXcds = 8;                  // workgroup b runs on XCD b % 8
 constexpr int kChunks = kCols / 64;       // 64-column chunks: four MFMAs each
 constexpr int kMaxSlots = 3;
 constexpr int kMaxDma = 5;                // copies per wave per 32-row tile (k = 4: 32 rows x 9 granules)
@@ -67,7 +68,17 @@ __global__ __launch_bounds__(kThreads) void axis0_kernel(const uint32_t* __restr
   const int i = lane & 15, q = lane >> 4;
   const int M = g.M;
   const int64_t R = g.R, C = g.C;
-  const int cgi = (int)(blockIdx.x % g.ncg), s = (int)(blockIdx.x / g.ncg);
+  // Workgroup order: a row's blocks of 4 consecutive column groups fill
+  // exactly k 128-byte lines, and neighbouring groups share the lines
+  // between them.  Each unit (quad of column groups, row split) therefore
+  // runs its 4 workgroups on one XCD (workgroup b runs on XCD b % 8), so every
+  // line is fetched into a single L2.
+  const int xcd = (int)(blockIdx.x % kXcds), j = (int)(blockIdx.x / kXcds);
+  const int unit = (j >> 2) * kXcds + xcd;
+  const int nq = (g.ncg + 3) >> 2;
+  if (unit >= nq * g.S) return;
+  const int cgi = 4 * (unit % nq) + (j & 3), s = unit / nq;
+  if (cgi >= g.ncg) return;
   const int64_t r0 = (int64_t)s * g.rps;
   const int nr = (int)((R - r0 < g.rps) ? R - r0 : g.rps);   // rows of this split (>= 1)
   const int nblk = (nr + 31) >> 5;
@@ -401,8 +412,10 @@ hipError_t axis0_launch(const uint32_t* codes, const uint16_t* scales, const uin
     if (e != hipSuccess) return e;
     lds_attr |= bit;
   }
-  hipLaunchKernelGGL((axis0_kernel<K>), dim3((unsigned)(g.ncg * g.S)), dim3(kThreads), g.total, stream, codes,
-                     scales, x, partial, g);
+  const int units = ((g.ncg + 3) / 4) * g.S;
+  const unsigned grid = (unsigned)(4 * kXcds * ((units + kXcds - 1) / kXcds));
+  hipLaunchKernelGGL((axis0_kernel<K>), dim3(grid), dim3(kThreads), g.total, stream, codes, scales, x,
+                     partial, g);
   return hipGetLastError();
 }
 
