@@ -84,3 +84,20 @@ def test_graph_axis0():
     _check_replays(lambda: tq.matvec_axis0(dc, ds, dx, k, out=out, workspace=ws), out,
                    lambda: (ws.fill_(0x7F), tq.matvec_axis0(dc, ds, dx.flip(0).contiguous(), k, out=junk,
                                                             workspace=ws)))
+
+
+@pytest.mark.parametrize("algo", [tq.PREFILL_FUSED, tq.PREFILL_EXPAND_GEMM])
+def test_graph_prefill(algo):
+    # 1000 x 1024 at M = 40: 8 fused tiles, all split along C (main kernel + fold);
+    # the expand + GEMM plan is tuned by the eager call before capture.
+    rng = np.random.default_rng(74)
+    R, C, M, k = 1000, 1024, 40, 3
+    c, s = ti.codes(rng, R, C, k), ti.scales(rng, R)
+    x = ti.activations(rng, M, C)
+    dc, ds, dx = _d(c, torch.int32), _d(s, torch.float16), _d(x, torch.bfloat16)
+    ws = torch.empty(max(tq.prefill_workspace_bytes(R, C, M, k, algo), 256), dtype=torch.uint8, device=DEV)
+    out = torch.empty((M, R), dtype=torch.bfloat16, device=DEV)
+    junk = torch.empty((M, R), dtype=torch.bfloat16, device=DEV)
+    _check_replays(lambda: tq.prefill(dc, ds, dx, k, algo=algo, out=out, workspace=ws), out,
+                   lambda: (ws.fill_(0x7F), tq.prefill(dc, ds, dx.flip(0).contiguous(), k, algo=algo, out=junk,
+                                                        workspace=ws)))

@@ -108,10 +108,15 @@ constexpr size_t kGemmWorkspace = (size_t)64 << 20;
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+constexpr int kGemmCandidates = 16;
+
 struct GemmPlan {
   hipblasLtMatmulDesc_t desc = nullptr;
   hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, lc = nullptr;
-  hipblasLtMatmulAlgo_t algo;
+  hipblasLtMatmulAlgo_t algo;                                  // in use
+  hipblasLtMatmulHeuristicResult_t cand[kGemmCandidates];      // hipBLASLt's candidates, best first
+  int ncand = 0;
+  bool tuned = false;
 };
 
 std::mutex g_lt_mu;
@@ -140,8 +145,6 @@ int gemm_bf16_nt(const char* fn, const uint16_t* W, const uint16_t* x, uint16_t*
     hipblasOperation_t ta = HIPBLAS_OP_T, tb = HIPBLAS_OP_N;
     uint64_t wsb = kGemmWorkspace;
     hipblasLtMatmulPreference_t pref = nullptr;
-    constexpr int kCandidates = 16;
-    hipblasLtMatmulHeuristicResult_t heur[kCandidates];
     int returned = 0;
     bool good = hipblasLtMatmulDescCreate(&p.desc, HIPBLAS_COMPUTE_32F, HIP_R_32F) == HIPBLAS_STATUS_SUCCESS &&
                 hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSA, &ta, sizeof(ta)) == HIPBLAS_STATUS_SUCCESS &&
@@ -151,7 +154,7 @@ int gemm_bf16_nt(const char* fn, const uint16_t* W, const uint16_t* x, uint16_t*
                 hipblasLtMatrixLayoutCreate(&p.lc, HIP_R_16BF, (uint64_t)R, (uint64_t)M, R) == HIPBLAS_STATUS_SUCCESS &&
                 hipblasLtMatmulPreferenceCreate(&pref) == HIPBLAS_STATUS_SUCCESS &&
                 hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &wsb, sizeof(wsb)) == HIPBLAS_STATUS_SUCCESS &&
-                hipblasLtMatmulAlgoGetHeuristic(h, p.desc, p.la, p.lb, p.lc, p.lc, pref, kCandidates, heur, &returned) == HIPBLAS_STATUS_SUCCESS &&
+                hipblasLtMatmulAlgoGetHeuristic(h, p.desc, p.la, p.lb, p.lc, p.lc, pref, kGemmCandidates, p.cand, &returned) == HIPBLAS_STATUS_SUCCESS &&
                 returned > 0;
     if (pref) hipblasLtMatmulPreferenceDestroy(pref);
     if (!good) {
@@ -162,50 +165,42 @@ int gemm_bf16_nt(const char* fn, const uint16_t* W, const uint16_t* x, uint16_t*
       return fail(TRELLIS_EHIP, "%s: no hipBLASLt bf16 GEMM for %lld x %lld x %lld", fn, (long long)M,
                   (long long)R, (long long)C);
     }
-    p.algo = heur[0].algo;
-    // First call for this shape: time every candidate on the caller's
-    // buffers (each writes the same product into out; the final call below
-    // writes it once more) and keep the fastest.  Under stream capture
-    // nothing can be timed, so the top heuristic is used and not cached.
-    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-    const bool capturing = hipStreamIsCapturing(stream, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone;
-    if (capturing) {
+    p.algo = p.cand[0].algo;
+    p.ncand = returned;
+    pit = g_lt_plans.emplace(key, p).first;
+  }
+  // First uncaptured call for this shape: time every candidate on the
+  // caller's buffers (each writes the same product into out; the call below
+  // writes it once more) and keep the fastest.  Under stream capture nothing
+  // can be timed, so the top heuristic runs until an uncaptured call tunes.
+  GemmPlan& tp = pit->second;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  const bool capturing = hipStreamIsCapturing(stream, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone;
+  if (!tp.tuned && !capturing) {
+    tp.tuned = true;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (tp.ncand > 1 && hipEventCreate(&e0) == hipSuccess && hipEventCreate(&e1) == hipSuccess) {
       const float alpha = 1.0f, beta = 0.0f;
-      hipblasStatus_t st = hipblasLtMatmul(h, p.desc, &alpha, W, p.la, x, p.lb, &beta, out, p.lc, out,
-                                           p.lc, &p.algo, ws, ws_bytes, stream);
-      hipblasLtMatrixLayoutDestroy(p.la);
-      hipblasLtMatrixLayoutDestroy(p.lb);
-      hipblasLtMatrixLayoutDestroy(p.lc);
-      hipblasLtMatmulDescDestroy(p.desc);
-      if (st != HIPBLAS_STATUS_SUCCESS) return fail(TRELLIS_EHIP, "%s: hipblasLtMatmul status %d", fn, (int)st);
-      return ok();
-    }
-    if (returned > 1) {
-      hipEvent_t e0 = nullptr, e1 = nullptr;
-      if (hipEventCreate(&e0) == hipSuccess && hipEventCreate(&e1) == hipSuccess) {
-        const float alpha = 1.0f, beta = 0.0f;
-        float best = -1.0f;
-        for (int i = 0; i < returned; ++i) {
-          if (heur[i].workspaceSize > ws_bytes) continue;
-          bool run_ok = hipblasLtMatmul(h, p.desc, &alpha, W, p.la, x, p.lb, &beta, out, p.lc, out, p.lc,
-                                        &heur[i].algo, ws, ws_bytes, stream) == HIPBLAS_STATUS_SUCCESS;
-          run_ok = run_ok && hipEventRecord(e0, stream) == hipSuccess;
-          for (int rep = 0; run_ok && rep < 3; ++rep)
-            run_ok = hipblasLtMatmul(h, p.desc, &alpha, W, p.la, x, p.lb, &beta, out, p.lc, out, p.lc,
-                                     &heur[i].algo, ws, ws_bytes, stream) == HIPBLAS_STATUS_SUCCESS;
-          run_ok = run_ok && hipEventRecord(e1, stream) == hipSuccess && hipEventSynchronize(e1) == hipSuccess;
-          float ms = 0.0f;
-          if (run_ok && hipEventElapsedTime(&ms, e0, e1) == hipSuccess && (best < 0.0f || ms < best)) {
-            best = ms;
-            p.algo = heur[i].algo;
-          }
+      float best = -1.0f;
+      for (int i = 0; i < tp.ncand; ++i) {
+        if (tp.cand[i].workspaceSize > ws_bytes) continue;
+        bool run_ok = hipblasLtMatmul(h, tp.desc, &alpha, W, tp.la, x, tp.lb, &beta, out, tp.lc, out, tp.lc,
+                                      &tp.cand[i].algo, ws, ws_bytes, stream) == HIPBLAS_STATUS_SUCCESS;
+        run_ok = run_ok && hipEventRecord(e0, stream) == hipSuccess;
+        for (int rep = 0; run_ok && rep < 3; ++rep)
+          run_ok = hipblasLtMatmul(h, tp.desc, &alpha, W, tp.la, x, tp.lb, &beta, out, tp.lc, out, tp.lc,
+                                   &tp.cand[i].algo, ws, ws_bytes, stream) == HIPBLAS_STATUS_SUCCESS;
+        run_ok = run_ok && hipEventRecord(e1, stream) == hipSuccess && hipEventSynchronize(e1) == hipSuccess;
+        float ms = 0.0f;
+        if (run_ok && hipEventElapsedTime(&ms, e0, e1) == hipSuccess && (best < 0.0f || ms < best)) {
+          best = ms;
+          tp.algo = tp.cand[i].algo;
         }
       }
-      if (e0) hipEventDestroy(e0);
-      if (e1) hipEventDestroy(e1);
-      (void)hipGetLastError();
     }
-    pit = g_lt_plans.emplace(key, p).first;
+    if (e0) hipEventDestroy(e0);
+    if (e1) hipEventDestroy(e1);
+    (void)hipGetLastError();
   }
   const float alpha = 1.0f, beta = 0.0f;
   const GemmPlan& p = pit->second;
