@@ -243,6 +243,23 @@ def test_prefill_small(algo, k, R, C, M):
     tol.assert_bf16_close(got, want, f"prefill algo={algo} R={R} C={C} M={M} k={k}")
 
 
+@pytest.mark.parametrize("k", [2, 3])
+def test_prefill_fused_stream_pieces(k):
+    # 200 tiles of 512 x 128 on a 256-CU part: the leftover tiles fill more than half of the CUs,
+    # so the fused kernel deals the 200 x 40 steps out in ranges of 32 steps that cross tile
+    # boundaries (whole tiles stored directly, the pieces folded).  Sampled rows and x rows.
+    rng = np.random.default_rng(90 + k)
+    R, C, M = 25600, 1280, 64
+    codes, scales = rand_matrix(rng, R, C, k)
+    x = ti.activations(rng, M, C)
+    got = tq.prefill(d_codes(codes), d_half(scales), d_bf16(x), k, algo=tq.PREFILL_FUSED)
+    ms = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, 6)]))
+    rows = np.unique(np.concatenate([[0, 127, 128, 5119, 5120, R - 1], rng.integers(0, R, 120)]))
+    want = oracle.prefill_sums(codes, scales, x, M, R, C, k, L, T, ms, rows)
+    sub = h_u16(got[torch.as_tensor(ms, device=DEV)][:, torch.as_tensor(rows, device=DEV)])
+    tol.assert_bf16_close(sub, want, f"prefill stream pieces k={k}")
+
+
 @pytest.fixture(scope="module")
 def prefill_workload():
     return ti.prefill()

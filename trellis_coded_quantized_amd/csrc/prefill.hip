@@ -113,16 +113,26 @@ __device__ __forceinline__ void decode_run8(const uint32_t (&w)[Run16<K>::kLoad]
   for (int p = 0; p < 4; ++p) pk[p] = pack_bf16x2(f[2 * p], f[2 * p + 1]);
 }
 
-// Work plan.  The first nfull tiles run whole, in the XCD-aware order below.
-// When the tiles left after the full rounds would fill at most half of the
-// CUs, each of those nsplit tiles is cut instead into S segments of seg steps
-// (a multiple of 4), one workgroup each, which leave f32 partial tiles in
-// the workspace; prefill_fold_kernel adds them up.
+// Work plan, in one of two modes.
+//  * Rounds (stream == 0): the first nfull tiles run whole, in the XCD-aware
+//    order below.  When the tiles left after the full rounds would fill at
+//    most half of the CUs, each of those nsplit tiles is cut instead into S
+//    segments of seg steps (a multiple of 4), one workgroup each, which leave
+//    f32 partial tiles in slots unit = (tile - nfull) * S + segment.
+//  * Stream (stream == 1, when the leftover tiles would fill more than half
+//    of the CUs): the ntiles * nsteps steps are dealt out as G contiguous
+//    ranges of U steps (U a multiple of 4), one persistent workgroup each.
+//    A range crosses tile boundaries; whole tiles inside it are stored
+//    directly, the piece of a tile at its start goes to slot 2 g and the
+//    piece at its end to slot 2 g + 1.
+// prefill_fold_kernel adds up the partial tiles of every split tile.
 struct PrefillPlan {
   int nn;            // tiles along the weight rows
-  int ntiles;
-  int nfull, per;    // whole tiles; per XCD
+  int ntiles, nsteps;
+  int stream;
+  int nfull, per;    // rounds: whole tiles; per XCD
   int nsplit, S, seg;
+  int U, G;          // stream: steps per workgroup, workgroups
 };
 
 constexpr int kPartFloats = kBM * kBN;   // one partial tile: 256 floats per thread, float4-interleaved
@@ -142,21 +152,11 @@ __global__ __launch_bounds__(256, 1) void prefill_fused_kernel(
   __shared__ __attribute__((aligned(16))) u32x4 Xs0[kWaves][kWM * kChunkLines];
   __shared__ __attribute__((aligned(16))) u32x4 Xs1[kWaves][kWM * kChunkLines];
 
-  // XCD-aware tile order: workgroup b runs on XCD b % 8; that XCD takes a
-  // contiguous range of tiles, which share their 512 x rows.  Split
-  // segments come after all whole tiles.
   const int nsteps = C / kBK;
-  const int bid = blockIdx.x;
-  int tile, unit = -1, t_begin = 0, t_end = nsteps;
-  if (bid < kXcds * plan.per) {
-    tile = (bid % kXcds) * plan.per + bid / kXcds;
-    if (tile >= plan.nfull) return;
-  } else {
-    unit = bid - kXcds * plan.per;                 // split unit: tile nfull + unit / S, segment unit % S
-    tile = plan.nfull + unit / plan.S;
-    t_begin = (unit % plan.S) * plan.seg;
-    t_end = min(nsteps, t_begin + plan.seg);
-  }
+
+  // One piece: steps [t_begin, t_end) of `tile` (t_begin a multiple of 4);
+  // its accumulators go to partial slot `unit`, or to out when unit < 0.
+  auto piece = [&](const int tile, const int t_begin, const int t_end, const int unit) {
   const int mb = tile / plan.nn, nb = tile - mb * plan.nn;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -397,30 +397,89 @@ __global__ __launch_bounds__(256, 1) void prefill_fused_kernel(
         }
       }
   }
+  };
+
+  // Pieces of this workgroup.  Rounds: one (a whole tile in the XCD-aware
+  // order -- workgroup b runs on XCD b % 8 and that XCD takes a contiguous
+  // range of tiles, which share their 512 x rows -- or one split segment,
+  // after all whole tiles).  Stream: the pieces of its range of steps.
+  const int bid = blockIdx.x;
+  int tile = 0, tb = 0, te = nsteps, unit = -1, pos = 0, start = 0, end = 0;
+  if (!plan.stream) {
+    if (bid < kXcds * plan.per) {
+      tile = (bid % kXcds) * plan.per + bid / kXcds;
+      if (tile >= plan.nfull) return;
+    } else {
+      unit = bid - kXcds * plan.per;               // split unit: tile nfull + unit / S, segment unit % S
+      tile = plan.nfull + unit / plan.S;
+      tb = (unit % plan.S) * plan.seg;
+      te = min(nsteps, tb + plan.seg);
+    }
+  } else {
+    start = bid * plan.U;
+    end = min(plan.ntiles * nsteps, start + plan.U);
+    pos = start;
+  }
+  for (;;) {
+    if (plan.stream) {
+      tile = pos / nsteps;
+      tb = pos - tile * nsteps;
+      te = min(nsteps, tb + (end - pos));
+      unit = (tb == 0 && te == nsteps) ? -1 : 2 * bid + (pos == start ? 0 : 1);
+    }
+    piece(tile, tb, te, unit);
+    if (!plan.stream) break;
+    pos += te - tb;
+    if (pos >= end) break;
+    __syncthreads();                               // the next piece reuses the LDS buffers
+  }
 }
 
-// Sum the S partial tiles of every split tile and store bf16: workgroup
-// (split tile, float4 group g4), thread tid; the element mapping is the one
-// of the main kernel's epilogue.
+// Sum the partial tiles of every split tile and store bf16: workgroup
+// (tile, float4 group g4), thread tid; the element mapping is the one of the
+// main kernel's epilogue.  Rounds: the split tiles are nfull + blockIdx / 64,
+// with slots ts * S .. ts * S + S - 1.  Stream: every tile has a workgroup;
+// tile t is split when its steps span the ranges of workgroups ga < gb, and
+// its piece of workgroup g sits in slot 2 g (g's first piece) or 2 g + 1 (ga,
+// whose range began in an earlier tile).
 __global__ __launch_bounds__(256) void prefill_fold_kernel(const float* __restrict__ part,
                                                            uint16_t* __restrict__ out, int R, int M,
                                                            PrefillPlan plan) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ts = blockIdx.x / 64, g4 = blockIdx.x % 64;
-  const int tile = plan.nfull + ts;
+  const float4* base = reinterpret_cast<const float4*>(part) + g4 * 256 + tid;
+  constexpr size_t kSlot = kPartFloats / 4;
+  int tile;
+  float4 v;
+  if (!plan.stream) {
+    tile = plan.nfull + ts;
+    const float4* src = base + (size_t)ts * plan.S * kSlot;
+    v = src[0];
+    for (int s = 1; s < plan.S; ++s) {
+      const float4 w = src[(size_t)s * kSlot];
+      v.x += w.x;
+      v.y += w.y;
+      v.z += w.z;
+      v.w += w.w;
+    }
+  } else {
+    tile = ts;
+    const int ga = tile * plan.nsteps / plan.U, gb = ((tile + 1) * plan.nsteps - 1) / plan.U;
+    if (ga == gb) return;                          // whole inside one range: stored by the main kernel
+    const int first_of_ga = (ga * plan.U) / plan.nsteps == tile;
+    v = base[(size_t)(2 * ga + (first_of_ga ? 0 : 1)) * kSlot];
+    for (int g = ga + 1; g <= gb; ++g) {
+      const float4 w = base[(size_t)(2 * g) * kSlot];
+      v.x += w.x;
+      v.y += w.y;
+      v.z += w.z;
+      v.w += w.w;
+    }
+  }
   const int mb = tile / plan.nn, nb = tile - mb * plan.nn;
   const int i = g4 / (kFN * 4), j = (g4 / 4) % kFN, g = g4 % 4;
   const int m = mb * kBM + wave * kWM + 32 * i + (lane & 31);
   const int n = nb * kBN + 32 * j + 8 * g + 4 * (lane >> 5);
-  const float4* src = reinterpret_cast<const float4*>(part) + (size_t)ts * plan.S * (kPartFloats / 4) + g4 * 256 + tid;
-  float4 v = src[0];
-  for (int s = 1; s < plan.S; ++s) {
-    const float4 w = src[(size_t)s * (kPartFloats / 4)];
-    v.x += w.x;
-    v.y += w.y;
-    v.z += w.z;
-    v.w += w.w;
-  }
   if (m >= M) return;
   uint16_t* orow = out + (size_t)m * (size_t)R;
   if ((R & 3) == 0 && n + 3 < R) {
@@ -440,6 +499,7 @@ PrefillPlan make_plan(int64_t R, int64_t C, int64_t M) {
   const int cus = device_cus();
   const int nsteps = (int)(C / kBK), quads = nsteps / 4;
   const int rem = p.ntiles % cus;
+  p.nsteps = nsteps;
   p.nfull = p.ntiles;
   p.nsplit = 0;
   p.S = 1;
@@ -450,6 +510,11 @@ PrefillPlan make_plan(int64_t R, int64_t C, int64_t M) {
     p.S = (nsteps + p.seg - 1) / p.seg;
     p.nsplit = rem;
     p.nfull = p.ntiles - rem;
+  } else if (rem > 0 && quads >= 2) {
+    const int64_t total = (int64_t)p.ntiles * nsteps;
+    p.stream = 1;
+    p.U = (int)(4 * ((total + 4 * (int64_t)cus - 1) / (4 * (int64_t)cus)));
+    p.G = (int)((total + p.U - 1) / p.U);
   }
   p.per = (p.nfull + kXcds - 1) / kXcds;
   return p;
@@ -458,14 +523,17 @@ PrefillPlan make_plan(int64_t R, int64_t C, int64_t M) {
 }  // namespace
 
 bool prefill_fused_supported(int64_t R, int64_t C, int64_t M, int k) {
-  // 32-bit buffer offsets: x and one weight matrix's codes below 2 GiB
+  // 32-bit buffer offsets (x and one weight matrix's codes below 2 GiB)
+  // and 32-bit step counters over the whole problem
+  const int64_t steps = ((M + kBM - 1) / kBM) * ((R + kBN - 1) / kBN) * (C / kBK);
   return k >= 2 && k <= 4 && C % (4 * kBK) == 0 && M * C * 2 < ((int64_t)1 << 31) &&
-         R * C * k / 8 < ((int64_t)1 << 31);
+         R * C * k / 8 < ((int64_t)1 << 31) && steps < ((int64_t)1 << 30);
 }
 
 size_t prefill_fused_workspace_bytes(int64_t R, int64_t C, int64_t M) {
   const PrefillPlan p = make_plan(R, C, M);
-  return (size_t)p.nsplit * (size_t)p.S * kPartFloats * sizeof(float);
+  const size_t slots = p.stream ? 2 * (size_t)p.G : (size_t)p.nsplit * (size_t)p.S;
+  return slots * kPartFloats * sizeof(float);
 }
 
 hipError_t launch_prefill_fused(const uint32_t* codes, const uint16_t* scales, const uint16_t* x,
@@ -473,7 +541,7 @@ hipError_t launch_prefill_fused(const uint32_t* codes, const uint16_t* scales, c
                                 void* workspace, hipStream_t stream) {
   const PrefillPlan p = make_plan(R, C, M);
   float* part = reinterpret_cast<float*>(workspace);
-  const dim3 grid((unsigned)(kXcds * p.per + p.nsplit * p.S)), block(256);
+  const dim3 grid((unsigned)(p.stream ? p.G : kXcds * p.per + p.nsplit * p.S)), block(256);
   const int r = (int)R, c = (int)C, m = (int)M;
   switch (k) {
     case 2: hipLaunchKernelGGL(prefill_fused_kernel<2>, grid, block, 0, stream, codes, scales, x, out, part, r, c, m, p); break;
@@ -482,8 +550,9 @@ hipError_t launch_prefill_fused(const uint32_t* codes, const uint16_t* scales, c
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.nsplit == 0) return e;
-  hipLaunchKernelGGL(prefill_fold_kernel, dim3((unsigned)(p.nsplit * 64)), dim3(256), 0, stream, part, out, r, m, p);
+  if (e != hipSuccess || (!p.stream && p.nsplit == 0)) return e;
+  const unsigned fold_blocks = (unsigned)((p.stream ? p.ntiles : p.nsplit) * 64);
+  hipLaunchKernelGGL(prefill_fold_kernel, dim3(fold_blocks), dim3(256), 0, stream, part, out, r, m, p);
   return hipGetLastError();
 }
 
