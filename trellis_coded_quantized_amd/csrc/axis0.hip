@@ -54,6 +54,56 @@ struct Axis0Geom {
   uint32_t slot_bytes, xt_off, scr_off, total;
 };
 
+// Row pairs of one chunk word: ds_read2_b32 of tile rows (0,1), (2,3), (4,5),
+// (6,7) from address operand A, rows S dwords apart.
+#define TRELLIS_A0_ROWS(O0, O1, O2, O3, A, S0, S1, S2, S3, S4, S5, S6, S7)  \
+  "ds_read2_b32 %" #O0 ", %" #A " offset0:" #S0 " offset1:" #S1 "\n\t"     \
+  "ds_read2_b32 %" #O1 ", %" #A " offset0:" #S2 " offset1:" #S3 "\n\t"     \
+  "ds_read2_b32 %" #O2 ", %" #A " offset0:" #S4 " offset1:" #S5 "\n\t"     \
+  "ds_read2_b32 %" #O3 ", %" #A " offset0:" #S6 " offset1:" #S7 "\n\t"
+#define TRELLIS_A0_BLOCK(...)                                                \
+  TRELLIS_A0_ROWS(0, 1, 2, 3, 17, __VA_ARGS__)                               \
+  TRELLIS_A0_ROWS(4, 5, 6, 7, 18, __VA_ARGS__)                               \
+  TRELLIS_A0_ROWS(8, 9, 10, 11, 19, __VA_ARGS__)                             \
+  TRELLIS_A0_ROWS(12, 13, 14, 15, 20, __VA_ARGS__)                           \
+  "ds_read_b128 %16, %21\n\ts_waitcnt lgkmcnt(0)"
+#define TRELLIS_A0_OPERANDS                                                  \
+  : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]),  \
+    "=&v"(o[7]), "=&v"(o[8]), "=&v"(o[9]), "=&v"(o[10]), "=&v"(o[11]), "=&v"(o[12]),           \
+    "=&v"(o[13]), "=&v"(o[14]), "=&v"(o[15]), "=&v"(bv)                                          \
+  : "v"(a0[0]), "v"(a1[0]), "v"(a0[1]), "v"(a1[1]), "v"(ab)                                    \
+  : "memory"
+
+// The words of two 64-column chunks for the lane's eight tile rows, read from
+// the ring and waited for in one block: W[c][rr][0] at LDS byte address
+// a0[c] and W[c][rr][1] at a1[c], row rr lying rr * (2K + 1) * 4 dwords
+// further (one block plus one pad granule per row); also the 16 bytes at ab.
+template <int K>
+__device__ __forceinline__ void lds_read_chunks2(const uint32_t (&a0)[2], const uint32_t (&a1)[2], uint32_t ab,
+                                                 uint32_t (&W)[2][8][2], lds_u32x4& bv) {
+  static_assert(words_per_block(K) / 4 + 1 == 2 * K + 1, "tile rows are one block plus one granule");
+  lds_u32x2 o[16];
+  if constexpr (K == 2) {
+    asm volatile(TRELLIS_A0_BLOCK(0, 20, 40, 60, 80, 100, 120, 140) TRELLIS_A0_OPERANDS);
+  } else if constexpr (K == 3) {
+    asm volatile(TRELLIS_A0_BLOCK(0, 28, 56, 84, 112, 140, 168, 196) TRELLIS_A0_OPERANDS);
+  } else {
+    asm volatile(TRELLIS_A0_BLOCK(0, 36, 72, 108, 144, 180, 216, 252) TRELLIS_A0_OPERANDS);
+  }
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int pr = 0; pr < 4; ++pr) {
+      W[c][2 * pr][0] = o[8 * c + pr][0];
+      W[c][2 * pr + 1][0] = o[8 * c + pr][1];
+      W[c][2 * pr][1] = o[8 * c + 4 + pr][0];
+      W[c][2 * pr + 1][1] = o[8 * c + 4 + pr][1];
+    }
+}
+#undef TRELLIS_A0_OPERANDS
+#undef TRELLIS_A0_BLOCK
+#undef TRELLIS_A0_ROWS
+
 template <int K>
 __global__ __launch_bounds__(kThreads) void axis0_kernel(const uint32_t* __restrict__ codes,
                                                          const uint16_t* __restrict__ scales,
@@ -148,10 +198,15 @@ __global__ __launch_bounds__(kThreads) void axis0_kernel(const uint32_t* __restr
     uint16_t sb[8];
     if (fast) {
       wait_vmcnt(nwd * next0);                 // the x and scale copies have landed
+      uint32_t sa[5];
+#pragma unroll
+      for (int c = 0; c < 5; ++c) sa[c] = lds_addr(stg) + (uint32_t)(c * 1024 + lane * 16);
+      lds_u32x4 sv[5];
+      lds_read_b128x5(sa, sv);                 // lanes without copies read stale bytes, masked here
 #pragma unroll
       for (int n = 0; n < 4; ++n)
-        xb[n] = (hold && n < M) ? *reinterpret_cast<const uint4*>(stg + n * 1024 + lane * 16) : make_uint4(0u, 0u, 0u, 0u);
-      const uint4 v = hold ? *reinterpret_cast<const uint4*>(stg + 4 * 1024 + lane * 16) : make_uint4(0u, 0u, 0u, 0u);
+        xb[n] = (hold && n < M) ? make_uint4(sv[n][0], sv[n][1], sv[n][2], sv[n][3]) : make_uint4(0u, 0u, 0u, 0u);
+      const uint4 v = hold ? make_uint4(sv[4][0], sv[4][1], sv[4][2], sv[4][3]) : make_uint4(0u, 0u, 0u, 0u);
       const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int h = 0; h < 8; ++h) sb[h] = (uint16_t)(w4[h >> 1] >> (16 * (h & 1)));
@@ -209,8 +264,8 @@ __global__ __launch_bounds__(kThreads) void axis0_kernel(const uint32_t* __restr
         hw[h >> 1] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
         lw[h >> 1] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
       }
-      *reinterpret_cast<uint4*>(xt + n * g.rps + rl) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-      *reinterpret_cast<uint4*>(xt + (4 + n) * g.rps + rl) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+      lds_write_b128(lds_addr(xt + n * g.rps + rl), lds_u32x4{hw[0], hw[1], hw[2], hw[3]});
+      lds_write_b128(lds_addr(xt + (4 + n) * g.rps + rl), lds_u32x4{lw[0], lw[1], lw[2], lw[3]});
     }
   }
 
@@ -231,11 +286,11 @@ __global__ __launch_bounds__(kThreads) void axis0_kernel(const uint32_t* __restr
     offa[ch] = p0 & 31;
   }
   // B of a 32-row block: lane (n', q) holds xt[n'][8q .. 8q+7] (n' < 8), zero otherwise
-  auto load_b = [&](int blk) {
-    const int nn = i < 8 ? i : 0;
-    const half8 v = *reinterpret_cast<const half8*>(xt + nn * g.rps + blk * 32 + 8 * q);
-    return i < 8 ? v : half8{0, 0, 0, 0, 0, 0, 0, 0};
+  auto b_addr = [&](int blk) { return lds_addr(xt + (i < 8 ? i : 0) * g.rps + blk * 32 + 8 * q); };
+  auto b_operand = [&](lds_u32x4 v) {
+    return i < 8 ? __builtin_bit_cast(half8, v) : half8{0, 0, 0, 0, 0, 0, 0, 0};
   };
+  auto load_b = [&](int blk) { return b_operand(lds_read_b128(b_addr(blk))); };
   // the byte-sum bias over this wave's blocks: 510 * 2^-24 * sum_r B[r][n'] in every row
   f32x4 bias = f32x4{0.f, 0.f, 0.f, 0.f};
   const half8 a510 = __builtin_bit_cast(half8, u32x4{0x01FE01FEu, 0x01FE01FEu, 0x01FE01FEu, 0x01FE01FEu});
@@ -253,17 +308,8 @@ __global__ __launch_bounds__(kThreads) void axis0_kernel(const uint32_t* __restr
   for (int t = 0; t < nmy; ++t) {
     wait_vmcnt(nwd * (next - 1 - t));          // tile t has landed
     const int blk = wave + kWaves * t;
-    const half8 Bv = load_b(blk);
+    half8 Bv;
     const uint8_t* tile = ring + (size_t)(t % NS) * g.slot_bytes + (size_t)(8 * q) * gsr * 16;
-    // the words of chunk ch for rows 8q .. 8q+7 (read one chunk ahead of the decode)
-    auto load_chunk = [&](int ch, uint32_t (&W)[8][2]) {
-#pragma unroll
-      for (int rr = 0; rr < 8; ++rr) {
-        const uint32_t* rowp = reinterpret_cast<const uint32_t*>(tile + (size_t)rr * gsr * 16);
-        W[rr][0] = rowp[wia[ch]];
-        W[rr][1] = rowp[wna[ch]];
-      }
-    };
     // 8 rows x 4 columns: windows, then 1MAD words, then row-paired byte sums
     auto decode_chunk = [&](int ch, const uint32_t (&W)[8][2]) {
       uint32_t st[8][4];
@@ -287,14 +333,18 @@ __global__ __launch_bounds__(kThreads) void axis0_kernel(const uint32_t* __restr
         acc[ch][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, A), Bv, acc[ch][j], 0, 0, 0);
       }
     };
-    uint32_t Wa[8][2], Wb[8][2];
-    load_chunk(0, Wa);
+    // two chunks per read block (the first also brings this block's B)
+    const uint32_t ta = lds_addr(tile), ab = b_addr(blk);
 #pragma unroll
     for (int ch = 0; ch < kChunks; ch += 2) {
-      load_chunk(ch + 1, Wb);
-      decode_chunk(ch, Wa);
-      if (ch + 2 < kChunks) load_chunk(ch + 2, Wa);
-      decode_chunk(ch + 1, Wb);
+      const uint32_t a0[2] = {ta + (uint32_t)wia[ch] * 4u, ta + (uint32_t)wia[ch + 1] * 4u};
+      const uint32_t a1[2] = {ta + (uint32_t)wna[ch] * 4u, ta + (uint32_t)wna[ch + 1] * 4u};
+      uint32_t W[2][8][2];
+      lds_u32x4 bv;
+      lds_read_chunks2<K>(a0, a1, ab, W, bv);
+      if (ch == 0) Bv = b_operand(bv);
+      decode_chunk(ch, W[0]);
+      decode_chunk(ch + 1, W[1]);
     }
     __atomic_signal_fence(__ATOMIC_SEQ_CST);   // this tile's reads stay before its slot is refilled
     if (next < nmy && next <= t + NS) issue_tile(next++);

@@ -54,10 +54,6 @@ struct Axis1Geom {
   uint32_t slot_bytes, part_off, total;
 };
 
-__device__ __forceinline__ half8 load_half8(const uint8_t* p) {
-  return __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(p));
-}
-
 __device__ __forceinline__ uint32_t max_abs8(const uint4& v) {
   const uint32_t u4[4] = {v.x, v.y, v.z, v.w};
   uint32_t r = 0u;
@@ -93,24 +89,78 @@ __device__ __forceinline__ void decode_run_sub(const uint32_t (&w)[K + 1], uint3
     A[v >> 2][v & 3] = __builtin_amdgcn_sad_u8(xw[2 * v], 0u, __builtin_amdgcn_sad_hi_u8(xw[2 * v + 1], 0u, 0u));
 }
 
+// The code words of five run groups of one tile row, read from the ring and
+// waited for in one block: for group g the K words at LDS byte address aw[g]
+// and the spill word at as[g] (the word after the run, wrapped in its block).
 template <int K>
-__device__ __forceinline__ void read_words(const uint8_t* trow, int wo, int so, uint32_t (&W)[K + 1]) {
-  const uint32_t* t32 = reinterpret_cast<const uint32_t*>(trow);
+__device__ __forceinline__ void lds_read_runs5(const uint32_t (&aw)[5], const uint32_t (&as)[5],
+                                               uint32_t (&W)[5][K + 1]) {
   if constexpr (K == 2) {
-    const uint2 v = *reinterpret_cast<const uint2*>(t32 + wo);
-    W[0] = v.x;
-    W[1] = v.y;
-  } else if constexpr (K == 4) {
-    const uint4 v = *reinterpret_cast<const uint4*>(t32 + wo);
-    W[0] = v.x;
-    W[1] = v.y;
-    W[2] = v.z;
-    W[3] = v.w;
-  } else {
+    lds_u32x2 p[5];
+    uint32_t sp[5];
+    asm volatile(
+        "ds_read_b64 %0, %10\n\tds_read_b32 %1, %11\n\t"
+        "ds_read_b64 %2, %12\n\tds_read_b32 %3, %13\n\t"
+        "ds_read_b64 %4, %14\n\tds_read_b32 %5, %15\n\t"
+        "ds_read_b64 %6, %16\n\tds_read_b32 %7, %17\n\t"
+        "ds_read_b64 %8, %18\n\tds_read_b32 %9, %19\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(p[0]), "=&v"(sp[0]), "=&v"(p[1]), "=&v"(sp[1]), "=&v"(p[2]), "=&v"(sp[2]), "=&v"(p[3]),
+          "=&v"(sp[3]), "=&v"(p[4]), "=&v"(sp[4])
+        : "v"(aw[0]), "v"(as[0]), "v"(aw[1]), "v"(as[1]), "v"(aw[2]), "v"(as[2]), "v"(aw[3]), "v"(as[3]),
+          "v"(aw[4]), "v"(as[4])
+        : "memory");
 #pragma unroll
-    for (int m = 0; m < K; ++m) W[m] = t32[wo + m];
+    for (int g = 0; g < 5; ++g) {
+      W[g][0] = p[g][0];
+      W[g][1] = p[g][1];
+      W[g][2] = sp[g];
+    }
+  } else if constexpr (K == 4) {
+    lds_u32x4 p[5];
+    uint32_t sp[5];
+    asm volatile(
+        "ds_read_b128 %0, %10\n\tds_read_b32 %1, %11\n\t"
+        "ds_read_b128 %2, %12\n\tds_read_b32 %3, %13\n\t"
+        "ds_read_b128 %4, %14\n\tds_read_b32 %5, %15\n\t"
+        "ds_read_b128 %6, %16\n\tds_read_b32 %7, %17\n\t"
+        "ds_read_b128 %8, %18\n\tds_read_b32 %9, %19\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(p[0]), "=&v"(sp[0]), "=&v"(p[1]), "=&v"(sp[1]), "=&v"(p[2]), "=&v"(sp[2]), "=&v"(p[3]),
+          "=&v"(sp[3]), "=&v"(p[4]), "=&v"(sp[4])
+        : "v"(aw[0]), "v"(as[0]), "v"(aw[1]), "v"(as[1]), "v"(aw[2]), "v"(as[2]), "v"(aw[3]), "v"(as[3]),
+          "v"(aw[4]), "v"(as[4])
+        : "memory");
+#pragma unroll
+    for (int g = 0; g < 5; ++g) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) W[g][m] = p[g][m];
+      W[g][4] = sp[g];
+    }
+  } else {                                     // K == 3: words 4-byte aligned only
+    lds_u32x2 p[5];
+    uint32_t t3[5], sp[5];
+    asm volatile(
+        "ds_read2_b32 %0, %15 offset1:1\n\tds_read_b32 %1, %15 offset:8\n\tds_read_b32 %2, %16\n\t"
+        "ds_read2_b32 %3, %17 offset1:1\n\tds_read_b32 %4, %17 offset:8\n\tds_read_b32 %5, %18\n\t"
+        "ds_read2_b32 %6, %19 offset1:1\n\tds_read_b32 %7, %19 offset:8\n\tds_read_b32 %8, %20\n\t"
+        "ds_read2_b32 %9, %21 offset1:1\n\tds_read_b32 %10, %21 offset:8\n\tds_read_b32 %11, %22\n\t"
+        "ds_read2_b32 %12, %23 offset1:1\n\tds_read_b32 %13, %23 offset:8\n\tds_read_b32 %14, %24\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(p[0]), "=&v"(t3[0]), "=&v"(sp[0]), "=&v"(p[1]), "=&v"(t3[1]), "=&v"(sp[1]), "=&v"(p[2]),
+          "=&v"(t3[2]), "=&v"(sp[2]), "=&v"(p[3]), "=&v"(t3[3]), "=&v"(sp[3]), "=&v"(p[4]), "=&v"(t3[4]),
+          "=&v"(sp[4])
+        : "v"(aw[0]), "v"(as[0]), "v"(aw[1]), "v"(as[1]), "v"(aw[2]), "v"(as[2]), "v"(aw[3]), "v"(as[3]),
+          "v"(aw[4]), "v"(as[4])
+        : "memory");
+#pragma unroll
+    for (int g = 0; g < 5; ++g) {
+      W[g][0] = p[g][0];
+      W[g][1] = p[g][1];
+      W[g][2] = t3[g];
+      W[g][3] = sp[g];
+    }
   }
-  W[K] = t32[so];
 }
 
 template <int K, bool GATEUP, int NG>
@@ -205,11 +255,20 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
   // ---- 2. exponent of the slice per vector: its largest |x[n]| * 2^e lands
   // in [2^14, 2^15); then x' = f16(x 2^e) in place
   // every lane holds at most kXPer granules of the slice (M * C / 8 / 64 <= 5 * 64 granules per wave)
+  static_assert(kXPer == 5, "x granules are read five at a time");
   uint4 xr[kXPer];
+  {
+    uint32_t xa[kXPer];
 #pragma unroll
-  for (int u = 0; u < kXPer; ++u) {
-    const int p = lane + 64 * u;
-    xr[u] = p < nxg ? *reinterpret_cast<const uint4*>(xsl + (size_t)p * 16) : make_uint4(0u, 0u, 0u, 0u);
+    for (int u = 0; u < kXPer; ++u) {          // granules past the slice re-read its last one
+      const int p = lane + 64 * u;
+      xa[u] = lds_addr(xsl) + (uint32_t)(p < nxg ? p : nxg - 1) * 16u;
+    }
+    lds_u32x4 xv[kXPer];
+    lds_read_b128x5(xa, xv);
+#pragma unroll
+    for (int u = 0; u < kXPer; ++u)
+      xr[u] = lane + 64 * u < nxg ? make_uint4(xv[u][0], xv[u][1], xv[u][2], xv[u][3]) : make_uint4(0u, 0u, 0u, 0u);
   }
   uint32_t mx0 = 0u, mx1 = 0u, mx2 = 0u, mx3 = 0u;
 #pragma unroll
@@ -249,7 +308,7 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
       const _Float16 hi = (_Float16)ldexpf(bf16_bits_to_f32(u4[h] >> 16), en);
       o[h] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
     }
-    if (p < nxg) *reinterpret_cast<uint4*>(xsl + (size_t)p * 16) = make_uint4(o[0], o[1], o[2], o[3]);
+    if (p < nxg) lds_write_b128(lds_addr(xsl) + (uint32_t)p * 16u, lds_u32x4{o[0], o[1], o[2], o[3]});
   }
 
   // ---- 3. B operand in registers: lane (n, q) of group gg holds
@@ -274,8 +333,10 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
     wo[gg] = blk * WPB + w0;
     so[gg] = blk * WPB + (w0 + K == WPB ? 0 : w0 + K);   // word after the run, wrapping in the block
     const uint8_t* bp = xsl + ((size_t)(i < M ? i : 0) * gx * 8 + (size_t)(runc - rb) * 32) * 2;
+    lds_u32x4 bv[4];
+    lds_read_b128x4(lds_addr(bp), bv);         // in-slice address for every lane
 #pragma unroll
-    for (int u = 0; u < 4; ++u) B[gg][u] = load_half8(bp + 16 * u);   // in-slice address for every lane
+    for (int u = 0; u < 4; ++u) B[gg][u] = __builtin_bit_cast(half8, bv[u]);
   }
 #pragma unroll
   for (int gg = 0; gg < NG; ++gg) {
@@ -308,20 +369,21 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
       for (int u = 0; u < 4; ++u)
         acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, A[u]), Bg[u], acc[u], 0, 0, 0);
     };
-    // LDS word reads run one group ahead of the decode (ping-pong)
-    uint32_t Wa[K + 1], Wb[K + 1];
-    read_words<K>(trow, wo[0], so[0], Wa);
+    // the words of every group of the tile in one read block; groups past
+    // the B capacity re-read group 0 (their words are not used)
+    static_assert(NG <= 5, "at most five run groups per tile row");
+    uint32_t aw[5], as[5];
+    const uint32_t tb = lds_addr(trow);
 #pragma unroll
-    for (int gg = 0; gg < NG; gg += 2) {
-      const int g1 = gg + 1 < NG ? gg + 1 : NG - 1;
-      const int g2 = gg + 2 < NG ? gg + 2 : NG - 1;
-      if (gg < ngw) {
-        if (gg + 1 < NG && gg + 1 < ngw) read_words<K>(trow, wo[g1], so[g1], Wb);
-        consume(Wa, B[gg]);
-        if (gg + 2 < NG && gg + 2 < ngw) read_words<K>(trow, wo[g2], so[g2], Wa);
-        if (gg + 1 < NG && gg + 1 < ngw) consume(Wb, B[g1]);
-      }
+    for (int gg = 0; gg < 5; ++gg) {
+      aw[gg] = tb + (uint32_t)wo[gg < NG ? gg : 0] * 4u;
+      as[gg] = tb + (uint32_t)so[gg < NG ? gg : 0] * 4u;
     }
+    uint32_t W[5][K + 1];
+    lds_read_runs5<K>(aw, as, W);
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg)
+      if (gg < ngw) consume(W[gg], B[gg]);
     // partial D tile of this slice: lane (n, q) holds rows 4q .. 4q+3 of
     // column n; scaled back by 2^-e_n (exact) into common units
     const f32x4 sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);

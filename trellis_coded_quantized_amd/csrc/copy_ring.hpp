@@ -1,7 +1,8 @@
 // copy_ring.hpp -- device helpers shared by the kernels that stream packed
 // codes HBM -> LDS with global_load_lds and wait for them with explicit
-// vmcnt counts: the counted wait, an LDS-only workgroup barrier (no wait on
-// copies in flight), and a wave-wide maximum through DPP.
+// vmcnt counts: the counted wait, LDS reads and writes that do not wait for
+// copies in flight, an LDS-only workgroup barrier, and a wave-wide maximum
+// through DPP.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -31,6 +32,59 @@ __device__ __forceinline__ void wait_vmcnt(int n) {   // n is wave-uniform
 #undef TRELLIS_VM
     default: break;                  // the counter holds at most 63: always satisfied
   }
+}
+
+// ---- LDS next to copies in flight.  After a global_load_lds the compiler
+// treats every later LDS access as one that may touch that copy's target and
+// waits for all copies in flight (vmcnt(0)) before it, which would void a
+// ring's prefetch.  LDS that copies can reach is therefore read and written
+// through the inline-asm blocks below.  A read block issues its reads and
+// waits for them (lgkmcnt(0)) inside the block, so no output register is
+// live before its data has arrived.  The order against the copies is the
+// kernel's own vmcnt wait; LDS operations of one wave complete in issue order.
+typedef uint32_t lds_u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t lds_u32x4 __attribute__((ext_vector_type(4)));
+
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
+
+__device__ __forceinline__ void lds_write_b128(uint32_t a, lds_u32x4 v) {
+  asm volatile("ds_write_b128 %0, %1" : : "v"(a), "v"(v) : "memory");
+}
+
+__device__ __forceinline__ lds_u32x4 lds_read_b128(uint32_t a) {
+  lds_u32x4 r;
+  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(r) : "v"(a) : "memory");
+  return r;
+}
+
+// four consecutive 16-byte reads at a
+__device__ __forceinline__ void lds_read_b128x4(uint32_t a, lds_u32x4 (&o)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %4 offset:16\n\t"
+      "ds_read_b128 %2, %4 offset:32\n\t"
+      "ds_read_b128 %3, %4 offset:48\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])
+      : "v"(a)
+      : "memory");
+}
+
+// five 16-byte reads at independent addresses
+__device__ __forceinline__ void lds_read_b128x5(const uint32_t (&a)[5], lds_u32x4 (&o)[5]) {
+  asm volatile(
+      "ds_read_b128 %0, %5\n\t"
+      "ds_read_b128 %1, %6\n\t"
+      "ds_read_b128 %2, %7\n\t"
+      "ds_read_b128 %3, %8\n\t"
+      "ds_read_b128 %4, %9\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4])
+      : "memory");
 }
 
 // Workgroup barrier that orders LDS only: it does not wait for copies in flight.
