@@ -42,6 +42,17 @@ sys.path.insert(0, ROOT)
 METRIC = "decode matvec GB/s of packed codes (% HBM peak) at M=1..4; prefill TFLOP/s"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+# VALU issue slots of the chip: 256 CUs x 4 SIMDs x 16 lanes at 2.4 GHz.  The
+# decode of one weight takes 4 of them on gfx950 (window extract 1, the 1MAD
+# multiply-add v_mad_u64_u32 2 (half rate), byte sum 1); the products with x
+# run on MFMA.  The matvec roofline is the lower of this and HBM.
+VALU_LANE_SLOTS_PER_S = 256 * 4 * 16 * 2.4e9
+DECODE_SLOTS_PER_WEIGHT = 4
+
+
+def decode_alu_peak_gbs(k):
+    """Packed-code GB/s at which the decode alone fills every VALU issue slot."""
+    return VALU_LANE_SLOTS_PER_S / DECODE_SLOTS_PER_WEIGHT * k / 8 / 1e9
 L, T = 12, 256
 ROTATE_BYTES = 1 << 30
 CSRC = os.path.join(ROOT, "trellis_coded_quantized_amd", "csrc")
@@ -124,6 +135,8 @@ PREFILL_SOURCES = ("prefill.hip", "mfma_common.hpp", "trellis_device.hpp")
 
 
 class GateUp(Workload):
+    bound = "alu"
+
     def __init__(self, args, np, torch, dev):
         import trellis_coded_quantized_amd as tq
         import trellis_inputs as ti
@@ -132,6 +145,7 @@ class GateUp(Workload):
         self.g, self.u = g, u = w.mats
         codes, half, bf16 = _dev_tensors(np, torch, dev)
         self.code_bytes = g.codes.nbytes + u.codes.nbytes
+        self.alu_k = g.k
         self.nrep = _nrep(self.code_bytes)
         self.gcs = [codes(g.codes)]
         self.ucs = [codes(u.codes)]
@@ -178,9 +192,12 @@ class GateUp(Workload):
 class Matvec(Workload):
     """Calls of the axis-1 / axis-0 matvec entry points, one per matrix, per M."""
 
+    bound = "alu"
+
     def __init__(self, w, Ms, label, profile, sources, args, np, torch, dev):
         import trellis_coded_quantized_amd as tq
         self.np, self.tq, self.w, self.Ms = np, tq, w, Ms
+        self.alu_k = min(m.k for m in w.mats)
         codes, half, bf16 = _dev_tensors(np, torch, dev)
         self.code_bytes = sum(m.codes.nbytes for m in w.mats)
         self.nrep = _nrep(self.code_bytes)
@@ -286,6 +303,7 @@ class Copy(Workload):
     """Plain device-to-device copy of 1 GiB: the HBM reference point, and the
     known-size kernel that calibrates the FETCH_SIZE / WRITE_SIZE counters."""
     dtype = "u8"
+    bound = "hbm"
     graph = False
 
     def __init__(self, args, np, torch, dev):
@@ -382,7 +400,9 @@ def main():
     scale = 1e9 if wl.unit == "GB/s" else 1e12
     per_launch_units = wl.units_per_step / wl.kernels_per_step
     achieved = per_launch_units / (launch_ms * 1e-3) / scale
-    peak = HBM_PEAK_GBS if wl.bound == "hbm" else BF16_PEAK_TFLOPS
+    peak = {"hbm": HBM_PEAK_GBS, "mfma": BF16_PEAK_TFLOPS}.get(wl.bound)
+    if wl.bound == "alu":
+        peak = min(decode_alu_peak_gbs(wl.alu_k), HBM_PEAK_GBS)
     traffic = committed_traffic(wl.profile, wl.profile_sources) if wl.profile else None
     cpu = None
     if not args.no_cpu_baseline:
@@ -394,10 +414,15 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
         "data": DATA, "config": dict(wl.config, mode=mode),
         "roofline": {"bound": wl.bound, "achieved": achieved, "peak": peak,
-                     "unit": "GB/s" if wl.bound == "hbm" else "TFLOP/s", "frac": achieved / peak,
+                     "unit": wl.unit, "frac": achieved / peak,
                      "traffic": traffic, "kernel": wl.kernel, "mean_launch_us": launch_ms * 1e3},
         "cpu_baseline": cpu,
     }
+    if wl.bound == "alu":
+        line["roofline"].update({
+            "peak_basis": f"decode VALU bound: {VALU_LANE_SLOTS_PER_S:.4g} lane-slots/s / "
+                          f"{DECODE_SLOTS_PER_WEIGHT} slots per weight x k/8 bytes (k={wl.alu_k})",
+            "hbm_peak": HBM_PEAK_GBS, "hbm_frac": achieved / HBM_PEAK_GBS})
     print(json.dumps(line), flush=True)
 
 
