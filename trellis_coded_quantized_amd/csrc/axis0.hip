@@ -306,6 +306,11 @@ __global__ __launch_bounds__(kThreads) void axis0_kernel(const uint32_t* __restr
   const uint32_t mul = kMul;
   const uint64_t add64 = kAdd;
   for (int t = 0; t < nmy; ++t) {
+    // the two waves of a SIMD (w, w + 4) take turns at the higher issue
+    // priority, one block each, so neither runs ahead and leaves the other
+    // to finish alone
+    if ((t + (wave >> 2)) & 1) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
     wait_vmcnt(nwd * (next - 1 - t));          // tile t has landed
     const int blk = wave + kWaves * t;
     half8 Bv;

@@ -356,6 +356,11 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
   const uint32_t mul = kMul;
   const uint64_t add64 = kAdd;
   for (int t = 0; t < nmine; ++t) {
+    // the two waves of a SIMD (w, w + 4) take turns at the higher issue
+    // priority, one row group each, so neither runs ahead and leaves the
+    // other to finish alone
+    if ((t + (wave >> 2)) & 1) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
     wait_vmcnt(nwd * (next - 1 - t));          // tile t has landed (tiles after it may be in flight)
     const uint8_t* trow = ring + (size_t)(t % NS) * g.slot_bytes + (size_t)i * gsw * 16;
     f32x4 acc[4];
