@@ -272,7 +272,7 @@ class Prefill(Workload):
         self.kernels_per_step = 1 if self.graph else 2
         self.units_per_step = 2.0 * M * m.R * m.C
         self.name = w.name
-        self.kernel = ("prefill_fused_kernel (+ prefill_fold_kernel for split tiles), one step" if self.graph
+        self.kernel = ("prefill_xlayout_kernel + prefill_fused_kernel (+ prefill_fold_kernel for split tiles), one step" if self.graph
                        else "expand_kernel + hipBLASLt GEMM (per call)")
         self.profile = "prefill_17408x5120_k2_m2048.md" if (self.graph and M == 2048) else None
         self.profile_sources = PREFILL_SOURCES

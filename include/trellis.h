@@ -126,10 +126,11 @@ int trellis_expand_bf16(const uint32_t* codes, const uint16_t* scales, uint16_t*
  *   codes uint32 [R, C*k/32];  scales fp16 [R];  x bf16 [M, C];  out bf16 [M, R]
  *   M >= 1;  algo = TRELLIS_PREFILL_FUSED or TRELLIS_PREFILL_EXPAND_GEMM.
  * The EXPAND_GEMM workspace holds the bf16 [R, C] expansion.  The FUSED
- * workspace holds f32 partial tiles when the last round of 512 x 128 output
- * tiles would leave most compute units idle and those tiles are split along C
- * (zero bytes otherwise; the size depends on the device's compute-unit count).
- * FUSED returns TRELLIS_EUNSUPPORTED when x (M*C*2 bytes) or the codes
+ * workspace holds x rewritten in the MFMA operand order (ceil(M/32)*32*C*2
+ * bytes), then f32 partial tiles when the last round of 512 x 128 output
+ * tiles would leave most compute units idle and those tiles are split along
+ * C (the size of that part depends on the device's compute-unit count).
+ * FUSED returns TRELLIS_EUNSUPPORTED when the rewritten x or the codes
  * (R*C*k/8 bytes) reach 2 GiB (its loads use 32-bit buffer offsets).
  */
 size_t trellis_prefill_workspace_bytes(int64_t R, int64_t C, int64_t M, int k, int L, int T,

@@ -14,21 +14,21 @@
 // Every decoded weight therefore serves 512 rows of x, which keeps the VALU
 // decode (about nine operations per weight) under the MFMA time of a step.
 //
-// x path.  Each wave's 128 rows of x are its own.  They arrive in chunks of
-// 64 columns (one 128-byte line per row) with loads that read 8 whole lines
-// per instruction, go through registers into a double-buffered, XOR-swizzled
-// LDS area of that wave, and are read back in the MFMA operand layout.  (An
-// operand-layout load spans 32 rows per instruction and reaches well under
-// half the L2 bandwidth; LDS DMA would save the registers, but the compiler
-// cannot tell its two buffers apart and waits for the prefetch.)
+// x path.  Each wave's 128 rows of x are its own, so x needs no LDS: a
+// first pass (prefill_xlayout_kernel) writes x once in the MFMA operand
+// order, one 1 KB fragment per (32 rows, step, half step), and the main
+// kernel loads every fragment it needs with one 16-byte load per lane, two
+// steps' worth in a register ring.  LDS holds only the decoded weight tile,
+// which all four waves share.
 //
 // Per step of 32 columns:
 //   * each thread decodes 16 consecutive positions of one weight row for the
 //     next step, between this step's MFMAs, into the other half of a
 //     double-buffered LDS weight tile; its code words are loaded three
 //     steps ahead;
-//   * the loads of an x chunk are issued two steps before they are written
-//     to LDS, and the chunk is read one step after that;
+//   * the x fragments of the next step are loaded during this one: half 0
+//     at the start, half 1 once the previous step's half 1 has gone into the
+//     MFMAs (it frees those registers);
 //   * one workgroup barrier per step (for the weight tile), straddled by the
 //     MFMAs: the interval between two barriers runs the second half of the
 //     previous step from registers and then the first half of this step, so
@@ -56,8 +56,7 @@ constexpr int kWM = kBM / kWaves;        // x rows per wave
 constexpr int kFM = kWM / 32;            // MFMA tiles along x rows
 constexpr int kFN = kBN / 32;            // MFMA tiles along weight rows
 constexpr int kRow = kBK + 8;            // padded LDS row (bf16): 80 bytes spread the 16-byte reads
-constexpr int kChunkLines = 8;          // 16-byte blocks per x row in one chunk (64 columns)
-constexpr int kXLoads = kWM / 8;         // x chunk loads per wave (8 rows x 128 bytes each)
+constexpr int kFrag = 1024;              // bytes of one x operand fragment (64 lanes x 16 bytes)
 constexpr int kXcds = 8;
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format
 
@@ -140,17 +139,15 @@ constexpr int kPartFloats = kBM * kBN;   // one partial tile: 256 floats per thr
 template <int K>
 __global__ __launch_bounds__(256, 1) void prefill_fused_kernel(
     const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scales,
-    const uint16_t* __restrict__ x, uint16_t* __restrict__ out, float* __restrict__ part, int R,
+    const uint16_t* __restrict__ xf, uint16_t* __restrict__ out, float* __restrict__ part, int R,
     int C, int M, PrefillPlan plan) {
   constexpr int WPB = words_per_block(K);
   constexpr int NL = Run16<K>::kLoad;
-  // Separate LDS objects for every buffer, so the compiler knows a step's
-  // writes (next weight tile, next x chunk) never alias its reads and can
-  // move the decode in between the MFMAs.
+  // Separate LDS objects for the two weight tiles, so the compiler knows a
+  // step's writes (the next tile) never alias its reads and can move the
+  // decode in between the MFMAs.
   __shared__ __attribute__((aligned(16))) uint16_t Bs0[kBN * kRow];
   __shared__ __attribute__((aligned(16))) uint16_t Bs1[kBN * kRow];
-  __shared__ __attribute__((aligned(16))) u32x4 Xs0[kWaves][kWM * kChunkLines];
-  __shared__ __attribute__((aligned(16))) u32x4 Xs1[kWaves][kWM * kChunkLines];
 
   const int nsteps = C / kBK;
 
@@ -163,30 +160,19 @@ __global__ __launch_bounds__(256, 1) void prefill_fused_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: offsets stay in SGPRs
   const int m_wave = mb * kBM + wave * kWM;
   const int n0 = nb * kBN;
-  const int nchunks = nsteps / 2;
 
-  // x chunk loads: instruction q reads rows 8 q .. 8 q + 7 of the wave, lane
-  // l the 16 bytes at column block l % 8 of row 8 q + l / 8 (rows past M are
-  // clamped to M - 1: their results are never stored).  LDS keeps row r's
-  // block c in slot c ^ ((r / 2) % 8): the operand reads (16 consecutive rows
-  // at one block) then cover all 64 banks once.
+  // x fragments: fragment (b, t, h) of 32-row block b, step t and half h
+  // sits at byte ((b * nsteps + t) * 2 + h) * kFrag of xf, lane l's 16 bytes
+  // at l * 16 (row 32 b + l % 32, columns 16 (l / 32) + 8 h .. + 7 of the
+  // step).  Blocks past the last row of x re-read the last block (their
+  // results are never stored).
+  const int nblk = (M + 31) / 32;
   const __amdgpu_buffer_rsrc_t xr =
-      __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, M * C * 2, kRsrcWord3);
-  uint32_t xo[kXLoads];
+      __builtin_amdgcn_make_buffer_rsrc((void*)xf, (short)0, nblk * nsteps * 2 * kFrag, kRsrcWord3);
+  uint32_t xvo[kFM];
 #pragma unroll
-  for (int q = 0; q < kXLoads; ++q) {
-    const int row = min(m_wave + 8 * q + (lane >> 3), M - 1);
-    xo[q] = (uint32_t)row * (uint32_t)C * 2u + (uint32_t)(lane & 7) * 16u;
-  }
-  // slot of lane l in instruction q: row 8 q + l / 8, swizzle 4 (q % 2) + l / 16
-  const int xw_even = (lane >> 3) * 8 + ((lane & 7) ^ (lane >> 4));
-  const int xw_odd = (lane >> 3) * 8 + ((lane & 7) ^ (4 + (lane >> 4)));
-  // Operand reads: for half h of a step, lane l supplies columns
-  // 16 (l / 32) + 8 h .. + 7 of the step (any assignment shared by both
-  // operands is a valid split of the contraction); row 32 i + l % 32.
-  const int xr_row = lane & 31, xr_swz = (xr_row >> 1) & 7;
-  const u32x4* const xrd0 = &Xs0[wave][xr_row * kChunkLines];  // + 32 i rows
-  const u32x4* const xrd1 = &Xs1[wave][xr_row * kChunkLines];
+  for (int i = 0; i < kFM; ++i)
+    xvo[i] = (uint32_t)min(m_wave / 32 + i, nblk - 1) * (uint32_t)(nsteps * 2 * kFrag) + (uint32_t)lane * 16u;
 
   // Decode assignment: weight row n0 + dr (clamped), positions 16 dh .. + 15
   // of every step; dh is uniform over a wave.
@@ -206,19 +192,16 @@ __global__ __launch_bounds__(256, 1) void prefill_fused_kernel(
 #pragma unroll
     for (int j = 0; j < kFN; ++j) acc[i][j] = f32x16{};
 
-  u32x4 xs[kXLoads];        // x chunk in flight (registers, two steps)
+  // x operand ring: xh[h][slot][i] holds half h of the step with parity slot
+  u32x4 xh[2][2][kFM];
   uint32_t cw[4][NL];       // code words of steps t + 1 .. t + 3
 
-  // Loads past the end re-read the last chunk / step (in bounds, unused), so
-  // the loop body has no branches.
-  auto load_chunk = [&](int c) {
-    const int soff = min(c, nchunks - 1) * 2 * kBK * 2;
+  // Loads past the end re-read the last step (in bounds, unused), so the
+  // loop body has no branches.
+  auto load_x = [&](int t, int h, u32x4 (&dst)[kFM]) {
+    const int soff = (min(t, nsteps - 1) * 2 + h) * kFrag;
 #pragma unroll
-    for (int q = 0; q < kXLoads; ++q) xs[q] = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)xo[q], soff, 0);
-  };
-  auto store_chunk = [&](u32x4 (*dst)[kWM * kChunkLines]) {
-#pragma unroll
-    for (int q = 0; q < kXLoads; ++q) dst[wave][q * 64 + ((q & 1) ? xw_odd : xw_even)] = xs[q];
+    for (int i = 0; i < kFM; ++i) dst[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)xvo[i], soff, 0);
   };
   // Run of step t: block t / 8, first position q0 = 32 (t % 8) + 16 dh,
   // lowest window bit (240 - q0) K; words wrap within the block.
@@ -245,14 +228,12 @@ __global__ __launch_bounds__(256, 1) void prefill_fused_kernel(
   using H1 = std::integral_constant<int, 1>;
 
   // prologue (t_begin is a multiple of 4): words of the first three steps,
-  // the first x chunk into LDS and the second into registers, weights of
-  // the first step
+  // x of the first step, weights of the first step
   load_w(cw[0], t_begin);
   load_w(cw[1], t_begin + 1);
   load_w(cw[2], t_begin + 2);
-  load_chunk(t_begin / 2);
-  store_chunk(Xs0);
-  load_chunk(t_begin / 2 + 1);
+  load_x(t_begin, 0, xh[0][0]);
+  load_x(t_begin, 1, xh[1][0]);
   {
     uint32_t pk[4];
     decode_half(cw[0], t_begin, pk, H0{});
@@ -262,66 +243,56 @@ __global__ __launch_bounds__(256, 1) void prefill_fused_kernel(
   }
   __syncthreads();
 
-  // MFMA operands of one half h of a step: weights b[j] (rows 32 j + l % 32)
-  // and x a[i] (rows 32 i + l % 32), columns 16 (l / 32) + 8 h .. + 7.
+  // weight operand of one half h of a step: b[j] holds rows 32 j + l % 32,
+  // columns 16 (l / 32) + 8 h .. + 7 (the columns of the x fragments; any
+  // assignment shared by both operands is a valid split of the contraction)
   const int bofs = (lane & 31) * kRow + 16 * (lane >> 5);
-  auto read_half = [&](int t, int h, const uint16_t* bbuf, const u32x4* xrd, bf16x8 (&b)[kFN],
-                       bf16x8 (&a)[kFM]) {
+  auto read_b = [&](int h, const uint16_t* bbuf, bf16x8 (&b)[kFN]) {
 #pragma unroll
     for (int j = 0; j < kFN; ++j) b[j] = *reinterpret_cast<const bf16x8*>(bbuf + bofs + 32 * j * kRow + 8 * h);
-    const int blk = 4 * (t & 1) + 2 * (lane >> 5) + h;      // 16-byte block of the chunk row
-#pragma unroll
-    for (int i = 0; i < kFM; ++i)
-      a[i] = __builtin_bit_cast(bf16x8, xrd[32 * i * kChunkLines + (blk ^ xr_swz)]);
   };
-  auto mfma_half = [&](const bf16x8 (&b)[kFN], const bf16x8 (&a)[kFM]) {
+  auto mfma_half = [&](const bf16x8 (&b)[kFN], const u32x4 (&a)[kFM]) {
 #pragma unroll
     for (int i = 0; i < kFM; ++i)
 #pragma unroll
       for (int j = 0; j < kFN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], __builtin_bit_cast(bf16x8, a[i]), acc[i][j], 0, 0, 0);
   };
 
   // Software pipeline across the per-step barrier.  Interval t (between the
   // barriers of steps t - 1 and t) runs the second half of step t - 1 from
-  // registers, then the first half of step t, while it reads the operands of
+  // registers, then the first half of step t, while it reads the weights of
   // step t from LDS and decodes step t + 1.  After each barrier the wave has
   // MFMA work whose operands are already in registers, so the matrix core
   // does not wait for the LDS reads of the new step.
-  bf16x8 bp[kFN], ap[kFM];     // second half of the previous step
-  bf16x8 bc[kFN], ac[kFM];     // first half of the current step
+  bf16x8 bp[kFN];              // weights, second half of the previous step
+  bf16x8 bc[kFN];              // weights, first half of the current step
 #pragma unroll
   for (int j = 0; j < kFN; ++j) bp[j] = bf16x8{};
 #pragma unroll
-  for (int i = 0; i < kFM; ++i) ap[i] = bf16x8{};
+  for (int i = 0; i < kFM; ++i) xh[1][1][i] = u32x4{0u, 0u, 0u, 0u};   // "step t_begin - 1": adds zero
 
-  // Four steps (two x chunks) per iteration: the step count is a multiple
-  // of 8, every buffer index below is a compile-time constant.  Chunk j of
-  // x is loaded at the start of step 2 j - 3 and written to LDS at the end of
-  // step 2 j - 2 (two steps for the loads to land; every wait below then
-  // covers loads issued at least two steps earlier).
+  // Four steps per iteration (the step count is a multiple of 8), so every
+  // buffer and ring index below is a compile-time constant.
   for (int t0 = t_begin; t0 < t_end; t0 += 4) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int t = t0 + u;
-      const bool odd = (u & 1) != 0;
+      const int sl = u & 1;                     // ring slot of step t (t0 is even)
       const uint16_t* bcur = (u & 1) ? Bs1 : Bs0;
       uint16_t* bnext = (u & 1) ? Bs0 : Bs1;
-      const u32x4* xcur = (u & 2) ? xrd1 : xrd0;
       uint32_t pk0[4], pk1[4];
 
-      // first region: loads, operands of step t (half 0), MFMAs of step
-      // t - 1 (half 1), decode of step t + 1 (half 0)
-      if (odd) load_chunk((t + 3) / 2);
+      // first region: loads (words of step t + 3, x of step t + 1 half 0),
+      // weights of step t (half 0), MFMAs of step t - 1 (half 1), decode of
+      // step t + 1 (half 0)
       load_w(cw[(u + 3) & 3], t + 3);
-      read_half(t, 0, bcur, xcur, bc, ac);
-      mfma_half(bp, ap);
+      load_x(t + 1, 0, xh[0][sl ^ 1]);
+      read_b(0, bcur, bc);
+      mfma_half(bp, xh[1][sl ^ 1]);
       decode_half(cw[(u + 1) & 3], t + 1, pk0, H0{});
-      if (odd)
-        __builtin_amdgcn_sched_group_barrier(0x020, kXLoads + NL, 0);              // VMEM reads
-      else
-        __builtin_amdgcn_sched_group_barrier(0x020, NL, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, kFN + kFM, 0);                  // DS reads
+      __builtin_amdgcn_sched_group_barrier(0x020, kFM + NL, 0);                   // VMEM reads
+      __builtin_amdgcn_sched_group_barrier(0x100, kFN, 0);                        // DS reads
 #pragma unroll
       for (int g = 0; g < kFM * kFN; ++g) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                         // MFMA
@@ -329,31 +300,30 @@ __global__ __launch_bounds__(256, 1) void prefill_fused_kernel(
       }
       __builtin_amdgcn_sched_barrier(0);
 
-      // second region: operands of step t (half 1), MFMAs of step t (half
+      // second region: x of step t + 1 half 1 (into the registers the MFMAs
+      // above have read), weights of step t (half 1), MFMAs of step t (half
       // 0), decode of step t + 1 (half 1), LDS writes
-      read_half(t, 1, bcur, xcur, bp, ap);
-      mfma_half(bc, ac);
+      load_x(t + 1, 1, xh[1][sl ^ 1]);
+      read_b(1, bcur, bp);
+      mfma_half(bc, xh[0][sl]);
       decode_half(cw[(u + 1) & 3], t + 1, pk1, H1{});
       store_half(pk0, bnext, 0);
       store_half(pk1, bnext, 1);
-      if (!odd) store_chunk((u & 2) ? Xs0 : Xs1);     // chunk t / 2 + 1 into the other x buffer
-      __builtin_amdgcn_sched_group_barrier(0x100, kFN + kFM, 0);                  // DS reads
+      __builtin_amdgcn_sched_group_barrier(0x020, kFM, 0);                        // VMEM reads
+      __builtin_amdgcn_sched_group_barrier(0x100, kFN, 0);                        // DS reads
 #pragma unroll
       for (int g = 0; g < kFM * kFN; ++g) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                         // MFMA
         __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);                         // VALU
       }
-      if (odd)
-        __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);                         // DS writes
-      else
-        __builtin_amdgcn_sched_group_barrier(0x200, 2 + kXLoads, 0);
+      __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);                          // DS writes
       __syncthreads();
       // MFMAs touch no memory, so without a fence the scheduler would move
       // them across the barrier.
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  mfma_half(bp, ap);           // second half of the last step
+  mfma_half(bp, xh[1][1]);     // second half of the last step (t_end - 1 is odd: slot 1)
 
   if (unit >= 0) {
     // Split segment: the accumulators go to partial tile `unit`, float4 g4
@@ -433,6 +403,25 @@ __global__ __launch_bounds__(256, 1) void prefill_fused_kernel(
     if (pos >= end) break;
     __syncthreads();                               // the next piece reuses the LDS buffers
   }
+}
+
+// x in MFMA operand order for the main kernel: 16-byte unit u of xf is lane
+// u % 64 of fragment f = u / 64 = (b * nsteps + t) * 2 + h, i.e. row
+// 32 b + u % 32 of x and columns 32 t + 16 ((u % 64) / 32) + 8 h .. + 7 (zero
+// past the last row).
+__global__ __launch_bounds__(256) void prefill_xlayout_kernel(const uint16_t* __restrict__ x,
+                                                              uint4* __restrict__ xf, int M, int C,
+                                                              int64_t nunits) {
+  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (u >= nunits) return;
+  const int nsteps = C / kBK;
+  const int l = (int)(u & 63);
+  const int64_t f = u >> 6;
+  const int h = (int)(f & 1);
+  const int64_t bt = f >> 1;
+  const int t = (int)(bt % nsteps), b = (int)(bt / nsteps);
+  const int row = 32 * b + (l & 31), col = kBK * t + 16 * (l >> 5) + 8 * h;
+  xf[u] = row < M ? *reinterpret_cast<const uint4*>(x + (int64_t)row * C + col) : make_uint4(0u, 0u, 0u, 0u);
 }
 
 // Sum the partial tiles of every split tile and store bf16: workgroup
@@ -522,34 +511,46 @@ PrefillPlan make_plan(int64_t R, int64_t C, int64_t M) {
 
 }  // namespace
 
+// bytes of x in operand order: whole 32-row blocks
+int64_t prefill_xf_bytes(int64_t C, int64_t M) { return (M + 31) / 32 * 32 * C * 2; }
+
 bool prefill_fused_supported(int64_t R, int64_t C, int64_t M, int k) {
-  // 32-bit buffer offsets (x and one weight matrix's codes below 2 GiB)
-  // and 32-bit step counters over the whole problem
+  // 32-bit buffer offsets (x in operand order and one weight matrix's codes
+  // below 2 GiB) and 32-bit step counters over the whole problem
   const int64_t steps = ((M + kBM - 1) / kBM) * ((R + kBN - 1) / kBN) * (C / kBK);
-  return k >= 2 && k <= 4 && C % (4 * kBK) == 0 && M * C * 2 < ((int64_t)1 << 31) &&
+  return k >= 2 && k <= 4 && C % (4 * kBK) == 0 && prefill_xf_bytes(C, M) < ((int64_t)1 << 31) &&
          R * C * k / 8 < ((int64_t)1 << 31) && steps < ((int64_t)1 << 30);
 }
 
+// workspace: x in operand order, then the f32 partial tiles of split tiles
 size_t prefill_fused_workspace_bytes(int64_t R, int64_t C, int64_t M) {
   const PrefillPlan p = make_plan(R, C, M);
   const size_t slots = p.stream ? 2 * (size_t)p.G : (size_t)p.nsplit * (size_t)p.S;
-  return slots * kPartFloats * sizeof(float);
+  const size_t xfb = ((size_t)prefill_xf_bytes(C, M) + 255) / 256 * 256;
+  return xfb + slots * kPartFloats * sizeof(float);
 }
 
 hipError_t launch_prefill_fused(const uint32_t* codes, const uint16_t* scales, const uint16_t* x,
                                 uint16_t* out, int64_t R, int64_t C, int64_t M, int k,
                                 void* workspace, hipStream_t stream) {
   const PrefillPlan p = make_plan(R, C, M);
-  float* part = reinterpret_cast<float*>(workspace);
-  const dim3 grid((unsigned)(p.stream ? p.G : kXcds * p.per + p.nsplit * p.S)), block(256);
+  uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
+  uint16_t* xf = reinterpret_cast<uint16_t*>(ws);
+  float* part = reinterpret_cast<float*>(ws + ((size_t)prefill_xf_bytes(C, M) + 255) / 256 * 256);
   const int r = (int)R, c = (int)C, m = (int)M;
+  const int64_t nunits = prefill_xf_bytes(C, M) / 16;
+  hipLaunchKernelGGL(prefill_xlayout_kernel, dim3((unsigned)((nunits + 255) / 256)), dim3(256), 0, stream, x,
+                     reinterpret_cast<uint4*>(xf), m, c, nunits);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)(p.stream ? p.G : kXcds * p.per + p.nsplit * p.S)), block(256);
   switch (k) {
-    case 2: hipLaunchKernelGGL(prefill_fused_kernel<2>, grid, block, 0, stream, codes, scales, x, out, part, r, c, m, p); break;
-    case 3: hipLaunchKernelGGL(prefill_fused_kernel<3>, grid, block, 0, stream, codes, scales, x, out, part, r, c, m, p); break;
-    case 4: hipLaunchKernelGGL(prefill_fused_kernel<4>, grid, block, 0, stream, codes, scales, x, out, part, r, c, m, p); break;
+    case 2: hipLaunchKernelGGL(prefill_fused_kernel<2>, grid, block, 0, stream, codes, scales, xf, out, part, r, c, m, p); break;
+    case 3: hipLaunchKernelGGL(prefill_fused_kernel<3>, grid, block, 0, stream, codes, scales, xf, out, part, r, c, m, p); break;
+    case 4: hipLaunchKernelGGL(prefill_fused_kernel<4>, grid, block, 0, stream, codes, scales, xf, out, part, r, c, m, p); break;
     default: return hipErrorInvalidValue;
   }
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess || (!p.stream && p.nsplit == 0)) return e;
   const unsigned fold_blocks = (unsigned)((p.stream ? p.ntiles : p.nsplit) * 64);
   hipLaunchKernelGGL(prefill_fold_kernel, dim3(fold_blocks), dim3(256), 0, stream, part, out, r, m, p);
