@@ -13,6 +13,10 @@
 // lane (the 32 x 32 form keeps each accumulator in place across the loop).
 // Every decoded weight therefore serves 512 rows of x, which keeps the VALU
 // decode (about nine operations per weight) under the MFMA time of a step.
+// For M <= 128 the workgroup owns 128 rows of x instead (32 per wave, one
+// MFMA tile along x, 64 accumulators), two workgroups share a CU, and the
+// decode is the cost: a 512-row tile would spend most of its MFMA work on
+// rows past M.
 //
 // x path.  Each wave's 128 rows of x are its own, so x needs no LDS: a
 // first pass (prefill_xlayout_kernel) writes x once in the MFMA operand
@@ -49,11 +53,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
-constexpr int kBM = 512;                 // x rows per workgroup
+constexpr int kBMLarge = 512;            // x rows per workgroup, M > 128
+constexpr int kBMSmall = 128;            // x rows per workgroup, M <= 128
 constexpr int kBN = 128;                 // weight rows per workgroup
 constexpr int kBK = 32;                  // columns per step
-constexpr int kWM = kBM / kWaves;        // x rows per wave
-constexpr int kFM = kWM / 32;            // MFMA tiles along x rows
 constexpr int kFN = kBN / 32;            // MFMA tiles along weight rows
 constexpr int kRow = kBK + 8;            // padded LDS row (bf16): 80 bytes spread the 16-byte reads
 constexpr int kFrag = 1024;              // bytes of one x operand fragment (64 lanes x 16 bytes)
@@ -134,13 +137,27 @@ struct PrefillPlan {
   int U, G;          // stream: steps per workgroup, workgroups
 };
 
-constexpr int kPartFloats = kBM * kBN;   // one partial tile: 256 floats per thread, float4-interleaved
+// Shapes that follow from the x rows BM of a workgroup tile.
+template <int BM>
+struct XTile {
+  static constexpr int kWM = BM / kWaves;            // x rows per wave
+  static constexpr int kFM = kWM / 32;               // MFMA tiles along x rows
+  static constexpr int kPartFloats = BM * kBN;       // one partial tile (float4-interleaved per thread)
+  static constexpr int kG4 = kFM * kFN * 4;          // float4 groups of one thread's accumulators
+  static constexpr int kOcc = BM == kBMSmall ? 2 : 1;  // workgroups per CU (registers allow two at 128 rows)
+};
 
-template <int K>
-__global__ __launch_bounds__(256, 1) void prefill_fused_kernel(
+// x rows per workgroup tile: small M takes 128-row tiles (a 512-row tile
+// would spend 3/4 or more of its MFMA work on rows past M).
+int tile_rows(int64_t M) { return M <= kBMSmall ? kBMSmall : kBMLarge; }
+
+template <int K, int BM>
+__global__ __launch_bounds__(256, XTile<BM>::kOcc) void prefill_fused_kernel(
     const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ xf, uint16_t* __restrict__ out, float* __restrict__ part, int R,
     int C, int M, PrefillPlan plan) {
+  constexpr int kBM = BM, kWM = XTile<BM>::kWM, kFM = XTile<BM>::kFM;
+  constexpr int kPartFloats = XTile<BM>::kPartFloats;
   constexpr int WPB = words_per_block(K);
   constexpr int NL = Run16<K>::kLoad;
   // Separate LDS objects for the two weight tiles, so the compiler knows a
@@ -426,18 +443,20 @@ __global__ __launch_bounds__(256) void prefill_xlayout_kernel(const uint16_t* __
 
 // Sum the partial tiles of every split tile and store bf16: workgroup
 // (tile, float4 group g4), thread tid; the element mapping is the one of the
-// main kernel's epilogue.  Rounds: the split tiles are nfull + blockIdx / 64,
+// main kernel's epilogue.  Rounds: the split tiles are nfull + blockIdx / kG4,
 // with slots ts * S .. ts * S + S - 1.  Stream: every tile has a workgroup;
 // tile t is split when its steps span the ranges of workgroups ga < gb, and
 // its piece of workgroup g sits in slot 2 g (g's first piece) or 2 g + 1 (ga,
 // whose range began in an earlier tile).
+template <int BM>
 __global__ __launch_bounds__(256) void prefill_fold_kernel(const float* __restrict__ part,
                                                            uint16_t* __restrict__ out, int R, int M,
                                                            PrefillPlan plan) {
+  constexpr int kWM = XTile<BM>::kWM, kG4 = XTile<BM>::kG4;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int ts = blockIdx.x / 64, g4 = blockIdx.x % 64;
+  const int ts = blockIdx.x / kG4, g4 = blockIdx.x % kG4;
   const float4* base = reinterpret_cast<const float4*>(part) + g4 * 256 + tid;
-  constexpr size_t kSlot = kPartFloats / 4;
+  constexpr size_t kSlot = XTile<BM>::kPartFloats / 4;
   int tile;
   float4 v;
   if (!plan.stream) {
@@ -467,7 +486,7 @@ __global__ __launch_bounds__(256) void prefill_fold_kernel(const float* __restri
   }
   const int mb = tile / plan.nn, nb = tile - mb * plan.nn;
   const int i = g4 / (kFN * 4), j = (g4 / 4) % kFN, g = g4 % 4;
-  const int m = mb * kBM + wave * kWM + 32 * i + (lane & 31);
+  const int m = mb * BM + wave * kWM + 32 * i + (lane & 31);
   const int n = nb * kBN + 32 * j + 8 * g + 4 * (lane >> 5);
   if (m >= M) return;
   uint16_t* orow = out + (size_t)m * (size_t)R;
@@ -482,10 +501,12 @@ __global__ __launch_bounds__(256) void prefill_fold_kernel(const float* __restri
 
 PrefillPlan make_plan(int64_t R, int64_t C, int64_t M) {
   PrefillPlan p{};
-  const int nm = (int)((M + kBM - 1) / kBM);
+  const int bm = tile_rows(M);
+  const int nm = (int)((M + bm - 1) / bm);
+  const int occ = bm == kBMSmall ? XTile<kBMSmall>::kOcc : XTile<kBMLarge>::kOcc;
   p.nn = (int)((R + kBN - 1) / kBN);
   p.ntiles = nm * p.nn;
-  const int cus = device_cus();
+  const int cus = device_cus() * occ;          // workgroup slots
   const int nsteps = (int)(C / kBK), quads = nsteps / 4;
   const int rem = p.ntiles % cus;
   p.nsteps = nsteps;
@@ -517,7 +538,7 @@ int64_t prefill_xf_bytes(int64_t C, int64_t M) { return (M + 31) / 32 * 32 * C *
 bool prefill_fused_supported(int64_t R, int64_t C, int64_t M, int k) {
   // 32-bit buffer offsets (x in operand order and one weight matrix's codes
   // below 2 GiB) and 32-bit step counters over the whole problem
-  const int64_t steps = ((M + kBM - 1) / kBM) * ((R + kBN - 1) / kBN) * (C / kBK);
+  const int64_t steps = ((M + tile_rows(M) - 1) / tile_rows(M)) * ((R + kBN - 1) / kBN) * (C / kBK);
   return k >= 2 && k <= 4 && C % (4 * kBK) == 0 && prefill_xf_bytes(C, M) < ((int64_t)1 << 31) &&
          R * C * k / 8 < ((int64_t)1 << 31) && steps < ((int64_t)1 << 30);
 }
@@ -527,7 +548,8 @@ size_t prefill_fused_workspace_bytes(int64_t R, int64_t C, int64_t M) {
   const PrefillPlan p = make_plan(R, C, M);
   const size_t slots = p.stream ? 2 * (size_t)p.G : (size_t)p.nsplit * (size_t)p.S;
   const size_t xfb = ((size_t)prefill_xf_bytes(C, M) + 255) / 256 * 256;
-  return xfb + slots * kPartFloats * sizeof(float);
+  const size_t tile_floats = (size_t)tile_rows(M) * kBN;
+  return xfb + slots * tile_floats * sizeof(float);
 }
 
 hipError_t launch_prefill_fused(const uint32_t* codes, const uint16_t* scales, const uint16_t* x,
@@ -544,16 +566,29 @@ hipError_t launch_prefill_fused(const uint32_t* codes, const uint16_t* scales, c
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)(p.stream ? p.G : kXcds * p.per + p.nsplit * p.S)), block(256);
-  switch (k) {
-    case 2: hipLaunchKernelGGL(prefill_fused_kernel<2>, grid, block, 0, stream, codes, scales, xf, out, part, r, c, m, p); break;
-    case 3: hipLaunchKernelGGL(prefill_fused_kernel<3>, grid, block, 0, stream, codes, scales, xf, out, part, r, c, m, p); break;
-    case 4: hipLaunchKernelGGL(prefill_fused_kernel<4>, grid, block, 0, stream, codes, scales, xf, out, part, r, c, m, p); break;
+  const bool small = tile_rows(M) == kBMSmall;
+#define TRELLIS_PREFILL_LAUNCH(KK, BMM)                                                                   \
+  hipLaunchKernelGGL((prefill_fused_kernel<KK, BMM>), grid, block, 0, stream, codes, scales, xf, out, part, r, \
+                     c, m, p)
+  switch (k * 2 + (small ? 1 : 0)) {
+    case 4: TRELLIS_PREFILL_LAUNCH(2, kBMLarge); break;
+    case 5: TRELLIS_PREFILL_LAUNCH(2, kBMSmall); break;
+    case 6: TRELLIS_PREFILL_LAUNCH(3, kBMLarge); break;
+    case 7: TRELLIS_PREFILL_LAUNCH(3, kBMSmall); break;
+    case 8: TRELLIS_PREFILL_LAUNCH(4, kBMLarge); break;
+    case 9: TRELLIS_PREFILL_LAUNCH(4, kBMSmall); break;
     default: return hipErrorInvalidValue;
   }
+#undef TRELLIS_PREFILL_LAUNCH
   e = hipGetLastError();
   if (e != hipSuccess || (!p.stream && p.nsplit == 0)) return e;
-  const unsigned fold_blocks = (unsigned)((p.stream ? p.ntiles : p.nsplit) * 64);
-  hipLaunchKernelGGL(prefill_fold_kernel, dim3(fold_blocks), dim3(256), 0, stream, part, out, r, m, p);
+  const unsigned ntile = (unsigned)(p.stream ? p.ntiles : p.nsplit);
+  if (small)
+    hipLaunchKernelGGL(prefill_fold_kernel<kBMSmall>, dim3(ntile * XTile<kBMSmall>::kG4), dim3(256), 0, stream,
+                       part, out, r, m, p);
+  else
+    hipLaunchKernelGGL(prefill_fold_kernel<kBMLarge>, dim3(ntile * XTile<kBMLarge>::kG4), dim3(256), 0, stream,
+                       part, out, r, m, p);
   return hipGetLastError();
 }
 
