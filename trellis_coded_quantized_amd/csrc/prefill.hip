@@ -345,9 +345,11 @@ __global__ __launch_bounds__(256, XTile<BM>::kOcc) void prefill_fused_kernel(
   if (unit >= 0) {
     // Split segment: the accumulators go to partial tile `unit`, float4 g4
     // (16 per MFMA tile (i, j)) of thread tid at float4 index g4 * 256 + tid.
+    // Rows past M are neither stored nor folded.
     float4* dst = reinterpret_cast<float4*>(part) + (size_t)unit * (kPartFloats / 4);
 #pragma unroll
-    for (int i = 0; i < kFM; ++i)
+    for (int i = 0; i < kFM; ++i) {
+      if (m_wave + 32 * i + (lane & 31) >= M) continue;
 #pragma unroll
       for (int j = 0; j < kFN; ++j)
 #pragma unroll
@@ -355,6 +357,7 @@ __global__ __launch_bounds__(256, XTile<BM>::kOcc) void prefill_fused_kernel(
           const f32x16 v = acc[i][j];
           dst[((i * kFN + j) * 4 + g) * 256 + tid] = make_float4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
         }
+    }
     return;
   }
 
@@ -457,10 +460,14 @@ __global__ __launch_bounds__(256) void prefill_fold_kernel(const float* __restri
   const int ts = blockIdx.x / kG4, g4 = blockIdx.x % kG4;
   const float4* base = reinterpret_cast<const float4*>(part) + g4 * 256 + tid;
   constexpr size_t kSlot = XTile<BM>::kPartFloats / 4;
-  int tile;
+  const int i = g4 / (kFN * 4), j = (g4 / 4) % kFN, g = g4 % 4;
+  const int tile = plan.stream ? ts : plan.nfull + ts;
+  const int mb = tile / plan.nn, nb = tile - mb * plan.nn;
+  const int m = mb * BM + wave * kWM + 32 * i + (lane & 31);
+  const int n = nb * kBN + 32 * j + 8 * g + 4 * (lane >> 5);
+  if (m >= M) return;                            // rows past M were not stored
   float4 v;
   if (!plan.stream) {
-    tile = plan.nfull + ts;
     const float4* src = base + (size_t)ts * plan.S * kSlot;
     v = src[0];
     for (int s = 1; s < plan.S; ++s) {
@@ -471,24 +478,18 @@ __global__ __launch_bounds__(256) void prefill_fold_kernel(const float* __restri
       v.w += w.w;
     }
   } else {
-    tile = ts;
     const int ga = tile * plan.nsteps / plan.U, gb = ((tile + 1) * plan.nsteps - 1) / plan.U;
     if (ga == gb) return;                          // whole inside one range: stored by the main kernel
     const int first_of_ga = (ga * plan.U) / plan.nsteps == tile;
     v = base[(size_t)(2 * ga + (first_of_ga ? 0 : 1)) * kSlot];
-    for (int g = ga + 1; g <= gb; ++g) {
-      const float4 w = base[(size_t)(2 * g) * kSlot];
+    for (int gw = ga + 1; gw <= gb; ++gw) {
+      const float4 w = base[(size_t)(2 * gw) * kSlot];
       v.x += w.x;
       v.y += w.y;
       v.z += w.z;
       v.w += w.w;
     }
   }
-  const int mb = tile / plan.nn, nb = tile - mb * plan.nn;
-  const int i = g4 / (kFN * 4), j = (g4 / 4) % kFN, g = g4 % 4;
-  const int m = mb * BM + wave * kWM + 32 * i + (lane & 31);
-  const int n = nb * kBN + 32 * j + 8 * g + 4 * (lane >> 5);
-  if (m >= M) return;
   uint16_t* orow = out + (size_t)m * (size_t)R;
   if ((R & 3) == 0 && n + 3 < R) {
     *reinterpret_cast<uint2*>(orow + n) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
