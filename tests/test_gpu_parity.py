@@ -244,12 +244,14 @@ def test_prefill_small(algo, k, R, C, M):
 
 
 @pytest.mark.parametrize("k", [2, 3])
-def test_prefill_fused_stream_pieces(k):
-    # 200 tiles of 512 x 128 on a 256-CU part: the leftover tiles fill more than half of the CUs,
-    # so the fused kernel deals the 200 x 40 steps out in ranges of 32 steps that cross tile
-    # boundaries (whole tiles stored directly, the pieces folded).  Sampled rows and x rows.
-    rng = np.random.default_rng(90 + k)
-    R, C, M = 25600, 1280, 64
+@pytest.mark.parametrize("R,M", [(25600, 300), (38400, 64)])
+def test_prefill_fused_stream_pieces(k, R, M):
+    # M = 300: 200 tiles of 512 x 128 on a 256-CU part; M = 64: 300 tiles of 128 x 128 with two
+    # workgroups per CU.  Either way the leftover tiles fill more than half of the workgroup
+    # slots, so the fused kernel deals the steps out in ranges that cross tile boundaries (whole
+    # tiles stored directly, the pieces folded).  Sampled rows and x rows.
+    rng = np.random.default_rng(90 + k + M)
+    C = 1280
     codes, scales = rand_matrix(rng, R, C, k)
     x = ti.activations(rng, M, C)
     got = tq.prefill(d_codes(codes), d_half(scales), d_bf16(x), k, algo=tq.PREFILL_FUSED)

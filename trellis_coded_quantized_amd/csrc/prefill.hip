@@ -13,7 +13,7 @@
 // lane (the 32 x 32 form keeps each accumulator in place across the loop).
 // Every decoded weight therefore serves 512 rows of x, which keeps the VALU
 // decode (about nine operations per weight) under the MFMA time of a step.
-// For M <= 128 the workgroup owns 128 rows of x instead (32 per wave, one
+// For M <= 256 the workgroup owns 128 rows of x instead (32 per wave, one
 // MFMA tile along x, 64 accumulators), two workgroups share a CU, and the
 // decode is the cost: a 512-row tile would spend most of its MFMA work on
 // rows past M.
@@ -53,8 +53,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
-constexpr int kBMLarge = 512;            // x rows per workgroup, M > 128
-constexpr int kBMSmall = 128;            // x rows per workgroup, M <= 128
+constexpr int kBMLarge = 512;            // x rows per workgroup, M > 256
+constexpr int kBMSmall = 128;            // x rows per workgroup, M <= 256
 constexpr int kBN = 128;                 // weight rows per workgroup
 constexpr int kBK = 32;                  // columns per step
 constexpr int kFN = kBN / 32;            // MFMA tiles along weight rows
@@ -147,9 +147,12 @@ struct XTile {
   static constexpr int kOcc = BM == kBMSmall ? 2 : 1;  // workgroups per CU (registers allow two at 128 rows)
 };
 
-// x rows per workgroup tile: small M takes 128-row tiles (a 512-row tile
-// would spend 3/4 or more of its MFMA work on rows past M).
-int tile_rows(int64_t M) { return M <= kBMSmall ? kBMSmall : kBMLarge; }
+// x rows per workgroup tile: M <= 256 takes 128-row tiles (a 512-row tile
+// would spend half or more of its MFMA work on rows past M; measured
+// crossover: 128-row tiles win at M = 256, lose at M = 512, where the decode
+// they repeat per row tile costs more than the MFMA work they save).
+constexpr int kSmallTileMaxM = 256;
+int tile_rows(int64_t M) { return M <= kSmallTileMaxM ? kBMSmall : kBMLarge; }
 
 template <int K, int BM>
 __global__ __launch_bounds__(256, XTile<BM>::kOcc) void prefill_fused_kernel(
