@@ -8,6 +8,7 @@ in HBM; code buffers rotate over >= 1 GiB of replicas so the 256 MB
 Infinity Cache cannot serve repeats).  Other workloads (--workload) print
 the same JSON line for their own metric: the 512 x 2048 reduce matvec, the
 17408 x 5120 k = 3 down-projection scatter, the k = 4 decoder-layer chain,
+the MLP (gate/up + SwiGLU, then the down projection, in one call),
 and the 17408 x 5120 prefill at M in {32, 512, 2048} (fused or expand +
 GEMM), plus a plain device copy used as the HBM reference point.
 
@@ -251,6 +252,69 @@ class Matvec(Workload):
                           f"{nbytes} code bytes in {dt:.2f} s"}
 
 
+class Mlp(Workload):
+    """The decoder-layer MLP for M = 1..4: gate/up + SwiGLU (17408 x 5120, k = 2), then the
+    down projection stored transposed (17408 x 5120, k = 3), one trellis_mlp_decode call each."""
+    bound = "alu"
+
+    def __init__(self, args, np, torch, dev):
+        import trellis_coded_quantized_amd as tq
+        import trellis_inputs as ti
+        self.np, self.tq = np, tq
+        w = ti.gateup()
+        self.g, self.u = g, u = w.mats
+        self.d = d = ti.axis0().mats[0]
+        self.x = w.x[0]
+        codes, half, bf16 = _dev_tensors(np, torch, dev)
+        self.code_bytes = g.codes.nbytes + u.codes.nbytes + d.codes.nbytes
+        weights = 2 * g.R * g.C + d.R * d.C
+        self.alu_peak_gbs = VALU_LANE_SLOTS_PER_S / DECODE_SLOTS_PER_WEIGHT * (self.code_bytes / weights) / 1e9
+        self.alu_k = None
+        self.nrep = _nrep(self.code_bytes)
+        self.reps = [[codes(g.codes), codes(u.codes), codes(d.codes)]]
+        for _ in range(self.nrep - 1):
+            self.reps.append([c.clone() for c in self.reps[0]])
+        self.gs, self.us, self.ds = half(g.scales), half(u.scales), half(d.scales)
+        self.dx = bf16(self.x)
+        self.Ms = (1, 2, 3, 4)
+        lib = tq.load_library()
+        self.outs = {M: torch.empty((M, d.C), dtype=torch.bfloat16, device=dev) for M in self.Ms}
+        self.wss = {M: torch.zeros(lib.trellis_mlp_decode_workspace_bytes(g.R, g.C, d.C, M, g.k, d.k, L, T),
+                                   dtype=torch.uint8, device=dev) for M in self.Ms}
+        self.period = self.nrep // math.gcd(self.nrep, len(self.Ms))
+        self.kernels_per_step = len(self.Ms)
+        self.units_per_step = len(self.Ms) * self.code_bytes
+        self.name = "mlp_17408x5120_k2_k3"
+        self.kernel = "trellis_mlp_decode (gate/up + SwiGLU, axis-0 down + fold), one call per M"
+        self.config = {"workload": self.name, "M": list(self.Ms), "R": g.R, "C": g.C, "C_out": d.C,
+                       "k_gate_up": g.k, "k_down": d.k, "L": L, "T": T, "code_bytes_per_call": self.code_bytes,
+                       "replicas": self.nrep}
+
+    def step(self, s):
+        for j, M in enumerate(self.Ms):
+            gc, uc, dc = self.reps[(s * len(self.Ms) + j) % self.nrep]
+            self.tq.mlp_decode(gc, self.gs, uc, self.us, dc, self.ds, self.dx[:M], self.g.k, self.d.k,
+                               out=self.outs[M], workspace=self.wss[M])
+
+    def cpu_baseline(self, seconds):
+        import oracle
+        g, u, d, np = self.g, self.u, self.d, self.np
+        t0 = time.perf_counter()
+        nbytes, passes = 0, 0
+        while True:
+            for M in self.Ms:
+                _, _, hidden = oracle.gateup_swiglu(g.codes, g.scales, u.codes, u.scales, self.x, M, g.R, g.C, g.k,
+                                                    L, T)
+                oracle.matvec_axis0(d.codes, d.scales, hidden, M, d.R, d.C, d.k, L, T)
+                nbytes += self.code_bytes
+            passes += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        dt = time.perf_counter() - t0
+        return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+                "sample": f"{passes} whole steps (gate/up then down, M = 1..4), {nbytes} code bytes in {dt:.2f} s"}
+
+
 class Prefill(Workload):
     unit, bound, dtype = "TFLOP/s", "mfma", "bf16"
 
@@ -336,7 +400,7 @@ def workload_axis1_m1(args, np, torch, dev):
     return Matvec(ti.axis1_m1(), (1,), "axis1_kernel (reduce)", None, AXIS1_SOURCES, args, np, torch, dev)
 
 
-WORKLOADS = {"copy": Copy, "gateup": GateUp, "prefill": Prefill, "axis0": workload_axis0,
+WORKLOADS = {"copy": Copy, "gateup": GateUp, "prefill": Prefill, "axis0": workload_axis0, "mlp": Mlp,
              "layer_chain": workload_layer_chain, "axis1_m1": workload_axis1_m1}
 
 
@@ -402,7 +466,8 @@ def main():
     achieved = per_launch_units / (launch_ms * 1e-3) / scale
     peak = {"hbm": HBM_PEAK_GBS, "mfma": BF16_PEAK_TFLOPS}.get(wl.bound)
     if wl.bound == "alu":
-        peak = min(decode_alu_peak_gbs(wl.alu_k), HBM_PEAK_GBS)
+        alu = getattr(wl, "alu_peak_gbs", None) or decode_alu_peak_gbs(wl.alu_k)
+        peak = min(alu, HBM_PEAK_GBS)
     traffic = committed_traffic(wl.profile, wl.profile_sources) if wl.profile else None
     cpu = None
     if not args.no_cpu_baseline:
@@ -421,7 +486,8 @@ def main():
     if wl.bound == "alu":
         line["roofline"].update({
             "peak_basis": f"decode VALU bound: {VALU_LANE_SLOTS_PER_S:.4g} lane-slots/s / "
-                          f"{DECODE_SLOTS_PER_WEIGHT} slots per weight x k/8 bytes (k={wl.alu_k})",
+                          f"{DECODE_SLOTS_PER_WEIGHT} slots per weight x k/8 bytes "
+                          + (f"(k={wl.alu_k})" if wl.alu_k else "(k weighted over the matrices)"),
             "hbm_peak": HBM_PEAK_GBS, "hbm_frac": achieved / HBM_PEAK_GBS})
     print(json.dumps(line), flush=True)
 

@@ -107,6 +107,33 @@ int trellis_matvec_axis0(const uint32_t* codes, const uint16_t* scales, const ui
                          int L, int T, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * trellis_mlp_decode -- the MLP of a decoder layer for M <= 4 rows:
+ *   hidden = silu(gate(x)) * up(x)        (trellis_gateup_swiglu, bf16)
+ *   out    = down(hidden)                 (trellis_matvec_axis0, bf16)
+ * on one stream with no host round trip; gate and up are axis-1 matrices
+ * [R, C], down is stored transposed (axis 0) as W_down^T [R, C_out].
+ * Source: mlx-bun 0.2.0 -> 0.4.0 diff (page 55), the MLP forward of the
+ * Qwen layer: for at most TRELLIS_MATVEC_MAX_M rows and eligible gate/up
+ * projections, the fused gate/up SwiGLU kernel, then the down projection of
+ * the hidden vectors.
+ *   gcodes, ucodes uint32 [R, C*k_gu/32];  gscales, uscales fp16 [R]
+ *   dcodes uint32 [R, C_out*k_down/32];   dscales fp16 [R]
+ *   x bf16 [M, C];  out bf16 [M, C_out];  1 <= M <= 4
+ *   hidden bf16 [M, R] (may be NULL): receives the hidden vectors, which
+ *     otherwise live in the workspace
+ * The workspace (trellis_mlp_decode_workspace_bytes) holds the hidden
+ * vectors and the down projection's partials.  Errors as for the two calls
+ * it makes; nothing is launched unless both would be accepted.
+ */
+size_t trellis_mlp_decode_workspace_bytes(int64_t R, int64_t C, int64_t C_out, int M, int k_gu,
+                                          int k_down, int L, int T);
+int trellis_mlp_decode(const uint32_t* gcodes, const uint16_t* gscales, const uint32_t* ucodes,
+                       const uint16_t* uscales, const uint32_t* dcodes, const uint16_t* dscales,
+                       const uint16_t* x, uint16_t* hidden, uint16_t* out, int64_t R, int64_t C, int64_t C_out,
+                       int M, int k_gu, int k_down, int L, int T, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/*
  * trellis_expand_bf16 -- out[r, c] = bf16(value(r, c) * scales[r]) for the
  * stored matrix (stored orientation; an axis-0 caller gets W^T).  value is
  * y/d correctly rounded to f32; the product is rounded to f32, then to bf16

@@ -125,3 +125,31 @@ def test_tolerance_helpers():
     two[0] += 2
     assert tol.bf16_band_violations(two, o)[0]
     assert tol.bf16_key(np.array([0x8000], np.uint16))[0] == tol.bf16_key(np.array([0], np.uint16))[0]
+
+
+def call_mlp(x=FAKE, out=FAKE, hidden=None, R=1024, C=2048, C_out=1024, M=2, kg=2, kd=3, ws=None, wsb=0):
+    lib = tq.load_library()
+    return lib.trellis_mlp_decode(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, x, hidden, out, R, C, C_out, M, kg, kd, 12,
+                                  256, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(M=5), tq.EINVAL, "M=5"),
+    (dict(M=0), tq.EINVAL, "M=0"),
+    (dict(kd=5), tq.EUNSUPPORTED, "k=5"),
+    (dict(kg=1), tq.EUNSUPPORTED, "k=1"),
+    (dict(C_out=1000), tq.EINVAL, "C=1000"),
+    (dict(x=MIS), tq.EINVAL, "x not 16-byte aligned"),
+    (dict(hidden=MIS), tq.EINVAL, "hidden not 16-byte aligned"),
+])
+def test_mlp_decode_rejects(kw, status, needle):
+    assert call_mlp(**kw) == status
+    assert needle in tq.load_library().trellis_last_error().decode()
+
+
+def test_mlp_decode_workspace_is_checked():
+    lib = tq.load_library()
+    need = lib.trellis_mlp_decode_workspace_bytes(1024, 2048, 1024, 2, 2, 3, 12, 256)
+    assert need >= 2 * 1024 * 2                  # at least the hidden vectors
+    assert call_mlp(ws=FAKE, wsb=need - 1) == tq.EWORKSPACE
+    assert lib.trellis_mlp_decode_workspace_bytes(1024, 2048, 1024, 5, 2, 3, 12, 256) == 0

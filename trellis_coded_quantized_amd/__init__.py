@@ -31,6 +31,7 @@ EXPORTS = (
     "trellis_matvec_axis1_workspace_bytes", "trellis_matvec_axis1",
     "trellis_gateup_swiglu_workspace_bytes", "trellis_gateup_swiglu",
     "trellis_matvec_axis0_workspace_bytes", "trellis_matvec_axis0",
+    "trellis_mlp_decode_workspace_bytes", "trellis_mlp_decode",
     "trellis_expand_bf16", "trellis_prefill_workspace_bytes", "trellis_prefill",
     "trellis_decode_states", "trellis_last_error", "trellis_version",
 )
@@ -64,6 +65,9 @@ def load_library():
         "trellis_matvec_axis0_workspace_bytes": (_sz, [_i64, _i64, _int, _int, _int, _int]),
         "trellis_matvec_axis0": (_int, [_vp, _vp, _vp, _vp, _int, _i64, _i64, _int, _int, _int, _int,
                                         _vp, _sz, _vp]),
+        "trellis_mlp_decode_workspace_bytes": (_sz, [_i64, _i64, _i64, _int, _int, _int, _int, _int]),
+        "trellis_mlp_decode": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int,
+                                      _int, _int, _int, _int, _vp, _sz, _vp]),
         "trellis_expand_bf16": (_int, [_vp, _vp, _vp, _i64, _i64, _int, _int, _int, _vp]),
         "trellis_prefill_workspace_bytes": (_sz, [_i64, _i64, _i64, _int, _int, _int, _int]),
         "trellis_prefill": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int, _int,
@@ -191,6 +195,39 @@ def matvec_axis0(codes_t, scales, x, k, L=12, T=256, out_dtype=torch.bfloat16, o
                          workspace)
     _check(lib.trellis_matvec_axis0(_ptr(codes_t), _ptr(scales), _ptr(x), _ptr(out), od, R, C, M, k,
                                     L, T, _ptr(ws), wsb, _stream(x.device)))
+    return out
+
+
+def mlp_decode(gcodes, gscales, ucodes, uscales, dcodes_t, dscales, x, k_gu, k_down, L=12, T=256,
+               hidden=None, out=None, workspace=None):
+    """down(silu(gate(x)) * up(x)) for M <= 4 rows: the gate/up SwiGLU kernel,
+    then the axis-0 down projection (dcodes_t is the stored W_down^T
+    [R, C_out*k_down/32]).  `hidden` (bf16 [M, R]) receives the hidden
+    vectors if given."""
+    for t, n in ((gcodes, "gcodes"), (ucodes, "ucodes"), (dcodes_t, "dcodes")):
+        _need(t, n, _CODES, 2)
+    for t, n in ((gscales, "gscales"), (uscales, "uscales"), (dscales, "dscales")):
+        _need(t, n, (torch.float16,), 1)
+    _need(x, "x", (torch.bfloat16,), 2)
+    R, C = _geometry(gcodes, k_gu)
+    if _geometry(ucodes, k_gu) != (R, C):
+        raise ValueError("gate and up codes differ in shape")
+    Rd, C_out = _geometry(dcodes_t, k_down)
+    if Rd != R:
+        raise ValueError(f"down projection has {Rd} stored rows, the hidden width is {R}")
+    M = x.shape[0]
+    if x.shape[1] != C:
+        raise ValueError(f"x has {x.shape[1]} features, gate/up take {C}")
+    if out is None:
+        out = torch.empty((M, C_out), dtype=torch.bfloat16, device=x.device)
+    if hidden is not None:
+        _need(hidden, "hidden", (torch.bfloat16,), 2)
+    lib = load_library()
+    ws, wsb = _workspace(lib.trellis_mlp_decode_workspace_bytes(R, C, C_out, M, k_gu, k_down, L, T), x.device,
+                         workspace)
+    _check(lib.trellis_mlp_decode(_ptr(gcodes), _ptr(gscales), _ptr(ucodes), _ptr(uscales), _ptr(dcodes_t),
+                                  _ptr(dscales), _ptr(x), _ptr(hidden), _ptr(out),
+                                  R, C, C_out, M, k_gu, k_down, L, T, _ptr(ws), wsb, _stream(x.device)))
     return out
 
 

@@ -294,6 +294,50 @@ int trellis_matvec_axis0(const uint32_t* codes, const uint16_t* scales, const ui
                                               R_in, C_out, M, k, workspace, (hipStream_t)stream));
 }
 
+size_t trellis_mlp_decode_workspace_bytes(int64_t R, int64_t C, int64_t C_out, int M, int k_gu,
+                                          int k_down, int L, int T) {
+  if (check_geometry("trellis_mlp_decode_workspace_bytes", R, C, k_gu, L, T) != TRELLIS_OK) return 0;
+  if (check_geometry("trellis_mlp_decode_workspace_bytes", R, C_out, k_down, L, T) != TRELLIS_OK) return 0;
+  if (M < 1 || M > TRELLIS_MATVEC_MAX_M) return 0;
+  // the bf16 hidden vectors [M, R], then the down projection's own workspace
+  return align_up((size_t)M * (size_t)R * 2, 256) + align_up(trellis::axis1_workspace_bytes(R, C, M, k_gu), 256) +
+         trellis::axis0_workspace_bytes(R, C_out, M, k_down);
+}
+
+int trellis_mlp_decode(const uint32_t* gcodes, const uint16_t* gscales, const uint32_t* ucodes,
+                       const uint16_t* uscales, const uint32_t* dcodes, const uint16_t* dscales,
+                       const uint16_t* x, uint16_t* hidden, uint16_t* out, int64_t R, int64_t C, int64_t C_out,
+                       int M, int k_gu, int k_down, int L, int T, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  const char* fn = "trellis_mlp_decode";
+  TRY(check_geometry(fn, R, C, k_gu, L, T));
+  TRY(check_geometry(fn, R, C_out, k_down, L, T));
+  TRY(check_m(fn, M, TRELLIS_MATVEC_MAX_M));
+  TRY(check_ptr(fn, "gcodes", gcodes, 16));
+  TRY(check_ptr(fn, "gscales", gscales, 2));
+  TRY(check_ptr(fn, "ucodes", ucodes, 16));
+  TRY(check_ptr(fn, "uscales", uscales, 2));
+  TRY(check_ptr(fn, "dcodes", dcodes, 16));
+  TRY(check_ptr(fn, "dscales", dscales, 2));
+  TRY(check_ptr(fn, "x", x, 16));
+  TRY(check_ptr(fn, "out", out, 16));
+  if (hidden) TRY(check_ptr(fn, "hidden", hidden, 16));
+  TRY(check_axis1_shape(fn, R, C, M, k_gu, true));
+  if (!trellis::axis0_supported(R, C_out, M, k_down))
+    return fail(TRELLIS_EUNSUPPORTED, "%s: down shape R=%lld C_out=%lld M=%d k=%d does not fit the kernel's LDS plan",
+                fn, (long long)R, (long long)C_out, M, k_down);
+  TRY(check_workspace(fn, workspace, workspace_bytes,
+                      trellis_mlp_decode_workspace_bytes(R, C, C_out, M, k_gu, k_down, L, T)));
+  char* ws = reinterpret_cast<char*>(workspace);
+  const size_t hb = align_up((size_t)M * (size_t)R * 2, 256);
+  const size_t w1 = align_up(trellis::axis1_workspace_bytes(R, C, M, k_gu), 256);
+  uint16_t* mid = hidden ? hidden : reinterpret_cast<uint16_t*>(ws);
+  hipStream_t s = (hipStream_t)stream;
+  TRY(hip_status(fn, trellis::launch_axis1(gcodes, gscales, ucodes, uscales, x, mid, 0, nullptr, nullptr, R, C,
+                                           M, k_gu, w1 ? ws + hb : nullptr, s)));
+  return hip_status(fn, trellis::launch_axis0(dcodes, dscales, mid, out, 0, R, C_out, M, k_down, ws + hb + w1, s));
+}
+
 int trellis_expand_bf16(const uint32_t* codes, const uint16_t* scales, uint16_t* out, int64_t R,
                         int64_t C, int k, int L, int T, void* stream) {
   const char* fn = "trellis_expand_bf16";
