@@ -53,6 +53,8 @@ def _load():
         "tro_expand_bf16": (None, [_u32p, _u16p, _i64, _i64, _int, _int, _int, _i64, _i64, _u16p]),
         "tro_prefill": (None, [_u32p, _u16p, _u16p, _i64, _i64, _i64, _int, _int, _int,
                                _i64p, _i64, _i64p, _i64, _f64p]),
+        "tro_prefill_axis0": (None, [_u32p, _u16p, _u16p, _i64, _i64, _i64, _int, _int, _int,
+                                     _i64p, _i64, _i64p, _i64, _f64p]),
         "tro_num_threads": (_int, []),
     }
     for name, (res, args) in sig.items():
@@ -190,4 +192,15 @@ def prefill_sums(codes, scales, x, M, R, C, k, L, T, ms, rows) -> np.ndarray:
     out = np.empty((msa.size, rsa.size), np.float64)
     _load().tro_prefill(_ptr(c, _u32p), _ptr(s, _u16p), _ptr(xx, _u16p), M, R, C, k, L, T,
                         _ptr(msa, _i64p), msa.size, _ptr(rsa, _i64p), rsa.size, _ptr(out, _f64p))
+    return out
+
+
+def prefill_axis0_sums(codes, scales, x, M, R, C, k, L, T, ms, cols) -> np.ndarray:
+    """float64 [len(ms), len(cols)] sums over the stored rows of bf16 weights
+    times bf16 x, for a matrix stored transposed (axis 0)."""
+    c, s, xx = _c(codes, np.uint32), _c(scales, np.uint16), _c(x, np.uint16)
+    msa, csa = _c(ms, np.int64), _c(cols, np.int64)
+    out = np.empty((msa.size, csa.size), np.float64)
+    _load().tro_prefill_axis0(_ptr(c, _u32p), _ptr(s, _u16p), _ptr(xx, _u16p), M, R, C, k, L, T,
+                              _ptr(msa, _i64p), msa.size, _ptr(csa, _i64p), csa.size, _ptr(out, _f64p))
     return out

@@ -304,6 +304,31 @@ void tro_prefill(const uint32_t* codes, const uint16_t* scales, const uint16_t* 
 }
 
 /* Worker threads OpenMP will use (1 without OpenMP). */
+/* Axis-0 prefill ([TL] forward expand-then-matmul fallback, for the stored
+ * transpose of the SCATTER kernel's layout): sum[a, b] = sum_r wb(r, cols_b)
+ * * x[ms_a, r] over ALL stored rows, wb the bf16 expansion weight of stored
+ * row r (its own scale); each product exact in double.  x: bf16 [M, R];
+ * sums: double [nm, nc].  The layer output is the bf16 rounding of each sum. */
+void tro_prefill_axis0(const uint32_t* codes, const uint16_t* scales, const uint16_t* x,
+                       int64_t M, int64_t R, int64_t C, int k, int L, int T,
+                       const int64_t* ms, int64_t nm, const int64_t* cols, int64_t nc, double* sums) {
+  (void)M;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t b = 0; b < nc; ++b) {
+    const int64_t c = cols[b];
+    double* wcol = (double*)malloc(sizeof(double) * (size_t)R);
+    for (int64_t r = 0; r < R; ++r)
+      wcol[r] = tro_weight_bf16(tro_state_rc(codes, r, c, C, k, L, T), tro_half_to_double(scales[r]));
+    for (int64_t a = 0; a < nm; ++a) {
+      const uint16_t* xr = x + ms[a] * R;
+      double acc = 0.0;
+      for (int64_t r = 0; r < R; ++r) acc += wcol[r] * tro_bf16_to_double(xr[r]);
+      sums[a * nc + b] = acc;
+    }
+    free(wcol);
+  }
+}
+
 int tro_num_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

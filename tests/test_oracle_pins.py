@@ -326,6 +326,25 @@ def test_prefill_dense():
     assert np.array_equal(sub, got[np.ix_([M - 1, 2], [0, R - 1])])
 
 
+@pytest.mark.parametrize("k", KS)
+def test_prefill_axis0_dense_and_one_hot(k):
+    # stored W^T [R, C]: sums over the stored rows of the expansion times x; a
+    # one-hot x over stored rows picks one expansion row exactly
+    rng = np.random.default_rng(41 + k)
+    R, C, M = 37, 512, 5
+    codes = rng.integers(0, 2 ** 32, (R, C * k // 32), dtype=np.uint32)
+    sc = rand_scales(rng, R)
+    x = rand_bf16(rng, (M, R))
+    Wb = bf16_bits_to_f64(oracle.expand_bf16(codes, sc, R, C, k, L, T))     # [R, C]
+    got = oracle.prefill_axis0_sums(codes, sc, x, M, R, C, k, L, T, np.arange(M), np.arange(C))
+    np.testing.assert_allclose(got, bf16_bits_to_f64(x) @ Wb, rtol=1e-12, atol=1e-12)
+    one = np.zeros((2, R), np.uint16)
+    one[0, 3] = 0x3F80                                                      # bf16 1.0
+    one[1, R - 1] = 0xBF80                                                  # bf16 -1.0
+    e = oracle.prefill_axis0_sums(codes, sc, one, 2, R, C, k, L, T, [0, 1], np.arange(C))
+    assert np.array_equal(e[0], Wb[3]) and np.array_equal(e[1], -Wb[R - 1])
+
+
 def test_expansion_size_matches_page():
     # TL file header: the dense bf16 transient at the 5120 -> 17408 shape is ~178 MB
     assert round(17408 * 5120 * 2 / 1e6) == GOLD["expansion_megabytes_17408x5120"]["value"]
