@@ -8,7 +8,8 @@ in HBM; code buffers rotate over >= 1 GiB of replicas so the 256 MB
 Infinity Cache cannot serve repeats).  Other workloads (--workload) print
 the same JSON line for their own metric: the 512 x 2048 reduce matvec, the
 17408 x 5120 k = 3 down-projection scatter, the k = 4 decoder-layer chain,
-the MLP (gate/up + SwiGLU, then the down projection, in one call),
+the MLP (gate/up + SwiGLU, then the down projection, in one call), the
+axis-0 (down projection) prefill through expansion and GEMM,
 and the 17408 x 5120 prefill at M in {32, 512, 2048} (fused or expand +
 GEMM), plus a plain device copy used as the HBM reference point.
 
@@ -363,6 +364,52 @@ class Prefill(Workload):
                 "sample": f"{n} of {m.R} weight rows at M={M}: {f:.3e} flop in {dt:.2f} s"}
 
 
+class PrefillAxis0(Workload):
+    """Axis-0 prefill: the MLP down projection for M rows, stored W^T 17408 x 5120, k = 3,
+    x [M, 17408]; expansion into the workspace, then one bf16 GEMM (per call, eager)."""
+    unit, bound, dtype = "TFLOP/s", "mfma", "bf16"
+    graph = False
+
+    def __init__(self, args, np, torch, dev):
+        import trellis_coded_quantized_amd as tq
+        import trellis_inputs as ti
+        self.np, self.tq = np, tq
+        M = args.m or 2048
+        self.M = M
+        self.m = m = ti.axis0().mats[0]
+        self.x = ti.activations(np.random.default_rng(2000 + M), M, m.R)
+        codes, half, bf16 = _dev_tensors(np, torch, dev)
+        self.dc, self.ds, self.dx = codes(m.codes), half(m.scales), bf16(self.x)
+        self.out = torch.empty((M, m.C), dtype=torch.bfloat16, device=dev)
+        nbytes = tq.load_library().trellis_prefill_axis0_workspace_bytes(m.R, m.C, M, m.k, L, T,
+                                                                          tq.PREFILL_EXPAND_GEMM)
+        self.ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+        self.kernels_per_step = 2
+        self.units_per_step = 2.0 * M * m.R * m.C
+        self.name = f"prefill_axis0_{m.R}x{m.C}_k{m.k}_m{M}"
+        self.kernel = "expand_kernel + hipBLASLt GEMM (per call)"
+        self.config = {"workload": self.name, "M": M, "R_in": m.R, "C_out": m.C, "k": m.k, "L": L, "T": T,
+                       "algo": "expand_gemm"}
+
+    def step(self, s):
+        self.tq.prefill_axis0(self.dc, self.ds, self.dx, self.m.k, out=self.out, workspace=self.ws)
+
+    def cpu_baseline(self, seconds):
+        import oracle
+        np, m, M = self.np, self.m, self.M
+
+        def run(n):
+            t0 = time.perf_counter()
+            oracle.prefill_axis0_sums(m.codes, m.scales, self.x, M, m.R, m.C, m.k, L, T, np.arange(M), np.arange(n))
+            return time.perf_counter() - t0
+        dt = run(4)
+        n = int(min(m.C, max(4, 4 * seconds / max(dt, 1e-6))))
+        dt = run(n)
+        f = 2.0 * M * n * m.R
+        return {"value": f / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+                "sample": f"{n} of {m.C} output columns at M={M}: {f:.3e} flop in {dt:.2f} s"}
+
+
 class Copy(Workload):
     """Plain device-to-device copy of 1 GiB: the HBM reference point, and the
     known-size kernel that calibrates the FETCH_SIZE / WRITE_SIZE counters."""
@@ -401,6 +448,7 @@ def workload_axis1_m1(args, np, torch, dev):
 
 
 WORKLOADS = {"copy": Copy, "gateup": GateUp, "prefill": Prefill, "axis0": workload_axis0, "mlp": Mlp,
+             "prefill_axis0": PrefillAxis0,
              "layer_chain": workload_layer_chain, "axis1_m1": workload_axis1_m1}
 
 

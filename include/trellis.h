@@ -167,6 +167,29 @@ int trellis_prefill(const uint32_t* codes, const uint16_t* scales, const uint16_
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * trellis_prefill_axis0 -- out[m, c] = bf16(sum_r wb(r, c) * x[m, r]) for a
+ * matrix stored transposed (axis 0: codes W^T [R_in, C_out*k/32], coded
+ * along the outputs), wb the expansion weight of trellis_expand_bf16; f32
+ * accumulation.  The down projection of an MLP for more than
+ * TRELLIS_MATVEC_MAX_M rows.
+ * Source: mlx-bun 0.2.0 -> 0.4.0 diff (page 55), the expand-then-matmul
+ * fallback of TrellisLinear.forward, here for the transposed layout of the
+ * SCATTER kernel's matrices.
+ *   codes uint32 [R_in, C_out*k/32];  scales fp16 [R_in]
+ *   x bf16 [M, R_in];  out bf16 [M, C_out];  M >= 1
+ * algo must be TRELLIS_PREFILL_EXPAND_GEMM: the expansion (stored
+ * orientation, R_in*C_out*2 bytes) goes into the workspace, then one bf16
+ * GEMM.  TRELLIS_PREFILL_FUSED returns TRELLIS_EUNSUPPORTED (no fused kernel
+ * for this layout yet).  The first call for a shape times hipBLASLt's
+ * candidate kernels on the caller's buffers, as trellis_prefill does.
+ */
+size_t trellis_prefill_axis0_workspace_bytes(int64_t R_in, int64_t C_out, int64_t M, int k, int L, int T,
+                                             int algo);
+int trellis_prefill_axis0(const uint32_t* codes, const uint16_t* scales, const uint16_t* x, uint16_t* out,
+                          int64_t R_in, int64_t C_out, int64_t M, int k, int L, int T, int algo,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * trellis_decode_states -- test export of the decode primitive: for every
  * weight of the stored [R, C] matrix, its L-bit state, its 1MAD code y and
  * the f32 code value y/d (correctly rounded).  Any output may be NULL.

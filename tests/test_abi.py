@@ -153,3 +153,17 @@ def test_mlp_decode_workspace_is_checked():
     assert need >= 2 * 1024 * 2                  # at least the hidden vectors
     assert call_mlp(ws=FAKE, wsb=need - 1) == tq.EWORKSPACE
     assert lib.trellis_mlp_decode_workspace_bytes(1024, 2048, 1024, 5, 2, 3, 12, 256) == 0
+
+
+def test_prefill_axis0_rejects_fused_and_checks_workspace():
+    lib = tq.load_library()
+    st = lib.trellis_prefill_axis0(FAKE, FAKE, FAKE, FAKE, 6144, 5120, 64, 4, 12, 256, tq.PREFILL_FUSED, None, 0, None)
+    assert st == tq.EUNSUPPORTED and "no fused axis-0" in lib.trellis_last_error().decode()
+    need = lib.trellis_prefill_axis0_workspace_bytes(6144, 5120, 64, 4, 12, 256, tq.PREFILL_EXPAND_GEMM)
+    assert need >= 6144 * 5120 * 2
+    st = lib.trellis_prefill_axis0(FAKE, FAKE, FAKE, FAKE, 6144, 5120, 64, 4, 12, 256, tq.PREFILL_EXPAND_GEMM,
+                                   FAKE, need - 1, None)
+    assert st == tq.EWORKSPACE
+    st = lib.trellis_prefill_axis0(FAKE, FAKE, MIS, FAKE, 6144, 5120, 64, 4, 12, 256, tq.PREFILL_EXPAND_GEMM,
+                                   FAKE, need, None)
+    assert st == tq.EINVAL and "x not 16-byte aligned" in lib.trellis_last_error().decode()

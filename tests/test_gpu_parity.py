@@ -280,3 +280,31 @@ def test_prefill_workload_17408x5120_k2(prefill_workload, algo, M):
     want = oracle.prefill_sums(m.codes, m.scales, x, M, m.R, m.C, m.k, L, T, ms, rows)
     sub = h_u16(got[torch.as_tensor(ms, device=DEV)][:, torch.as_tensor(rows, device=DEV)])
     tol.assert_bf16_close(sub, want, f"{w.name} algo={algo} M={M}")
+
+
+# ------------------------------------------------------------------ axis-0 prefill
+
+@pytest.mark.parametrize("k", [2, 3, 4])
+@pytest.mark.parametrize("R,C,M", [(300, 512, 40), (1000, 1280, 5)])
+def test_prefill_axis0_small(k, R, C, M):
+    rng = np.random.default_rng(R + C + M + 7 * k)
+    codes, scales = rand_matrix(rng, R, C, k)
+    x = ti.activations(rng, M, R)
+    got = h_u16(tq.prefill_axis0(d_codes(codes), d_half(scales), d_bf16(x), k))
+    want = oracle.prefill_axis0_sums(codes, scales, x, M, R, C, k, L, T, np.arange(M), np.arange(C))
+    tol.assert_bf16_close(got, want, f"prefill axis0 R={R} C={C} M={M} k={k}")
+
+
+@pytest.mark.parametrize("M", [32, 512])
+def test_prefill_axis0_down_17408x5120_k3(axis0_workload, M):
+    # the down projection of the MLP prefill: stored W^T 17408 x 5120, k = 3; x [M, 17408]
+    w, _ = axis0_workload
+    m = w.mats[0]
+    rng = np.random.default_rng(M)
+    x = ti.activations(rng, M, m.R)
+    got = tq.prefill_axis0(d_codes(m.codes), d_half(m.scales), d_bf16(x), m.k)
+    ms = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, 6)]))
+    cols = np.unique(np.concatenate([[0, 255, 256, m.C - 1], rng.integers(0, m.C, 60)]))
+    want = oracle.prefill_axis0_sums(m.codes, m.scales, x, M, m.R, m.C, m.k, L, T, ms, cols)
+    sub = h_u16(got[torch.as_tensor(ms, device=DEV)][:, torch.as_tensor(cols, device=DEV)])
+    tol.assert_bf16_close(sub, want, f"prefill axis0 down M={M}")

@@ -33,6 +33,7 @@ EXPORTS = (
     "trellis_matvec_axis0_workspace_bytes", "trellis_matvec_axis0",
     "trellis_mlp_decode_workspace_bytes", "trellis_mlp_decode",
     "trellis_expand_bf16", "trellis_prefill_workspace_bytes", "trellis_prefill",
+    "trellis_prefill_axis0_workspace_bytes", "trellis_prefill_axis0",
     "trellis_decode_states", "trellis_last_error", "trellis_version",
 )
 
@@ -72,6 +73,9 @@ def load_library():
         "trellis_prefill_workspace_bytes": (_sz, [_i64, _i64, _i64, _int, _int, _int, _int]),
         "trellis_prefill": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int, _int,
                                    _vp, _sz, _vp]),
+        "trellis_prefill_axis0_workspace_bytes": (_sz, [_i64, _i64, _i64, _int, _int, _int, _int]),
+        "trellis_prefill_axis0": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int, _int,
+                                         _vp, _sz, _vp]),
         "trellis_decode_states": (_int, [_vp, _i64, _i64, _int, _int, _int, _vp, _vp, _vp, _vp]),
         "trellis_last_error": (ctypes.c_char_p, []),
         "trellis_version": (ctypes.c_char_p, []),
@@ -259,6 +263,25 @@ def prefill(codes, scales, x, k, L=12, T=256, algo=PREFILL_FUSED, out=None, work
                          workspace)
     _check(lib.trellis_prefill(_ptr(codes), _ptr(scales), _ptr(x), _ptr(out), R, C, M, k, L, T, algo,
                                _ptr(ws), wsb, _stream(x.device)))
+    return out
+
+
+def prefill_axis0(codes_t, scales, x, k, L=12, T=256, algo=PREFILL_EXPAND_GEMM, out=None, workspace=None):
+    """out[m, c] = bf16(sum_r wb(r, c) x[m, r]) for a matrix stored transposed
+    (axis 0): codes_t [R_in, C_out*k/32], x bf16 [M, R_in]; expand + GEMM."""
+    _need(codes_t, "codes", _CODES, 2)
+    _need(scales, "scales", (torch.float16,), 1)
+    _need(x, "x", (torch.bfloat16,), 2)
+    R, C = _geometry(codes_t, k)
+    M = x.shape[0]
+    if x.shape[1] != R:
+        raise ValueError(f"x has {x.shape[1]} features, stored rows are {R}")
+    if out is None:
+        out = torch.empty((M, C), dtype=torch.bfloat16, device=x.device)
+    lib = load_library()
+    ws, wsb = _workspace(lib.trellis_prefill_axis0_workspace_bytes(R, C, M, k, L, T, algo), x.device, workspace)
+    _check(lib.trellis_prefill_axis0(_ptr(codes_t), _ptr(scales), _ptr(x), _ptr(out), R, C, M, k, L, T, algo,
+                                     _ptr(ws), wsb, _stream(x.device)))
     return out
 
 

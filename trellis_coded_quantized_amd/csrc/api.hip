@@ -121,12 +121,14 @@ struct GemmPlan {
 
 std::mutex g_lt_mu;
 std::map<int, hipblasLtHandle_t> g_lt_handles;
-std::map<std::tuple<int, int64_t, int64_t, int64_t>, GemmPlan> g_lt_plans;
+std::map<std::tuple<int, int64_t, int64_t, int64_t, int>, GemmPlan> g_lt_plans;
 
-// out[M, R] (row-major) = x[M, C] * W[R, C]^T.  Column-major view:
-// D (R x M, ld R) = op_T(A: C x R, ld C) * op_N(B: C x M, ld C).
-int gemm_bf16_nt(const char* fn, const uint16_t* W, const uint16_t* x, uint16_t* out, int64_t R,
-                 int64_t C, int64_t M, void* ws, size_t ws_bytes, hipStream_t stream) {
+// Axis 1 (nn = false): out[M, R] (row-major) = x[M, C] * W[R, C]^T.
+// Column-major view: D (R x M, ld R) = op_T(A: C x R, ld C) * op_N(B: C x M, ld C).
+// Axis 0 (nn = true): out[M, R] = x[M, C] * W[C, R], W the stored [C, R]
+// expansion.  Column-major view: D (R x M, ld R) = op_N(A: R x C, ld R) * op_N(B: C x M, ld C).
+int gemm_bf16(const char* fn, const uint16_t* W, const uint16_t* x, uint16_t* out, int64_t R, int64_t C,
+              int64_t M, bool nn, void* ws, size_t ws_bytes, hipStream_t stream) {
   int dev = 0;
   hipError_t he = hipGetDevice(&dev);
   if (he != hipSuccess) return hip_status(fn, he);
@@ -138,18 +140,19 @@ int gemm_bf16_nt(const char* fn, const uint16_t* W, const uint16_t* x, uint16_t*
     hit = g_lt_handles.emplace(dev, h).first;
   }
   hipblasLtHandle_t h = hit->second;
-  auto key = std::make_tuple(dev, R, C, M);
+  auto key = std::make_tuple(dev, R, C, M, nn ? 1 : 0);
   auto pit = g_lt_plans.find(key);
   if (pit == g_lt_plans.end()) {
     GemmPlan p;
-    hipblasOperation_t ta = HIPBLAS_OP_T, tb = HIPBLAS_OP_N;
+    hipblasOperation_t ta = nn ? HIPBLAS_OP_N : HIPBLAS_OP_T, tb = HIPBLAS_OP_N;
     uint64_t wsb = kGemmWorkspace;
     hipblasLtMatmulPreference_t pref = nullptr;
     int returned = 0;
     bool good = hipblasLtMatmulDescCreate(&p.desc, HIPBLAS_COMPUTE_32F, HIP_R_32F) == HIPBLAS_STATUS_SUCCESS &&
                 hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSA, &ta, sizeof(ta)) == HIPBLAS_STATUS_SUCCESS &&
                 hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSB, &tb, sizeof(tb)) == HIPBLAS_STATUS_SUCCESS &&
-                hipblasLtMatrixLayoutCreate(&p.la, HIP_R_16BF, (uint64_t)C, (uint64_t)R, C) == HIPBLAS_STATUS_SUCCESS &&
+                (nn ? hipblasLtMatrixLayoutCreate(&p.la, HIP_R_16BF, (uint64_t)R, (uint64_t)C, R)
+                    : hipblasLtMatrixLayoutCreate(&p.la, HIP_R_16BF, (uint64_t)C, (uint64_t)R, C)) == HIPBLAS_STATUS_SUCCESS &&
                 hipblasLtMatrixLayoutCreate(&p.lb, HIP_R_16BF, (uint64_t)C, (uint64_t)M, C) == HIPBLAS_STATUS_SUCCESS &&
                 hipblasLtMatrixLayoutCreate(&p.lc, HIP_R_16BF, (uint64_t)R, (uint64_t)M, R) == HIPBLAS_STATUS_SUCCESS &&
                 hipblasLtMatmulPreferenceCreate(&pref) == HIPBLAS_STATUS_SUCCESS &&
@@ -382,8 +385,40 @@ int trellis_prefill(const uint32_t* codes, const uint16_t* scales, const uint16_
   uint16_t* wexp = reinterpret_cast<uint16_t*>(workspace);
   const size_t wexp_bytes = align_up((size_t)R * (size_t)C * 2, 256);
   TRY(hip_status(fn, trellis::launch_expand(codes, scales, wexp, R, C, k, s)));
-  return gemm_bf16_nt(fn, wexp, x, out, R, C, M, reinterpret_cast<char*>(workspace) + wexp_bytes,
-                      workspace_bytes - wexp_bytes, s);
+  return gemm_bf16(fn, wexp, x, out, R, C, M, false, reinterpret_cast<char*>(workspace) + wexp_bytes,
+                   workspace_bytes - wexp_bytes, s);
+}
+
+size_t trellis_prefill_axis0_workspace_bytes(int64_t R_in, int64_t C_out, int64_t M, int k, int L, int T,
+                                             int algo) {
+  if (check_geometry("trellis_prefill_axis0_workspace_bytes", R_in, C_out, k, L, T) != TRELLIS_OK) return 0;
+  if (algo != TRELLIS_PREFILL_EXPAND_GEMM || M < 1) return 0;
+  return align_up((size_t)R_in * (size_t)C_out * 2, 256) + kGemmWorkspace;
+}
+
+int trellis_prefill_axis0(const uint32_t* codes, const uint16_t* scales, const uint16_t* x, uint16_t* out,
+                          int64_t R_in, int64_t C_out, int64_t M, int k, int L, int T, int algo,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "trellis_prefill_axis0";
+  TRY(check_geometry(fn, R_in, C_out, k, L, T));
+  TRY(check_m(fn, M, kMaxDim - 1));
+  if (M * C_out >= kMaxElems || M * R_in >= kMaxElems)
+    return fail(TRELLIS_EINVAL, "%s: M=%lld too large", fn, (long long)M);
+  if (algo == TRELLIS_PREFILL_FUSED)
+    return fail(TRELLIS_EUNSUPPORTED, "%s: no fused axis-0 prefill kernel; use TRELLIS_PREFILL_EXPAND_GEMM", fn);
+  if (algo != TRELLIS_PREFILL_EXPAND_GEMM) return fail(TRELLIS_EINVAL, "%s: algo=%d unknown", fn, algo);
+  TRY(check_ptr(fn, "codes", codes, 16));
+  TRY(check_ptr(fn, "scales", scales, 2));
+  TRY(check_ptr(fn, "x", x, 16));
+  TRY(check_ptr(fn, "out", out, 16));
+  TRY(check_workspace(fn, workspace, workspace_bytes,
+                      trellis_prefill_axis0_workspace_bytes(R_in, C_out, M, k, L, T, algo)));
+  hipStream_t s = (hipStream_t)stream;
+  uint16_t* wexp = reinterpret_cast<uint16_t*>(workspace);     // W^T expanded in stored orientation [R_in, C_out]
+  const size_t wexp_bytes = align_up((size_t)R_in * (size_t)C_out * 2, 256);
+  TRY(hip_status(fn, trellis::launch_expand(codes, scales, wexp, R_in, C_out, k, s)));
+  return gemm_bf16(fn, wexp, x, out, C_out, R_in, M, true, reinterpret_cast<char*>(workspace) + wexp_bytes,
+                   workspace_bytes - wexp_bytes, s);
 }
 
 int trellis_decode_states(const uint32_t* codes, int64_t R, int64_t C, int k, int L, int T,
