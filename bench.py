@@ -203,7 +203,7 @@ class Matvec(Workload):
         codes, half, bf16 = _dev_tensors(np, torch, dev)
         self.code_bytes = sum(m.codes.nbytes for m in w.mats)
         self.nrep = _nrep(self.code_bytes)
-        self.reps = [[codes(m.codes) for m in w.mats]]
+        self.reps = [[codes(self._stored(m)) for m in w.mats]]
         for _ in range(self.nrep - 1):
             self.reps.append([c.clone() for c in self.reps[0]])
         self.scs = [half(m.scales) for m in w.mats]
@@ -225,6 +225,15 @@ class Matvec(Workload):
         self.config = {"workload": w.name, "M": list(Ms), "k": w.mats[0].k, "L": L, "T": T,
                        "matrices": [f"axis{m.axis} {m.R}x{m.C}" for m in w.mats],
                        "code_bytes_per_call": self.code_bytes, "replicas": self.nrep}
+
+    interleaved = False
+
+    def _stored(self, m):
+        """codes as stored: row-major, or the block-interleaved k = 3 axis-0 layout"""
+        if not self.interleaved:
+            return m.codes
+        wpb = 256 * m.k // 32
+        return self.np.ascontiguousarray(m.codes.reshape(m.R, m.C // 512, 2 * wpb).transpose(1, 0, 2))
 
     def step(self, s):
         for j, M in enumerate(self.Ms):
@@ -436,6 +445,19 @@ def workload_axis0(args, np, torch, dev):
                   args, np, torch, dev)
 
 
+class MatvecInterleaved(Matvec):
+    interleaved = True
+
+
+def workload_axis0_il(args, np, torch, dev):
+    import trellis_inputs as ti
+    Ms = (args.m,) if args.m else (1, 2, 3, 4)
+    wl = MatvecInterleaved(ti.axis0(), Ms, "axis0 scatter + fold, block-interleaved codes [C/512, R, 48]", None,
+                           AXIS0_SOURCES, args, np, torch, dev)
+    wl.name = wl.config["workload"] = "axis0_interleaved_17408x5120_k3"
+    return wl
+
+
 def workload_layer_chain(args, np, torch, dev):
     import trellis_inputs as ti
     return Matvec(ti.layer_chain(), (4,), "4-launch chain (3 x axis1_kernel, axis0 scatter + fold)", None,
@@ -448,7 +470,7 @@ def workload_axis1_m1(args, np, torch, dev):
 
 
 WORKLOADS = {"copy": Copy, "gateup": GateUp, "prefill": Prefill, "axis0": workload_axis0, "mlp": Mlp,
-             "prefill_axis0": PrefillAxis0,
+             "prefill_axis0": PrefillAxis0, "axis0_il": workload_axis0_il,
              "layer_chain": workload_layer_chain, "axis1_m1": workload_axis1_m1}
 
 

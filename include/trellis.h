@@ -146,6 +146,28 @@ int trellis_expand_bf16(const uint32_t* codes, const uint16_t* scales, uint16_t*
                         int64_t C, int k, int L, int T, void* stream);
 
 /*
+ * Block-interleaved layout of k = 3 axis-0 matrices: codes [C/512, R, 48]
+ * uint32, i.e. for every pair of 256-column blocks (2g, 2g+1) the rows one
+ * after another, each row's two 24-word blocks side by side.  Only k = 3,
+ * L = 12, T = 256 and C % 512 == 0 (TRELLIS_EUNSUPPORTED / TRELLIS_EINVAL
+ * otherwise).  The results equal those of the row-major calls on the same
+ * symbols.
+ * Source: mlx-bun 0.2.0 -> 0.4.0 diff (page 55), trellis-linear.ts file
+ * header (the optional k3/axis0 layout) and trellisGeometry (3-D codes
+ * [groups, rows, 48]); the SCATTER and EXPAND kernels' INTERLEAVE addressing.
+ *
+ * trellis_matvec_axis0_il -- trellis_matvec_axis0 on interleaved codes; the
+ *   workspace size is trellis_matvec_axis0_workspace_bytes.
+ * trellis_expand_bf16_il -- trellis_expand_bf16 on interleaved codes; out is
+ *   bf16 [R, C] in stored orientation.
+ */
+int trellis_matvec_axis0_il(const uint32_t* codes, const uint16_t* scales, const uint16_t* x,
+                            void* out, int out_dtype, int64_t R_in, int64_t C_out, int M, int k,
+                            int L, int T, void* workspace, size_t workspace_bytes, void* stream);
+int trellis_expand_bf16_il(const uint32_t* codes, const uint16_t* scales, uint16_t* out, int64_t R,
+                           int64_t C, int k, int L, int T, void* stream);
+
+/*
  * trellis_prefill -- out[m, r] = bf16(sum_c wb(r, c) * x[m, c]) for axis 1,
  * where wb is the expansion weight of trellis_expand_bf16; f32 accumulation.
  * Source: trellis-tiled-prefill.ts (page 56) and the expand-then-matmul

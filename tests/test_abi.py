@@ -167,3 +167,15 @@ def test_prefill_axis0_rejects_fused_and_checks_workspace():
     st = lib.trellis_prefill_axis0(FAKE, FAKE, MIS, FAKE, 6144, 5120, 64, 4, 12, 256, tq.PREFILL_EXPAND_GEMM,
                                    FAKE, need, None)
     assert st == tq.EINVAL and "x not 16-byte aligned" in lib.trellis_last_error().decode()
+
+
+@pytest.mark.parametrize("k,C,status,needle", [
+    (2, 1024, tq.EUNSUPPORTED, "k=3 only"),
+    (3, 768, tq.EINVAL, "not a multiple of 512"),
+])
+def test_interleaved_layout_rejects(k, C, status, needle):
+    lib = tq.load_library()
+    assert lib.trellis_matvec_axis0_il(FAKE, FAKE, FAKE, FAKE, 0, 1024, C, 2, k, 12, 256, None, 0, None) == status
+    assert needle in lib.trellis_last_error().decode()
+    assert lib.trellis_expand_bf16_il(FAKE, FAKE, FAKE, 1024, C, k, 12, 256, None) == status
+    assert needle in lib.trellis_last_error().decode()

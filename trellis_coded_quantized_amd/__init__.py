@@ -32,6 +32,7 @@ EXPORTS = (
     "trellis_gateup_swiglu_workspace_bytes", "trellis_gateup_swiglu",
     "trellis_matvec_axis0_workspace_bytes", "trellis_matvec_axis0",
     "trellis_mlp_decode_workspace_bytes", "trellis_mlp_decode",
+    "trellis_matvec_axis0_il", "trellis_expand_bf16_il",
     "trellis_expand_bf16", "trellis_prefill_workspace_bytes", "trellis_prefill",
     "trellis_prefill_axis0_workspace_bytes", "trellis_prefill_axis0",
     "trellis_decode_states", "trellis_last_error", "trellis_version",
@@ -70,6 +71,9 @@ def load_library():
         "trellis_mlp_decode": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int,
                                       _int, _int, _int, _int, _vp, _sz, _vp]),
         "trellis_expand_bf16": (_int, [_vp, _vp, _vp, _i64, _i64, _int, _int, _int, _vp]),
+        "trellis_matvec_axis0_il": (_int, [_vp, _vp, _vp, _vp, _int, _i64, _i64, _int, _int, _int, _int,
+                                           _vp, _sz, _vp]),
+        "trellis_expand_bf16_il": (_int, [_vp, _vp, _vp, _i64, _i64, _int, _int, _int, _vp]),
         "trellis_prefill_workspace_bytes": (_sz, [_i64, _i64, _i64, _int, _int, _int, _int]),
         "trellis_prefill": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int, _int,
                                    _vp, _sz, _vp]),
@@ -128,6 +132,18 @@ def _geometry(codes, k):
     return rows, words * 32 // k
 
 
+def _axis0_geometry(codes, k):
+    """(rows, cols, interleaved) of axis-0 codes: row-major [R, C*k/32], or the
+    block-interleaved k = 3 layout [C/512, R, 48] (identified by its shape)."""
+    if codes.dim() == 3:
+        groups, rows, words = codes.shape
+        if k != 3 or words != 48:
+            raise ValueError(f"interleaved codes must be k = 3 with 48 words per row pair, got k={k}, {words}")
+        return rows, groups * 512, True
+    rows, cols = _geometry(codes, k)
+    return rows, cols, False
+
+
 def _workspace(nbytes, device, workspace):
     if nbytes == 0:
         return None, 0
@@ -183,11 +199,12 @@ def gateup_swiglu(gcodes, gscales, ucodes, uscales, x, k, L=12, T=256, out=None,
 
 def matvec_axis0(codes_t, scales, x, k, L=12, T=256, out_dtype=torch.bfloat16, out=None,
                  workspace=None):
-    """y[m, c] = sum_r w(r, c) x[m, r]; codes_t is the stored W^T [R_in, C_out*k/32]."""
-    _need(codes_t, "codes", _CODES, 2)
+    """y[m, c] = sum_r w(r, c) x[m, r]; codes_t is the stored W^T [R_in, C_out*k/32],
+    or for k = 3 the block-interleaved [C_out/512, R_in, 48]."""
+    _need(codes_t, "codes", _CODES, codes_t.dim() if codes_t.dim() == 3 else 2)
     _need(scales, "scales", (torch.float16,), 1)
     _need(x, "x", (torch.bfloat16,), 2)
-    R, C = _geometry(codes_t, k)
+    R, C, il = _axis0_geometry(codes_t, k)
     M = x.shape[0]
     if x.shape[1] != R:
         raise ValueError(f"x has {x.shape[1]} features, stored rows are {R}")
@@ -197,8 +214,9 @@ def matvec_axis0(codes_t, scales, x, k, L=12, T=256, out_dtype=torch.bfloat16, o
     lib = load_library()
     ws, wsb = _workspace(lib.trellis_matvec_axis0_workspace_bytes(R, C, M, k, L, T), x.device,
                          workspace)
-    _check(lib.trellis_matvec_axis0(_ptr(codes_t), _ptr(scales), _ptr(x), _ptr(out), od, R, C, M, k,
-                                    L, T, _ptr(ws), wsb, _stream(x.device)))
+    fn = lib.trellis_matvec_axis0_il if il else lib.trellis_matvec_axis0
+    _check(fn(_ptr(codes_t), _ptr(scales), _ptr(x), _ptr(out), od, R, C, M, k, L, T, _ptr(ws), wsb,
+              _stream(x.device)))
     return out
 
 
@@ -236,14 +254,16 @@ def mlp_decode(gcodes, gscales, ucodes, uscales, dcodes_t, dscales, x, k_gu, k_d
 
 
 def expand_bf16(codes, scales, k, L=12, T=256, out=None):
-    """bf16 [R, C] decode of the stored matrix (stored orientation)."""
-    _need(codes, "codes", _CODES, 2)
+    """bf16 [R, C] decode of the stored matrix (stored orientation); codes
+    [R, C*k/32], or for k = 3 the block-interleaved axis-0 layout [C/512, R, 48]."""
+    _need(codes, "codes", _CODES, codes.dim() if codes.dim() == 3 else 2)
     _need(scales, "scales", (torch.float16,), 1)
-    R, C = _geometry(codes, k)
+    R, C, il = _axis0_geometry(codes, k)
     if out is None:
         out = torch.empty((R, C), dtype=torch.bfloat16, device=codes.device)
-    _check(load_library().trellis_expand_bf16(_ptr(codes), _ptr(scales), _ptr(out), R, C, k, L, T,
-                                              _stream(codes.device)))
+    lib = load_library()
+    fn = lib.trellis_expand_bf16_il if il else lib.trellis_expand_bf16
+    _check(fn(_ptr(codes), _ptr(scales), _ptr(out), R, C, k, L, T, _stream(codes.device)))
     return out
 
 

@@ -341,6 +341,46 @@ int trellis_mlp_decode(const uint32_t* gcodes, const uint16_t* gscales, const ui
   return hip_status(fn, trellis::launch_axis0(dcodes, dscales, mid, out, 0, R, C_out, M, k_down, ws + hb + w1, s));
 }
 
+// The block-interleaved k = 3 layout of axis-0 matrices: codes [C/512, R, 48].
+int check_interleaved(const char* fn, int64_t C, int k) {
+  if (k != 3) return fail(TRELLIS_EUNSUPPORTED, "%s: the interleaved layout is k=3 only (k=%d)", fn, k);
+  if (C % 512 != 0)
+    return fail(TRELLIS_EINVAL, "%s: C=%lld not a multiple of 512 (two blocks per group)", fn, (long long)C);
+  return TRELLIS_OK;
+}
+
+int trellis_matvec_axis0_il(const uint32_t* codes, const uint16_t* scales, const uint16_t* x,
+                            void* out, int out_dtype, int64_t R_in, int64_t C_out, int M, int k,
+                            int L, int T, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "trellis_matvec_axis0_il";
+  TRY(check_geometry(fn, R_in, C_out, k, L, T));
+  TRY(check_interleaved(fn, C_out, k));
+  TRY(check_m(fn, M, TRELLIS_MATVEC_MAX_M));
+  if (out_dtype != TRELLIS_OUT_BF16 && out_dtype != TRELLIS_OUT_F32)
+    return fail(TRELLIS_EINVAL, "%s: out_dtype=%d unknown", fn, out_dtype);
+  TRY(check_ptr(fn, "codes", codes, 16));
+  TRY(check_ptr(fn, "scales", scales, 2));
+  TRY(check_ptr(fn, "x", x, 16));
+  TRY(check_ptr(fn, "out", out, 16));
+  if (!trellis::axis0_supported(R_in, C_out, M, k))
+    return fail(TRELLIS_EUNSUPPORTED, "%s: shape R=%lld C=%lld M=%d k=%d does not fit the kernel's LDS plan", fn,
+                (long long)R_in, (long long)C_out, M, k);
+  TRY(check_workspace(fn, workspace, workspace_bytes, trellis::axis0_workspace_bytes(R_in, C_out, M, k)));
+  return hip_status(fn, trellis::launch_axis0(codes, scales, x, out, out_dtype == TRELLIS_OUT_F32, R_in, C_out,
+                                              M, k, workspace, (hipStream_t)stream, 1));
+}
+
+int trellis_expand_bf16_il(const uint32_t* codes, const uint16_t* scales, uint16_t* out, int64_t R,
+                           int64_t C, int k, int L, int T, void* stream) {
+  const char* fn = "trellis_expand_bf16_il";
+  TRY(check_geometry(fn, R, C, k, L, T));
+  TRY(check_interleaved(fn, C, k));
+  TRY(check_ptr(fn, "codes", codes, 16));
+  TRY(check_ptr(fn, "scales", scales, 2));
+  TRY(check_ptr(fn, "out", out, 16));
+  return hip_status(fn, trellis::launch_expand(codes, scales, out, R, C, k, (hipStream_t)stream, 1));
+}
+
 int trellis_expand_bf16(const uint32_t* codes, const uint16_t* scales, uint16_t* out, int64_t R,
                         int64_t C, int k, int L, int T, void* stream) {
   const char* fn = "trellis_expand_bf16";

@@ -45,7 +45,8 @@ constexpr size_t kLdsBudget = 160 * 1024;
 struct Axis0Geom {
   int64_t R, C;
   int M, ncg, S, rps;     // column groups, row splits, rows per split (multiple of 32)
-  int64_t row_bytes;
+  int64_t row_bytes;       // stride between stored rows (2 blocks when interleaved)
+  int interleave;          // codes in the block-interleaved layout [C/512, R, 2 wpb]
   int gsr;                // granules per tile row in LDS (the group's block + one pad granule)
   int nwd;                // copies per wave per tile
   int nslots;
@@ -148,7 +149,9 @@ __global__ __launch_bounds__(kThreads) void axis0_kernel(const uint32_t* __restr
     const int rr = p / gsr, gg = p - rr * gsr;
     dd[j] = (j < nwd && p < 32 * gsr && gg < gsr - 1) ? (1u << 31) | ((uint32_t)rr << 16) | (uint32_t)(gg * 16) : 0u;
   }
-  const uint8_t* cb = reinterpret_cast<const uint8_t*>(codes) + (int64_t)cgi * BLK;
+  // this column group's block of row 0; rows follow at g.row_bytes
+  const uint8_t* cb = reinterpret_cast<const uint8_t*>(codes) +
+                      (g.interleave ? ((int64_t)(cgi >> 1) * R * 2 + (cgi & 1)) * BLK : (int64_t)cgi * BLK);
   auto issue_tile = [&](int t) {             // t-th block of this wave
     const int64_t rowb = r0 + (int64_t)(wave + kWaves * t) * 32;
     uint8_t* slot = ring + (size_t)(t % NS) * g.slot_bytes;
@@ -434,6 +437,7 @@ bool axis0_geom(int64_t R, int64_t C, int M, int k, Axis0Geom& g) {
   g.rps = (int)rps;
   g.S = (int)((R + rps - 1) / rps);
   g.row_bytes = C * k / 8;
+  g.interleave = 0;
   g.gsr = blk / 16 + 1;
   g.nwd = (32 * g.gsr + 63) / 64;
   if (g.nwd > kMaxDma) return false;
@@ -489,9 +493,14 @@ size_t axis0_workspace_bytes(int64_t R, int64_t C, int M, int k) {
 
 hipError_t launch_axis0(const uint32_t* codes, const uint16_t* scales, const uint16_t* x,
                         void* out, int out_f32, int64_t R, int64_t C, int M, int k,
-                        void* workspace, hipStream_t stream) {
+                        void* workspace, hipStream_t stream, int interleave) {
   Axis0Geom g;
   if (!axis0_geom(R, C, M, k, g)) return hipErrorInvalidValue;
+  if (interleave) {
+    if (C % 512 != 0) return hipErrorInvalidValue;
+    g.interleave = 1;
+    g.row_bytes = 2 * (256 * k / 8);
+  }
   g.scales16 = reinterpret_cast<uintptr_t>(scales) % 16 == 0;
   g.x16 = reinterpret_cast<uintptr_t>(x) % 16 == 0 && R % 8 == 0;
   float* partial = reinterpret_cast<float*>(workspace);

@@ -27,7 +27,8 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 template <int K>
 __global__ __launch_bounds__(256) void expand_kernel(const uint32_t* __restrict__ codes,
                                                      const uint16_t* __restrict__ scales,
-                                                     uint16_t* __restrict__ out, int R, int C) {
+                                                     uint16_t* __restrict__ out, int R, int C,
+                                                     int interleave) {
   constexpr int WPB = words_per_block(K);
   __shared__ u32x4 tb[256 * 4];                              // 4 KB per wave
   const int runs = C / 32;                                   // runs per row
@@ -38,7 +39,10 @@ __global__ __launch_bounds__(256) void expand_kernel(const uint32_t* __restrict_
   const int blk = run >> 3, j = run & 7;
   // Positions 32 j .. 32 j + 31 of the block: lowest window bit (224 - 32 j) K,
   // i.e. word (7 - j) K; position 32 j + i sits (31 - i) K bits above it.
-  const uint32_t* bw = codes + (int64_t)r * (C / kT) * WPB + blk * WPB;
+  // row-major [R, C*k/32], or block-interleaved [C/512, R, 2 WPB] (two blocks
+  // of a row side by side, rows one after another within each pair of blocks)
+  const uint32_t* bw = interleave ? codes + (((int64_t)(blk >> 1) * R + r) * 2 + (blk & 1)) * WPB
+                                  : codes + (int64_t)r * (C / kT) * WPB + blk * WPB;
   const int w0 = (7 - j) * K;
   uint32_t w[K + 1];
 #pragma unroll
@@ -105,15 +109,15 @@ __global__ __launch_bounds__(256) void decode_states_kernel(const uint32_t* __re
 }  // namespace
 
 hipError_t launch_expand(const uint32_t* codes, const uint16_t* scales, uint16_t* out, int64_t R,
-                         int64_t C, int k, hipStream_t stream) {
+                         int64_t C, int k, hipStream_t stream, int interleave) {
   const int64_t n = R * (C / 32);
   if (n >= ((int64_t)1 << 31)) return hipErrorInvalidValue;   // one thread per run, 32-bit indices
   const dim3 grid((unsigned)((n + 255) / 256)), block(256);
   const int r = (int)R, c = (int)C;
   switch (k) {
-    case 2: hipLaunchKernelGGL(expand_kernel<2>, grid, block, 0, stream, codes, scales, out, r, c); break;
-    case 3: hipLaunchKernelGGL(expand_kernel<3>, grid, block, 0, stream, codes, scales, out, r, c); break;
-    case 4: hipLaunchKernelGGL(expand_kernel<4>, grid, block, 0, stream, codes, scales, out, r, c); break;
+    case 2: hipLaunchKernelGGL(expand_kernel<2>, grid, block, 0, stream, codes, scales, out, r, c, interleave); break;
+    case 3: hipLaunchKernelGGL(expand_kernel<3>, grid, block, 0, stream, codes, scales, out, r, c, interleave); break;
+    case 4: hipLaunchKernelGGL(expand_kernel<4>, grid, block, 0, stream, codes, scales, out, r, c, interleave); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

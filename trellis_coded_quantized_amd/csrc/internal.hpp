@@ -23,13 +23,14 @@ hipError_t launch_axis1(const uint32_t* codes0, const uint16_t* scales0, const u
 // axis 0 (split-K over stored rows, MFMA on 32-row blocks, then a fold)
 bool axis0_supported(int64_t R, int64_t C, int M, int k);
 size_t axis0_workspace_bytes(int64_t R, int64_t C, int M, int k);
+// interleave: codes in the block-interleaved k = 3 layout [C/512, R, 48]
 hipError_t launch_axis0(const uint32_t* codes, const uint16_t* scales, const uint16_t* x,
                         void* out, int out_f32, int64_t R, int64_t C, int M, int k,
-                        void* workspace, hipStream_t stream);
+                        void* workspace, hipStream_t stream, int interleave = 0);
 
 // expansion and decode export
 hipError_t launch_expand(const uint32_t* codes, const uint16_t* scales, uint16_t* out, int64_t R,
-                         int64_t C, int k, hipStream_t stream);
+                         int64_t C, int k, hipStream_t stream, int interleave = 0);
 hipError_t launch_decode_states(const uint32_t* codes, int64_t R, int64_t C, int k,
                                 uint16_t* states, int16_t* y, float* value, hipStream_t stream);
 
