@@ -375,9 +375,9 @@ class Prefill(Workload):
 
 class PrefillAxis0(Workload):
     """Axis-0 prefill: the MLP down projection for M rows, stored W^T 17408 x 5120, k = 3,
-    x [M, 17408]; expansion into the workspace, then one bf16 GEMM (per call, eager)."""
+    x [M, 17408]; the fused decode-to-LDS MFMA kernel (one graph-replayed step), or expansion
+    into the workspace followed by one bf16 GEMM (per call, eager)."""
     unit, bound, dtype = "TFLOP/s", "mfma", "bf16"
-    graph = False
 
     def __init__(self, args, np, torch, dev):
         import trellis_coded_quantized_amd as tq
@@ -390,18 +390,20 @@ class PrefillAxis0(Workload):
         codes, half, bf16 = _dev_tensors(np, torch, dev)
         self.dc, self.ds, self.dx = codes(m.codes), half(m.scales), bf16(self.x)
         self.out = torch.empty((M, m.C), dtype=torch.bfloat16, device=dev)
-        nbytes = tq.load_library().trellis_prefill_axis0_workspace_bytes(m.R, m.C, M, m.k, L, T,
-                                                                          tq.PREFILL_EXPAND_GEMM)
+        self.algo = tq.PREFILL_EXPAND_GEMM if args.algo == "expand_gemm" else tq.PREFILL_FUSED
+        nbytes = tq.load_library().trellis_prefill_axis0_workspace_bytes(m.R, m.C, M, m.k, L, T, self.algo)
         self.ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
-        self.kernels_per_step = 2
+        self.graph = self.algo == tq.PREFILL_FUSED
+        self.kernels_per_step = 1 if self.graph else 2
         self.units_per_step = 2.0 * M * m.R * m.C
         self.name = f"prefill_axis0_{m.R}x{m.C}_k{m.k}_m{M}"
-        self.kernel = "expand_kernel + hipBLASLt GEMM (per call)"
+        self.kernel = ("prefill_xlayout_kernel + prefill_fused_kernel (+ prefill_fold_kernel for split tiles), one step"
+                       if self.graph else "expand_kernel + hipBLASLt GEMM (per call)")
         self.config = {"workload": self.name, "M": M, "R_in": m.R, "C_out": m.C, "k": m.k, "L": L, "T": T,
-                       "algo": "expand_gemm"}
+                       "algo": args.algo}
 
     def step(self, s):
-        self.tq.prefill_axis0(self.dc, self.ds, self.dx, self.m.k, out=self.out, workspace=self.ws)
+        self.tq.prefill_axis0(self.dc, self.ds, self.dx, self.m.k, algo=self.algo, out=self.out, workspace=self.ws)
 
     def cpu_baseline(self, seconds):
         import oracle

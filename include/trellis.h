@@ -199,11 +199,18 @@ int trellis_prefill(const uint32_t* codes, const uint16_t* scales, const uint16_
  * SCATTER kernel's matrices.
  *   codes uint32 [R_in, C_out*k/32];  scales fp16 [R_in]
  *   x bf16 [M, R_in];  out bf16 [M, C_out];  M >= 1
- * algo must be TRELLIS_PREFILL_EXPAND_GEMM: the expansion (stored
- * orientation, R_in*C_out*2 bytes) goes into the workspace, then one bf16
- * GEMM.  TRELLIS_PREFILL_FUSED returns TRELLIS_EUNSUPPORTED (no fused kernel
- * for this layout yet).  The first call for a shape times hipBLASLt's
- * candidate kernels on the caller's buffers, as trellis_prefill does.
+ * algo:
+ *   TRELLIS_PREFILL_EXPAND_GEMM: the expansion (stored orientation,
+ *     R_in*C_out*2 bytes) goes into the workspace, then one bf16 GEMM.  The
+ *     first call for a shape times hipBLASLt's candidate kernels on the
+ *     caller's buffers, as trellis_prefill does.
+ *   TRELLIS_PREFILL_FUSED: the fused kernel of trellis_prefill with the
+ *     outputs C_out as the tile's weight rows and the stored rows R_in as
+ *     the contraction; each weight is decoded once per 128 (M <= 256) or
+ *     512 rows of x and written transposed into the LDS tile.  Needs R_in a
+ *     multiple of 128 (else TRELLIS_EUNSUPPORTED; the workspace size query
+ *     then returns 0).  Workspace: x in operand order, then f32 partial
+ *     tiles, as for trellis_prefill.
  */
 size_t trellis_prefill_axis0_workspace_bytes(int64_t R_in, int64_t C_out, int64_t M, int k, int L, int T,
                                              int algo);

@@ -155,10 +155,20 @@ def test_mlp_decode_workspace_is_checked():
     assert lib.trellis_mlp_decode_workspace_bytes(1024, 2048, 1024, 5, 2, 3, 12, 256) == 0
 
 
-def test_prefill_axis0_rejects_fused_and_checks_workspace():
+def test_prefill_axis0_fused_needs_whole_steps_and_checks_workspace():
     lib = tq.load_library()
-    st = lib.trellis_prefill_axis0(FAKE, FAKE, FAKE, FAKE, 6144, 5120, 64, 4, 12, 256, tq.PREFILL_FUSED, None, 0, None)
-    assert st == tq.EUNSUPPORTED and "no fused axis-0" in lib.trellis_last_error().decode()
+    # the fused kernel takes the stored rows 32 per step, four steps at a time
+    assert lib.trellis_prefill_axis0_workspace_bytes(6100, 5120, 64, 4, 12, 256, tq.PREFILL_FUSED) == 0
+    st = lib.trellis_prefill_axis0(FAKE, FAKE, FAKE, FAKE, 6100, 5120, 64, 4, 12, 256, tq.PREFILL_FUSED, None, 0, None)
+    assert st == tq.EUNSUPPORTED and "multiple of 128" in lib.trellis_last_error().decode()
+    fneed = lib.trellis_prefill_axis0_workspace_bytes(6144, 5120, 64, 4, 12, 256, tq.PREFILL_FUSED)
+    assert fneed >= 64 * 6144 * 2                # at least x in operand order
+    st = lib.trellis_prefill_axis0(FAKE, FAKE, FAKE, FAKE, 6144, 5120, 64, 4, 12, 256, tq.PREFILL_FUSED,
+                                   FAKE, fneed - 1, None)
+    assert st == tq.EWORKSPACE
+    assert lib.trellis_prefill_axis0_workspace_bytes(6144, 5120, 64, 4, 12, 256, 7) == 0
+    st = lib.trellis_prefill_axis0(FAKE, FAKE, FAKE, FAKE, 6144, 5120, 64, 4, 12, 256, 7, FAKE, fneed, None)
+    assert st == tq.EINVAL and "algo=7" in lib.trellis_last_error().decode()
     need = lib.trellis_prefill_axis0_workspace_bytes(6144, 5120, 64, 4, 12, 256, tq.PREFILL_EXPAND_GEMM)
     assert need >= 6144 * 5120 * 2
     st = lib.trellis_prefill_axis0(FAKE, FAKE, FAKE, FAKE, 6144, 5120, 64, 4, 12, 256, tq.PREFILL_EXPAND_GEMM,

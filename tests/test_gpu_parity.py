@@ -295,14 +295,46 @@ def test_prefill_axis0_small(k, R, C, M):
     tol.assert_bf16_close(got, want, f"prefill axis0 R={R} C={C} M={M} k={k}")
 
 
-@pytest.mark.parametrize("M", [32, 512])
-def test_prefill_axis0_down_17408x5120_k3(axis0_workload, M):
+@pytest.mark.parametrize("k", [2, 3, 4])
+@pytest.mark.parametrize("R,C,M", [(384, 512, 40), (1280, 1280, 5), (640, 768, 300), (128, 256, 1)])
+def test_prefill_axis0_fused_small(k, R, C, M):
+    # R stored rows (the contraction, a multiple of 128), C outputs; M = 300 takes the 512-row x
+    # tiles, the others the 128-row tiles; all split their few tiles along the stored rows
+    rng = np.random.default_rng(R + C + M + 11 * k)
+    codes, scales = rand_matrix(rng, R, C, k)
+    x = ti.activations(rng, M, R)
+    got = h_u16(tq.prefill_axis0(d_codes(codes), d_half(scales), d_bf16(x), k, algo=tq.PREFILL_FUSED))
+    want = oracle.prefill_axis0_sums(codes, scales, x, M, R, C, k, L, T, np.arange(M), np.arange(C))
+    tol.assert_bf16_close(got, want, f"fused prefill axis0 R={R} C={C} M={M} k={k}")
+
+
+@pytest.mark.parametrize("k", [3])
+@pytest.mark.parametrize("C,M", [(25600, 300), (38400, 64)])
+def test_prefill_axis0_fused_stream_pieces(k, C, M):
+    # 200 (M = 300, 512-row tiles) or 300 (M = 64, 128-row tiles) output tiles leave more than half
+    # of the workgroup slots busy after the full rounds, so the steps are dealt out in ranges that
+    # cross tile boundaries and the fold adds the pieces of the tiles cut between ranges
+    R = 640                                      # 20 steps per tile: ranges of 16 or 12 steps
+    rng = np.random.default_rng(C + M)
+    codes, scales = rand_matrix(rng, R, C, k)
+    x = ti.activations(rng, M, R)
+    got = tq.prefill_axis0(d_codes(codes), d_half(scales), d_bf16(x), k, algo=tq.PREFILL_FUSED)
+    ms = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, 6)]))
+    cols = np.unique(np.concatenate([[0, 127, 128, C - 1], rng.integers(0, C, 120)]))
+    want = oracle.prefill_axis0_sums(codes, scales, x, M, R, C, k, L, T, ms, cols)
+    sub = h_u16(got[torch.as_tensor(ms, device=DEV)][:, torch.as_tensor(cols, device=DEV)])
+    tol.assert_bf16_close(sub, want, f"fused prefill axis0 stream C={C} M={M}")
+
+
+@pytest.mark.parametrize("algo,M", [(tq.PREFILL_EXPAND_GEMM, 32), (tq.PREFILL_EXPAND_GEMM, 512),
+                                    (tq.PREFILL_FUSED, 32), (tq.PREFILL_FUSED, 512), (tq.PREFILL_FUSED, 2048)])
+def test_prefill_axis0_down_17408x5120_k3(axis0_workload, algo, M):
     # the down projection of the MLP prefill: stored W^T 17408 x 5120, k = 3; x [M, 17408]
     w, _ = axis0_workload
     m = w.mats[0]
     rng = np.random.default_rng(M)
     x = ti.activations(rng, M, m.R)
-    got = tq.prefill_axis0(d_codes(m.codes), d_half(m.scales), d_bf16(x), m.k)
+    got = tq.prefill_axis0(d_codes(m.codes), d_half(m.scales), d_bf16(x), m.k, algo=algo)
     ms = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, 6)]))
     cols = np.unique(np.concatenate([[0, 255, 256, m.C - 1], rng.integers(0, m.C, 60)]))
     want = oracle.prefill_axis0_sums(m.codes, m.scales, x, M, m.R, m.C, m.k, L, T, ms, cols)

@@ -288,7 +288,8 @@ def prefill(codes, scales, x, k, L=12, T=256, algo=PREFILL_FUSED, out=None, work
 
 def prefill_axis0(codes_t, scales, x, k, L=12, T=256, algo=PREFILL_EXPAND_GEMM, out=None, workspace=None):
     """out[m, c] = bf16(sum_r wb(r, c) x[m, r]) for a matrix stored transposed
-    (axis 0): codes_t [R_in, C_out*k/32], x bf16 [M, R_in]; expand + GEMM."""
+    (axis 0): codes_t [R_in, C_out*k/32], x bf16 [M, R_in]; expand + GEMM, or
+    the fused decode-to-LDS MFMA kernel (R_in a multiple of 128)."""
     _need(codes_t, "codes", _CODES, 2)
     _need(scales, "scales", (torch.float16,), 1)
     _need(x, "x", (torch.bfloat16,), 2)

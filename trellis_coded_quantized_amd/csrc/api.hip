@@ -432,7 +432,11 @@ int trellis_prefill(const uint32_t* codes, const uint16_t* scales, const uint16_
 size_t trellis_prefill_axis0_workspace_bytes(int64_t R_in, int64_t C_out, int64_t M, int k, int L, int T,
                                              int algo) {
   if (check_geometry("trellis_prefill_axis0_workspace_bytes", R_in, C_out, k, L, T) != TRELLIS_OK) return 0;
-  if (algo != TRELLIS_PREFILL_EXPAND_GEMM || M < 1) return 0;
+  if (M < 1) return 0;
+  if (algo == TRELLIS_PREFILL_FUSED)   // outputs C_out, contraction R_in
+    return trellis::prefill_fused_supported(C_out, R_in, M, k) ? trellis::prefill_fused_workspace_bytes(C_out, R_in, M)
+                                                                 : 0;
+  if (algo != TRELLIS_PREFILL_EXPAND_GEMM) return 0;
   return align_up((size_t)R_in * (size_t)C_out * 2, 256) + kGemmWorkspace;
 }
 
@@ -444,9 +448,14 @@ int trellis_prefill_axis0(const uint32_t* codes, const uint16_t* scales, const u
   TRY(check_m(fn, M, kMaxDim - 1));
   if (M * C_out >= kMaxElems || M * R_in >= kMaxElems)
     return fail(TRELLIS_EINVAL, "%s: M=%lld too large", fn, (long long)M);
-  if (algo == TRELLIS_PREFILL_FUSED)
-    return fail(TRELLIS_EUNSUPPORTED, "%s: no fused axis-0 prefill kernel; use TRELLIS_PREFILL_EXPAND_GEMM", fn);
-  if (algo != TRELLIS_PREFILL_EXPAND_GEMM) return fail(TRELLIS_EINVAL, "%s: algo=%d unknown", fn, algo);
+  if (M > (int64_t)65535 * 128) return fail(TRELLIS_EINVAL, "%s: M=%lld too large", fn, (long long)M);
+  if (algo != TRELLIS_PREFILL_FUSED && algo != TRELLIS_PREFILL_EXPAND_GEMM)
+    return fail(TRELLIS_EINVAL, "%s: algo=%d unknown", fn, algo);
+  if (algo == TRELLIS_PREFILL_FUSED && !trellis::prefill_fused_supported(C_out, R_in, M, k))
+    return fail(TRELLIS_EUNSUPPORTED,
+                "%s: fused kernel needs R_in a multiple of 128 and x and codes below 2 GiB (M=%lld R_in=%lld "
+                "C_out=%lld)",
+                fn, (long long)M, (long long)R_in, (long long)C_out);
   TRY(check_ptr(fn, "codes", codes, 16));
   TRY(check_ptr(fn, "scales", scales, 2));
   TRY(check_ptr(fn, "x", x, 16));
@@ -454,6 +463,8 @@ int trellis_prefill_axis0(const uint32_t* codes, const uint16_t* scales, const u
   TRY(check_workspace(fn, workspace, workspace_bytes,
                       trellis_prefill_axis0_workspace_bytes(R_in, C_out, M, k, L, T, algo)));
   hipStream_t s = (hipStream_t)stream;
+  if (algo == TRELLIS_PREFILL_FUSED)
+    return hip_status(fn, trellis::launch_prefill_fused(codes, scales, x, out, C_out, R_in, M, k, workspace, s, 1));
   uint16_t* wexp = reinterpret_cast<uint16_t*>(workspace);     // W^T expanded in stored orientation [R_in, C_out]
   const size_t wexp_bytes = align_up((size_t)R_in * (size_t)C_out * 2, 256);
   TRY(hip_status(fn, trellis::launch_expand(codes, scales, wexp, R_in, C_out, k, s)));

@@ -38,11 +38,14 @@ hipError_t launch_decode_states(const uint32_t* codes, int64_t R, int64_t C, int
 int device_cus();
 
 // fused prefill (32-bit buffer offsets: x and the codes each below 2 GiB);
-// the workspace holds the f32 partial tiles of the tiles split along K
+// the workspace holds x in operand order and the f32 partial tiles of the
+// tiles split along the contraction.  R is the output count, C the
+// contraction length: axis 1 codes [R, C k / 32]; axis0 != 0: codes
+// [C, R k / 32] (the stored transpose), scales [C].
 bool prefill_fused_supported(int64_t R, int64_t C, int64_t M, int k);
 size_t prefill_fused_workspace_bytes(int64_t R, int64_t C, int64_t M);
 hipError_t launch_prefill_fused(const uint32_t* codes, const uint16_t* scales, const uint16_t* x,
                                 uint16_t* out, int64_t R, int64_t C, int64_t M, int k,
-                                void* workspace, hipStream_t stream);
+                                void* workspace, hipStream_t stream, int axis0 = 0);
 
 }  // namespace trellis

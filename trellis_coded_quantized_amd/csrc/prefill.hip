@@ -39,6 +39,15 @@
 //     the matrix core has work while the new step's operands leave LDS.
 // Workgroups are mapped so that the 32 CUs of one XCD work on the same 512
 // rows of x at the same time, which keeps that slice of x in the XCD's L2.
+//
+// Axis 0 (a matrix stored transposed, codes W^T [R_in, C_out k / 32], the
+// down projection): the same kernel with the outputs C_out as the tile's
+// weight rows and the stored rows R_in as the contraction.  A step is 32
+// stored rows; each thread decodes 16 consecutive positions (output columns)
+// of one stored row, the same 16 positions of the same block in every step,
+// and writes them transposed into the weight tile (one 2-byte LDS write per
+// weight).  The tile's 8-element chunks are swizzled per group of 16 rows so
+// that those writes, and the 16-byte operand reads, spread over the banks.
 #include <type_traits>
 
 #include "internal.hpp"
@@ -154,7 +163,10 @@ struct XTile {
 constexpr int kSmallTileMaxM = 256;
 int tile_rows(int64_t M) { return M <= kSmallTileMaxM ? kBMSmall : kBMLarge; }
 
-template <int K, int BM>
+// R: outputs per row of x (weight rows of the tile, the row stride of out);
+// C: contraction length (columns of x).  Axis 1: codes [R, C k / 32].  Axis
+// 0 (A0): codes [C, R k / 32], scales [C].
+template <int K, int BM, bool A0>
 __global__ __launch_bounds__(256, XTile<BM>::kOcc) void prefill_fused_kernel(
     const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ xf, uint16_t* __restrict__ out, float* __restrict__ part, int R,
@@ -194,17 +206,36 @@ __global__ __launch_bounds__(256, XTile<BM>::kOcc) void prefill_fused_kernel(
   for (int i = 0; i < kFM; ++i)
     xvo[i] = (uint32_t)min(m_wave / 32 + i, nblk - 1) * (uint32_t)(nsteps * 2 * kFrag) + (uint32_t)lane * 16u;
 
-  // Decode assignment: weight row n0 + dr (clamped), positions 16 dh .. + 15
-  // of every step; dh is uniform over a wave.
+  // Decode assignment.  Axis 1: weight row n0 + dr (clamped), positions
+  // 16 dh .. + 15 of every step; dh is uniform over a wave.  Axis 0: stored
+  // row 32 t + sr in step t, positions q0 .. q0 + 15 of block n0 / 256 (the
+  // tile's columns 16 pg .. + 15) in every step.
   const int dr = lane + 64 * (wave >> 1), dh = wave & 1;
+  const int sr = tid >> 3, pg = tid & 7;
   const int grow = min(n0 + dr, R - 1);
-  const int row_bytes = (C / kT) * WPB * 4;
+  const int row_bytes = ((A0 ? R : C) / kT) * WPB * 4;
   const __amdgpu_buffer_rsrc_t cr =
-      __builtin_amdgcn_make_buffer_rsrc((void*)codes, (short)0, R * row_bytes, kRsrcWord3);
+      __builtin_amdgcn_make_buffer_rsrc((void*)codes, (short)0, (A0 ? C : R) * row_bytes, kRsrcWord3);
   const int cvo = grow * row_bytes;
-  const float sc = half_bits_to_f32(scales[grow]);
+  float sc = 0.f;
+  if constexpr (!A0) sc = half_bits_to_f32(scales[grow]);
   const uint32_t mul = kMul;
   const uint64_t add64 = kAdd;
+  // axis 0: the run's word offsets in its stored row (words wrap within the
+  // block) and whether it starts 16 bits into a word; fixed for the piece
+  uint32_t avo[NL];
+  bool a0_shift = false;
+  if constexpr (A0) {
+    const int q0 = (n0 & (kT - 1)) + 16 * pg;
+    const int rb = (kT - 16 - q0) * K;
+    a0_shift = (rb & 31) != 0;
+    const int w0 = rb >> 5;
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      const int wj = (w0 + j >= WPB) ? w0 + j - WPB : w0 + j;
+      avo[j] = (uint32_t)(sr * row_bytes + (n0 / kT) * WPB * 4 + wj * 4);
+    }
+  }
 
   f32x16 acc[kFM][kFN];
 #pragma unroll
@@ -215,6 +246,7 @@ __global__ __launch_bounds__(256, XTile<BM>::kOcc) void prefill_fused_kernel(
   // x operand ring: xh[h][slot][i] holds half h of the step with parity slot
   u32x4 xh[2][2][kFM];
   uint32_t cw[4][NL];       // code words of steps t + 1 .. t + 3
+  uint32_t scw[4] = {0u, 0u, 0u, 0u};   // axis 0: fp16 scale bits of those steps' stored rows
 
   // Loads past the end re-read the last step (in bounds, unused), so the
   // loop body has no branches.
@@ -226,39 +258,60 @@ __global__ __launch_bounds__(256, XTile<BM>::kOcc) void prefill_fused_kernel(
   // Run of step t: block t / 8, first position q0 = 32 (t % 8) + 16 dh,
   // lowest window bit (240 - q0) K; words wrap within the block.
   auto run_bits = [&](int t) { return (kT - 16 - (kBK * (t & 7) + 16 * dh)) * K; };
-  auto load_w = [&](uint32_t (&dst)[NL], int t) {
+  auto load_w = [&](uint32_t (&dst)[NL], uint32_t& sdst, int t) {
     t = min(t, nsteps - 1);
-    const int w0 = run_bits(t) >> 5;
-    const int base = (t >> 3) * WPB * 4;
+    if constexpr (A0) {
+      const int so = t * kBK * row_bytes;        // stored row 32 t
 #pragma unroll
-    for (int j = 0; j < NL; ++j) {
-      const int wj = (w0 + j >= WPB) ? w0 + j - WPB : w0 + j;
-      dst[j] = __builtin_amdgcn_raw_buffer_load_b32(cr, cvo, base + wj * 4, 0);
+      for (int j = 0; j < NL; ++j) dst[j] = __builtin_amdgcn_raw_buffer_load_b32(cr, (int)avo[j], so, 0);
+      sdst = scales[t * kBK + sr];
+    } else {
+      const int w0 = run_bits(t) >> 5;
+      const int base = (t >> 3) * WPB * 4;
+#pragma unroll
+      for (int j = 0; j < NL; ++j) {
+        const int wj = (w0 + j >= WPB) ? w0 + j - WPB : w0 + j;
+        dst[j] = __builtin_amdgcn_raw_buffer_load_b32(cr, cvo, base + wj * 4, 0);
+      }
     }
   };
   // Half H of the weights of step t (16 bytes per thread) into an LDS
   // buffer (past the last step: a buffer nobody reads again).
-  auto decode_half = [&](const uint32_t (&w)[NL], int t, uint32_t (&pk)[4], auto half) {
-    decode_run8<K, decltype(half)::value>(w, (run_bits(t) & 31) != 0, sc, mul, add64, pk);
+  auto decode_half = [&](const uint32_t (&w)[NL], uint32_t sbits, int t, uint32_t (&pk)[4], auto half) {
+    if constexpr (A0)
+      decode_run8<K, decltype(half)::value>(w, a0_shift, half_bits_to_f32((uint16_t)sbits), mul, add64, pk);
+    else
+      decode_run8<K, decltype(half)::value>(w, (run_bits(t) & 31) != 0, sc, mul, add64, pk);
   };
+  // Axis 0: weight (tile row c, contraction index s) sits in 8-element chunk
+  // (s / 8) ^ ((c / 16) % 4) of LDS row c; here c = 16 pg + 8 half + e.
   auto store_half = [&](const uint32_t (&pk)[4], uint16_t* buf, int half) {
-    *reinterpret_cast<u32x4*>(&buf[dr * kRow + 16 * dh + 8 * half]) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+    if constexpr (A0) {
+      uint16_t* p = buf + (16 * pg + 8 * half) * kRow + 8 * ((sr >> 3) ^ (pg & 3)) + (sr & 7);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        p[(2 * e) * kRow] = (uint16_t)pk[e];
+        p[(2 * e + 1) * kRow] = (uint16_t)(pk[e] >> 16);
+      }
+    } else {
+      *reinterpret_cast<u32x4*>(&buf[dr * kRow + 16 * dh + 8 * half]) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+    }
   };
   using H0 = std::integral_constant<int, 0>;
   using H1 = std::integral_constant<int, 1>;
 
   // prologue (t_begin is a multiple of 4): words of the first three steps,
   // x of the first step, weights of the first step
-  load_w(cw[0], t_begin);
-  load_w(cw[1], t_begin + 1);
-  load_w(cw[2], t_begin + 2);
+  load_w(cw[0], scw[0], t_begin);
+  load_w(cw[1], scw[1], t_begin + 1);
+  load_w(cw[2], scw[2], t_begin + 2);
   load_x(t_begin, 0, xh[0][0]);
   load_x(t_begin, 1, xh[1][0]);
   {
     uint32_t pk[4];
-    decode_half(cw[0], t_begin, pk, H0{});
+    decode_half(cw[0], scw[0], t_begin, pk, H0{});
     store_half(pk, Bs0, 0);
-    decode_half(cw[0], t_begin, pk, H1{});
+    decode_half(cw[0], scw[0], t_begin, pk, H1{});
     store_half(pk, Bs0, 1);
   }
   __syncthreads();
@@ -267,9 +320,17 @@ __global__ __launch_bounds__(256, XTile<BM>::kOcc) void prefill_fused_kernel(
   // columns 16 (l / 32) + 8 h .. + 7 (the columns of the x fragments; any
   // assignment shared by both operands is a valid split of the contraction)
   const int bofs = (lane & 31) * kRow + 16 * (lane >> 5);
+  // axis 0: logical chunk 2 (l / 32) + h of row 32 j + l % 32 is physical
+  // chunk (2 (l / 32) + (l / 16) % 2) ^ (h + 2 (j % 2)); one offset per mask
+  int bsw[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) bsw[q] = (lane & 31) * kRow + 8 * ((2 * (lane >> 5) + ((lane >> 4) & 1)) ^ q);
   auto read_b = [&](int h, const uint16_t* bbuf, bf16x8 (&b)[kFN]) {
 #pragma unroll
-    for (int j = 0; j < kFN; ++j) b[j] = *reinterpret_cast<const bf16x8*>(bbuf + bofs + 32 * j * kRow + 8 * h);
+    for (int j = 0; j < kFN; ++j) {
+      const int off = A0 ? bsw[h + 2 * (j & 1)] : bofs + 8 * h;
+      b[j] = *reinterpret_cast<const bf16x8*>(bbuf + off + 32 * j * kRow);
+    }
   };
   auto mfma_half = [&](const bf16x8 (&b)[kFN], const u32x4 (&a)[kFM]) {
 #pragma unroll
@@ -306,12 +367,12 @@ __global__ __launch_bounds__(256, XTile<BM>::kOcc) void prefill_fused_kernel(
       // first region: loads (words of step t + 3, x of step t + 1 half 0),
       // weights of step t (half 0), MFMAs of step t - 1 (half 1), decode of
       // step t + 1 (half 0)
-      load_w(cw[(u + 3) & 3], t + 3);
+      load_w(cw[(u + 3) & 3], scw[(u + 3) & 3], t + 3);
       load_x(t + 1, 0, xh[0][sl ^ 1]);
       read_b(0, bcur, bc);
       mfma_half(bp, xh[1][sl ^ 1]);
-      decode_half(cw[(u + 1) & 3], t + 1, pk0, H0{});
-      __builtin_amdgcn_sched_group_barrier(0x020, kFM + NL, 0);                   // VMEM reads
+      decode_half(cw[(u + 1) & 3], scw[(u + 1) & 3], t + 1, pk0, H0{});
+      __builtin_amdgcn_sched_group_barrier(0x020, kFM + NL + (A0 ? 1 : 0), 0);    // VMEM reads
       __builtin_amdgcn_sched_group_barrier(0x100, kFN, 0);                        // DS reads
 #pragma unroll
       for (int g = 0; g < kFM * kFN; ++g) {
@@ -326,7 +387,7 @@ __global__ __launch_bounds__(256, XTile<BM>::kOcc) void prefill_fused_kernel(
       load_x(t + 1, 1, xh[1][sl ^ 1]);
       read_b(1, bcur, bp);
       mfma_half(bc, xh[0][sl]);
-      decode_half(cw[(u + 1) & 3], t + 1, pk1, H1{});
+      decode_half(cw[(u + 1) & 3], scw[(u + 1) & 3], t + 1, pk1, H1{});
       store_half(pk0, bnext, 0);
       store_half(pk1, bnext, 1);
       __builtin_amdgcn_sched_group_barrier(0x020, kFM, 0);                        // VMEM reads
@@ -336,7 +397,7 @@ __global__ __launch_bounds__(256, XTile<BM>::kOcc) void prefill_fused_kernel(
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                         // MFMA
         __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);                         // VALU
       }
-      __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);                          // DS writes
+      __builtin_amdgcn_sched_group_barrier(0x200, A0 ? 16 : 2, 0);                // DS writes
       __syncthreads();
       // MFMAs touch no memory, so without a fence the scheduler would move
       // them across the barrier.
@@ -558,7 +619,7 @@ size_t prefill_fused_workspace_bytes(int64_t R, int64_t C, int64_t M) {
 
 hipError_t launch_prefill_fused(const uint32_t* codes, const uint16_t* scales, const uint16_t* x,
                                 uint16_t* out, int64_t R, int64_t C, int64_t M, int k,
-                                void* workspace, hipStream_t stream) {
+                                void* workspace, hipStream_t stream, int axis0) {
   const PrefillPlan p = make_plan(R, C, M);
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
   uint16_t* xf = reinterpret_cast<uint16_t*>(ws);
@@ -571,16 +632,22 @@ hipError_t launch_prefill_fused(const uint32_t* codes, const uint16_t* scales, c
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)(p.stream ? p.G : kXcds * p.per + p.nsplit * p.S)), block(256);
   const bool small = tile_rows(M) == kBMSmall;
-#define TRELLIS_PREFILL_LAUNCH(KK, BMM)                                                                   \
-  hipLaunchKernelGGL((prefill_fused_kernel<KK, BMM>), grid, block, 0, stream, codes, scales, xf, out, part, r, \
-                     c, m, p)
-  switch (k * 2 + (small ? 1 : 0)) {
-    case 4: TRELLIS_PREFILL_LAUNCH(2, kBMLarge); break;
-    case 5: TRELLIS_PREFILL_LAUNCH(2, kBMSmall); break;
-    case 6: TRELLIS_PREFILL_LAUNCH(3, kBMLarge); break;
-    case 7: TRELLIS_PREFILL_LAUNCH(3, kBMSmall); break;
-    case 8: TRELLIS_PREFILL_LAUNCH(4, kBMLarge); break;
-    case 9: TRELLIS_PREFILL_LAUNCH(4, kBMSmall); break;
+#define TRELLIS_PREFILL_LAUNCH(KK, BMM, AX0)                                                              \
+  hipLaunchKernelGGL((prefill_fused_kernel<KK, BMM, AX0>), grid, block, 0, stream, codes, scales, xf, out, part, \
+                     r, c, m, p)
+  switch ((k * 2 + (small ? 1 : 0)) * 2 + (axis0 ? 1 : 0)) {
+    case 8: TRELLIS_PREFILL_LAUNCH(2, kBMLarge, false); break;
+    case 9: TRELLIS_PREFILL_LAUNCH(2, kBMLarge, true); break;
+    case 10: TRELLIS_PREFILL_LAUNCH(2, kBMSmall, false); break;
+    case 11: TRELLIS_PREFILL_LAUNCH(2, kBMSmall, true); break;
+    case 12: TRELLIS_PREFILL_LAUNCH(3, kBMLarge, false); break;
+    case 13: TRELLIS_PREFILL_LAUNCH(3, kBMLarge, true); break;
+    case 14: TRELLIS_PREFILL_LAUNCH(3, kBMSmall, false); break;
+    case 15: TRELLIS_PREFILL_LAUNCH(3, kBMSmall, true); break;
+    case 16: TRELLIS_PREFILL_LAUNCH(4, kBMLarge, false); break;
+    case 17: TRELLIS_PREFILL_LAUNCH(4, kBMLarge, true); break;
+    case 18: TRELLIS_PREFILL_LAUNCH(4, kBMSmall, false); break;
+    case 19: TRELLIS_PREFILL_LAUNCH(4, kBMSmall, true); break;
     default: return hipErrorInvalidValue;
   }
 #undef TRELLIS_PREFILL_LAUNCH
