@@ -399,6 +399,8 @@ class PrefillAxis0(Workload):
         self.name = f"prefill_axis0_{m.R}x{m.C}_k{m.k}_m{M}"
         self.kernel = ("prefill_xlayout_kernel + prefill_fused_kernel (+ prefill_fold_kernel for split tiles), one step"
                        if self.graph else "expand_kernel + hipBLASLt GEMM (per call)")
+        self.profile = "prefill_axis0_fused_17408x5120_k3_m2048.md" if (self.graph and M == 2048) else None
+        self.profile_sources = PREFILL_SOURCES
         self.config = {"workload": self.name, "M": M, "R_in": m.R, "C_out": m.C, "k": m.k, "L": L, "T": T,
                        "algo": args.algo}
 

@@ -52,6 +52,10 @@ extern "C" {
 /* prefill algorithms */
 #define TRELLIS_PREFILL_FUSED 0        /* decode into LDS tiles feeding bf16 MFMA */
 #define TRELLIS_PREFILL_EXPAND_GEMM 1  /* trellis_expand_bf16 into the workspace, then a GEMM */
+/* FUSED where it measured at least as fast on MI355X (axis 1: M <= 128;
+ * axis 0: M <= 512) and the shape allows it, else EXPAND_GEMM; the workspace
+ * size query answers for the algorithm chosen, with the same arguments. */
+#define TRELLIS_PREFILL_AUTO 2
 
 /* Largest M accepted by the packed matvecs (the pages' matvec/prefill
  * crossover, trellis-linear.ts MATVEC_MAX_M). */
@@ -173,7 +177,8 @@ int trellis_expand_bf16_il(const uint32_t* codes, const uint16_t* scales, uint16
  * Source: trellis-tiled-prefill.ts (page 56) and the expand-then-matmul
  * fallback of TrellisLinear.forward (page 55).
  *   codes uint32 [R, C*k/32];  scales fp16 [R];  x bf16 [M, C];  out bf16 [M, R]
- *   M >= 1;  algo = TRELLIS_PREFILL_FUSED or TRELLIS_PREFILL_EXPAND_GEMM.
+ *   M >= 1;  algo = TRELLIS_PREFILL_FUSED, TRELLIS_PREFILL_EXPAND_GEMM or
+ *   TRELLIS_PREFILL_AUTO.
  * The EXPAND_GEMM workspace holds the bf16 [R, C] expansion.  The FUSED
  * workspace holds x rewritten in the MFMA operand order (ceil(M/32)*32*C*2
  * bytes), then f32 partial tiles when the last round of 512 x 128 output
@@ -211,6 +216,7 @@ int trellis_prefill(const uint32_t* codes, const uint16_t* scales, const uint16_
  *     multiple of 128 (else TRELLIS_EUNSUPPORTED; the workspace size query
  *     then returns 0).  Workspace: x in operand order, then f32 partial
  *     tiles, as for trellis_prefill.
+ *   TRELLIS_PREFILL_AUTO: one of the two (see its definition).
  */
 size_t trellis_prefill_axis0_workspace_bytes(int64_t R_in, int64_t C_out, int64_t M, int k, int L, int T,
                                              int algo);

@@ -189,3 +189,17 @@ def test_interleaved_layout_rejects(k, C, status, needle):
     assert needle in lib.trellis_last_error().decode()
     assert lib.trellis_expand_bf16_il(FAKE, FAKE, FAKE, 1024, C, k, 12, 256, None) == status
     assert needle in lib.trellis_last_error().decode()
+
+
+def test_prefill_auto_workspace_follows_the_chosen_algo():
+    lib = tq.load_library()
+    F, E, A = tq.PREFILL_FUSED, tq.PREFILL_EXPAND_GEMM, tq.PREFILL_AUTO
+    ws = lib.trellis_prefill_workspace_bytes
+    for M, algo in ((32, F), (128, F), (129, E), (2048, E)):
+        assert ws(1024, 2048, M, 2, 12, 256, A) == ws(1024, 2048, M, 2, 12, 256, algo), M
+    assert ws(1024, 2048, 32, 2, 12, 256, F) != ws(1024, 2048, 32, 2, 12, 256, E)
+    ws0 = lib.trellis_prefill_axis0_workspace_bytes
+    for R_in, M, algo in ((6144, 64, F), (6144, 512, F), (6144, 513, E), (6144, 2048, E), (6100, 64, E)):
+        assert ws0(R_in, 5120, M, 3, 12, 256, A) == ws0(R_in, 5120, M, 3, 12, 256, algo), (R_in, M)
+    assert ws(1024, 2048, 32, 2, 12, 256, 3) == 0
+

@@ -326,6 +326,21 @@ def test_prefill_axis0_fused_stream_pieces(k, C, M):
     tol.assert_bf16_close(sub, want, f"fused prefill axis0 stream C={C} M={M}")
 
 
+@pytest.mark.parametrize("axis0,R,C,M,chosen", [
+    (False, 512, 1024, 40, tq.PREFILL_FUSED), (False, 512, 1024, 200, tq.PREFILL_EXPAND_GEMM),
+    (True, 384, 512, 40, tq.PREFILL_FUSED), (True, 300, 512, 40, tq.PREFILL_EXPAND_GEMM)])
+def test_prefill_auto_matches_the_chosen_algo(axis0, R, C, M, chosen):
+    # AUTO runs exactly one of the two algorithms: its output is bit-identical to that one's
+    rng = np.random.default_rng(R + C + M + 5)
+    k = 3
+    codes, scales = rand_matrix(rng, R, C, k)
+    x = d_bf16(ti.activations(rng, M, R if axis0 else C))
+    fn = tq.prefill_axis0 if axis0 else tq.prefill
+    want = h_u16(fn(d_codes(codes), d_half(scales), x, k, algo=chosen))   # picks the GEMM kernel first
+    auto = h_u16(fn(d_codes(codes), d_half(scales), x, k, algo=tq.PREFILL_AUTO))
+    np.testing.assert_array_equal(auto, want)
+
+
 @pytest.mark.parametrize("algo,M", [(tq.PREFILL_EXPAND_GEMM, 32), (tq.PREFILL_EXPAND_GEMM, 512),
                                     (tq.PREFILL_FUSED, 32), (tq.PREFILL_FUSED, 512), (tq.PREFILL_FUSED, 2048)])
 def test_prefill_axis0_down_17408x5120_k3(axis0_workload, algo, M):

@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libtrellis.so")
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
 OUT_BF16, OUT_F32 = 0, 1
-PREFILL_FUSED, PREFILL_EXPAND_GEMM = 0, 1
+PREFILL_FUSED, PREFILL_EXPAND_GEMM, PREFILL_AUTO = 0, 1, 2
 MATVEC_MAX_M = 4
 
 # every symbol include/trellis.h declares

@@ -391,11 +391,32 @@ int trellis_expand_bf16(const uint32_t* codes, const uint16_t* scales, uint16_t*
   return hip_status(fn, trellis::launch_expand(codes, scales, out, R, C, k, (hipStream_t)stream));
 }
 
+namespace {
+
+// TRELLIS_PREFILL_AUTO: the fused kernel up to the M where it measured at
+// least as fast as expansion + GEMM on 17408 x 5120, else expansion + GEMM.
+// Axis 1: one 128-row x tile, M <= 128 (at M = 256 the weights are decoded
+// twice and the GEMM is faster).  Axis 0: M <= 512 (the transposed GEMM is
+// slower there; from M = 768 it wins).  R_out: outputs, C_con: contraction.
+constexpr int64_t kAutoFusedMaxM = 128;
+constexpr int64_t kAutoFusedMaxMAxis0 = 512;
+
+int resolve_prefill_algo(int algo, int64_t R_out, int64_t C_con, int64_t M, int k, bool axis0) {
+  if (algo != TRELLIS_PREFILL_AUTO) return algo;
+  const int64_t max_m = axis0 ? kAutoFusedMaxMAxis0 : kAutoFusedMaxM;
+  return M <= max_m && trellis::prefill_fused_supported(R_out, C_con, M, k) ? TRELLIS_PREFILL_FUSED
+                                                                            : TRELLIS_PREFILL_EXPAND_GEMM;
+}
+
+}  // namespace
+
 size_t trellis_prefill_workspace_bytes(int64_t R, int64_t C, int64_t M, int k, int L, int T,
                                        int algo) {
   if (check_geometry("trellis_prefill_workspace_bytes", R, C, k, L, T) != TRELLIS_OK) return 0;
+  if (M < 1) return 0;
+  algo = resolve_prefill_algo(algo, R, C, M, k, false);
   if (algo == TRELLIS_PREFILL_EXPAND_GEMM) return align_up((size_t)R * (size_t)C * 2, 256) + kGemmWorkspace;
-  if (M < 1 || !trellis::prefill_fused_supported(R, C, M, k)) return 0;
+  if (algo != TRELLIS_PREFILL_FUSED || !trellis::prefill_fused_supported(R, C, M, k)) return 0;
   return trellis::prefill_fused_workspace_bytes(R, C, M);
 }
 
@@ -408,8 +429,9 @@ int trellis_prefill(const uint32_t* codes, const uint16_t* scales, const uint16_
   if (M * C >= kMaxElems || M * R >= kMaxElems)
     return fail(TRELLIS_EINVAL, "%s: M=%lld too large", fn, (long long)M);
   if (M > (int64_t)65535 * 128) return fail(TRELLIS_EINVAL, "%s: M=%lld too large", fn, (long long)M);
-  if (algo != TRELLIS_PREFILL_FUSED && algo != TRELLIS_PREFILL_EXPAND_GEMM)
+  if (algo != TRELLIS_PREFILL_FUSED && algo != TRELLIS_PREFILL_EXPAND_GEMM && algo != TRELLIS_PREFILL_AUTO)
     return fail(TRELLIS_EINVAL, "%s: algo=%d unknown", fn, algo);
+  algo = resolve_prefill_algo(algo, R, C, M, k, false);
   TRY(check_ptr(fn, "codes", codes, 16));
   TRY(check_ptr(fn, "scales", scales, 2));
   TRY(check_ptr(fn, "x", x, 16));
@@ -433,6 +455,7 @@ size_t trellis_prefill_axis0_workspace_bytes(int64_t R_in, int64_t C_out, int64_
                                              int algo) {
   if (check_geometry("trellis_prefill_axis0_workspace_bytes", R_in, C_out, k, L, T) != TRELLIS_OK) return 0;
   if (M < 1) return 0;
+  algo = resolve_prefill_algo(algo, C_out, R_in, M, k, true);
   if (algo == TRELLIS_PREFILL_FUSED)   // outputs C_out, contraction R_in
     return trellis::prefill_fused_supported(C_out, R_in, M, k) ? trellis::prefill_fused_workspace_bytes(C_out, R_in, M)
                                                                  : 0;
@@ -449,8 +472,9 @@ int trellis_prefill_axis0(const uint32_t* codes, const uint16_t* scales, const u
   if (M * C_out >= kMaxElems || M * R_in >= kMaxElems)
     return fail(TRELLIS_EINVAL, "%s: M=%lld too large", fn, (long long)M);
   if (M > (int64_t)65535 * 128) return fail(TRELLIS_EINVAL, "%s: M=%lld too large", fn, (long long)M);
-  if (algo != TRELLIS_PREFILL_FUSED && algo != TRELLIS_PREFILL_EXPAND_GEMM)
+  if (algo != TRELLIS_PREFILL_FUSED && algo != TRELLIS_PREFILL_EXPAND_GEMM && algo != TRELLIS_PREFILL_AUTO)
     return fail(TRELLIS_EINVAL, "%s: algo=%d unknown", fn, algo);
+  algo = resolve_prefill_algo(algo, C_out, R_in, M, k, true);
   if (algo == TRELLIS_PREFILL_FUSED && !trellis::prefill_fused_supported(C_out, R_in, M, k))
     return fail(TRELLIS_EUNSUPPORTED,
                 "%s: fused kernel needs R_in a multiple of 128 and x and codes below 2 GiB (M=%lld R_in=%lld "
