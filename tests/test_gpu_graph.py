@@ -101,3 +101,24 @@ def test_graph_prefill(algo):
     _check_replays(lambda: tq.prefill(dc, ds, dx, k, algo=algo, out=out, workspace=ws), out,
                    lambda: (ws.fill_(0x7F), tq.prefill(dc, ds, dx.flip(0).contiguous(), k, algo=algo, out=junk,
                                                         workspace=ws)))
+
+
+@pytest.mark.parametrize("R_in,C_out", [(384, 1024), (640, 38400)])
+def test_graph_prefill_axis0_fused(R_in, C_out):
+    # M = 40 (128-row x tiles, two workgroups per CU): 1024 outputs make 8 tiles, all split along
+    # the stored rows; 38400 make 300 tiles, dealt out stream-K (pieces folded)
+    rng = np.random.default_rng(75)
+    M, k = 40, 3
+    c, s = ti.codes(rng, R_in, C_out, k), ti.scales(rng, R_in)
+    x = ti.activations(rng, M, R_in)
+    dc, ds, dx = _d(c, torch.int32), _d(s, torch.float16), _d(x, torch.bfloat16)
+    lib = tq.load_library()
+    nbytes = lib.trellis_prefill_axis0_workspace_bytes(R_in, C_out, M, k, 12, 256, tq.PREFILL_FUSED)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=DEV)
+    out = torch.empty((M, C_out), dtype=torch.bfloat16, device=DEV)
+    junk = torch.empty((M, C_out), dtype=torch.bfloat16, device=DEV)
+    fused = tq.PREFILL_FUSED
+    _check_replays(lambda: tq.prefill_axis0(dc, ds, dx, k, algo=fused, out=out, workspace=ws), out,
+                   lambda: (ws.fill_(0x7F), tq.prefill_axis0(dc, ds, dx.flip(0).contiguous(), k, algo=fused,
+                                                             out=junk, workspace=ws)))
+
