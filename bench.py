@@ -462,10 +462,41 @@ def workload_axis0_il(args, np, torch, dev):
     return wl
 
 
+class LayerChainGrouped(Matvec):
+    """The decoder-layer set with its three axis-1 projections in one grouped
+    launch over one x (as q / k / v read the same hidden state), then the
+    axis-0 call: 2 calls, 3 kernels per step."""
+
+    def __init__(self, *a):
+        super().__init__(*a)
+        self.kernels_per_step = 2 * len(self.Ms)
+
+    def step(self, s):
+        for j, M in enumerate(self.Ms):
+            rep = self.reps[(s * len(self.Ms) + j) % self.nrep]
+            a1 = [i for i, m in enumerate(self.w.mats) if m.axis == 1]
+            self.tq.matvec_axis1_group([rep[i] for i in a1], [self.scs[i] for i in a1], self.xs[a1[0]][:M],
+                                       self.w.mats[a1[0]].k, outs=[self.outs[(i, M)] for i in a1])
+            for i, m in enumerate(self.w.mats):
+                if m.axis == 0:
+                    self.tq.matvec_axis0(rep[i], self.scs[i], self.xs[i][:M], m.k, out=self.outs[(i, M)],
+                                         workspace=self.wss[i])
+
+
 def workload_layer_chain(args, np, torch, dev):
     import trellis_inputs as ti
-    return Matvec(ti.layer_chain(), (4,), "4-launch chain (3 x axis1_kernel, axis0 scatter + fold)", None,
-                  AXIS1_SOURCES, args, np, torch, dev)
+    wl = LayerChainGrouped(ti.layer_chain(), (4,), "grouped axis1_kernel (3 projections, one launch), then axis0 "
+                           "scatter + fold", None, AXIS1_SOURCES, args, np, torch, dev)
+    wl.config["axis1"] = "one grouped launch over a shared x"
+    return wl
+
+
+def workload_layer_chain_calls(args, np, torch, dev):
+    import trellis_inputs as ti
+    wl = Matvec(ti.layer_chain(), (4,), "4-launch chain (3 x axis1_kernel, axis0 scatter + fold)", None,
+                AXIS1_SOURCES, args, np, torch, dev)
+    wl.name = wl.config["workload"] = "layer_chain_k4_m4_calls"
+    return wl
 
 
 def workload_axis1_m1(args, np, torch, dev):
@@ -475,7 +506,8 @@ def workload_axis1_m1(args, np, torch, dev):
 
 WORKLOADS = {"copy": Copy, "gateup": GateUp, "prefill": Prefill, "axis0": workload_axis0, "mlp": Mlp,
              "prefill_axis0": PrefillAxis0, "axis0_il": workload_axis0_il,
-             "layer_chain": workload_layer_chain, "axis1_m1": workload_axis1_m1}
+             "layer_chain": workload_layer_chain, "layer_chain_calls": workload_layer_chain_calls,
+             "axis1_m1": workload_axis1_m1}
 
 
 def main():

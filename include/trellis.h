@@ -61,6 +61,9 @@ extern "C" {
  * crossover, trellis-linear.ts MATVEC_MAX_M). */
 #define TRELLIS_MATVEC_MAX_M 4
 
+/* Most matrices in one trellis_matvec_axis1_group call. */
+#define TRELLIS_GROUP_MAX 4
+
 /*
  * trellis_matvec_axis1 -- y[m, r] = sum_c w(r, c) * x[m, c]   (axis = 1).
  * Source: trellis-linear.ts (page 55), REDUCE kernel comment and
@@ -77,6 +80,24 @@ size_t trellis_matvec_axis1_workspace_bytes(int64_t R, int64_t C, int M, int k, 
 int trellis_matvec_axis1(const uint32_t* codes, const uint16_t* scales, const uint16_t* x,
                          void* out, int out_dtype, int64_t R, int64_t C, int M, int k, int L,
                          int T, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * trellis_matvec_axis1_group -- trellis_matvec_axis1 for n matrices that
+ * share x, C and k (a layer's projections of one input), in one launch.
+ * Source: the REDUCE kernel of trellis-linear.ts (page 55), per matrix;
+ * running a projection set as one launch is this library's addition.
+ *   codes[j]  uint32 [R[j], C*k/32];  scales[j] fp16 [R[j]]
+ *   out[j]    [M, R[j]] in out_dtype;  x bf16 [M, C];  1 <= M <= 4
+ *   1 <= n <= TRELLIS_GROUP_MAX
+ * codes, scales, out and R are host arrays of n entries (read during the
+ * call; the buffers they point to are device memory).  Each out[j] equals
+ * what trellis_matvec_axis1 writes for matrix j, bit for bit.  The launch
+ * spans the 16-row groups of all n matrices, so small projections share the
+ * machine with the large ones instead of running alone.  No workspace.
+ */
+int trellis_matvec_axis1_group(const uint32_t* const* codes, const uint16_t* const* scales, void* const* out,
+                               const int64_t* R, int n, const uint16_t* x, int out_dtype, int64_t C, int M,
+                               int k, int L, int T, void* stream);
 
 /*
  * trellis_gateup_swiglu -- out[m, r] = bf16(silu(bf16 g) * bf16 u), where

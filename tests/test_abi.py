@@ -203,3 +203,22 @@ def test_prefill_auto_workspace_follows_the_chosen_algo():
         assert ws0(R_in, 5120, M, 3, 12, 256, A) == ws0(R_in, 5120, M, 3, 12, 256, algo), (R_in, M)
     assert ws(1024, 2048, 32, 2, 12, 256, 3) == 0
 
+
+def test_axis1_group_rejects_on_host():
+    lib = tq.load_library()
+    P = ctypes.c_void_p * 5
+    I = ctypes.c_int64 * 5
+    ptrs, sc, outs, Rs = P(*[FAKE.value] * 5), P(*[FAKE.value] * 5), P(*[FAKE.value] * 5), I(*[64] * 5)
+
+    def call(n=3, codes=ptrs, R=Rs, k=2, M=4, C=1024, x=FAKE):
+        return lib.trellis_matvec_axis1_group(codes, sc, outs, R, n, x, tq.OUT_BF16, C, M, k, 12, 256, None)
+    for kw, status, needle in (
+            (dict(n=0), tq.EINVAL, "n=0"), (dict(n=5), tq.EINVAL, "n=5"),
+            (dict(codes=None), tq.EINVAL, "NULL pointer array"), (dict(k=5), tq.EUNSUPPORTED, "k=5"),
+            (dict(M=5), tq.EINVAL, "M=5"), (dict(x=MIS), tq.EINVAL, "x not 16-byte aligned"),
+            (dict(R=I(64, 0, 64, 64, 64)), tq.EINVAL, "empty matrix"),
+            (dict(codes=P(FAKE.value, MIS.value, FAKE.value, FAKE.value, FAKE.value)), tq.EINVAL, "codes[j]"),
+            (dict(C=6144), tq.EUNSUPPORTED, "C=6144")):
+        st = call(**kw)
+        assert st == status and needle in lib.trellis_last_error().decode(), (kw, st, lib.trellis_last_error())
+

@@ -25,10 +25,11 @@ OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
 OUT_BF16, OUT_F32 = 0, 1
 PREFILL_FUSED, PREFILL_EXPAND_GEMM, PREFILL_AUTO = 0, 1, 2
 MATVEC_MAX_M = 4
+GROUP_MAX = 4
 
 # every symbol include/trellis.h declares
 EXPORTS = (
-    "trellis_matvec_axis1_workspace_bytes", "trellis_matvec_axis1",
+    "trellis_matvec_axis1_workspace_bytes", "trellis_matvec_axis1", "trellis_matvec_axis1_group",
     "trellis_gateup_swiglu_workspace_bytes", "trellis_gateup_swiglu",
     "trellis_matvec_axis0_workspace_bytes", "trellis_matvec_axis0",
     "trellis_mlp_decode_workspace_bytes", "trellis_mlp_decode",
@@ -61,6 +62,8 @@ def load_library():
         "trellis_matvec_axis1_workspace_bytes": (_sz, [_i64, _i64, _int, _int, _int, _int]),
         "trellis_matvec_axis1": (_int, [_vp, _vp, _vp, _vp, _int, _i64, _i64, _int, _int, _int, _int,
                                         _vp, _sz, _vp]),
+        "trellis_matvec_axis1_group": (_int, [_vp, _vp, _vp, _vp, _int, _vp, _int, _i64, _int, _int, _int, _int,
+                                              _vp]),
         "trellis_gateup_swiglu_workspace_bytes": (_sz, [_i64, _i64, _int, _int, _int, _int]),
         "trellis_gateup_swiglu": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _int,
                                          _int, _int, _int, _vp, _sz, _vp]),
@@ -170,6 +173,34 @@ def matvec_axis1(codes, scales, x, k, L=12, T=256, out_dtype=torch.bfloat16, out
     _check(lib.trellis_matvec_axis1(_ptr(codes), _ptr(scales), _ptr(x), _ptr(out), od, R, C, M, k, L,
                                     T, _ptr(ws), wsb, _stream(x.device)))
     return out
+
+
+def matvec_axis1_group(codes, scales, x, k, L=12, T=256, out_dtype=torch.bfloat16, outs=None):
+    """matvec_axis1 of every matrix in `codes` (same C and k, same x) in one launch;
+    returns the list of outputs [M, R_j]."""
+    n = len(codes)
+    if n != len(scales) or not 1 <= n <= GROUP_MAX:
+        raise ValueError(f"{n} code tensors, {len(scales)} scale tensors (1..{GROUP_MAX} matrices)")
+    _need(x, "x", (torch.bfloat16,), 2)
+    Rs = []
+    for c, s in zip(codes, scales):
+        _need(c, "codes", _CODES, 2)
+        _need(s, "scales", (torch.float16,), 1)
+        R, C = _geometry(c, k)
+        if x.shape[1] != C:
+            raise ValueError(f"x has {x.shape[1]} features, codes encode {C}")
+        Rs.append(R)
+    M = x.shape[0]
+    if outs is None:
+        outs = [torch.empty((M, R), dtype=out_dtype, device=x.device) for R in Rs]
+    od = OUT_F32 if outs[0].dtype == torch.float32 else OUT_BF16
+    if any(o.dtype != outs[0].dtype for o in outs):
+        raise ValueError("outputs of one grouped call share a dtype")
+    P = ctypes.c_void_p * n
+    _check(load_library().trellis_matvec_axis1_group(
+        P(*[c.data_ptr() for c in codes]), P(*[s.data_ptr() for s in scales]), P(*[o.data_ptr() for o in outs]),
+        (ctypes.c_int64 * n)(*Rs), n, _ptr(x), od, x.shape[1], M, k, L, T, _stream(x.device)))
+    return outs
 
 
 def gateup_swiglu(gcodes, gscales, ucodes, uscales, x, k, L=12, T=256, out=None,

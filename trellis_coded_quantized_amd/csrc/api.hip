@@ -245,6 +245,31 @@ int trellis_matvec_axis1(const uint32_t* codes, const uint16_t* scales, const ui
                                               M, k, workspace, (hipStream_t)stream));
 }
 
+int trellis_matvec_axis1_group(const uint32_t* const* codes, const uint16_t* const* scales, void* const* out,
+                               const int64_t* R, int n, const uint16_t* x, int out_dtype, int64_t C, int M,
+                               int k, int L, int T, void* stream) {
+  const char* fn = "trellis_matvec_axis1_group";
+  if (n < 1 || n > TRELLIS_GROUP_MAX)
+    return fail(TRELLIS_EINVAL, "%s: n=%d matrices, must be 1..%d", fn, n, TRELLIS_GROUP_MAX);
+  if (!codes || !scales || !out || !R) return fail(TRELLIS_EINVAL, "%s: NULL pointer array", fn);
+  TRY(check_m(fn, M, TRELLIS_MATVEC_MAX_M));
+  if (out_dtype != TRELLIS_OUT_BF16 && out_dtype != TRELLIS_OUT_F32)
+    return fail(TRELLIS_EINVAL, "%s: out_dtype=%d unknown", fn, out_dtype);
+  TRY(check_ptr(fn, "x", x, 16));
+  for (int j = 0; j < n; ++j) {
+    TRY(check_geometry(fn, R[j], C, k, L, T));
+    TRY(check_ptr(fn, "codes[j]", codes[j], 16));
+    TRY(check_ptr(fn, "scales[j]", scales[j], 2));
+    TRY(check_ptr(fn, "out[j]", out[j], 16));
+  }
+  TRY(check_axis1_shape(fn, R[0], C, M, k, false));
+  if (!trellis::axis1_group_supported(R, n, C, M, k))
+    return fail(TRELLIS_EUNSUPPORTED, "%s: %d matrices of C=%lld exceed the LDS staging limit", fn, n,
+                (long long)C);
+  return hip_status(fn, trellis::launch_axis1_group(codes, scales, out, R, n, x, out_dtype == TRELLIS_OUT_F32,
+                                                    C, M, k, (hipStream_t)stream));
+}
+
 size_t trellis_gateup_swiglu_workspace_bytes(int64_t R, int64_t C, int M, int k, int L, int T) {
   if (check_geometry("trellis_gateup_swiglu_workspace_bytes", R, C, k, L, T) != TRELLIS_OK) return 0;
   return trellis::axis1_workspace_bytes(R, C, M, k);

@@ -41,10 +41,20 @@ constexpr int kMaxSlots = 4;           // tile ring depth per wave
 constexpr int kMaxDma = 7;             // copies per wave per tile (C <= 5120, k <= 4: 16 rows x 25 granules)
 constexpr int kXPer = 5;               // x granules per lane of a wave's slice (M * C <= 4 * 5120)
 constexpr uint32_t kPartBytes = kWaves * 4 * 16 * 4;   // one row group's partial tiles: f32 [wave][n][16 rows]
+constexpr int kMaxGroup = 4;           // matrices of one grouped call
 
 // Geometry shared by the host (LDS sizing) and the kernel.
 struct Axis1Geom {
   int64_t R, C, nrg, row_bytes;
+  // Grouped call (plain axis 1 only): ngroup matrices of the same C and k
+  // over the same x.  Matrix j owns the launch's row groups [gend[j - 1],
+  // gend[j]) (gend[-1] = 0) and has gR[j] rows; matrix 0 is the kernel's
+  // codes0 / scales0 / out and R.  ngroup == 1 for every other call.
+  int ngroup;
+  int64_t gend[kMaxGroup], gR[kMaxGroup];
+  const uint32_t* gcodes[kMaxGroup];
+  const uint16_t* gscales[kMaxGroup];
+  void* gout[kMaxGroup];
   int M;
   int per;              // runs of 32 columns per wave (C / 256)
   int gsw;              // granules per tile row of a wave's window (its blocks + one pad granule)
@@ -183,6 +193,29 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
   uint8_t* ring = smem + (size_t)wave * NS * g.slot_bytes;                      // this wave's slots
   float* part = reinterpret_cast<float*>(smem + g.part_off);
 
+  // Grouped calls: the matrix gi of row group rg and its row group lrg in
+  // that matrix (compile-time indices only, so the table stays in SGPRs).
+  auto locate = [&](int64_t rg, int& gi, int64_t& lrg) {
+    gi = 0;
+    int64_t start = 0;
+    if constexpr (!GATEUP) {
+#pragma unroll
+      for (int j = 0; j + 1 < kMaxGroup; ++j)
+        if (j + 1 < g.ngroup && rg >= g.gend[j]) {
+          gi = j + 1;
+          start = g.gend[j];
+        }
+    }
+    lrg = rg - start;
+  };
+  auto pick = [&](auto p0, auto const (&tab)[kMaxGroup], int gi) {
+    auto p = p0;
+#pragma unroll
+    for (int j = 1; j < kMaxGroup; ++j)
+      if (gi == j) p = tab[j];
+    return p;
+  };
+
   // ---- this wave's slice: runs [rb, re) of 32 columns, held in packed
   // blocks [b0, b1]; a tile row of the wave's window is those blocks
   const int per = g.per;
@@ -205,9 +238,13 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
   const uint8_t* cb1 = reinterpret_cast<const uint8_t*>(GATEUP ? codes1 : codes0);
   const uint32_t row_bytes = (uint32_t)g.row_bytes;
   auto issue_tile = [&](int t) {
-    const int64_t rg = (int64_t)blockIdx.x + (int64_t)t * gridDim.x;
+    int gi;
+    int64_t rg;
+    locate((int64_t)blockIdx.x + (int64_t)t * gridDim.x, gi, rg);
+    const int64_t Rm = pick(R, g.gR, gi);
+    const uint8_t* cbm = GATEUP ? cb0 : reinterpret_cast<const uint8_t*>(pick(codes0, g.gcodes, gi));
     uint8_t* slot = ring + (size_t)(t % NS) * g.slot_bytes;
-    const bool full = rg * ROWS + ROWS <= R;   // ragged last row group: rows past R read row R - 1
+    const bool full = rg * ROWS + ROWS <= Rm;  // ragged last row group: rows past Rm read row Rm - 1
     const int64_t gbase = rg * ROWS * g.row_bytes;
 #pragma unroll
     for (int j = 0; j < kMaxDma; ++j) {
@@ -216,13 +253,13 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
         if (d >> 31) {
           const uint32_t r = (d >> 16) & 15u;
           const uint32_t rr = GATEUP ? (r & 7u) : r;
-          const uint8_t* base = (GATEUP && r >= 8u) ? cb1 : cb0;
+          const uint8_t* base = (GATEUP && r >= 8u) ? cb1 : cbm;
           const uint8_t* src;
           if (full) {
             src = base + gbase + (rr * row_bytes + (d & 0xFFFFu));
           } else {
             int64_t row = rg * ROWS + rr;
-            row = row < R ? row : R - 1;
+            row = row < Rm ? row : Rm - 1;
             src = base + row * g.row_bytes + (d & 0xFFFFu);
           }
           __builtin_amdgcn_global_load_lds(src, slot + (size_t)j * 1024, 16, 0, 0);
@@ -410,14 +447,18 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
   for (int idx = tid; idx < nmine * per_t; idx += kThreads) {
     const int t = idx / per_t, r = idx - t * per_t;
     const int m = r / ROWS, row = r - m * ROWS;
-    const int64_t orow = ((int64_t)blockIdx.x + (int64_t)t * gridDim.x) * ROWS + row;
-    if (orow >= R) continue;
-    const int64_t o = (int64_t)m * R + orow;
+    int gi;
+    int64_t lrg;
+    locate((int64_t)blockIdx.x + (int64_t)t * gridDim.x, gi, lrg);
+    const int64_t Rm = pick(R, g.gR, gi);
+    const int64_t orow = lrg * ROWS + row;
+    if (orow >= Rm) continue;
+    const int64_t o = (int64_t)m * Rm + orow;
     const float* pp = part + ((size_t)t * kWaves * 4 + m) * 16 + row;
     float d0 = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) d0 += pp[w * 64];
-    const float v0 = ldexpf(d0 * (half_bits_to_f32(scales0[orow]) * kRcp), 24);
+    const float v0 = ldexpf(d0 * (half_bits_to_f32(pick(scales0, g.gscales, gi)[orow]) * kRcp), 24);
     if constexpr (GATEUP) {
       float d1 = 0.f;
 #pragma unroll
@@ -431,8 +472,9 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
       const float silu = round_bf16(gT * sig);
       reinterpret_cast<uint16_t*>(out)[o] = f32_to_bf16_bits(silu * uT);
     } else {
-      if (out_f32) reinterpret_cast<float*>(out)[o] = v0;
-      else reinterpret_cast<uint16_t*>(out)[o] = f32_to_bf16_bits(v0);
+      void* om = pick(out, g.gout, gi);
+      if (out_f32) reinterpret_cast<float*>(om)[o] = v0;
+      else reinterpret_cast<uint16_t*>(om)[o] = f32_to_bf16_bits(v0);
     }
   }
 }
@@ -448,14 +490,21 @@ int axis1_ng(int64_t C) {
 }
 
 // Host geometry; returns false if the shape does not fit (LDS or registers).
-bool axis1_geom(int64_t R, int64_t C, int M, int k, bool gateup, int64_t grid, Axis1Geom& g) {
+// nrg_total: row groups of the launch (0: those of R; a grouped call passes
+// the sum over its matrices).
+bool axis1_geom(int64_t R, int64_t C, int M, int k, bool gateup, int64_t grid, Axis1Geom& g,
+                int64_t nrg_total = 0) {
   const int rows = gateup ? 8 : 16;
   if (M < 1 || M > 4 || C % 256 != 0 || axis1_ng(C) == 0) return false;
   const int blk = 256 * k / 8;                 // bytes per block
+  g = Axis1Geom{};
   g.R = R;
   g.C = C;
   g.M = M;
-  g.nrg = (R + rows - 1) / rows;
+  g.nrg = nrg_total > 0 ? nrg_total : (R + rows - 1) / rows;
+  g.ngroup = 1;
+  g.gend[0] = g.nrg;
+  g.gR[0] = R;
   g.row_bytes = C * k / 8;
   g.per = (int)(C / 256);
   int nb = 0;                                  // widest wave window in blocks
@@ -493,9 +542,9 @@ bool axis1_geom(int64_t R, int64_t C, int M, int k, bool gateup, int64_t grid, A
   return g.total <= kAxis1MaxLdsBytes;
 }
 
-int64_t axis1_grid(int64_t R, bool gateup) {
+int64_t axis1_grid(int64_t R, bool gateup, int64_t nrg_total = 0) {
   const int64_t rows = gateup ? 8 : 16;
-  const int64_t nrg = (R + rows - 1) / rows;
+  const int64_t nrg = nrg_total > 0 ? nrg_total : (R + rows - 1) / rows;
   const int64_t cus = device_cus();
   return nrg < cus ? nrg : cus;
 }
@@ -542,9 +591,61 @@ hipError_t axis1_main(const uint32_t* c0, const uint16_t* s0, const uint32_t* c1
   }
 }
 
+template <int K>
+hipError_t axis1_group_main(const uint32_t* const* codes, const uint16_t* const* scales, void* const* outs,
+                            const int64_t* R, int n, const uint16_t* x, int out_f32, int64_t C, int M,
+                            hipStream_t stream) {
+  int64_t nrg = 0;
+  for (int j = 0; j < n; ++j) nrg += (R[j] + 15) / 16;
+  const int64_t grid = axis1_grid(R[0], false, nrg);
+  Axis1Geom g;
+  if (!axis1_geom(R[0], C, M, K, false, grid, g, nrg)) return hipErrorInvalidValue;
+  g.ngroup = n;
+  int64_t end = 0;
+  for (int j = 0; j < n; ++j) {
+    end += (R[j] + 15) / 16;
+    g.gend[j] = end;
+    g.gR[j] = R[j];
+    g.gcodes[j] = codes[j];
+    g.gscales[j] = scales[j];
+    g.gout[j] = outs[j];
+  }
+  switch (axis1_ng(C)) {
+    case 2:
+      return axis1_launch_one<K, false, 2>(codes[0], scales[0], nullptr, nullptr, x, outs[0], out_f32, nullptr,
+                                           nullptr, g, grid, stream);
+    case 5:
+      return axis1_launch_one<K, false, 5>(codes[0], scales[0], nullptr, nullptr, x, outs[0], out_f32, nullptr,
+                                           nullptr, g, grid, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace
 
 size_t axis1_workspace_bytes(int64_t, int64_t, int, int) { return 0; }
+
+int axis1_max_group() { return kMaxGroup; }
+
+bool axis1_group_supported(const int64_t* R, int n, int64_t C, int M, int k) {
+  if (n < 1 || n > kMaxGroup) return false;
+  int64_t nrg = 0;
+  for (int j = 0; j < n; ++j) nrg += (R[j] + 15) / 16;
+  Axis1Geom g;
+  return axis1_geom(R[0], C, M, k, false, axis1_grid(R[0], false, nrg), g, nrg);
+}
+
+hipError_t launch_axis1_group(const uint32_t* const* codes, const uint16_t* const* scales, void* const* outs,
+                              const int64_t* R, int n, const uint16_t* x, int out_f32, int64_t C, int M, int k,
+                              hipStream_t stream) {
+  if (n < 1 || n > kMaxGroup) return hipErrorInvalidValue;
+  switch (k) {
+    case 2: return axis1_group_main<2>(codes, scales, outs, R, n, x, out_f32, C, M, stream);
+    case 3: return axis1_group_main<3>(codes, scales, outs, R, n, x, out_f32, C, M, stream);
+    case 4: return axis1_group_main<4>(codes, scales, outs, R, n, x, out_f32, C, M, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 bool axis1_supported(int64_t R, int64_t C, int M, int k, bool gateup) {
   Axis1Geom g;

@@ -14,6 +14,13 @@ namespace trellis {
 // whether a shape fits (LDS and register budget), checked on the host.
 constexpr size_t kAxis1MaxLdsBytes = 160 * 1024;
 bool axis1_supported(int64_t R, int64_t C, int M, int k, bool gateup);
+// grouped plain axis-1 call: n <= axis1_max_group() matrices of the same C
+// and k over the same x, one launch (the row groups of all of them)
+int axis1_max_group();
+bool axis1_group_supported(const int64_t* R, int n, int64_t C, int M, int k);
+hipError_t launch_axis1_group(const uint32_t* const* codes, const uint16_t* const* scales, void* const* outs,
+                              const int64_t* R, int n, const uint16_t* x, int out_f32, int64_t C, int M, int k,
+                              hipStream_t stream);
 size_t axis1_workspace_bytes(int64_t R, int64_t C, int M, int k);
 hipError_t launch_axis1(const uint32_t* codes0, const uint16_t* scales0, const uint32_t* codes1,
                         const uint16_t* scales1, const uint16_t* x, void* out, int out_f32,
