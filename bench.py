@@ -485,17 +485,16 @@ class LayerChainGrouped(Matvec):
 
 def workload_layer_chain(args, np, torch, dev):
     import trellis_inputs as ti
+    return Matvec(ti.layer_chain(), (4,), "4-launch chain (3 x axis1_kernel, axis0 scatter + fold)", None,
+                  AXIS1_SOURCES, args, np, torch, dev)
+
+
+def workload_layer_chain_grouped(args, np, torch, dev):
+    import trellis_inputs as ti
     wl = LayerChainGrouped(ti.layer_chain(), (4,), "grouped axis1_kernel (3 projections, one launch), then axis0 "
                            "scatter + fold", None, AXIS1_SOURCES, args, np, torch, dev)
+    wl.name = wl.config["workload"] = "layer_chain_k4_m4_grouped"
     wl.config["axis1"] = "one grouped launch over a shared x"
-    return wl
-
-
-def workload_layer_chain_calls(args, np, torch, dev):
-    import trellis_inputs as ti
-    wl = Matvec(ti.layer_chain(), (4,), "4-launch chain (3 x axis1_kernel, axis0 scatter + fold)", None,
-                AXIS1_SOURCES, args, np, torch, dev)
-    wl.name = wl.config["workload"] = "layer_chain_k4_m4_calls"
     return wl
 
 
@@ -506,7 +505,7 @@ def workload_axis1_m1(args, np, torch, dev):
 
 WORKLOADS = {"copy": Copy, "gateup": GateUp, "prefill": Prefill, "axis0": workload_axis0, "mlp": Mlp,
              "prefill_axis0": PrefillAxis0, "axis0_il": workload_axis0_il,
-             "layer_chain": workload_layer_chain, "layer_chain_calls": workload_layer_chain_calls,
+             "layer_chain": workload_layer_chain, "layer_chain_grouped": workload_layer_chain_grouped,
              "axis1_m1": workload_axis1_m1}
 
 
