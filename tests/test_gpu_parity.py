@@ -262,6 +262,30 @@ def test_prefill_fused_stream_pieces(k, R, M):
     tol.assert_bf16_close(sub, want, f"prefill stream pieces k={k}")
 
 
+@pytest.mark.parametrize("M", [128, 129, 256, 257])
+def test_prefill_fused_tile_size_boundaries(M):
+    # M = 256 is the last size on 128-row x tiles (2 row tiles), 257 the first on 512-row tiles
+    # (rows 257..511 of the tile padded); 128 / 129 straddle the one-tile case.  Every output.
+    R, C, k = 640, 1024, 2
+    rng = np.random.default_rng(400 + M)
+    codes, scales = rand_matrix(rng, R, C, k)
+    x = ti.activations(rng, M, C)
+    got = h_u16(tq.prefill(d_codes(codes), d_half(scales), d_bf16(x), k, algo=tq.PREFILL_FUSED))
+    want = oracle.prefill_sums(codes, scales, x, M, R, C, k, L, T, np.arange(M), np.arange(R))
+    tol.assert_bf16_close(got, want, f"fused prefill tile boundary M={M}")
+
+
+@pytest.mark.parametrize("M", [256, 257])
+def test_prefill_axis0_fused_tile_size_boundaries(M):
+    R_in, C_out, k = 512, 768, 4
+    rng = np.random.default_rng(410 + M)
+    codes, scales = rand_matrix(rng, R_in, C_out, k)
+    x = ti.activations(rng, M, R_in)
+    got = h_u16(tq.prefill_axis0(d_codes(codes), d_half(scales), d_bf16(x), k, algo=tq.PREFILL_FUSED))
+    want = oracle.prefill_axis0_sums(codes, scales, x, M, R_in, C_out, k, L, T, np.arange(M), np.arange(C_out))
+    tol.assert_bf16_close(got, want, f"fused prefill axis0 tile boundary M={M}")
+
+
 @pytest.fixture(scope="module")
 def prefill_workload():
     return ti.prefill()
