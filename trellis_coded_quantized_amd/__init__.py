@@ -152,7 +152,34 @@ def _workspace(nbytes, device, workspace):
         return None, 0
     if workspace is None:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    elif not (isinstance(workspace, torch.Tensor) and workspace.device.type == "cuda" and workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous device tensor")
     return workspace, workspace.numel() * workspace.element_size()
+
+
+def _rows(scales, n, name="scales"):
+    if scales.numel() != n:
+        raise ValueError(f"{name} has {scales.numel()} entries, the matrix has {n} stored rows")
+
+
+def _out(t, name, shape, dtypes, device):
+    """A caller's output buffer (exactly `shape`, contiguous, on the device), or a new one."""
+    if t is None:
+        return torch.empty(shape, dtype=dtypes[0], device=device)
+    _need(t, name, dtypes, len(shape))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+_F = (torch.bfloat16, torch.float32)
+
+
+def _odt(out_dtype):
+    """output dtypes a matvec accepts, the requested one first"""
+    if out_dtype not in _F:
+        raise ValueError(f"out_dtype {out_dtype} not in {_F}")
+    return (out_dtype,) + _F
 
 
 def matvec_axis1(codes, scales, x, k, L=12, T=256, out_dtype=torch.bfloat16, out=None,
@@ -162,11 +189,11 @@ def matvec_axis1(codes, scales, x, k, L=12, T=256, out_dtype=torch.bfloat16, out
     _need(scales, "scales", (torch.float16,), 1)
     _need(x, "x", (torch.bfloat16,), 2)
     R, C = _geometry(codes, k)
+    _rows(scales, R)
     M = x.shape[0]
     if x.shape[1] != C:
         raise ValueError(f"x has {x.shape[1]} features, codes encode {C}")
-    if out is None:
-        out = torch.empty((M, R), dtype=out_dtype, device=x.device)
+    out = _out(out, "out", (M, R), _odt(out_dtype), x.device)
     od = OUT_F32 if out.dtype == torch.float32 else OUT_BF16
     lib = load_library()
     ws, wsb = _workspace(lib.trellis_matvec_axis1_workspace_bytes(R, C, M, k, L, T), x.device, workspace)
@@ -187,12 +214,16 @@ def matvec_axis1_group(codes, scales, x, k, L=12, T=256, out_dtype=torch.bfloat1
         _need(c, "codes", _CODES, 2)
         _need(s, "scales", (torch.float16,), 1)
         R, C = _geometry(c, k)
+        _rows(s, R)
         if x.shape[1] != C:
             raise ValueError(f"x has {x.shape[1]} features, codes encode {C}")
         Rs.append(R)
     M = x.shape[0]
     if outs is None:
-        outs = [torch.empty((M, R), dtype=out_dtype, device=x.device) for R in Rs]
+        outs = [None] * n
+    if len(outs) != n:
+        raise ValueError(f"{len(outs)} outputs for {n} matrices")
+    outs = [_out(o, f"outs[{j}]", (M, R), _odt(out_dtype), x.device) for j, (o, R) in enumerate(zip(outs, Rs))]
     od = OUT_F32 if outs[0].dtype == torch.float32 else OUT_BF16
     if any(o.dtype != outs[0].dtype for o in outs):
         raise ValueError("outputs of one grouped call share a dtype")
@@ -214,11 +245,16 @@ def gateup_swiglu(gcodes, gscales, ucodes, uscales, x, k, L=12, T=256, out=None,
     if gcodes.shape != ucodes.shape:
         raise ValueError("gate and up codes differ in shape")
     R, C = _geometry(gcodes, k)
+    _rows(gscales, R, "gscales")
+    _rows(uscales, R, "uscales")
     M = x.shape[0]
     if x.shape[1] != C:
         raise ValueError(f"x has {x.shape[1]} features, codes encode {C}")
-    if out is None:
-        out = torch.empty((M, R), dtype=torch.bfloat16, device=x.device)
+    out = _out(out, "out", (M, R), (torch.bfloat16,), x.device)
+    if gate_f32 is not None:
+        _out(gate_f32, "gate_f32", (M, R), (torch.float32,), x.device)
+    if up_f32 is not None:
+        _out(up_f32, "up_f32", (M, R), (torch.float32,), x.device)
     lib = load_library()
     ws, wsb = _workspace(lib.trellis_gateup_swiglu_workspace_bytes(R, C, M, k, L, T), x.device,
                          workspace)
@@ -236,11 +272,11 @@ def matvec_axis0(codes_t, scales, x, k, L=12, T=256, out_dtype=torch.bfloat16, o
     _need(scales, "scales", (torch.float16,), 1)
     _need(x, "x", (torch.bfloat16,), 2)
     R, C, il = _axis0_geometry(codes_t, k)
+    _rows(scales, R)
     M = x.shape[0]
     if x.shape[1] != R:
         raise ValueError(f"x has {x.shape[1]} features, stored rows are {R}")
-    if out is None:
-        out = torch.empty((M, C), dtype=out_dtype, device=x.device)
+    out = _out(out, "out", (M, C), _odt(out_dtype), x.device)
     od = OUT_F32 if out.dtype == torch.float32 else OUT_BF16
     lib = load_library()
     ws, wsb = _workspace(lib.trellis_matvec_axis0_workspace_bytes(R, C, M, k, L, T), x.device,
@@ -271,10 +307,12 @@ def mlp_decode(gcodes, gscales, ucodes, uscales, dcodes_t, dscales, x, k_gu, k_d
     M = x.shape[0]
     if x.shape[1] != C:
         raise ValueError(f"x has {x.shape[1]} features, gate/up take {C}")
-    if out is None:
-        out = torch.empty((M, C_out), dtype=torch.bfloat16, device=x.device)
+    _rows(gscales, R, "gscales")
+    _rows(uscales, R, "uscales")
+    _rows(dscales, Rd, "dscales")
+    out = _out(out, "out", (M, C_out), (torch.bfloat16,), x.device)
     if hidden is not None:
-        _need(hidden, "hidden", (torch.bfloat16,), 2)
+        _out(hidden, "hidden", (M, R), (torch.bfloat16,), x.device)
     lib = load_library()
     ws, wsb = _workspace(lib.trellis_mlp_decode_workspace_bytes(R, C, C_out, M, k_gu, k_down, L, T), x.device,
                          workspace)
@@ -290,8 +328,8 @@ def expand_bf16(codes, scales, k, L=12, T=256, out=None):
     _need(codes, "codes", _CODES, codes.dim() if codes.dim() == 3 else 2)
     _need(scales, "scales", (torch.float16,), 1)
     R, C, il = _axis0_geometry(codes, k)
-    if out is None:
-        out = torch.empty((R, C), dtype=torch.bfloat16, device=codes.device)
+    _rows(scales, R)
+    out = _out(out, "out", (R, C), (torch.bfloat16,), codes.device)
     lib = load_library()
     fn = lib.trellis_expand_bf16_il if il else lib.trellis_expand_bf16
     _check(fn(_ptr(codes), _ptr(scales), _ptr(out), R, C, k, L, T, _stream(codes.device)))
@@ -304,11 +342,11 @@ def prefill(codes, scales, x, k, L=12, T=256, algo=PREFILL_FUSED, out=None, work
     _need(scales, "scales", (torch.float16,), 1)
     _need(x, "x", (torch.bfloat16,), 2)
     R, C = _geometry(codes, k)
+    _rows(scales, R)
     M = x.shape[0]
     if x.shape[1] != C:
         raise ValueError(f"x has {x.shape[1]} features, codes encode {C}")
-    if out is None:
-        out = torch.empty((M, R), dtype=torch.bfloat16, device=x.device)
+    out = _out(out, "out", (M, R), (torch.bfloat16,), x.device)
     lib = load_library()
     ws, wsb = _workspace(lib.trellis_prefill_workspace_bytes(R, C, M, k, L, T, algo), x.device,
                          workspace)
@@ -325,11 +363,11 @@ def prefill_axis0(codes_t, scales, x, k, L=12, T=256, algo=PREFILL_EXPAND_GEMM, 
     _need(scales, "scales", (torch.float16,), 1)
     _need(x, "x", (torch.bfloat16,), 2)
     R, C = _geometry(codes_t, k)
+    _rows(scales, R)
     M = x.shape[0]
     if x.shape[1] != R:
         raise ValueError(f"x has {x.shape[1]} features, stored rows are {R}")
-    if out is None:
-        out = torch.empty((M, C), dtype=torch.bfloat16, device=x.device)
+    out = _out(out, "out", (M, C), (torch.bfloat16,), x.device)
     lib = load_library()
     ws, wsb = _workspace(lib.trellis_prefill_axis0_workspace_bytes(R, C, M, k, L, T, algo), x.device, workspace)
     _check(lib.trellis_prefill_axis0(_ptr(codes_t), _ptr(scales), _ptr(x), _ptr(out), R, C, M, k, L, T, algo,
