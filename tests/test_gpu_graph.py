@@ -86,12 +86,13 @@ def test_graph_axis0():
                                                             workspace=ws)))
 
 
-@pytest.mark.parametrize("algo", [tq.PREFILL_FUSED, tq.PREFILL_EXPAND_GEMM])
-def test_graph_prefill(algo):
-    # 1000 x 1024 at M = 40: 8 fused tiles, all split along C (main kernel + fold);
-    # the expand + GEMM plan is tuned by the eager call before capture.
+@pytest.mark.parametrize("algo,M", [(tq.PREFILL_FUSED, 24), (tq.PREFILL_FUSED, 100), (tq.PREFILL_EXPAND_GEMM, 40)])
+def test_graph_prefill(algo, M):
+    # 1000 x 1024: at M = 24 the register-direct kernel (column chunks + fold); at M = 100 8 tiles
+    # of 128 x 128, all split along C (main kernel + fold); the expand + GEMM plan is tuned by the
+    # eager call before capture.
     rng = np.random.default_rng(74)
-    R, C, M, k = 1000, 1024, 40, 3
+    R, C, k = 1000, 1024, 3
     c, s = ti.codes(rng, R, C, k), ti.scales(rng, R)
     x = ti.activations(rng, M, C)
     dc, ds, dx = _d(c, torch.int32), _d(s, torch.float16), _d(x, torch.bfloat16)

@@ -244,9 +244,9 @@ def test_prefill_small(algo, k, R, C, M):
 
 
 @pytest.mark.parametrize("k", [2, 3])
-@pytest.mark.parametrize("R,M", [(25600, 300), (38400, 64)])
+@pytest.mark.parametrize("R,M", [(25600, 300), (38400, 100)])
 def test_prefill_fused_stream_pieces(k, R, M):
-    # M = 300: 200 tiles of 512 x 128 on a 256-CU part; M = 64: 300 tiles of 128 x 128 with two
+    # M = 300: 200 tiles of 512 x 128 on a 256-CU part; M = 100: 300 tiles of 128 x 128 with two
     # workgroups per CU.  Either way the leftover tiles fill more than half of the workgroup
     # slots, so the fused kernel deals the steps out in ranges that cross tile boundaries (whole
     # tiles stored directly, the pieces folded).  Sampled rows and x rows.
@@ -262,9 +262,24 @@ def test_prefill_fused_stream_pieces(k, R, M):
     tol.assert_bf16_close(sub, want, f"prefill stream pieces k={k}")
 
 
-@pytest.mark.parametrize("M", [128, 129, 256, 257])
+@pytest.mark.parametrize("k", [2, 3, 4])
+@pytest.mark.parametrize("R,C,M", [(1000, 1024, 1), (1000, 1024, 32), (777, 512, 9), (40, 256, 17),
+                                   (4096, 5120, 32)])
+def test_prefill_direct(k, R, C, M):
+    # M <= 32 runs the register-direct kernel: 32-row weight tiles (a ragged last one when
+    # R % 32 != 0), column chunks split over workgroups and waves, one x tile; every output
+    rng = np.random.default_rng(500 + R + C + M + k)
+    codes, scales = rand_matrix(rng, R, C, k)
+    x = ti.activations(rng, M, C)
+    got = h_u16(tq.prefill(d_codes(codes), d_half(scales), d_bf16(x), k, algo=tq.PREFILL_FUSED))
+    want = oracle.prefill_sums(codes, scales, x, M, R, C, k, L, T, np.arange(M), np.arange(R))
+    tol.assert_bf16_close(got, want, f"direct prefill R={R} C={C} M={M} k={k}")
+
+
+@pytest.mark.parametrize("M", [32, 33, 64, 128, 129, 256, 257])
 def test_prefill_fused_tile_size_boundaries(M):
-    # M = 256 is the last size on 128-row x tiles (2 row tiles), 257 the first on 512-row tiles
+    # M = 32 is the last size on the register-direct kernel, 33 the first on 128-row x tiles;
+    # M = 256 is the last size on 128-row tiles (2 row tiles), 257 the first on 512-row tiles
     # (rows 257..511 of the tile padded); 128 / 129 straddle the one-tile case.  Every output.
     R, C, k = 640, 1024, 2
     rng = np.random.default_rng(400 + M)

@@ -482,7 +482,7 @@ size_t trellis_prefill_axis0_workspace_bytes(int64_t R_in, int64_t C_out, int64_
   if (M < 1) return 0;
   algo = resolve_prefill_algo(algo, C_out, R_in, M, k, true);
   if (algo == TRELLIS_PREFILL_FUSED)   // outputs C_out, contraction R_in
-    return trellis::prefill_fused_supported(C_out, R_in, M, k) ? trellis::prefill_fused_workspace_bytes(C_out, R_in, M)
+    return trellis::prefill_fused_supported(C_out, R_in, M, k) ? trellis::prefill_fused_workspace_bytes(C_out, R_in, M, 1)
                                                                  : 0;
   if (algo != TRELLIS_PREFILL_EXPAND_GEMM) return 0;
   return align_up((size_t)R_in * (size_t)C_out * 2, 256) + kGemmWorkspace;

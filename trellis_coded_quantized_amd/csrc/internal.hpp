@@ -50,7 +50,7 @@ int device_cus();
 // contraction length: axis 1 codes [R, C k / 32]; axis0 != 0: codes
 // [C, R k / 32] (the stored transpose), scales [C].
 bool prefill_fused_supported(int64_t R, int64_t C, int64_t M, int k);
-size_t prefill_fused_workspace_bytes(int64_t R, int64_t C, int64_t M);
+size_t prefill_fused_workspace_bytes(int64_t R, int64_t C, int64_t M, int axis0 = 0);
 hipError_t launch_prefill_fused(const uint32_t* codes, const uint16_t* scales, const uint16_t* x,
                                 uint16_t* out, int64_t R, int64_t C, int64_t M, int k,
                                 void* workspace, hipStream_t stream, int axis0 = 0);

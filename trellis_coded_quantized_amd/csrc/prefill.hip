@@ -48,6 +48,7 @@
 // and writes them transposed into the weight tile (one 2-byte LDS write per
 // weight).  The tile's 8-element chunks are swizzled per group of 16 rows so
 // that those writes, and the 16-byte operand reads, spread over the banks.
+#include <algorithm>
 #include <type_traits>
 
 #include "internal.hpp"
@@ -564,6 +565,162 @@ __global__ __launch_bounds__(256) void prefill_fold_kernel(const float* __restri
   }
 }
 
+// ---- register-direct prefill for M <= 32 -----------------------------------
+//
+// With few rows of x the tile kernel above is bound by its decode, and its
+// per-step LDS round trip and barrier slow that decode down.  Here each lane
+// decodes exactly the weights of its own MFMA operand: for step t (32
+// columns) and half h, lane l holds weight row r0 + l % 32, positions
+// 16 (l / 32) + 8 h .. + 7 of the step -- the same split of the contraction
+// as the x fragments of prefill_xlayout_kernel -- so the 8 bf16 weights go
+// straight from the decode into v_mfma_f32_32x32x16_bf16, with no LDS and no
+// barrier in the loop.  A workgroup takes 32 weight rows and one of S chunks
+// of the columns; its 4 waves split the chunk, meet once in LDS at the end,
+// and store bf16 (S == 1) or an f32 partial [S][M][R] that
+// prefill_direct_fold_kernel adds up.  Waves are many and independent, so the
+// machine stays evenly loaded.  One 32-row x tile: from 33 rows on, the tile
+// kernel above is faster (its code words are shared through LDS; here every
+// lane loads its own row's words, and the address unit is the bound).
+constexpr int kDirectMaxM = 32;
+
+template <int K>
+__global__ __launch_bounds__(256) void prefill_direct_kernel(
+    const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scales,
+    const uint16_t* __restrict__ xf, uint16_t* __restrict__ out, float* __restrict__ part, int R, int C,
+    int M, int S) {
+  constexpr int WPB = words_per_block(K);
+  constexpr int NL = Run16<K>::kLoad;
+  constexpr int FM = 1;                                               // x tiles of 32 rows
+  __shared__ __attribute__((aligned(16))) float red[3][FM][16][64];   // waves 1..3's accumulators
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tile = (int)(blockIdx.x / (unsigned)S), s = (int)(blockIdx.x % (unsigned)S);
+  const int r0 = tile * 32;
+  const int nsteps = C / kBK;
+  const int cs = (int)((int64_t)s * nsteps / S), ce = (int)((int64_t)(s + 1) * nsteps / S);
+  const int t_begin = cs + (ce - cs) * wave / 4, t_end = cs + (ce - cs) * (wave + 1) / 4;
+
+  const int row = min(r0 + (lane & 31), R - 1);   // rows past R decode row R - 1 (never stored)
+  const int dh = lane >> 5;
+  const int row_bytes = (C / kT) * WPB * 4;
+  const __amdgpu_buffer_rsrc_t cr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)codes, (short)0, R * row_bytes, kRsrcWord3);
+  const int cvo = row * row_bytes;
+  const float sc = half_bits_to_f32(scales[row]);
+  const int nblk = (M + 31) / 32;
+  const __amdgpu_buffer_rsrc_t xr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)xf, (short)0, nblk * nsteps * 2 * kFrag, kRsrcWord3);
+  uint32_t xvo[FM];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) xvo[i] = (uint32_t)min(i, nblk - 1) * (uint32_t)(nsteps * 2 * kFrag) + lane * 16u;
+
+  // run of step t: block t / 8, first position 32 (t % 8) + 16 dh
+  auto run_bits = [&](int t) { return (kT - 16 - (kBK * (t & 7) + 16 * dh)) * K; };
+  auto load_w = [&](uint32_t (&dst)[NL], int t) {
+    t = min(t, nsteps - 1);
+    const int w0 = run_bits(t) >> 5;
+    const int base = (t >> 3) * WPB * 4;
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      const int wj = (w0 + j >= WPB) ? w0 + j - WPB : w0 + j;
+      dst[j] = __builtin_amdgcn_raw_buffer_load_b32(cr, cvo + wj * 4, base, 0);
+    }
+  };
+  auto load_x = [&](u32x4 (&dst)[2][FM], int t) {
+    t = min(t, nsteps - 1);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        dst[h][i] = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)xvo[i], (t * 2 + h) * kFrag, 0);
+  };
+
+  f32x16 acc[FM];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) acc[i] = f32x16{};
+  const uint32_t mul = kMul;
+  const uint64_t add64 = kAdd;
+  // two steps in flight: words and x of step t + 1 load while step t decodes
+  uint32_t cw[2][NL];
+  u32x4 xv[2][2][FM];
+  load_w(cw[0], t_begin);
+  load_x(xv[0], t_begin);
+  for (int t = t_begin; t < t_end; t += 2) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int tt = t + u;
+      load_w(cw[u ^ 1], tt + 1);
+      load_x(xv[u ^ 1], tt + 1);
+      if (tt < t_end) {
+        const bool sh = (run_bits(tt) & 31) != 0;
+        uint32_t pk[4];
+        decode_run8<K, 0>(cw[u], sh, sc, mul, add64, pk);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]}),
+                                                          __builtin_bit_cast(bf16x8, xv[u][0][i]), acc[i], 0, 0, 0);
+        decode_run8<K, 1>(cw[u], sh, sc, mul, add64, pk);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]}),
+                                                          __builtin_bit_cast(bf16x8, xv[u][1][i]), acc[i], 0, 0, 0);
+      }
+    }
+  }
+
+  // the four waves' sums, added in wave order by wave 0
+  if (wave > 0) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) red[wave - 1][i][e][lane] = acc[i][e];
+  }
+  __syncthreads();
+  if (wave > 0) return;
+#pragma unroll
+  for (int w = 0; w < 3; ++w)
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][e] += red[w][i][e][lane];
+  // D of tile i: lane holds x row 32 i + lane % 32 and weight rows
+  // r0 + 8 g + 4 (lane / 32) + e
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int m = 32 * i + (lane & 31);
+    if (m >= M) continue;
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int n = r0 + 8 * g + 4 * dh + e;
+        if (n >= R) continue;
+        const float v = acc[i][4 * g + e];
+        if (S == 1) out[(size_t)m * R + n] = f32_to_bf16_bits(v);
+        else part[((size_t)s * M + m) * R + n] = v;
+      }
+  }
+}
+
+// out[e] = bf16(sum over s of part[s][e]), e over M * R, in split order.
+__global__ __launch_bounds__(256) void prefill_direct_fold_kernel(const float* __restrict__ part,
+                                                                  uint16_t* __restrict__ out, int S,
+                                                                  int64_t n) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= n) return;
+  float v = part[e];
+  for (int s = 1; s < S; ++s) v += part[(size_t)s * n + e];
+  out[e] = f32_to_bf16_bits(v);
+}
+
+// Column chunks per 32-row tile: enough workgroups for ~8 waves per SIMD,
+// at least 4 steps per chunk (one per wave).
+int direct_splits(int64_t R, int64_t C) {
+  const int64_t tiles = (R + 31) / 32, nsteps = C / kBK;
+  const int64_t want = ((int64_t)device_cus() * 4 * 8 + tiles * 4 - 1) / (tiles * 4);
+  return (int)std::max<int64_t>(1, std::min<int64_t>(want, nsteps / 4));
+}
+
 PrefillPlan make_plan(int64_t R, int64_t C, int64_t M) {
   PrefillPlan p{};
   const int bm = tile_rows(M);
@@ -609,7 +766,13 @@ bool prefill_fused_supported(int64_t R, int64_t C, int64_t M, int k) {
 }
 
 // workspace: x in operand order, then the f32 partial tiles of split tiles
-size_t prefill_fused_workspace_bytes(int64_t R, int64_t C, int64_t M) {
+// (register-direct path: the f32 partials [S][M][R] of its column chunks)
+size_t prefill_fused_workspace_bytes(int64_t R, int64_t C, int64_t M, int axis0) {
+  const size_t xfb0 = ((size_t)prefill_xf_bytes(C, M) + 255) / 256 * 256;
+  if (!axis0 && M <= kDirectMaxM) {
+    const int S = direct_splits(R, C);
+    return xfb0 + (S > 1 ? (size_t)S * M * R * sizeof(float) : 0);
+  }
   const PrefillPlan p = make_plan(R, C, M);
   const size_t slots = p.stream ? 2 * (size_t)p.G : (size_t)p.nsplit * (size_t)p.S;
   const size_t xfb = ((size_t)prefill_xf_bytes(C, M) + 255) / 256 * 256;
@@ -630,6 +793,22 @@ hipError_t launch_prefill_fused(const uint32_t* codes, const uint16_t* scales, c
                      reinterpret_cast<uint4*>(xf), m, c, nunits);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (!axis0 && M <= kDirectMaxM) {
+    const int S = direct_splits(R, C);
+    const dim3 dgrid((unsigned)(((R + 31) / 32) * S));
+    switch (k) {
+      case 2: hipLaunchKernelGGL(prefill_direct_kernel<2>, dgrid, dim3(256), 0, stream, codes, scales, xf, out, part, r, c, m, S); break;
+      case 3: hipLaunchKernelGGL(prefill_direct_kernel<3>, dgrid, dim3(256), 0, stream, codes, scales, xf, out, part, r, c, m, S); break;
+      case 4: hipLaunchKernelGGL(prefill_direct_kernel<4>, dgrid, dim3(256), 0, stream, codes, scales, xf, out, part, r, c, m, S); break;
+      default: return hipErrorInvalidValue;
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess || S == 1) return e;
+    const int64_t n = M * R;
+    hipLaunchKernelGGL(prefill_direct_fold_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, part,
+                       out, S, n);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)(p.stream ? p.G : kXcds * p.per + p.nsplit * p.S)), block(256);
   const bool small = tile_rows(M) == kBMSmall;
 #define TRELLIS_PREFILL_LAUNCH(KK, BMM, AX0)                                                              \
