@@ -713,11 +713,12 @@ __global__ __launch_bounds__(256) void prefill_direct_fold_kernel(const float* _
   out[e] = f32_to_bf16_bits(v);
 }
 
-// Column chunks per 32-row tile: enough workgroups for ~8 waves per SIMD,
-// at least 4 steps per chunk (one per wave).
+// Column chunks per 32-row tile: enough workgroups for ~4 waves per SIMD
+// (fewer, longer waves ran faster than ~8 per SIMD), at least 4 steps per
+// chunk (one per wave).
 int direct_splits(int64_t R, int64_t C) {
   const int64_t tiles = (R + 31) / 32, nsteps = C / kBK;
-  const int64_t want = ((int64_t)device_cus() * 4 * 8 + tiles * 4 - 1) / (tiles * 4);
+  const int64_t want = ((int64_t)device_cus() * 4 * 4 + tiles * 4 - 1) / (tiles * 4);
   return (int)std::max<int64_t>(1, std::min<int64_t>(want, nsteps / 4));
 }
 
