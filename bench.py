@@ -325,6 +325,18 @@ class Mlp(Workload):
                 "sample": f"{passes} whole steps (gate/up then down, M = 1..4), {nbytes} code bytes in {dt:.2f} s"}
 
 
+def _prefill_algo(tq, name):
+    return {"fused": tq.PREFILL_FUSED, "expand_gemm": tq.PREFILL_EXPAND_GEMM, "auto": tq.PREFILL_AUTO}[name]
+
+
+def _runs_fused(tq, algo, workspace_bytes):
+    """Whether a prefill call with `algo` runs the fused kernels: AUTO is resolved by the
+    library, and its workspace query answers for the algorithm it picks."""
+    if algo != tq.PREFILL_AUTO:
+        return algo == tq.PREFILL_FUSED
+    return workspace_bytes(algo) == workspace_bytes(tq.PREFILL_FUSED)
+
+
 class Prefill(Workload):
     unit, bound, dtype = "TFLOP/s", "mfma", "bf16"
 
@@ -339,10 +351,11 @@ class Prefill(Workload):
         codes, half, bf16 = _dev_tensors(np, torch, dev)
         self.dc, self.ds, self.dx = codes(m.codes), half(m.scales), bf16(w.x[0])
         self.out = torch.empty((M, m.R), dtype=torch.bfloat16, device=dev)
-        self.algo = tq.PREFILL_EXPAND_GEMM if args.algo == "expand_gemm" else tq.PREFILL_FUSED
-        nbytes = tq.prefill_workspace_bytes(m.R, m.C, M, m.k, self.algo)
+        self.algo = _prefill_algo(tq, args.algo)
+        wsb = lambda a: tq.prefill_workspace_bytes(m.R, m.C, M, m.k, a)
+        nbytes = wsb(self.algo)
         self.ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
-        self.graph = self.algo == tq.PREFILL_FUSED
+        self.graph = _runs_fused(tq, self.algo, wsb)
         self.kernels_per_step = 1 if self.graph else 2
         self.units_per_step = 2.0 * M * m.R * m.C
         self.name = w.name
@@ -352,6 +365,8 @@ class Prefill(Workload):
         self.profile_sources = PREFILL_SOURCES
         self.config = {"workload": w.name, "M": M, "R": m.R, "C": m.C, "k": m.k, "L": L, "T": T,
                        "algo": args.algo}
+        if args.algo == "auto":
+            self.config["auto_picked"] = "fused" if self.graph else "expand_gemm"
 
     def step(self, s):
         self.tq.prefill(self.dc, self.ds, self.dx, self.m.k, algo=self.algo, out=self.out, workspace=self.ws)
@@ -390,10 +405,11 @@ class PrefillAxis0(Workload):
         codes, half, bf16 = _dev_tensors(np, torch, dev)
         self.dc, self.ds, self.dx = codes(m.codes), half(m.scales), bf16(self.x)
         self.out = torch.empty((M, m.C), dtype=torch.bfloat16, device=dev)
-        self.algo = tq.PREFILL_EXPAND_GEMM if args.algo == "expand_gemm" else tq.PREFILL_FUSED
-        nbytes = tq.load_library().trellis_prefill_axis0_workspace_bytes(m.R, m.C, M, m.k, L, T, self.algo)
+        self.algo = _prefill_algo(tq, args.algo)
+        wsb = lambda a: tq.load_library().trellis_prefill_axis0_workspace_bytes(m.R, m.C, M, m.k, L, T, a)
+        nbytes = wsb(self.algo)
         self.ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
-        self.graph = self.algo == tq.PREFILL_FUSED
+        self.graph = _runs_fused(tq, self.algo, wsb)
         self.kernels_per_step = 1 if self.graph else 2
         self.units_per_step = 2.0 * M * m.R * m.C
         self.name = f"prefill_axis0_{m.R}x{m.C}_k{m.k}_m{M}"
@@ -403,6 +419,8 @@ class PrefillAxis0(Workload):
         self.profile_sources = PREFILL_SOURCES
         self.config = {"workload": self.name, "M": M, "R_in": m.R, "C_out": m.C, "k": m.k, "L": L, "T": T,
                        "algo": args.algo}
+        if args.algo == "auto":
+            self.config["auto_picked"] = "fused" if self.graph else "expand_gemm"
 
     def step(self, s):
         self.tq.prefill_axis0(self.dc, self.ds, self.dx, self.m.k, algo=self.algo, out=self.out, workspace=self.ws)
@@ -516,7 +534,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gateup", choices=sorted(WORKLOADS))
     ap.add_argument("--m", type=int, default=0, help="prefill rows (default 2048) / axis0 M")
-    ap.add_argument("--algo", default="fused", choices=["fused", "expand_gemm"])
+    ap.add_argument("--algo", default="fused", choices=["fused", "expand_gemm", "auto"])
     ap.add_argument("--eager", action="store_true", help="time plain calls instead of graph replays")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
