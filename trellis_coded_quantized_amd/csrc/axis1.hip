@@ -173,7 +173,9 @@ __device__ __forceinline__ void lds_read_runs5(const uint32_t (&aw)[5], const ui
   }
 }
 
-template <int K, bool GATEUP, int NG>
+// GROUP: the launch spans the row groups of several matrices (a grouped
+// call); the plain and gate/up instantiations compile the lookup out.
+template <int K, bool GATEUP, int NG, bool GROUP = false>
 __global__ __launch_bounds__(kThreads) void axis1_kernel(
     const uint32_t* __restrict__ codes0, const uint16_t* __restrict__ scales0,
     const uint32_t* __restrict__ codes1, const uint16_t* __restrict__ scales1,
@@ -198,7 +200,7 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
   auto locate = [&](int64_t rg, int& gi, int64_t& lrg) {
     gi = 0;
     int64_t start = 0;
-    if constexpr (!GATEUP) {
+    if constexpr (GROUP && !GATEUP) {
 #pragma unroll
       for (int j = 0; j + 1 < kMaxGroup; ++j)
         if (j + 1 < g.ngroup && rg >= g.gend[j]) {
@@ -210,9 +212,11 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
   };
   auto pick = [&](auto p0, auto const (&tab)[kMaxGroup], int gi) {
     auto p = p0;
+    if constexpr (GROUP) {
 #pragma unroll
-    for (int j = 1; j < kMaxGroup; ++j)
-      if (gi == j) p = tab[j];
+      for (int j = 1; j < kMaxGroup; ++j)
+        if (gi == j) p = tab[j];
+    }
     return p;
   };
 
@@ -549,7 +553,7 @@ int64_t axis1_grid(int64_t R, bool gateup, int64_t nrg_total = 0) {
   return nrg < cus ? nrg : cus;
 }
 
-template <int K, bool GU, int NG>
+template <int K, bool GU, int NG, bool GROUP = false>
 hipError_t axis1_launch_one(const uint32_t* c0, const uint16_t* s0, const uint32_t* c1,
                             const uint16_t* s1, const uint16_t* x, void* out, int out_f32,
                             float* gf, float* uf, const Axis1Geom& g, int64_t grid, hipStream_t stream) {
@@ -558,12 +562,12 @@ hipError_t axis1_launch_one(const uint32_t* c0, const uint16_t* s0, const uint32
   if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
   const uint64_t bit = 1ull << (dev & 63);
   if (!(lds_attr & bit)) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&axis1_kernel<K, GU, NG>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&axis1_kernel<K, GU, NG, GROUP>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kAxis1MaxLdsBytes);
     if (e != hipSuccess) return e;
     lds_attr |= bit;
   }
-  hipLaunchKernelGGL((axis1_kernel<K, GU, NG>), dim3((unsigned)grid), dim3(kThreads), g.total, stream,
+  hipLaunchKernelGGL((axis1_kernel<K, GU, NG, GROUP>), dim3((unsigned)grid), dim3(kThreads), g.total, stream,
                      c0, s0, c1, s1, x, out, out_f32, gf, uf, g);
   return hipGetLastError();
 }
@@ -612,11 +616,11 @@ hipError_t axis1_group_main(const uint32_t* const* codes, const uint16_t* const*
   }
   switch (axis1_ng(C)) {
     case 2:
-      return axis1_launch_one<K, false, 2>(codes[0], scales[0], nullptr, nullptr, x, outs[0], out_f32, nullptr,
-                                           nullptr, g, grid, stream);
+      return axis1_launch_one<K, false, 2, true>(codes[0], scales[0], nullptr, nullptr, x, outs[0], out_f32,
+                                                 nullptr, nullptr, g, grid, stream);
     case 5:
-      return axis1_launch_one<K, false, 5>(codes[0], scales[0], nullptr, nullptr, x, outs[0], out_f32, nullptr,
-                                           nullptr, g, grid, stream);
+      return axis1_launch_one<K, false, 5, true>(codes[0], scales[0], nullptr, nullptr, x, outs[0], out_f32,
+                                                 nullptr, nullptr, g, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }
