@@ -540,8 +540,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} requested; this build measures one GPU only "
-              f"(the path runs on a single MI355X; sharding is described in the design notes).", file=sys.stderr)
+        print(f"bench.py: --gpus {args.gpus} requested; only one GPU is measured: the library runs on a "
+              f"single MI355X and has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 
     _ensure_built()
