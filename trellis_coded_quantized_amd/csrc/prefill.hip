@@ -579,8 +579,7 @@ __global__ __launch_bounds__(256) void prefill_fold_kernel(const float* __restri
 // and store bf16 (S == 1) or an f32 partial [S][M][R] that
 // prefill_direct_fold_kernel adds up.  Waves are many and independent, so the
 // machine stays evenly loaded.  One 32-row x tile: from 33 rows on, the tile
-// kernel above is faster (its code words are shared through LDS; here every
-// lane loads its own row's words, and the address unit is the bound).
+// kernel above was faster.
 constexpr int kDirectMaxM = 32;
 
 template <int K>
@@ -614,18 +613,6 @@ __global__ __launch_bounds__(256) void prefill_direct_kernel(
 #pragma unroll
   for (int i = 0; i < FM; ++i) xvo[i] = (uint32_t)min(i, nblk - 1) * (uint32_t)(nsteps * 2 * kFrag) + lane * 16u;
 
-  // run of step t: block t / 8, first position 32 (t % 8) + 16 dh
-  auto run_bits = [&](int t) { return (kT - 16 - (kBK * (t & 7) + 16 * dh)) * K; };
-  auto load_w = [&](uint32_t (&dst)[NL], int t) {
-    t = min(t, nsteps - 1);
-    const int w0 = run_bits(t) >> 5;
-    const int base = (t >> 3) * WPB * 4;
-#pragma unroll
-    for (int j = 0; j < NL; ++j) {
-      const int wj = (w0 + j >= WPB) ? w0 + j - WPB : w0 + j;
-      dst[j] = __builtin_amdgcn_raw_buffer_load_b32(cr, cvo + wj * 4, base, 0);
-    }
-  };
   auto load_x = [&](u32x4 (&dst)[2][FM], int t) {
     t = min(t, nsteps - 1);
 #pragma unroll
@@ -640,31 +627,50 @@ __global__ __launch_bounds__(256) void prefill_direct_kernel(
   for (int i = 0; i < FM; ++i) acc[i] = f32x16{};
   const uint32_t mul = kMul;
   const uint64_t add64 = kAdd;
-  // two steps in flight: words and x of step t + 1 load while step t decodes
-  uint32_t cw[2][NL];
+  // The 8 steps of a block read only that block's WPB words: a lane loads its
+  // row's block once, 16 bytes at a time, and takes each step's run from it
+  // (word indices fixed per step; the two halves of a step, 16 positions
+  // apart, differ by a select on lane / 32).  x of step t + 1 loads while
+  // step t decodes.
   u32x4 xv[2][2][FM];
-  load_w(cw[0], t_begin);
-  load_x(xv[0], t_begin);
-  for (int t = t_begin; t < t_end; t += 2) {
+  if (t_begin & 1) load_x(xv[1], t_begin);
+  else load_x(xv[0], t_begin);
+  for (int blk = t_begin >> 3; blk <= (t_end - 1) >> 3; ++blk) {
+    uint32_t W[WPB];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int tt = t + u;
-      load_w(cw[u ^ 1], tt + 1);
-      load_x(xv[u ^ 1], tt + 1);
-      if (tt < t_end) {
-        const bool sh = (run_bits(tt) & 31) != 0;
-        uint32_t pk[4];
-        decode_run8<K, 0>(cw[u], sh, sc, mul, add64, pk);
+    for (int q = 0; q < WPB / 4; ++q) {
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(cr, cvo, (blk * WPB + 4 * q) * 4, 0);
+      W[4 * q] = v[0];
+      W[4 * q + 1] = v[1];
+      W[4 * q + 2] = v[2];
+      W[4 * q + 3] = v[3];
+    }
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
-          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]}),
-                                                          __builtin_bit_cast(bf16x8, xv[u][0][i]), acc[i], 0, 0, 0);
-        decode_run8<K, 1>(cw[u], sh, sc, mul, add64, pk);
+    for (int j = 0; j < 8; ++j) {
+      const int t = blk * 8 + j;
+      if (t < t_begin || t >= t_end) continue;
+      load_x(xv[(j + 1) & 1], t + 1);
+      // half-run dh: first position 32 j + 16 dh, lowest window bit (240 - 32 j - 16 dh) K
+      const int rb0 = (kT - 16 - kBK * j) * K, rb1 = (kT - 32 - kBK * j) * K;
+      uint32_t w[NL];
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
-          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]}),
-                                                          __builtin_bit_cast(bf16x8, xv[u][1][i]), acc[i], 0, 0, 0);
+      for (int i = 0; i < NL; ++i) {
+        const int i0 = (rb0 >> 5) + i, i1 = (rb1 >> 5) + i;
+        const uint32_t a0 = W[i0 >= WPB ? i0 - WPB : i0], a1 = W[i1 >= WPB ? i1 - WPB : i1];
+        w[i] = dh ? a1 : a0;
       }
+      const bool sh = dh ? (rb1 & 31) != 0 : (rb0 & 31) != 0;
+      uint32_t pk[4];
+      decode_run8<K, 0>(w, sh, sc, mul, add64, pk);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]}),
+                                                        __builtin_bit_cast(bf16x8, xv[j & 1][0][i]), acc[i], 0, 0, 0);
+      decode_run8<K, 1>(w, sh, sc, mul, add64, pk);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]}),
+                                                        __builtin_bit_cast(bf16x8, xv[j & 1][1][i]), acc[i], 0, 0, 0);
     }
   }
 
