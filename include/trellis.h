@@ -202,7 +202,7 @@ int trellis_expand_bf16_il(const uint32_t* codes, const uint16_t* scales, uint16
  *   TRELLIS_PREFILL_AUTO.
  * The EXPAND_GEMM workspace holds the bf16 [R, C] expansion.  The FUSED
  * workspace holds x rewritten in the MFMA operand order (ceil(M/32)*32*C*2
- * bytes), then f32 partial sums: for M <= 32 those of the column chunks the
+ * bytes), then f32 partial sums: for M <= 64 those of the column chunks the
  * weight rows are split into ([S][M][R]); above, the partial tiles of output
  * tiles split along C when whole tiles would leave compute units idle (the
  * size of that part depends on the device's compute-unit count).

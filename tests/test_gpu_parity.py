@@ -264,10 +264,11 @@ def test_prefill_fused_stream_pieces(k, R, M):
 
 @pytest.mark.parametrize("k", [2, 3, 4])
 @pytest.mark.parametrize("R,C,M", [(1000, 1024, 1), (1000, 1024, 32), (777, 512, 9), (40, 256, 17),
-                                   (4096, 5120, 32)])
+                                   (4096, 5120, 32), (1000, 1024, 33), (777, 512, 48), (4096, 5120, 64)])
 def test_prefill_direct(k, R, C, M):
-    # M <= 32 runs the register-direct kernel: 32-row weight tiles (a ragged last one when
-    # R % 32 != 0), column chunks split over workgroups and waves, one x tile; every output
+    # M <= 64 runs the register-direct kernel: 32-row weight tiles (a ragged last one when
+    # R % 32 != 0), column chunks split over workgroups and waves, one (M <= 32) or two x tiles;
+    # every output
     rng = np.random.default_rng(500 + R + C + M + k)
     codes, scales = rand_matrix(rng, R, C, k)
     x = ti.activations(rng, M, C)
@@ -276,9 +277,10 @@ def test_prefill_direct(k, R, C, M):
     tol.assert_bf16_close(got, want, f"direct prefill R={R} C={C} M={M} k={k}")
 
 
-@pytest.mark.parametrize("M", [32, 33, 64, 128, 129, 256, 257])
+@pytest.mark.parametrize("M", [32, 33, 64, 65, 128, 129, 256, 257])
 def test_prefill_fused_tile_size_boundaries(M):
-    # M = 32 is the last size on the register-direct kernel, 33 the first on 128-row x tiles;
+    # M = 32 / 33: one and two x tiles in the register-direct kernel; 64 is its last size, 65 the
+    # first on 128-row x tiles;
     # M = 256 is the last size on 128-row tiles (2 row tiles), 257 the first on 512-row tiles
     # (rows 257..511 of the tile padded); 128 / 129 straddle the one-tile case.  Every output.
     R, C, k = 640, 1024, 2

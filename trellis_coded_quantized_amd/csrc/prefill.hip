@@ -565,7 +565,7 @@ __global__ __launch_bounds__(256) void prefill_fold_kernel(const float* __restri
   }
 }
 
-// ---- register-direct prefill for M <= 32 -----------------------------------
+// ---- register-direct prefill for M <= 64 -----------------------------------
 //
 // With few rows of x the tile kernel above is bound by its decode, and its
 // per-step LDS round trip and barrier slow that decode down.  Here each lane
@@ -578,18 +578,17 @@ __global__ __launch_bounds__(256) void prefill_fold_kernel(const float* __restri
 // of the columns; its 4 waves split the chunk, meet once in LDS at the end,
 // and store bf16 (S == 1) or an f32 partial [S][M][R] that
 // prefill_direct_fold_kernel adds up.  Waves are many and independent, so the
-// machine stays evenly loaded.  One 32-row x tile: from 33 rows on, the tile
-// kernel above was faster.
-constexpr int kDirectMaxM = 32;
+// machine stays evenly loaded.  FM x tiles of 32 rows (M <= 64); from 65
+// rows on, the tile kernel above shares each decoded weight among more rows.
+constexpr int kDirectMaxM = 64;
 
-template <int K>
+template <int K, int FM>
 __global__ __launch_bounds__(256) void prefill_direct_kernel(
     const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ xf, uint16_t* __restrict__ out, float* __restrict__ part, int R, int C,
     int M, int S) {
   constexpr int WPB = words_per_block(K);
   constexpr int NL = Run16<K>::kLoad;
-  constexpr int FM = 1;                                               // x tiles of 32 rows
   __shared__ __attribute__((aligned(16))) float red[3][FM][16][64];   // waves 1..3's accumulators
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -804,9 +803,15 @@ hipError_t launch_prefill_fused(const uint32_t* codes, const uint16_t* scales, c
     const int S = direct_splits(R, C);
     const dim3 dgrid((unsigned)(((R + 31) / 32) * S));
     switch (k) {
-      case 2: hipLaunchKernelGGL(prefill_direct_kernel<2>, dgrid, dim3(256), 0, stream, codes, scales, xf, out, part, r, c, m, S); break;
-      case 3: hipLaunchKernelGGL(prefill_direct_kernel<3>, dgrid, dim3(256), 0, stream, codes, scales, xf, out, part, r, c, m, S); break;
-      case 4: hipLaunchKernelGGL(prefill_direct_kernel<4>, dgrid, dim3(256), 0, stream, codes, scales, xf, out, part, r, c, m, S); break;
+      case 2: if (M > 32) hipLaunchKernelGGL((prefill_direct_kernel<2, 2>), dgrid, dim3(256), 0, stream, codes, scales, xf, out, part, r, c, m, S);
+              else hipLaunchKernelGGL((prefill_direct_kernel<2, 1>), dgrid, dim3(256), 0, stream, codes, scales, xf, out, part, r, c, m, S);
+              break;
+      case 3: if (M > 32) hipLaunchKernelGGL((prefill_direct_kernel<3, 2>), dgrid, dim3(256), 0, stream, codes, scales, xf, out, part, r, c, m, S);
+              else hipLaunchKernelGGL((prefill_direct_kernel<3, 1>), dgrid, dim3(256), 0, stream, codes, scales, xf, out, part, r, c, m, S);
+              break;
+      case 4: if (M > 32) hipLaunchKernelGGL((prefill_direct_kernel<4, 2>), dgrid, dim3(256), 0, stream, codes, scales, xf, out, part, r, c, m, S);
+              else hipLaunchKernelGGL((prefill_direct_kernel<4, 1>), dgrid, dim3(256), 0, stream, codes, scales, xf, out, part, r, c, m, S);
+              break;
       default: return hipErrorInvalidValue;
     }
     e = hipGetLastError();
