@@ -44,17 +44,17 @@ def _load():
         "tro_value": (ctypes.c_float, [ctypes.c_int32]),
         "tro_decode": (None, [_u32p, _i64, _i64, _int, _int, _int, _u16p, _i16p, _f32p]),
         "tro_matvec_axis1": (None, [_u32p, _u16p, _u16p, _int, _i64, _i64, _int, _int, _int,
-                                    _i64p, _i64, _f64p]),
+                                    _i64p, _i64, _f64p, _f64p]),
         "tro_matvec_axis0": (None, [_u32p, _u16p, _u16p, _int, _i64, _i64, _int, _int, _int,
-                                    _i64p, _i64, _f64p]),
+                                    _i64p, _i64, _f64p, _f64p]),
         "tro_swiglu": (ctypes.c_uint16, [ctypes.c_double, ctypes.c_double]),
         "tro_gateup_swiglu": (None, [_u32p, _u16p, _u32p, _u16p, _u16p, _int, _i64, _i64, _int,
-                                     _int, _int, _i64p, _i64, _f64p, _f64p, _u16p]),
+                                     _int, _int, _i64p, _i64, _f64p, _f64p, _u16p, _f64p, _f64p]),
         "tro_expand_bf16": (None, [_u32p, _u16p, _i64, _i64, _int, _int, _int, _i64, _i64, _u16p]),
         "tro_prefill": (None, [_u32p, _u16p, _u16p, _i64, _i64, _i64, _int, _int, _int,
-                               _i64p, _i64, _i64p, _i64, _f64p]),
+                               _i64p, _i64, _i64p, _i64, _f64p, _f64p]),
         "tro_prefill_axis0": (None, [_u32p, _u16p, _u16p, _i64, _i64, _i64, _int, _int, _int,
-                                     _i64p, _i64, _i64p, _i64, _f64p]),
+                                     _i64p, _i64, _i64p, _i64, _f64p, _f64p]),
         "tro_num_threads": (_int, []),
     }
     for name, (res, args) in sig.items():
@@ -135,32 +135,41 @@ def _sel(sel, n):
     return s, s.size
 
 
-def matvec_axis1(codes, scales, x, M, R, C, k, L, T, rows=None) -> np.ndarray:
-    """float64 [M, nrows] exact-in-double sums (axis 1, coded along inputs)."""
+def _abs_buf(shape, with_abs):
+    return np.empty(shape, np.float64) if with_abs else None
+
+
+def matvec_axis1(codes, scales, x, M, R, C, k, L, T, rows=None, with_abs=False):
+    """float64 [M, nrows] exact-in-double sums (axis 1, coded along inputs);
+    with_abs: (sums, sums of |term|)."""
     c, s, xx = _c(codes, np.uint32), _c(scales, np.uint16), _c(x, np.uint16)
     sel, n = _sel(rows, R)
     out = np.empty((M, n), np.float64)
+    ab = _abs_buf((M, n), with_abs)
     _load().tro_matvec_axis1(_ptr(c, _u32p), _ptr(s, _u16p), _ptr(xx, _u16p), M, R, C, k, L, T,
-                             _ptr(sel, _i64p), n, _ptr(out, _f64p))
-    return out
+                             _ptr(sel, _i64p), n, _ptr(out, _f64p), _ptr(ab, _f64p))
+    return (out, ab) if with_abs else out
 
 
-def matvec_axis0(codes, scales, x, M, R, C, k, L, T, cols=None) -> np.ndarray:
-    """float64 [M, ncols] sums for the axis-0 (stored transpose) layout."""
+def matvec_axis0(codes, scales, x, M, R, C, k, L, T, cols=None, with_abs=False):
+    """float64 [M, ncols] sums for the axis-0 (stored transpose) layout;
+    with_abs: (sums, sums of |term|)."""
     c, s, xx = _c(codes, np.uint32), _c(scales, np.uint16), _c(x, np.uint16)
     sel, n = _sel(cols, C)
     out = np.empty((M, n), np.float64)
+    ab = _abs_buf((M, n), with_abs)
     _load().tro_matvec_axis0(_ptr(c, _u32p), _ptr(s, _u16p), _ptr(xx, _u16p), M, R, C, k, L, T,
-                             _ptr(sel, _i64p), n, _ptr(out, _f64p))
-    return out
+                             _ptr(sel, _i64p), n, _ptr(out, _f64p), _ptr(ab, _f64p))
+    return (out, ab) if with_abs else out
 
 
 def swiglu(gate: float, up: float) -> int:
     return int(_load().tro_swiglu(float(gate), float(up)))
 
 
-def gateup_swiglu(gcodes, gscales, ucodes, uscales, x, M, R, C, k, L, T, rows=None):
-    """(gate float64 [M, n], up float64 [M, n], out bf16 bits [M, n])."""
+def gateup_swiglu(gcodes, gscales, ucodes, uscales, x, M, R, C, k, L, T, rows=None, with_abs=False):
+    """(gate float64 [M, n], up float64 [M, n], out bf16 bits [M, n]); with_abs
+    appends the gate's and the up projection's sums of |term|."""
     gc, gs = _c(gcodes, np.uint32), _c(gscales, np.uint16)
     uc, us = _c(ucodes, np.uint32), _c(uscales, np.uint16)
     xx = _c(x, np.uint16)
@@ -168,10 +177,11 @@ def gateup_swiglu(gcodes, gscales, ucodes, uscales, x, M, R, C, k, L, T, rows=No
     g = np.empty((M, n), np.float64)
     u = np.empty((M, n), np.float64)
     o = np.empty((M, n), np.uint16)
+    ga, ua = _abs_buf((M, n), with_abs), _abs_buf((M, n), with_abs)
     _load().tro_gateup_swiglu(_ptr(gc, _u32p), _ptr(gs, _u16p), _ptr(uc, _u32p), _ptr(us, _u16p),
                               _ptr(xx, _u16p), M, R, C, k, L, T, _ptr(sel, _i64p), n,
-                              _ptr(g, _f64p), _ptr(u, _f64p), _ptr(o, _u16p))
-    return g, u, o
+                              _ptr(g, _f64p), _ptr(u, _f64p), _ptr(o, _u16p), _ptr(ga, _f64p), _ptr(ua, _f64p))
+    return (g, u, o, ga, ua) if with_abs else (g, u, o)
 
 
 def expand_bf16(codes, scales, R, C, k, L, T, r0=0, nr=None) -> np.ndarray:
@@ -185,22 +195,28 @@ def expand_bf16(codes, scales, R, C, k, L, T, r0=0, nr=None) -> np.ndarray:
     return out
 
 
-def prefill_sums(codes, scales, x, M, R, C, k, L, T, ms, rows) -> np.ndarray:
-    """float64 [len(ms), len(rows)] sums of bf16 weights times bf16 x."""
+def prefill_sums(codes, scales, x, M, R, C, k, L, T, ms, rows, with_abs=False):
+    """float64 [len(ms), len(rows)] sums of bf16 weights times bf16 x;
+    with_abs: (sums, sums of |term|)."""
     c, s, xx = _c(codes, np.uint32), _c(scales, np.uint16), _c(x, np.uint16)
     msa, rsa = _c(ms, np.int64), _c(rows, np.int64)
     out = np.empty((msa.size, rsa.size), np.float64)
+    ab = _abs_buf(out.shape, with_abs)
     _load().tro_prefill(_ptr(c, _u32p), _ptr(s, _u16p), _ptr(xx, _u16p), M, R, C, k, L, T,
-                        _ptr(msa, _i64p), msa.size, _ptr(rsa, _i64p), rsa.size, _ptr(out, _f64p))
-    return out
+                        _ptr(msa, _i64p), msa.size, _ptr(rsa, _i64p), rsa.size, _ptr(out, _f64p),
+                        _ptr(ab, _f64p))
+    return (out, ab) if with_abs else out
 
 
-def prefill_axis0_sums(codes, scales, x, M, R, C, k, L, T, ms, cols) -> np.ndarray:
+def prefill_axis0_sums(codes, scales, x, M, R, C, k, L, T, ms, cols, with_abs=False):
     """float64 [len(ms), len(cols)] sums over the stored rows of bf16 weights
-    times bf16 x, for a matrix stored transposed (axis 0)."""
+    times bf16 x, for a matrix stored transposed (axis 0); with_abs: (sums,
+    sums of |term|)."""
     c, s, xx = _c(codes, np.uint32), _c(scales, np.uint16), _c(x, np.uint16)
     msa, csa = _c(ms, np.int64), _c(cols, np.int64)
     out = np.empty((msa.size, csa.size), np.float64)
+    ab = _abs_buf(out.shape, with_abs)
     _load().tro_prefill_axis0(_ptr(c, _u32p), _ptr(s, _u16p), _ptr(xx, _u16p), M, R, C, k, L, T,
-                              _ptr(msa, _i64p), msa.size, _ptr(csa, _i64p), csa.size, _ptr(out, _f64p))
-    return out
+                              _ptr(msa, _i64p), msa.size, _ptr(csa, _i64p), csa.size, _ptr(out, _f64p),
+                              _ptr(ab, _f64p))
+    return (out, ab) if with_abs else out

@@ -190,43 +190,64 @@ void tro_decode(const uint32_t* codes, int64_t R, int64_t C, int k, int L, int T
 
 /* Axis 1 ([TL] REDUCE): out[m, i] = sum_c w(row_i, c) * x[m, c] for the
  * selected stored rows (rows == NULL selects all R).  x: bf16 [M, C];
- * out: double [M, nrows]. */
+ * out: double [M, nrows].  abs_out (double [M, nrows], may be NULL)
+ * receives sum_c |w(row_i, c) * x[m, c]|, the scale of the terms each sum
+ * cancels (the parity criterion measures rounding error against it). */
 void tro_matvec_axis1(const uint32_t* codes, const uint16_t* scales, const uint16_t* x,
                       int M, int64_t R, int64_t C, int k, int L, int T,
-                      const int64_t* rows, int64_t nrows, double* out) {
+                      const int64_t* rows, int64_t nrows, double* out, double* abs_out) {
   if (!rows) nrows = R;
 #pragma omp parallel for schedule(dynamic, 4)
   for (int64_t i = 0; i < nrows; ++i) {
     const int64_t r = rows ? rows[i] : i;
     const double scale = tro_half_to_double(scales[r]);
     double* acc = (double*)calloc((size_t)M, sizeof(double));
+    double* aacc = (double*)calloc((size_t)M, sizeof(double));
     for (int64_t c = 0; c < C; ++c) {
       const double w = (double)tro_weight_f32(tro_state_rc(codes, r, c, C, k, L, T), scale);
-      for (int m = 0; m < M; ++m) acc[m] += w * tro_bf16_to_double(x[(int64_t)m * C + c]);
+      for (int m = 0; m < M; ++m) {
+        const double t = w * tro_bf16_to_double(x[(int64_t)m * C + c]);
+        acc[m] += t;
+        aacc[m] += fabs(t);
+      }
     }
-    for (int m = 0; m < M; ++m) out[(int64_t)m * nrows + i] = acc[m];
+    for (int m = 0; m < M; ++m) {
+      out[(int64_t)m * nrows + i] = acc[m];
+      if (abs_out) abs_out[(int64_t)m * nrows + i] = aacc[m];
+    }
     free(acc);
+    free(aacc);
   }
 }
 
 /* Axis 0 ([TL] SCATTER + fold): stored matrix is W^T [R_in, C_out], coded
  * along C_out; out[m, j] = sum_r w(r, col_j) * x[m, r] over ALL stored rows,
- * with the stored row's scale.  x: bf16 [M, R]; out: double [M, ncols]. */
+ * with the stored row's scale.  x: bf16 [M, R]; out: double [M, ncols].
+ * abs_out (may be NULL): sum_r |w(r, col_j) * x[m, r]|. */
 void tro_matvec_axis0(const uint32_t* codes, const uint16_t* scales, const uint16_t* x,
                       int M, int64_t R, int64_t C, int k, int L, int T,
-                      const int64_t* cols, int64_t ncols, double* out) {
+                      const int64_t* cols, int64_t ncols, double* out, double* abs_out) {
   if (!cols) ncols = C;
 #pragma omp parallel for schedule(dynamic, 4)
   for (int64_t j = 0; j < ncols; ++j) {
     const int64_t c = cols ? cols[j] : j;
     double* acc = (double*)calloc((size_t)M, sizeof(double));
+    double* aacc = (double*)calloc((size_t)M, sizeof(double));
     for (int64_t r = 0; r < R; ++r) {
       const double w = (double)tro_weight_f32(tro_state_rc(codes, r, c, C, k, L, T),
                                               tro_half_to_double(scales[r]));
-      for (int m = 0; m < M; ++m) acc[m] += w * tro_bf16_to_double(x[(int64_t)m * R + r]);
+      for (int m = 0; m < M; ++m) {
+        const double t = w * tro_bf16_to_double(x[(int64_t)m * R + r]);
+        acc[m] += t;
+        aacc[m] += fabs(t);
+      }
     }
-    for (int m = 0; m < M; ++m) out[(int64_t)m * ncols + j] = acc[m];
+    for (int m = 0; m < M; ++m) {
+      out[(int64_t)m * ncols + j] = acc[m];
+      if (abs_out) abs_out[(int64_t)m * ncols + j] = aacc[m];
+    }
     free(acc);
+    free(aacc);
   }
 }
 
@@ -244,17 +265,19 @@ uint16_t tro_swiglu(double gate, double up) {
 
 /* Fused gate/up ([TL] fusedGateUpSwiglu): two axis-1 matvecs over the same
  * x, then the cast chain.  gate_out / up_out (double [M, nrows], may be
- * NULL) receive the raw sums; out receives bf16 bits [M, nrows]. */
+ * NULL) receive the raw sums, gate_abs / up_abs (may be NULL) their sums of
+ * absolute terms; out receives bf16 bits [M, nrows]. */
 void tro_gateup_swiglu(const uint32_t* gcodes, const uint16_t* gscales,
                        const uint32_t* ucodes, const uint16_t* uscales, const uint16_t* x,
                        int M, int64_t R, int64_t C, int k, int L, int T,
                        const int64_t* rows, int64_t nrows,
-                       double* gate_out, double* up_out, uint16_t* out) {
+                       double* gate_out, double* up_out, uint16_t* out,
+                       double* gate_abs, double* up_abs) {
   if (!rows) nrows = R;
   double* g = (double*)malloc(sizeof(double) * (size_t)M * (size_t)nrows);
   double* u = (double*)malloc(sizeof(double) * (size_t)M * (size_t)nrows);
-  tro_matvec_axis1(gcodes, gscales, x, M, R, C, k, L, T, rows, nrows, g);
-  tro_matvec_axis1(ucodes, uscales, x, M, R, C, k, L, T, rows, nrows, u);
+  tro_matvec_axis1(gcodes, gscales, x, M, R, C, k, L, T, rows, nrows, g, gate_abs);
+  tro_matvec_axis1(ucodes, uscales, x, M, R, C, k, L, T, rows, nrows, u, up_abs);
   for (int64_t i = 0; i < (int64_t)M * nrows; ++i) {
     if (gate_out) gate_out[i] = g[i];
     if (up_out) up_out[i] = u[i];
@@ -281,10 +304,12 @@ void tro_expand_bf16(const uint32_t* codes, const uint16_t* scales, int64_t R, i
 /* Axis-1 prefill ([TP]; [TL] forward expand-then-matmul fallback):
  * sum[a, b] = sum_c wb(rows_b, c) * x[ms_a, c] with bf16 expansion weights,
  * each product exact in double.  x: bf16 [M, C]; sums: double [nm, nr].
- * The layer output is the bf16 rounding of each sum. */
+ * The layer output is the bf16 rounding of each sum.  abs_sums (may be
+ * NULL) receives sum_c |wb(rows_b, c) * x[ms_a, c]|. */
 void tro_prefill(const uint32_t* codes, const uint16_t* scales, const uint16_t* x,
                  int64_t M, int64_t R, int64_t C, int k, int L, int T,
-                 const int64_t* ms, int64_t nm, const int64_t* rows, int64_t nr, double* sums) {
+                 const int64_t* ms, int64_t nm, const int64_t* rows, int64_t nr, double* sums,
+                 double* abs_sums) {
   (void)M;
   (void)R;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -295,23 +320,29 @@ void tro_prefill(const uint32_t* codes, const uint16_t* scales, const uint16_t* 
     for (int64_t c = 0; c < C; ++c) wrow[c] = tro_weight_bf16(tro_state_rc(codes, r, c, C, k, L, T), scale);
     for (int64_t a = 0; a < nm; ++a) {
       const uint16_t* xr = x + ms[a] * C;
-      double acc = 0.0;
-      for (int64_t c = 0; c < C; ++c) acc += wrow[c] * tro_bf16_to_double(xr[c]);
+      double acc = 0.0, aacc = 0.0;
+      for (int64_t c = 0; c < C; ++c) {
+        const double t = wrow[c] * tro_bf16_to_double(xr[c]);
+        acc += t;
+        aacc += fabs(t);
+      }
       sums[a * nr + b] = acc;
+      if (abs_sums) abs_sums[a * nr + b] = aacc;
     }
     free(wrow);
   }
 }
 
-/* Worker threads OpenMP will use (1 without OpenMP). */
 /* Axis-0 prefill ([TL] forward expand-then-matmul fallback, for the stored
  * transpose of the SCATTER kernel's layout): sum[a, b] = sum_r wb(r, cols_b)
  * * x[ms_a, r] over ALL stored rows, wb the bf16 expansion weight of stored
  * row r (its own scale); each product exact in double.  x: bf16 [M, R];
- * sums: double [nm, nc].  The layer output is the bf16 rounding of each sum. */
+ * sums: double [nm, nc].  The layer output is the bf16 rounding of each sum.
+ * abs_sums (may be NULL) receives sum_r |wb(r, cols_b) * x[ms_a, r]|. */
 void tro_prefill_axis0(const uint32_t* codes, const uint16_t* scales, const uint16_t* x,
                        int64_t M, int64_t R, int64_t C, int k, int L, int T,
-                       const int64_t* ms, int64_t nm, const int64_t* cols, int64_t nc, double* sums) {
+                       const int64_t* ms, int64_t nm, const int64_t* cols, int64_t nc, double* sums,
+                       double* abs_sums) {
   (void)M;
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t b = 0; b < nc; ++b) {
@@ -321,14 +352,20 @@ void tro_prefill_axis0(const uint32_t* codes, const uint16_t* scales, const uint
       wcol[r] = tro_weight_bf16(tro_state_rc(codes, r, c, C, k, L, T), tro_half_to_double(scales[r]));
     for (int64_t a = 0; a < nm; ++a) {
       const uint16_t* xr = x + ms[a] * R;
-      double acc = 0.0;
-      for (int64_t r = 0; r < R; ++r) acc += wcol[r] * tro_bf16_to_double(xr[r]);
+      double acc = 0.0, aacc = 0.0;
+      for (int64_t r = 0; r < R; ++r) {
+        const double t = wcol[r] * tro_bf16_to_double(xr[r]);
+        acc += t;
+        aacc += fabs(t);
+      }
       sums[a * nc + b] = acc;
+      if (abs_sums) abs_sums[a * nc + b] = aacc;
     }
     free(wcol);
   }
 }
 
+/* Worker threads OpenMP will use (1 without OpenMP). */
 int tro_num_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

@@ -345,6 +345,57 @@ def test_prefill_axis0_dense_and_one_hot(k):
     assert np.array_equal(e[0], Wb[3]) and np.array_equal(e[1], -Wb[R - 1])
 
 
+# ---------------------------------------------------------------- sums of |term|
+# The parity criterion measures rounding error against sum_c |w x|, which the
+# oracle returns beside each sum.  Pinned to the dense product of the absolute
+# weights and absolute activations, to the sum itself where no term cancels
+# (one-hot x), to sign invariance and to the triangle inequality.
+
+@pytest.mark.parametrize("R,C,M,k", CASES)
+def test_abs_sums_axis1_and_axis0(R, C, M, k):
+    rng = np.random.default_rng(R * 3000 + C + k)
+    codes = rng.integers(0, 2 ** 32, (R, C * k // 32), dtype=np.uint32)
+    sc = rand_scales(rng, R)
+    W = np.abs(dense_f32_weights(codes, sc, R, C, k).astype(np.float64))
+    x1 = rand_bf16(rng, (M, C))
+    s1, a1 = oracle.matvec_axis1(codes, sc, x1, M, R, C, k, L, T, with_abs=True)
+    np.testing.assert_allclose(a1, np.abs(bf16_bits_to_f64(x1)) @ W.T, rtol=1e-12, atol=0)
+    assert np.all(a1 >= np.abs(s1))
+    assert np.array_equal(oracle.matvec_axis1(codes, sc, x1 ^ np.uint16(0x8000), M, R, C, k, L, T,
+                                              with_abs=True)[1], a1)
+    x0 = rand_bf16(rng, (M, R))
+    s0, a0 = oracle.matvec_axis0(codes, sc, x0, M, R, C, k, L, T, with_abs=True)
+    np.testing.assert_allclose(a0, np.abs(bf16_bits_to_f64(x0)) @ W, rtol=1e-12, atol=0)
+    assert np.all(a0 >= np.abs(s0))
+    # one-hot: one term, nothing cancels
+    c = int(rng.integers(0, C))
+    e = np.zeros((1, C), np.uint16)
+    e[0, c] = torch_bf16_bits(-1.0)
+    s, a = oracle.matvec_axis1(codes, sc, e, 1, R, C, k, L, T, with_abs=True)
+    assert np.array_equal(a, np.abs(s))
+
+
+def test_abs_sums_gateup_and_prefill():
+    rng = np.random.default_rng(13)
+    R, C, M, k = 5, 512, 3, 3
+    gc = rng.integers(0, 2 ** 32, (R, C * k // 32), dtype=np.uint32)
+    uc = rng.integers(0, 2 ** 32, (R, C * k // 32), dtype=np.uint32)
+    gs, us = rand_scales(rng, R), rand_scales(rng, R)
+    x = rand_bf16(rng, (M, C))
+    g, u, _, ga, ua = oracle.gateup_swiglu(gc, gs, uc, us, x, M, R, C, k, L, T, with_abs=True)
+    assert np.array_equal(ga, oracle.matvec_axis1(gc, gs, x, M, R, C, k, L, T, with_abs=True)[1])
+    assert np.array_equal(ua, oracle.matvec_axis1(uc, us, x, M, R, C, k, L, T, with_abs=True)[1])
+    Wb = np.abs(bf16_bits_to_f64(oracle.expand_bf16(gc, gs, R, C, k, L, T)))
+    s, a = oracle.prefill_sums(gc, gs, x, M, R, C, k, L, T, np.arange(M), np.arange(R), with_abs=True)
+    np.testing.assert_allclose(a, np.abs(bf16_bits_to_f64(x)) @ Wb.T, rtol=1e-12, atol=0)
+    assert np.all(a >= np.abs(s))
+    # axis 0: stored [R, C] = gc, x over the stored rows
+    xa = rand_bf16(rng, (M, R))
+    s0, a0 = oracle.prefill_axis0_sums(gc, gs, xa, M, R, C, k, L, T, np.arange(M), np.arange(C), with_abs=True)
+    np.testing.assert_allclose(a0, np.abs(bf16_bits_to_f64(xa)) @ Wb, rtol=1e-12, atol=0)
+    assert np.all(a0 >= np.abs(s0))
+
+
 def test_expansion_size_matches_page():
     # TL file header: the dense bf16 transient at the 5120 -> 17408 shape is ~178 MB
     assert round(17408 * 5120 * 2 / 1e6) == GOLD["expansion_megabytes_17408x5120"]["value"]
