@@ -20,7 +20,9 @@
  *   - Supported geometry: k in {2, 3, 4}, L = 12, T = 256, C % T == 0,
  *     R >= 1, C >= 1 (others: TRELLIS_EUNSUPPORTED or TRELLIS_EINVAL).
  *   - `stream` is a hipStream_t (NULL = the device's default stream).  Calls
- *     are asynchronous on that stream and never synchronise the host.
+ *     are asynchronous on that stream and never synchronise the host -- the
+ *     two *_tune calls alone wait for their timing runs (they exist for
+ *     that).
  *   - All checks run on the host before any launch.  On any non-zero return
  *     nothing was launched and nothing was written; trellis_last_error()
  *     then describes the problem (thread-local, valid until the next call on
@@ -74,7 +76,13 @@ extern "C" {
  *   out     [M, R], bf16 (out_dtype = TRELLIS_OUT_BF16) or f32 (TRELLIS_OUT_F32)
  *   1 <= M <= TRELLIS_MATVEC_MAX_M.
  * w(r, c) is the f32 product of the code value and scales[r] (no bf16
- * rounding of weights); sums accumulate in f32.
+ * rounding of weights: the pages' default numerics); sums accumulate in f32.
+ * For the pages' variants 0-3 contract (weights rounded to bf16 first) see
+ * trellis_prefill, which computes it for any M.
+ * Workspace: none for C <= 5120.  Wider rows run as column chunks of at
+ * most 5120 columns whose f32 partial outputs ([chunks][M][R]) the workspace
+ * holds; trellis_matvec_axis1_workspace_bytes gives its size (0 when none is
+ * needed).
  */
 size_t trellis_matvec_axis1_workspace_bytes(int64_t R, int64_t C, int M, int k, int L, int T);
 int trellis_matvec_axis1(const uint32_t* codes, const uint16_t* scales, const uint16_t* x,
@@ -93,7 +101,9 @@ int trellis_matvec_axis1(const uint32_t* codes, const uint16_t* scales, const ui
  * call; the buffers they point to are device memory).  Each out[j] equals
  * what trellis_matvec_axis1 writes for matrix j, bit for bit.  The launch
  * spans the 16-row groups of all n matrices, so small projections share the
- * machine with the large ones instead of running alone.  No workspace.
+ * machine with the large ones instead of running alone.  No workspace, so
+ * C <= 5120 (one launch holds x in registers); wider rows:
+ * TRELLIS_EUNSUPPORTED.
  */
 int trellis_matvec_axis1_group(const uint32_t* const* codes, const uint16_t* const* scales, void* const* out,
                                const int64_t* R, int n, const uint16_t* x, int out_dtype, int64_t C, int M,
@@ -109,6 +119,8 @@ int trellis_matvec_axis1_group(const uint32_t* const* codes, const uint16_t* con
  *   gcodes, ucodes  uint32 [R, C*k/32];  gscales, uscales fp16 [R]
  *   x               bf16 [M, C];  out bf16 [M, R];  1 <= M <= 4
  *   gate_f32, up_f32  optional f32 [M, R] copies of the raw sums (NULL = none)
+ * Workspace as for trellis_matvec_axis1 (C > 5120 only), twice the size:
+ * gate and up partials per column chunk.
  */
 size_t trellis_gateup_swiglu_workspace_bytes(int64_t R, int64_t C, int M, int k, int L, int T);
 int trellis_gateup_swiglu(const uint32_t* gcodes, const uint16_t* gscales, const uint32_t* ucodes,
@@ -137,10 +149,10 @@ int trellis_matvec_axis0(const uint32_t* codes, const uint16_t* scales, const ui
  *   out    = down(hidden)                 (trellis_matvec_axis0, bf16)
  * on one stream with no host round trip; gate and up are axis-1 matrices
  * [R, C], down is stored transposed (axis 0) as W_down^T [R, C_out].
- * Source: mlx-bun 0.2.0 -> 0.4.0 diff (page 55), the MLP forward of the
- * Qwen layer: for at most TRELLIS_MATVEC_MAX_M rows and eligible gate/up
- * projections, the fused gate/up SwiGLU kernel, then the down projection of
- * the hidden vectors.
+ * Source: mlx-bun 0.2.0 -> 0.3.0 diff (page 42), src/model/qwen3_5.ts,
+ * Qwen3MLP (down of silu(gate) * up); the fused gate/up SwiGLU kernel it
+ * runs for at most TRELLIS_MATVEC_MAX_M rows is the GATEUP kernel of
+ * trellis-linear.ts on the mlx-bun 0.2.0 -> 0.4.0 diff (page 55).
  *   gcodes, ucodes uint32 [R, C*k_gu/32];  gscales, uscales fp16 [R]
  *   dcodes uint32 [R, C_out*k_down/32];   dscales fp16 [R]
  *   x bf16 [M, C];  out bf16 [M, C_out];  1 <= M <= 4
@@ -197,10 +209,20 @@ int trellis_expand_bf16_il(const uint32_t* codes, const uint16_t* scales, uint16
  * where wb is the expansion weight of trellis_expand_bf16; f32 accumulation.
  * Source: trellis-tiled-prefill.ts (page 56) and the expand-then-matmul
  * fallback of TrellisLinear.forward (page 55).
+ * For M <= TRELLIS_MATVEC_MAX_M this is also the matvec contract of the
+ * pages' decode variants 0-3 (trellis-linear.ts file header and HEADER
+ * TRELLIS_ROUND, page 55): every weight rounded to bf16 (value * scale),
+ * products with x summed in f32, the sum cast to bf16.  The matvec entry
+ * points keep the default numerics (f32 weights); this call gives the
+ * bf16-weight result of the same layer.
  *   codes uint32 [R, C*k/32];  scales fp16 [R];  x bf16 [M, C];  out bf16 [M, R]
  *   M >= 1;  algo = TRELLIS_PREFILL_FUSED, TRELLIS_PREFILL_EXPAND_GEMM or
  *   TRELLIS_PREFILL_AUTO.
- * The EXPAND_GEMM workspace holds the bf16 [R, C] expansion.  The FUSED
+ * The EXPAND_GEMM workspace holds the bf16 [R, C] expansion and the GEMM's
+ * own scratch; the GEMM runs hipBLASLt's top heuristic for the shape until
+ * trellis_prefill_tune picks the fastest candidate.  The GEMM plan is made
+ * before the expansion is launched, so a GEMM that cannot be planned
+ * launches nothing.  The FUSED
  * workspace holds x rewritten in the MFMA operand order (ceil(M/32)*32*C*2
  * bytes), then f32 partial sums: for M <= 64 those of the column chunks the
  * weight rows are split into ([S][M][R]); above, the partial tiles of output
@@ -228,9 +250,9 @@ int trellis_prefill(const uint32_t* codes, const uint16_t* scales, const uint16_
  *   x bf16 [M, R_in];  out bf16 [M, C_out];  M >= 1
  * algo:
  *   TRELLIS_PREFILL_EXPAND_GEMM: the expansion (stored orientation,
- *     R_in*C_out*2 bytes) goes into the workspace, then one bf16 GEMM.  The
- *     first call for a shape times hipBLASLt's candidate kernels on the
- *     caller's buffers, as trellis_prefill does.
+ *     R_in*C_out*2 bytes) goes into the workspace, then one bf16 GEMM (the
+ *     top heuristic until trellis_prefill_axis0_tune picks), planned before
+ *     anything is launched, as in trellis_prefill.
  *   TRELLIS_PREFILL_FUSED: the fused kernel of trellis_prefill with the
  *     outputs C_out as the tile's weight rows and the stored rows R_in as
  *     the contraction; each weight is decoded once per 128 (M <= 256) or
@@ -239,12 +261,46 @@ int trellis_prefill(const uint32_t* codes, const uint16_t* scales, const uint16_
  *     then returns 0).  Workspace: x in operand order, then f32 partial
  *     tiles, as for trellis_prefill.
  *   TRELLIS_PREFILL_AUTO: one of the two (see its definition).
+ * At M <= TRELLIS_MATVEC_MAX_M: the variants 0-3 (bf16-weight) result of
+ * the axis-0 matvec, as for trellis_prefill.
  */
 size_t trellis_prefill_axis0_workspace_bytes(int64_t R_in, int64_t C_out, int64_t M, int k, int L, int T,
                                              int algo);
 int trellis_prefill_axis0(const uint32_t* codes, const uint16_t* scales, const uint16_t* x, uint16_t* out,
                           int64_t R_in, int64_t C_out, int64_t M, int k, int L, int T, int algo,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * trellis_prefill_axis0_il -- trellis_prefill_axis0 on the block-interleaved
+ * k = 3 layout (codes [C_out/512, R_in, 48], see trellis_matvec_axis0_il);
+ * same algorithms, workspace (trellis_prefill_axis0_workspace_bytes) and
+ * result bits as the row-major call on the same symbols.
+ * Source: trellis-splitk-prefill.ts (page 56), the INTERLEAVE addressing of
+ * its partial kernel; trellis-linear.ts (page 55) file header.
+ */
+int trellis_prefill_axis0_il(const uint32_t* codes, const uint16_t* scales, const uint16_t* x, uint16_t* out,
+                             int64_t R_in, int64_t C_out, int64_t M, int k, int L, int T, int algo,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * trellis_prefill_tune / trellis_prefill_axis0_tune -- the EXPAND_GEMM
+ * algorithm of trellis_prefill / trellis_prefill_axis0, once, after timing
+ * every hipBLASLt candidate GEMM for this shape on the caller's buffers.
+ * The fastest becomes the GEMM that later EXPAND_GEMM calls of the same
+ * shape on this device enqueue (graph captures included).  These two calls
+ * SYNCHRONISE the host (they wait for the timing runs) and are meant for
+ * set-up, outside any stream capture.  Arguments, workspace and errors as
+ * for the call they tune with algo = TRELLIS_PREFILL_EXPAND_GEMM; out
+ * receives that call's result.  Which candidate wins can differ between
+ * processes, and with it the GEMM's summation order: results stay within
+ * the same contract, not bit-identical across tuned processes.
+ */
+int trellis_prefill_tune(const uint32_t* codes, const uint16_t* scales, const uint16_t* x, uint16_t* out,
+                         int64_t R, int64_t C, int64_t M, int k, int L, int T, void* workspace,
+                         size_t workspace_bytes, void* stream);
+int trellis_prefill_axis0_tune(const uint32_t* codes, const uint16_t* scales, const uint16_t* x, uint16_t* out,
+                               int64_t R_in, int64_t C_out, int64_t M, int k, int L, int T, void* workspace,
+                               size_t workspace_bytes, void* stream);
 
 /*
  * trellis_decode_states -- test export of the decode primitive: for every

@@ -116,15 +116,22 @@ def test_expand_and_decode_reject_on_host():
 
 def test_tolerance_helpers():
     o = np.array([1.0, -2.5, 3.0e-3, 0.0, 100.0])
-    assert tol.f32_rel_error(o * (1 + 5e-6), o).max() <= 1e-5
-    assert tol.f32_rel_error(o * (1 + 5e-5), o).max() > 1e-5
+    a = np.abs(o)                               # no cancellation: the floor is |o|
+    assert tol.f32_rel_error(o * (1 + 5e-6), o, a).max() <= 1e-5
+    assert tol.f32_rel_error(o * (1 + 5e-5), o, a).max() > 1e-5
     bits = tol.bf16_bits_from_f64(o)
-    assert not tol.bf16_band_violations(bits, o).any()
-    assert not tol.bf16_band_violations(bits + np.uint16(1), o).any()       # one ulp away (positive values)
+    assert not tol.bf16_band_violations(bits, o, a).any()
+    assert not tol.bf16_band_violations(bits + np.uint16(1), o, a).any()    # one ulp away (positive values)
     two = bits.copy()
     two[0] += 2
-    assert tol.bf16_band_violations(two, o)[0]
+    assert tol.bf16_band_violations(two, o, a)[0]
     assert tol.bf16_key(np.array([0x8000], np.uint16))[0] == tol.bf16_key(np.array([0], np.uint16))[0]
+    # a cancelling sum is measured against 2^-6 of its terms: an error of 1e-5 / 64 * a passes, 1e-5 / 32 * a
+    # does not
+    o2, a2 = np.array([1e-9]), np.array([64.0])
+    assert tol.f32_rel_error(o2 + 0.99e-5, o2, a2)[0] <= 1e-5
+    assert tol.f32_rel_error(o2 + 2e-5, o2, a2)[0] > 1e-5
+    assert abs(tol.roundoff_units(o2 + 64 * 2.0 ** -24, o2, a2) - 1.0) < 1e-9
 
 
 def call_mlp(x=FAKE, out=FAKE, hidden=None, R=1024, C=2048, C_out=1024, M=2, kg=2, kd=3, ws=None, wsb=0):

@@ -66,8 +66,8 @@ def test_axis0_interleaved(R, C, M):
     got = tq.matvec_axis0(dil, ds, dx, K, out_dtype=torch.float32)
     ref = tq.matvec_axis0(drm, ds, dx, K, out_dtype=torch.float32)
     assert torch.equal(got.view(torch.int32), ref.view(torch.int32))
-    tol.assert_f32_close(got.cpu().numpy(), oracle.matvec_axis0(codes, scales, x, M, R, C, K, L, T),
-                         f"axis0 interleaved R={R} C={C} M={M}")
+    want, cond = oracle.matvec_axis0(codes, scales, x, M, R, C, K, L, T, with_abs=True)
+    tol.assert_f32_close(got.cpu().numpy(), want, cond, f"axis0 interleaved R={R} C={C} M={M}")
     got16 = tq.matvec_axis0(dil, ds, dx, K)
     assert torch.equal(got16.view(torch.int16), tq.matvec_axis0(drm, ds, dx, K).view(torch.int16))
 
@@ -81,3 +81,30 @@ def test_axis0_interleaved_workload_17408x5120_k3():
         got = tq.matvec_axis0(dil, ds, dx[:M], K)
         ref = tq.matvec_axis0(drm, ds, dx[:M], K)
         assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), M
+
+
+@pytest.mark.parametrize("algo", [tq.PREFILL_FUSED, tq.PREFILL_EXPAND_GEMM, tq.PREFILL_AUTO])
+@pytest.mark.parametrize("R,C,M", [(384, 512, 40), (640, 1536, 300), (128, 1024, 5)])
+def test_prefill_axis0_interleaved(algo, R, C, M):
+    # the axis-0 prefill on block-interleaved codes: bit-identical to the row-major call, and the oracle
+    rng = np.random.default_rng(5 * R + C + M + algo)
+    codes, scales = ti.codes(rng, R, C, K), ti.scales(rng, R)
+    x = ti.activations(rng, M, R)
+    ds, dx = _d(scales, torch.float16), _d(x, torch.bfloat16)
+    got = tq.prefill_axis0(_d(interleave(codes, R, C), torch.int32), ds, dx, K, algo=algo)
+    ref = tq.prefill_axis0(_d(codes, torch.int32), ds, dx, K, algo=algo)
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+    want, cond = oracle.prefill_axis0_sums(codes, scales, x, M, R, C, K, L, T, np.arange(M), np.arange(C),
+                                           with_abs=True)
+    tol.assert_bf16_close(_u16(got), want, cond, f"prefill axis0 interleaved R={R} C={C} M={M} algo={algo}")
+
+
+def test_prefill_axis0_interleaved_down_17408x5120_k3():
+    m = ti.axis0().mats[0]
+    x = _d(ti.activations(np.random.default_rng(3), 512, m.R), torch.bfloat16)
+    ds = _d(m.scales, torch.float16)
+    dil, drm = _d(interleave(m.codes, m.R, m.C), torch.int32), _d(m.codes, torch.int32)
+    for algo in (tq.PREFILL_FUSED, tq.PREFILL_EXPAND_GEMM):
+        got = tq.prefill_axis0(dil, ds, x, K, algo=algo)
+        ref = tq.prefill_axis0(drm, ds, x, K, algo=algo)
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), algo

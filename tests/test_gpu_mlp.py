@@ -40,12 +40,12 @@ def check_mlp(g, u, d, x, R, C, C_out, M, k_gu, k_down, what, want_gu=None):
     out2 = tq.mlp_decode(dg, dgs, du, dus, dd, dds, dx, k_gu, k_down)
     torch.cuda.synchronize()
     if want_gu is None:
-        want_gu = oracle.gateup_swiglu(g.codes, g.scales, u.codes, u.scales, x, M, R, C, k_gu, L, T)
-    gw, uw, _ = want_gu
+        want_gu = oracle.gateup_swiglu(g.codes, g.scales, u.codes, u.scales, x, M, R, C, k_gu, L, T, with_abs=True)
+    gw, uw, _, ga, ua = want_gu
     h = _u16(hidden)
-    tol.assert_swiglu_close(h, gw[:M], uw[:M], what + " hidden")
-    want = oracle.matvec_axis0(d.codes, d.scales, h, M, R, C_out, k_down, L, T)
-    tol.assert_bf16_close(_u16(out), want, what + " out")
+    tol.assert_swiglu_close(h, gw[:M], uw[:M], ga[:M], ua[:M], what + " hidden")
+    want, cond = oracle.matvec_axis0(d.codes, d.scales, h, M, R, C_out, k_down, L, T, with_abs=True)
+    tol.assert_bf16_close(_u16(out), want, cond, what + " out")
     assert np.array_equal(_u16(out), _u16(out2)), what + ": hidden in the workspace changes the output"
 
 
@@ -76,7 +76,8 @@ def mlp_workload():
     w = ti.gateup()
     g, u = w.mats
     d = ti.axis0().mats[0]                      # stored W_down^T [17408, 5120], k = 3
-    want_gu = oracle.gateup_swiglu(g.codes, g.scales, u.codes, u.scales, w.x[0], 4, g.R, g.C, g.k, L, T)
+    want_gu = oracle.gateup_swiglu(g.codes, g.scales, u.codes, u.scales, w.x[0], 4, g.R, g.C, g.k, L, T,
+                                   with_abs=True)
     return w, d, want_gu
 
 

@@ -35,7 +35,8 @@ EXPORTS = (
     "trellis_mlp_decode_workspace_bytes", "trellis_mlp_decode",
     "trellis_matvec_axis0_il", "trellis_expand_bf16_il",
     "trellis_expand_bf16", "trellis_prefill_workspace_bytes", "trellis_prefill",
-    "trellis_prefill_axis0_workspace_bytes", "trellis_prefill_axis0",
+    "trellis_prefill_axis0_workspace_bytes", "trellis_prefill_axis0", "trellis_prefill_axis0_il",
+    "trellis_prefill_tune", "trellis_prefill_axis0_tune",
     "trellis_decode_states", "trellis_last_error", "trellis_version",
 )
 
@@ -83,6 +84,11 @@ def load_library():
         "trellis_prefill_axis0_workspace_bytes": (_sz, [_i64, _i64, _i64, _int, _int, _int, _int]),
         "trellis_prefill_axis0": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int, _int,
                                          _vp, _sz, _vp]),
+        "trellis_prefill_axis0_il": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int, _int,
+                                            _vp, _sz, _vp]),
+        "trellis_prefill_tune": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int, _vp, _sz, _vp]),
+        "trellis_prefill_axis0_tune": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int, _vp, _sz,
+                                              _vp]),
         "trellis_decode_states": (_int, [_vp, _i64, _i64, _int, _int, _int, _vp, _vp, _vp, _vp]),
         "trellis_last_error": (ctypes.c_char_p, []),
         "trellis_version": (ctypes.c_char_p, []),
@@ -336,8 +342,10 @@ def expand_bf16(codes, scales, k, L=12, T=256, out=None):
     return out
 
 
-def prefill(codes, scales, x, k, L=12, T=256, algo=PREFILL_FUSED, out=None, workspace=None):
-    """bf16 [M, R] = x [M, C] times the bf16 expansion of the axis-1 codes."""
+def prefill(codes, scales, x, k, L=12, T=256, algo=PREFILL_FUSED, out=None, workspace=None, tune=False):
+    """bf16 [M, R] = x [M, C] times the bf16 expansion of the axis-1 codes.
+    tune=True runs trellis_prefill_tune (expand + GEMM after timing the GEMM
+    candidates; synchronises the host) instead of trellis_prefill."""
     _need(codes, "codes", _CODES, 2)
     _need(scales, "scales", (torch.float16,), 1)
     _need(x, "x", (torch.bfloat16,), 2)
@@ -348,30 +356,48 @@ def prefill(codes, scales, x, k, L=12, T=256, algo=PREFILL_FUSED, out=None, work
         raise ValueError(f"x has {x.shape[1]} features, codes encode {C}")
     out = _out(out, "out", (M, R), (torch.bfloat16,), x.device)
     lib = load_library()
+    if tune:
+        algo = PREFILL_EXPAND_GEMM
     ws, wsb = _workspace(lib.trellis_prefill_workspace_bytes(R, C, M, k, L, T, algo), x.device,
                          workspace)
-    _check(lib.trellis_prefill(_ptr(codes), _ptr(scales), _ptr(x), _ptr(out), R, C, M, k, L, T, algo,
-                               _ptr(ws), wsb, _stream(x.device)))
+    if tune:
+        _check(lib.trellis_prefill_tune(_ptr(codes), _ptr(scales), _ptr(x), _ptr(out), R, C, M, k, L, T,
+                                        _ptr(ws), wsb, _stream(x.device)))
+    else:
+        _check(lib.trellis_prefill(_ptr(codes), _ptr(scales), _ptr(x), _ptr(out), R, C, M, k, L, T, algo,
+                                   _ptr(ws), wsb, _stream(x.device)))
     return out
 
 
-def prefill_axis0(codes_t, scales, x, k, L=12, T=256, algo=PREFILL_EXPAND_GEMM, out=None, workspace=None):
+def prefill_axis0(codes_t, scales, x, k, L=12, T=256, algo=PREFILL_EXPAND_GEMM, out=None, workspace=None,
+                  tune=False):
     """out[m, c] = bf16(sum_r wb(r, c) x[m, r]) for a matrix stored transposed
-    (axis 0): codes_t [R_in, C_out*k/32], x bf16 [M, R_in]; expand + GEMM, or
-    the fused decode-to-LDS MFMA kernel (R_in a multiple of 128)."""
-    _need(codes_t, "codes", _CODES, 2)
+    (axis 0): codes_t [R_in, C_out*k/32] (or for k = 3 the block-interleaved
+    [C_out/512, R_in, 48]), x bf16 [M, R_in]; expand + GEMM, or the fused
+    decode-to-LDS MFMA kernel (R_in a multiple of 128).  tune=True runs
+    trellis_prefill_axis0_tune (row-major codes; synchronises the host)."""
+    _need(codes_t, "codes", _CODES, codes_t.dim() if codes_t.dim() == 3 else 2)
     _need(scales, "scales", (torch.float16,), 1)
     _need(x, "x", (torch.bfloat16,), 2)
-    R, C = _geometry(codes_t, k)
+    R, C, il = _axis0_geometry(codes_t, k)
     _rows(scales, R)
     M = x.shape[0]
     if x.shape[1] != R:
         raise ValueError(f"x has {x.shape[1]} features, stored rows are {R}")
     out = _out(out, "out", (M, C), (torch.bfloat16,), x.device)
     lib = load_library()
+    if tune:
+        if il:
+            raise ValueError("tune takes row-major codes (the GEMM it tunes is the same for both layouts)")
+        algo = PREFILL_EXPAND_GEMM
     ws, wsb = _workspace(lib.trellis_prefill_axis0_workspace_bytes(R, C, M, k, L, T, algo), x.device, workspace)
-    _check(lib.trellis_prefill_axis0(_ptr(codes_t), _ptr(scales), _ptr(x), _ptr(out), R, C, M, k, L, T, algo,
-                                     _ptr(ws), wsb, _stream(x.device)))
+    if tune:
+        _check(lib.trellis_prefill_axis0_tune(_ptr(codes_t), _ptr(scales), _ptr(x), _ptr(out), R, C, M, k, L, T,
+                                              _ptr(ws), wsb, _stream(x.device)))
+        return out
+    fn = lib.trellis_prefill_axis0_il if il else lib.trellis_prefill_axis0
+    _check(fn(_ptr(codes_t), _ptr(scales), _ptr(x), _ptr(out), R, C, M, k, L, T, algo, _ptr(ws), wsb,
+              _stream(x.device)))
     return out
 
 

@@ -82,12 +82,20 @@ int check_workspace(const char* fn, const void* ws, size_t have, size_t need) {
   return check_ptr(fn, "workspace", ws, 256);
 }
 
-// The axis-1 kernel keeps x in registers (C <= 5120) and a ring of 16-row
-// code tiles in LDS; wider rows are not supported.
+// The axis-1 kernel keeps x in registers and a ring of 16-row code tiles in
+// LDS, 5120 columns per launch; wider rows run as column chunks.
 int check_axis1_shape(const char* fn, int64_t R, int64_t C, int M, int k, bool gateup) {
   if (!trellis::axis1_supported(R, C, M, k, gateup))
-    return fail(TRELLIS_EUNSUPPORTED, "%s: C=%lld (M=%d, k=%d) exceeds the register / LDS staging limit (C <= 5120)",
+    return fail(TRELLIS_EUNSUPPORTED, "%s: C=%lld (M=%d, k=%d) does not fit the kernel's register / LDS plan",
                 fn, (long long)C, M, k);
+  return TRELLIS_OK;
+}
+
+// The block-interleaved k = 3 layout of axis-0 matrices: codes [C/512, R, 48].
+int check_interleaved(const char* fn, int64_t C, int k) {
+  if (k != 3) return fail(TRELLIS_EUNSUPPORTED, "%s: the interleaved layout is k=3 only (k=%d)", fn, k);
+  if (C % 512 != 0)
+    return fail(TRELLIS_EINVAL, "%s: C=%lld not a multiple of 512 (two blocks per group)", fn, (long long)C);
   return TRELLIS_OK;
 }
 
@@ -113,10 +121,9 @@ constexpr int kGemmCandidates = 16;
 struct GemmPlan {
   hipblasLtMatmulDesc_t desc = nullptr;
   hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, lc = nullptr;
-  hipblasLtMatmulAlgo_t algo;                                  // in use
+  hipblasLtMatmulAlgo_t algo;                                  // in use: cand[0] until a tune call picks
   hipblasLtMatmulHeuristicResult_t cand[kGemmCandidates];      // hipBLASLt's candidates, best first
   int ncand = 0;
-  bool tuned = false;
 };
 
 std::mutex g_lt_mu;
@@ -127,12 +134,14 @@ std::map<std::tuple<int, int64_t, int64_t, int64_t, int>, GemmPlan> g_lt_plans;
 // Column-major view: D (R x M, ld R) = op_T(A: C x R, ld C) * op_N(B: C x M, ld C).
 // Axis 0 (nn = true): out[M, R] = x[M, C] * W[C, R], W the stored [C, R]
 // expansion.  Column-major view: D (R x M, ld R) = op_N(A: R x C, ld R) * op_N(B: C x M, ld C).
-int gemm_bf16(const char* fn, const uint16_t* W, const uint16_t* x, uint16_t* out, int64_t R, int64_t C,
-              int64_t M, bool nn, void* ws, size_t ws_bytes, hipStream_t stream) {
+//
+// The handle and plan of a shape are made before anything is launched, so
+// a failure here leaves the stream untouched.  Caller holds g_lt_mu.
+int gemm_plan_locked(const char* fn, int64_t R, int64_t C, int64_t M, bool nn, GemmPlan** plan,
+                     hipblasLtHandle_t* handle) {
   int dev = 0;
   hipError_t he = hipGetDevice(&dev);
   if (he != hipSuccess) return hip_status(fn, he);
-  std::lock_guard<std::mutex> lock(g_lt_mu);
   auto hit = g_lt_handles.find(dev);
   if (hit == g_lt_handles.end()) {
     hipblasLtHandle_t h = nullptr;
@@ -172,45 +181,74 @@ int gemm_bf16(const char* fn, const uint16_t* W, const uint16_t* x, uint16_t* ou
     p.ncand = returned;
     pit = g_lt_plans.emplace(key, p).first;
   }
-  // First uncaptured call for this shape: time every candidate on the
-  // caller's buffers (each writes the same product into out; the call below
-  // writes it once more) and keep the fastest.  Under stream capture nothing
-  // can be timed, so the top heuristic runs until an uncaptured call tunes.
-  GemmPlan& tp = pit->second;
-  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-  const bool capturing = hipStreamIsCapturing(stream, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone;
-  if (!tp.tuned && !capturing) {
-    tp.tuned = true;
-    hipEvent_t e0 = nullptr, e1 = nullptr;
-    if (tp.ncand > 1 && hipEventCreate(&e0) == hipSuccess && hipEventCreate(&e1) == hipSuccess) {
-      const float alpha = 1.0f, beta = 0.0f;
-      float best = -1.0f;
-      for (int i = 0; i < tp.ncand; ++i) {
-        if (tp.cand[i].workspaceSize > ws_bytes) continue;
-        bool run_ok = hipblasLtMatmul(h, tp.desc, &alpha, W, tp.la, x, tp.lb, &beta, out, tp.lc, out, tp.lc,
-                                      &tp.cand[i].algo, ws, ws_bytes, stream) == HIPBLAS_STATUS_SUCCESS;
-        run_ok = run_ok && hipEventRecord(e0, stream) == hipSuccess;
-        for (int rep = 0; run_ok && rep < 3; ++rep)
-          run_ok = hipblasLtMatmul(h, tp.desc, &alpha, W, tp.la, x, tp.lb, &beta, out, tp.lc, out, tp.lc,
-                                   &tp.cand[i].algo, ws, ws_bytes, stream) == HIPBLAS_STATUS_SUCCESS;
-        run_ok = run_ok && hipEventRecord(e1, stream) == hipSuccess && hipEventSynchronize(e1) == hipSuccess;
-        float ms = 0.0f;
-        if (run_ok && hipEventElapsedTime(&ms, e0, e1) == hipSuccess && (best < 0.0f || ms < best)) {
-          best = ms;
-          tp.algo = tp.cand[i].algo;
-        }
-      }
-    }
-    if (e0) hipEventDestroy(e0);
-    if (e1) hipEventDestroy(e1);
-    (void)hipGetLastError();
-  }
+  *plan = &pit->second;
+  *handle = h;
+  return TRELLIS_OK;
+}
+
+// Enqueue the GEMM with the plan's algorithm (no host synchronisation).
+// Caller holds g_lt_mu.
+int gemm_run_locked(const char* fn, const GemmPlan& p, hipblasLtHandle_t h, const uint16_t* W, const uint16_t* x,
+                    uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream) {
   const float alpha = 1.0f, beta = 0.0f;
-  const GemmPlan& p = pit->second;
   hipblasStatus_t st = hipblasLtMatmul(h, p.desc, &alpha, W, p.la, x, p.lb, &beta, out, p.lc, out,
                                        p.lc, &p.algo, ws, ws_bytes, stream);
   if (st != HIPBLAS_STATUS_SUCCESS) return fail(TRELLIS_EHIP, "%s: hipblasLtMatmul status %d", fn, (int)st);
   return ok();
+}
+
+// Time every candidate on the caller's buffers (each writes the same
+// product into out) and keep the fastest in the plan.  Synchronises the
+// host; only the explicit tune calls come here.  Caller holds g_lt_mu.
+int gemm_tune_locked(const char* fn, GemmPlan& tp, hipblasLtHandle_t h, const uint16_t* W, const uint16_t* x,
+                     uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+    if (e0) (void)hipEventDestroy(e0);
+    return fail(TRELLIS_EHIP, "%s: hipEventCreate failed", fn);
+  }
+  const float alpha = 1.0f, beta = 0.0f;
+  float best = -1.0f;
+  for (int i = 0; i < tp.ncand; ++i) {
+    if (tp.cand[i].workspaceSize > ws_bytes) continue;
+    bool run_ok = hipblasLtMatmul(h, tp.desc, &alpha, W, tp.la, x, tp.lb, &beta, out, tp.lc, out, tp.lc,
+                                  &tp.cand[i].algo, ws, ws_bytes, stream) == HIPBLAS_STATUS_SUCCESS;
+    run_ok = run_ok && hipEventRecord(e0, stream) == hipSuccess;
+    for (int rep = 0; run_ok && rep < 3; ++rep)
+      run_ok = hipblasLtMatmul(h, tp.desc, &alpha, W, tp.la, x, tp.lb, &beta, out, tp.lc, out, tp.lc,
+                               &tp.cand[i].algo, ws, ws_bytes, stream) == HIPBLAS_STATUS_SUCCESS;
+    run_ok = run_ok && hipEventRecord(e1, stream) == hipSuccess && hipEventSynchronize(e1) == hipSuccess;
+    float ms = 0.0f;
+    if (run_ok && hipEventElapsedTime(&ms, e0, e1) == hipSuccess && (best < 0.0f || ms < best)) {
+      best = ms;
+      tp.algo = tp.cand[i].algo;
+    }
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  const hipError_t le = hipGetLastError();
+  if (best < 0.0f) return fail(TRELLIS_EHIP, "%s: no hipBLASLt candidate ran (%s)", fn, hipGetErrorString(le));
+  return ok();
+}
+
+// Expansion into the workspace, then the GEMM: out = x times the expansion
+// (axis 1: W [R_out, C_con]; axis 0: the stored W^T [C_con, R_out]).  The
+// plan is made first, so a GEMM that cannot be planned launches nothing.
+int expand_gemm(const char* fn, const uint32_t* codes, const uint16_t* scales, const uint16_t* x, uint16_t* out,
+                int64_t R_out, int64_t C_con, int64_t M, int k, bool axis0, int interleave, bool tune,
+                void* workspace, size_t workspace_bytes, hipStream_t s) {
+  std::lock_guard<std::mutex> lock(g_lt_mu);
+  GemmPlan* plan = nullptr;
+  hipblasLtHandle_t h = nullptr;
+  TRY(gemm_plan_locked(fn, R_out, C_con, M, axis0, &plan, &h));
+  uint16_t* wexp = reinterpret_cast<uint16_t*>(workspace);
+  const size_t wexp_bytes = align_up((size_t)R_out * (size_t)C_con * 2, 256);
+  const int64_t er = axis0 ? C_con : R_out, ec = axis0 ? R_out : C_con;   // stored orientation
+  TRY(hip_status(fn, trellis::launch_expand(codes, scales, wexp, er, ec, k, s, interleave)));
+  void* gws = reinterpret_cast<char*>(workspace) + wexp_bytes;
+  const size_t gws_bytes = workspace_bytes - wexp_bytes;
+  if (tune) TRY(gemm_tune_locked(fn, *plan, h, wexp, x, out, gws, gws_bytes, s));
+  return gemm_run_locked(fn, *plan, h, wexp, x, out, gws, gws_bytes, s);
 }
 
 }  // namespace
@@ -223,7 +261,8 @@ const char* trellis_version(void) { return "trellis-mi355x 0.1.0 (gfx950)"; }
 
 size_t trellis_matvec_axis1_workspace_bytes(int64_t R, int64_t C, int M, int k, int L, int T) {
   if (check_geometry("trellis_matvec_axis1_workspace_bytes", R, C, k, L, T) != TRELLIS_OK) return 0;
-  return trellis::axis1_workspace_bytes(R, C, M, k);
+  if (M < 1 || M > TRELLIS_MATVEC_MAX_M) return 0;
+  return trellis::axis1_workspace_bytes(R, C, M, k, false);
 }
 
 int trellis_matvec_axis1(const uint32_t* codes, const uint16_t* scales, const uint16_t* x,
@@ -238,7 +277,7 @@ int trellis_matvec_axis1(const uint32_t* codes, const uint16_t* scales, const ui
   TRY(check_ptr(fn, "scales", scales, 2));
   TRY(check_ptr(fn, "x", x, 16));
   TRY(check_ptr(fn, "out", out, 16));
-  TRY(check_workspace(fn, workspace, workspace_bytes, trellis::axis1_workspace_bytes(R, C, M, k)));
+  TRY(check_workspace(fn, workspace, workspace_bytes, trellis::axis1_workspace_bytes(R, C, M, k, false)));
   TRY(check_axis1_shape(fn, R, C, M, k, false));
   return hip_status(fn, trellis::launch_axis1(codes, scales, nullptr, nullptr, x, out,
                                               out_dtype == TRELLIS_OUT_F32, nullptr, nullptr, R, C,
@@ -262,9 +301,8 @@ int trellis_matvec_axis1_group(const uint32_t* const* codes, const uint16_t* con
     TRY(check_ptr(fn, "scales[j]", scales[j], 2));
     TRY(check_ptr(fn, "out[j]", out[j], 16));
   }
-  TRY(check_axis1_shape(fn, R[0], C, M, k, false));
   if (!trellis::axis1_group_supported(R, n, C, M, k))
-    return fail(TRELLIS_EUNSUPPORTED, "%s: %d matrices of C=%lld exceed the LDS staging limit", fn, n,
+    return fail(TRELLIS_EUNSUPPORTED, "%s: %d matrices of C=%lld do not fit one launch (C <= 5120)", fn, n,
                 (long long)C);
   return hip_status(fn, trellis::launch_axis1_group(codes, scales, out, R, n, x, out_dtype == TRELLIS_OUT_F32,
                                                     C, M, k, (hipStream_t)stream));
@@ -272,7 +310,8 @@ int trellis_matvec_axis1_group(const uint32_t* const* codes, const uint16_t* con
 
 size_t trellis_gateup_swiglu_workspace_bytes(int64_t R, int64_t C, int M, int k, int L, int T) {
   if (check_geometry("trellis_gateup_swiglu_workspace_bytes", R, C, k, L, T) != TRELLIS_OK) return 0;
-  return trellis::axis1_workspace_bytes(R, C, M, k);
+  if (M < 1 || M > TRELLIS_MATVEC_MAX_M) return 0;
+  return trellis::axis1_workspace_bytes(R, C, M, k, true);
 }
 
 int trellis_gateup_swiglu(const uint32_t* gcodes, const uint16_t* gscales, const uint32_t* ucodes,
@@ -290,7 +329,7 @@ int trellis_gateup_swiglu(const uint32_t* gcodes, const uint16_t* gscales, const
   TRY(check_ptr(fn, "out", out, 16));
   if (gate_f32) TRY(check_ptr(fn, "gate_f32", gate_f32, 4));
   if (up_f32) TRY(check_ptr(fn, "up_f32", up_f32, 4));
-  TRY(check_workspace(fn, workspace, workspace_bytes, trellis::axis1_workspace_bytes(R, C, M, k)));
+  TRY(check_workspace(fn, workspace, workspace_bytes, trellis::axis1_workspace_bytes(R, C, M, k, true)));
   TRY(check_axis1_shape(fn, R, C, M, k, true));
   return hip_status(fn, trellis::launch_axis1(gcodes, gscales, ucodes, uscales, x, out, 0, gate_f32,
                                               up_f32, R, C, M, k, workspace, (hipStream_t)stream));
@@ -328,7 +367,7 @@ size_t trellis_mlp_decode_workspace_bytes(int64_t R, int64_t C, int64_t C_out, i
   if (check_geometry("trellis_mlp_decode_workspace_bytes", R, C_out, k_down, L, T) != TRELLIS_OK) return 0;
   if (M < 1 || M > TRELLIS_MATVEC_MAX_M) return 0;
   // the bf16 hidden vectors [M, R], then the down projection's own workspace
-  return align_up((size_t)M * (size_t)R * 2, 256) + align_up(trellis::axis1_workspace_bytes(R, C, M, k_gu), 256) +
+  return align_up((size_t)M * (size_t)R * 2, 256) + align_up(trellis::axis1_workspace_bytes(R, C, M, k_gu, true), 256) +
          trellis::axis0_workspace_bytes(R, C_out, M, k_down);
 }
 
@@ -358,20 +397,12 @@ int trellis_mlp_decode(const uint32_t* gcodes, const uint16_t* gscales, const ui
                       trellis_mlp_decode_workspace_bytes(R, C, C_out, M, k_gu, k_down, L, T)));
   char* ws = reinterpret_cast<char*>(workspace);
   const size_t hb = align_up((size_t)M * (size_t)R * 2, 256);
-  const size_t w1 = align_up(trellis::axis1_workspace_bytes(R, C, M, k_gu), 256);
+  const size_t w1 = align_up(trellis::axis1_workspace_bytes(R, C, M, k_gu, true), 256);
   uint16_t* mid = hidden ? hidden : reinterpret_cast<uint16_t*>(ws);
   hipStream_t s = (hipStream_t)stream;
   TRY(hip_status(fn, trellis::launch_axis1(gcodes, gscales, ucodes, uscales, x, mid, 0, nullptr, nullptr, R, C,
                                            M, k_gu, w1 ? ws + hb : nullptr, s)));
   return hip_status(fn, trellis::launch_axis0(dcodes, dscales, mid, out, 0, R, C_out, M, k_down, ws + hb + w1, s));
-}
-
-// The block-interleaved k = 3 layout of axis-0 matrices: codes [C/512, R, 48].
-int check_interleaved(const char* fn, int64_t C, int k) {
-  if (k != 3) return fail(TRELLIS_EUNSUPPORTED, "%s: the interleaved layout is k=3 only (k=%d)", fn, k);
-  if (C % 512 != 0)
-    return fail(TRELLIS_EINVAL, "%s: C=%lld not a multiple of 512 (two blocks per group)", fn, (long long)C);
-  return TRELLIS_OK;
 }
 
 int trellis_matvec_axis0_il(const uint32_t* codes, const uint16_t* scales, const uint16_t* x,
@@ -445,15 +476,17 @@ size_t trellis_prefill_workspace_bytes(int64_t R, int64_t C, int64_t M, int k, i
   return trellis::prefill_fused_workspace_bytes(R, C, M);
 }
 
-int trellis_prefill(const uint32_t* codes, const uint16_t* scales, const uint16_t* x,
-                    uint16_t* out, int64_t R, int64_t C, int64_t M, int k, int L, int T, int algo,
-                    void* workspace, size_t workspace_bytes, void* stream) {
-  const char* fn = "trellis_prefill";
+namespace {
+
+int prefill_common(const char* fn, const uint32_t* codes, const uint16_t* scales, const uint16_t* x,
+                   uint16_t* out, int64_t R, int64_t C, int64_t M, int k, int L, int T, int& algo, bool tune,
+                   void* workspace, size_t workspace_bytes) {
   TRY(check_geometry(fn, R, C, k, L, T));
   TRY(check_m(fn, M, kMaxDim - 1));
   if (M * C >= kMaxElems || M * R >= kMaxElems)
     return fail(TRELLIS_EINVAL, "%s: M=%lld too large", fn, (long long)M);
   if (M > (int64_t)65535 * 128) return fail(TRELLIS_EINVAL, "%s: M=%lld too large", fn, (long long)M);
+  if (tune) algo = TRELLIS_PREFILL_EXPAND_GEMM;
   if (algo != TRELLIS_PREFILL_FUSED && algo != TRELLIS_PREFILL_EXPAND_GEMM && algo != TRELLIS_PREFILL_AUTO)
     return fail(TRELLIS_EINVAL, "%s: algo=%d unknown", fn, algo);
   algo = resolve_prefill_algo(algo, R, C, M, k, false);
@@ -461,19 +494,33 @@ int trellis_prefill(const uint32_t* codes, const uint16_t* scales, const uint16_
   TRY(check_ptr(fn, "scales", scales, 2));
   TRY(check_ptr(fn, "x", x, 16));
   TRY(check_ptr(fn, "out", out, 16));
-  const size_t need = trellis_prefill_workspace_bytes(R, C, M, k, L, T, algo);
-  TRY(check_workspace(fn, workspace, workspace_bytes, need));
-  hipStream_t s = (hipStream_t)stream;
   if (algo == TRELLIS_PREFILL_FUSED && !trellis::prefill_fused_supported(R, C, M, k))
     return fail(TRELLIS_EUNSUPPORTED, "%s: fused kernel needs x and codes below 2 GiB (M=%lld R=%lld C=%lld)",
                 fn, (long long)M, (long long)R, (long long)C);
+  return check_workspace(fn, workspace, workspace_bytes, trellis_prefill_workspace_bytes(R, C, M, k, L, T, algo));
+}
+
+}  // namespace
+
+int trellis_prefill(const uint32_t* codes, const uint16_t* scales, const uint16_t* x,
+                    uint16_t* out, int64_t R, int64_t C, int64_t M, int k, int L, int T, int algo,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "trellis_prefill";
+  TRY(prefill_common(fn, codes, scales, x, out, R, C, M, k, L, T, algo, false, workspace, workspace_bytes));
+  hipStream_t s = (hipStream_t)stream;
   if (algo == TRELLIS_PREFILL_FUSED)
     return hip_status(fn, trellis::launch_prefill_fused(codes, scales, x, out, R, C, M, k, workspace, s));
-  uint16_t* wexp = reinterpret_cast<uint16_t*>(workspace);
-  const size_t wexp_bytes = align_up((size_t)R * (size_t)C * 2, 256);
-  TRY(hip_status(fn, trellis::launch_expand(codes, scales, wexp, R, C, k, s)));
-  return gemm_bf16(fn, wexp, x, out, R, C, M, false, reinterpret_cast<char*>(workspace) + wexp_bytes,
-                   workspace_bytes - wexp_bytes, s);
+  return expand_gemm(fn, codes, scales, x, out, R, C, M, k, false, 0, false, workspace, workspace_bytes, s);
+}
+
+int trellis_prefill_tune(const uint32_t* codes, const uint16_t* scales, const uint16_t* x, uint16_t* out,
+                         int64_t R, int64_t C, int64_t M, int k, int L, int T, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  const char* fn = "trellis_prefill_tune";
+  int algo = TRELLIS_PREFILL_EXPAND_GEMM;
+  TRY(prefill_common(fn, codes, scales, x, out, R, C, M, k, L, T, algo, true, workspace, workspace_bytes));
+  return expand_gemm(fn, codes, scales, x, out, R, C, M, k, false, 0, true, workspace, workspace_bytes,
+                     (hipStream_t)stream);
 }
 
 size_t trellis_prefill_axis0_workspace_bytes(int64_t R_in, int64_t C_out, int64_t M, int k, int L, int T,
@@ -488,15 +535,18 @@ size_t trellis_prefill_axis0_workspace_bytes(int64_t R_in, int64_t C_out, int64_
   return align_up((size_t)R_in * (size_t)C_out * 2, 256) + kGemmWorkspace;
 }
 
-int trellis_prefill_axis0(const uint32_t* codes, const uint16_t* scales, const uint16_t* x, uint16_t* out,
-                          int64_t R_in, int64_t C_out, int64_t M, int k, int L, int T, int algo,
-                          void* workspace, size_t workspace_bytes, void* stream) {
-  const char* fn = "trellis_prefill_axis0";
+namespace {
+
+int prefill_axis0_common(const char* fn, const uint32_t* codes, const uint16_t* scales, const uint16_t* x,
+                         uint16_t* out, int64_t R_in, int64_t C_out, int64_t M, int k, int L, int T, int& algo,
+                         bool tune, int interleave, void* workspace, size_t workspace_bytes) {
   TRY(check_geometry(fn, R_in, C_out, k, L, T));
+  if (interleave) TRY(check_interleaved(fn, C_out, k));
   TRY(check_m(fn, M, kMaxDim - 1));
   if (M * C_out >= kMaxElems || M * R_in >= kMaxElems)
     return fail(TRELLIS_EINVAL, "%s: M=%lld too large", fn, (long long)M);
   if (M > (int64_t)65535 * 128) return fail(TRELLIS_EINVAL, "%s: M=%lld too large", fn, (long long)M);
+  if (tune) algo = TRELLIS_PREFILL_EXPAND_GEMM;
   if (algo != TRELLIS_PREFILL_FUSED && algo != TRELLIS_PREFILL_EXPAND_GEMM && algo != TRELLIS_PREFILL_AUTO)
     return fail(TRELLIS_EINVAL, "%s: algo=%d unknown", fn, algo);
   algo = resolve_prefill_algo(algo, C_out, R_in, M, k, true);
@@ -509,16 +559,51 @@ int trellis_prefill_axis0(const uint32_t* codes, const uint16_t* scales, const u
   TRY(check_ptr(fn, "scales", scales, 2));
   TRY(check_ptr(fn, "x", x, 16));
   TRY(check_ptr(fn, "out", out, 16));
-  TRY(check_workspace(fn, workspace, workspace_bytes,
-                      trellis_prefill_axis0_workspace_bytes(R_in, C_out, M, k, L, T, algo)));
-  hipStream_t s = (hipStream_t)stream;
+  return check_workspace(fn, workspace, workspace_bytes,
+                         trellis_prefill_axis0_workspace_bytes(R_in, C_out, M, k, L, T, algo));
+}
+
+int prefill_axis0_run(const char* fn, const uint32_t* codes, const uint16_t* scales, const uint16_t* x,
+                      uint16_t* out, int64_t R_in, int64_t C_out, int64_t M, int k, int algo, bool tune,
+                      int interleave, void* workspace, size_t workspace_bytes, hipStream_t s) {
   if (algo == TRELLIS_PREFILL_FUSED)
-    return hip_status(fn, trellis::launch_prefill_fused(codes, scales, x, out, C_out, R_in, M, k, workspace, s, 1));
-  uint16_t* wexp = reinterpret_cast<uint16_t*>(workspace);     // W^T expanded in stored orientation [R_in, C_out]
-  const size_t wexp_bytes = align_up((size_t)R_in * (size_t)C_out * 2, 256);
-  TRY(hip_status(fn, trellis::launch_expand(codes, scales, wexp, R_in, C_out, k, s)));
-  return gemm_bf16(fn, wexp, x, out, C_out, R_in, M, true, reinterpret_cast<char*>(workspace) + wexp_bytes,
-                   workspace_bytes - wexp_bytes, s);
+    return hip_status(fn, trellis::launch_prefill_fused(codes, scales, x, out, C_out, R_in, M, k, workspace, s, 1,
+                                                        interleave));
+  return expand_gemm(fn, codes, scales, x, out, C_out, R_in, M, k, true, interleave, tune, workspace,
+                     workspace_bytes, s);
+}
+
+}  // namespace
+
+int trellis_prefill_axis0(const uint32_t* codes, const uint16_t* scales, const uint16_t* x, uint16_t* out,
+                          int64_t R_in, int64_t C_out, int64_t M, int k, int L, int T, int algo,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "trellis_prefill_axis0";
+  TRY(prefill_axis0_common(fn, codes, scales, x, out, R_in, C_out, M, k, L, T, algo, false, 0, workspace,
+                           workspace_bytes));
+  return prefill_axis0_run(fn, codes, scales, x, out, R_in, C_out, M, k, algo, false, 0, workspace, workspace_bytes,
+                           (hipStream_t)stream);
+}
+
+int trellis_prefill_axis0_il(const uint32_t* codes, const uint16_t* scales, const uint16_t* x, uint16_t* out,
+                             int64_t R_in, int64_t C_out, int64_t M, int k, int L, int T, int algo,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "trellis_prefill_axis0_il";
+  TRY(prefill_axis0_common(fn, codes, scales, x, out, R_in, C_out, M, k, L, T, algo, false, 1, workspace,
+                           workspace_bytes));
+  return prefill_axis0_run(fn, codes, scales, x, out, R_in, C_out, M, k, algo, false, 1, workspace, workspace_bytes,
+                           (hipStream_t)stream);
+}
+
+int trellis_prefill_axis0_tune(const uint32_t* codes, const uint16_t* scales, const uint16_t* x, uint16_t* out,
+                               int64_t R_in, int64_t C_out, int64_t M, int k, int L, int T, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  const char* fn = "trellis_prefill_axis0_tune";
+  int algo = TRELLIS_PREFILL_EXPAND_GEMM;
+  TRY(prefill_axis0_common(fn, codes, scales, x, out, R_in, C_out, M, k, L, T, algo, true, 0, workspace,
+                           workspace_bytes));
+  return prefill_axis0_run(fn, codes, scales, x, out, R_in, C_out, M, k, algo, true, 0, workspace, workspace_bytes,
+                           (hipStream_t)stream);
 }
 
 int trellis_decode_states(const uint32_t* codes, int64_t R, int64_t C, int k, int L, int T,

@@ -11,13 +11,15 @@
 // as the contraction dimension:
 //   A (16 columns x 32 rows): lane (i, q) decodes output columns 4i .. 4i+3
 //     of a 64-column chunk (one 32-bit funnel window holds their four states)
-//     for stored rows 8q .. 8q+7; the byte sum b = y + 510 of each 1MAD word
-//     becomes an f16 subnormal (b * 2^-24, exact), two rows per register via
-//     v_sad_hi_u8 / v_sad_u8.  Column 4i + j of the chunk is row i of MFMA j.
+//     for stored rows 8q .. 8q+7; each code y becomes an exact f16 integer,
+//     two rows per register (code_pair_y: the byte sums of two 1MAD words
+//     as f16 1026 + b, then one packed add of -1536).  Column 4i + j of the
+//     chunk is row i of MFMA j.
 //   B (32 rows x 16 n): x~[n, r] = scale[r] * x[n, r] (exact in f32) times a
-//     per-workgroup 2^e_n, split into f16 hi (column n) and lo (column 4 + n)
-//     halves, so hi + lo carries ~22 bits of every product operand.
-//   D: f32; 2^-24 * 510 * sum_r x~' is the byte-sum bias, subtracted once.
+//     per-wave 2^e_n, split into f16 hi (column n) and lo (column 4 + n)
+//     halves; hi + lo is exact for every |x~| down to 2^-21 of the wave's
+//     largest (below that, lo falls into f16 subnormals).
+//   D: f32 sums of signed products (no offset to cancel).
 // Work: workgroup (column group g of 256 columns, row split s) with 8 waves;
 // wave w takes the split's 32-row blocks w, w + 8, ... through its own LDS
 // ring (global_load_lds copies, explicit vmcnt waits, no barrier in the
@@ -293,11 +295,6 @@ __global__ __launch_bounds__(kThreads) void axis0_kernel(const uint32_t* __restr
   auto b_operand = [&](lds_u32x4 v) {
     return i < 8 ? __builtin_bit_cast(half8, v) : half8{0, 0, 0, 0, 0, 0, 0, 0};
   };
-  auto load_b = [&](int blk) { return b_operand(lds_read_b128(b_addr(blk))); };
-  // the byte-sum bias over this wave's blocks: 510 * 2^-24 * sum_r B[r][n'] in every row
-  f32x4 bias = f32x4{0.f, 0.f, 0.f, 0.f};
-  const half8 a510 = __builtin_bit_cast(half8, u32x4{0x01FE01FEu, 0x01FE01FEu, 0x01FE01FEu, 0x01FE01FEu});
-  for (int t = 0; t < nmy; ++t) bias = __builtin_amdgcn_mfma_f32_16x16x32_f16(a510, load_b(wave + kWaves * t), bias, 0, 0, 0);
 
   const int my_e = i == 0 ? e0 : i == 1 ? e1 : i == 2 ? e2 : e3;   // partial-sum scale of column n = i
   f32x4 acc[kChunks][4];
@@ -318,7 +315,7 @@ __global__ __launch_bounds__(kThreads) void axis0_kernel(const uint32_t* __restr
     const int blk = wave + kWaves * t;
     half8 Bv;
     const uint8_t* tile = ring + (size_t)(t % NS) * g.slot_bytes + (size_t)(8 * q) * gsr * 16;
-    // 8 rows x 4 columns: windows, then 1MAD words, then row-paired byte sums
+    // 8 rows x 4 columns: windows, then 1MAD words, then row-paired codes
     auto decode_chunk = [&](int ch, const uint32_t (&W)[8][2]) {
       uint32_t st[8][4];
 #pragma unroll
@@ -336,8 +333,7 @@ __global__ __launch_bounds__(kThreads) void axis0_kernel(const uint32_t* __restr
       for (int j = 0; j < 4; ++j) {
         u32x4 A;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          A[e] = __builtin_amdgcn_sad_u8(xw[2 * e][j], 0u, __builtin_amdgcn_sad_hi_u8(xw[2 * e + 1][j], 0u, 0u));
+        for (int e = 0; e < 4; ++e) A[e] = code_pair_y(xw[2 * e][j], xw[2 * e + 1][j]);
         acc[ch][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, A), Bv, acc[ch][j], 0, 0, 0);
       }
     };
@@ -358,14 +354,14 @@ __global__ __launch_bounds__(kThreads) void axis0_kernel(const uint32_t* __restr
     if (next < nmy && next <= t + NS) issue_tile(next++);
   }
 
-  // ---- 5. hi + lo, minus the bias, into LDS; the waves' tiles are added in a
-  // fixed order and scaled by 2^24 / d * 2^-e_n into the partial of this split
+  // ---- 5. hi + lo into LDS; the waves' tiles are added in a
+  // fixed order and scaled by 1 / d * 2^-e_n into the partial of this split
   float* red = scr;                            // f32 [wave][M][kCols]
 #pragma unroll
   for (int ch = 0; ch < kChunks; ++ch)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const f32x4 d = acc[ch][j] - bias;
+      const f32x4 d = acc[ch][j];
       f32x4 tot;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {            // lane n (< 4) adds lane n + 4 (the lo column)
@@ -386,7 +382,7 @@ __global__ __launch_bounds__(kThreads) void axis0_kernel(const uint32_t* __restr
     float v = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) v += red[(w * M + n) * kCols + col];
-    partial[((int64_t)s * M + n) * C + (int64_t)cgi * kCols + col] = ldexpf(v * kRcp, 24);
+    partial[((int64_t)s * M + n) * C + (int64_t)cgi * kCols + col] = v * kRcp;
   }
 }
 

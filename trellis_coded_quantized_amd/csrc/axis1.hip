@@ -8,15 +8,23 @@
 //
 // The sum is refactored so the inner product runs on v_mfma_f32_16x16x32_f16
 // with exact operands:
-//   A (16 rows x 32 k): the byte sum b = y + 510 of each 1MAD word, taken as
-//     an f16 subnormal bit pattern (value b * 2^-24, exact for b <= 1023);
-//     v_sad_hi_u8 / v_sad_u8 write two of them into one register directly.
+//   A (16 rows x 32 k): the code y of each weight as an exact f16 integer:
+//     v_sad_hi_u8 / v_sad_u8 write the byte sums b = y + 510 of two 1MAD
+//     words into one register as f16 1026 + b, and one packed f16 add of
+//     -1536 leaves y (code_pair_y).
 //   B (32 k x 16 n): x'[n, c] = f16(x[n, c] * 2^e), e chosen per vector and
 //     per column slice so the slice's largest |x| lands in [2^14, 2^15); every
 //     bf16 value down to 2^-17 of that maximum is exact in f16.
-//   D: f32, seeded with -510 * 2^-24 * sum_c x'[n, c] (the same MFMA against a
-//     constant A), so D = 2^-24 sum_c y x'.  Each slice's D is scaled back by
-//     2^-e; the sum over slices times 2^24 * scale / d is the output.
+//   D: f32, D = sum_c y x' (signed products: the accumulator carries no
+//     offset, so its rounding is relative to the terms themselves).  Each
+//     slice's D is scaled back by 2^-e; the sum over slices times scale / d
+//     is the output.
+//
+// Rows wider than one launch's register-resident x (C > 5120) run as column
+// chunks of at most 5120 columns, one launch each, into f32 partial outputs
+// in the caller's workspace; axis1_chunk_fold_kernel adds the chunks in
+// order and applies the output cast or the SwiGLU chain.  (The pages' REDUCE
+// and GATEUP kernels loop over any number of runs per row.)
 //
 // Schedule: one workgroup of 8 waves per CU walks row groups b, b + grid, ...
 // (16 A-rows each: 16 output rows, or 8 gate + 8 up rows sharing B).  Wave w
@@ -46,6 +54,7 @@ constexpr int kMaxGroup = 4;           // matrices of one grouped call
 // Geometry shared by the host (LDS sizing) and the kernel.
 struct Axis1Geom {
   int64_t R, C, nrg, row_bytes;
+  int64_t ldx;          // elements between rows of x (C, or the full width for a column chunk)
   // Grouped call (plain axis 1 only): ngroup matrices of the same C and k
   // over the same x.  Matrix j owns the launch's row groups [gend[j - 1],
   // gend[j]) (gend[-1] = 0) and has gR[j] rows; matrix 0 is the kernel's
@@ -72,8 +81,22 @@ __device__ __forceinline__ uint32_t max_abs8(const uint4& v) {
   return r;
 }
 
+// The fused gate/up epilogue: the SwiGLU cast chain of the pages' GATEUP
+// kernel -- gate and up to bf16, sigmoid of the bf16 gate to bf16, silu =
+// bf16(gate * sigmoid), out = bf16(silu * up).  The sigmoid takes e^-|g|, so
+// no exponential overflows: for g below about -88, 1 / (1 + e^-g) would
+// overflow f32 to 0 where the sigmoid is still a bf16 subnormal.
+__device__ __forceinline__ uint16_t swiglu_bf16(float gate, float up) {
+  const float gT = round_bf16(gate);
+  const float uT = round_bf16(up);
+  const float t = expf(-fabsf(gT));
+  const float sig = round_bf16(gT >= 0.0f ? 1.0f / (1.0f + t) : t / (1.0f + t));
+  const float silu = round_bf16(gT * sig);
+  return f32_to_bf16_bits(silu * uT);
+}
+
 // The 32 codes of one run as four MFMA A operands of 8 f16 subnormals
-// (A[u] element e = byte sum of position 8u + e of the run, times 2^-24).
+// (A[u] element e = code y of position 8u + e of the run).
 template <int K>
 __device__ __forceinline__ void decode_run_sub(const uint32_t (&w)[K + 1], uint32_t mul, uint64_t add64,
                                                u32x4 (&A)[4]) {
@@ -84,7 +107,7 @@ __device__ __forceinline__ void decode_run_sub(const uint32_t (&w)[K + 1], uint3
     a[2 * m + 1] = __builtin_amdgcn_alignbit(w[m + 1], w[m], 16);
   }
   // three phases, so no 1MAD result is consumed right after it is produced:
-  // all 32 windows, all 32 1MAD words, then the 16 byte-sum pairs
+  // all 32 windows, all 32 1MAD words, then the 16 code pairs
   uint32_t st[32];
 #pragma unroll
   for (int p = 0; p < 32; ++p) {
@@ -95,8 +118,7 @@ __device__ __forceinline__ void decode_run_sub(const uint32_t (&w)[K + 1], uint3
 #pragma unroll
   for (int p = 0; p < 32; ++p) xw[p] = onemad_word_mad64(st[p], mul, add64);
 #pragma unroll
-  for (int v = 0; v < 16; ++v)
-    A[v >> 2][v & 3] = __builtin_amdgcn_sad_u8(xw[2 * v], 0u, __builtin_amdgcn_sad_hi_u8(xw[2 * v + 1], 0u, 0u));
+  for (int v = 0; v < 16; ++v) A[v >> 2][v & 3] = code_pair_y(xw[2 * v], xw[2 * v + 1]);
 }
 
 // The code words of five run groups of one tile row, read from the ring and
@@ -189,7 +211,7 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int i = lane & 15, q = lane >> 4;
   const int M = g.M;
-  const int64_t R = g.R, C = g.C;
+  const int64_t R = g.R;
   const int NS = g.nslots, nwd = g.nwd, gsw = g.gsw;
   const int nmine = (int)((g.nrg - 1 - (int64_t)blockIdx.x) / gridDim.x + 1);   // grid <= nrg
   uint8_t* ring = smem + (size_t)wave * NS * g.slot_bytes;                      // this wave's slots
@@ -282,7 +304,7 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
     const int p = j * 64 + lane;
     if (p < nxg) {
       const int n = (p >= gx) + (p >= 2 * gx) + (p >= 3 * gx), jj = p - n * gx;
-      __builtin_amdgcn_global_load_lds(x + (int64_t)n * C + (int64_t)rb * 32 + jj * 8, xsl + (size_t)j * 1024,
+      __builtin_amdgcn_global_load_lds(x + (int64_t)n * g.ldx + (int64_t)rb * 32 + jj * 8, xsl + (size_t)j * 1024,
                                        16, 0, 0);
     }
   }
@@ -354,15 +376,9 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
 
   // ---- 3. B operand in registers: lane (n, q) of group gg holds
   // x'[n, run * 32 + 8u .. +7] for run = rb + 4 gg + q (zero past the M
-  // vectors or past the slice, whose A lanes then decode run rb).  The bias
-  // 510 * 2^-24 * sum x'[n, slice] comes from the same MFMA with a constant A
-  // (every element the subnormal 510 * 2^-24) and seeds every accumulator.
+  // vectors or past the slice, whose A lanes then decode run rb).
   half8 B[NG][4];
   int wo[NG], so[NG];
-  f32x4 bacc[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) bacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const half8 a510 = __builtin_bit_cast(half8, u32x4{0x01FE01FEu, 0x01FE01FEu, 0x01FE01FEu, 0x01FE01FEu});
   const int ngw = (per + 3) >> 2;              // groups of four runs (<= NG)
 #pragma unroll
   for (int gg = 0; gg < NG; ++gg) {
@@ -383,12 +399,9 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
   for (int gg = 0; gg < NG; ++gg) {
     const bool keep = (rb + 4 * gg + q < re) && i < M;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 4; ++u)
       if (!keep) B[gg][u] = half8{0, 0, 0, 0, 0, 0, 0, 0};
-      if (gg < ngw) bacc[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a510, B[gg][u], bacc[u], 0, 0, 0);
-    }
   }
-  const f32x4 nbias = -((bacc[0] + bacc[1]) + (bacc[2] + bacc[3]));   // every row of column n: the bias
   const int my_e = i == 0 ? e0 : i == 1 ? e1 : i == 2 ? e2 : e3;     // scale of column n = i
 
   __atomic_signal_fence(__ATOMIC_SEQ_CST);     // the x' reads above stay before any later copy
@@ -405,9 +418,8 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
     wait_vmcnt(nwd * (next - 1 - t));          // tile t has landed (tiles after it may be in flight)
     const uint8_t* trow = ring + (size_t)(t % NS) * g.slot_bytes + (size_t)i * gsw * 16;
     f32x4 acc[4];
-    acc[0] = nbias;
 #pragma unroll
-    for (int u = 1; u < 4; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < 4; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
     auto consume = [&](const uint32_t (&W)[K + 1], const half8 (&Bg)[4]) {
       u32x4 A[4];
       decode_run_sub<K>(W, mul, add64, A);
@@ -445,7 +457,7 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
   }
 
   // ---- 5. one barrier, then every output: the eight slices' partials in a
-  // fixed order, times 2^24 * scale / d, and the epilogue
+  // fixed order, times scale / d, and the epilogue
   lds_barrier();
   const int per_t = M * ROWS;
   for (int idx = tid; idx < nmine * per_t; idx += kThreads) {
@@ -462,19 +474,15 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
     float d0 = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) d0 += pp[w * 64];
-    const float v0 = ldexpf(d0 * (half_bits_to_f32(pick(scales0, g.gscales, gi)[orow]) * kRcp), 24);
+    const float v0 = d0 * (half_bits_to_f32(pick(scales0, g.gscales, gi)[orow]) * kRcp);
     if constexpr (GATEUP) {
       float d1 = 0.f;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) d1 += pp[w * 64 + 8];
-      const float v1 = ldexpf(d1 * (half_bits_to_f32(scales1[orow]) * kRcp), 24);
+      const float v1 = d1 * (half_bits_to_f32(scales1[orow]) * kRcp);
       if (gate_f32) gate_f32[o] = v0;
       if (up_f32) up_f32[o] = v1;
-      const float gT = round_bf16(v0);
-      const float uT = round_bf16(v1);
-      const float sig = round_bf16(1.0f / (1.0f + expf(-gT)));
-      const float silu = round_bf16(gT * sig);
-      reinterpret_cast<uint16_t*>(out)[o] = f32_to_bf16_bits(silu * uT);
+      if (out) reinterpret_cast<uint16_t*>(out)[o] = swiglu_bf16(v0, v1);   // no out: a column chunk
     } else {
       void* om = pick(out, g.gout, gi);
       if (out_f32) reinterpret_cast<float*>(om)[o] = v0;
@@ -483,6 +491,45 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
   }
 }
 
+
+// Sum of the column chunks' f32 partial outputs ([n][M * R], or [n][2][M *
+// R] gate and up for GATEUP), in chunk order, then the output cast or the
+// SwiGLU chain.
+template <bool GATEUP>
+__global__ __launch_bounds__(256) void axis1_chunk_fold_kernel(const float* __restrict__ part, int n, int64_t MR,
+                                                               void* __restrict__ out, int out_f32,
+                                                               float* __restrict__ gate_f32,
+                                                               float* __restrict__ up_f32) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= MR) return;
+  const int64_t stride = GATEUP ? 2 * MR : MR;
+  float v0 = 0.f, v1 = 0.f;
+  for (int j = 0; j < n; ++j) {
+    v0 += part[j * stride + i];
+    if constexpr (GATEUP) v1 += part[j * stride + MR + i];
+  }
+  if constexpr (GATEUP) {
+    if (gate_f32) gate_f32[i] = v0;
+    if (up_f32) up_f32[i] = v1;
+    reinterpret_cast<uint16_t*>(out)[i] = swiglu_bf16(v0, v1);
+  } else if (out_f32) {
+    reinterpret_cast<float*>(out)[i] = v0;
+  } else {
+    reinterpret_cast<uint16_t*>(out)[i] = f32_to_bf16_bits(v0);
+  }
+}
+
+// Column chunks of a row: at most kChunkBlocks 256-column blocks each (x of
+// a chunk stays in registers), the blocks dealt out evenly.
+constexpr int64_t kChunkBlocks = 20;
+
+int64_t axis1_nchunks(int64_t C) {
+  const int64_t nb = C / 256;
+  return nb < 1 ? 1 : (nb + kChunkBlocks - 1) / kChunkBlocks;
+}
+
+// first block of chunk j of n over nb blocks (chunk j is [first(j), first(j + 1)))
+int64_t axis1_chunk_first(int64_t nb, int64_t n, int64_t j) { return j * nb / n; }
 
 // MFMA groups of four runs per wave -> the register-resident B capacity
 // instantiated for it (2 or 5 groups: C <= 2048 or C <= 5120); 0 if C is too
@@ -504,6 +551,7 @@ bool axis1_geom(int64_t R, int64_t C, int M, int k, bool gateup, int64_t grid, A
   g = Axis1Geom{};
   g.R = R;
   g.C = C;
+  g.ldx = C;
   g.M = M;
   g.nrg = nrg_total > 0 ? nrg_total : (R + rows - 1) / rows;
   g.ngroup = 1;
@@ -581,18 +629,56 @@ hipError_t axis1_dispatch_gu(const uint32_t* c0, const uint16_t* s0, const uint3
 }
 
 template <int K>
-hipError_t axis1_main(const uint32_t* c0, const uint16_t* s0, const uint32_t* c1,
-                      const uint16_t* s1, const uint16_t* x, void* out, int out_f32, float* gf,
-                      float* uf, int64_t R, int64_t C, int M, hipStream_t stream) {
-  const bool gu = c1 != nullptr;
-  const int64_t grid = axis1_grid(R, gu);
-  Axis1Geom g;
-  if (!axis1_geom(R, C, M, K, gu, grid, g)) return hipErrorInvalidValue;
-  switch (axis1_ng(C)) {
+hipError_t axis1_launch_geom(const uint32_t* c0, const uint16_t* s0, const uint32_t* c1, const uint16_t* s1,
+                             const uint16_t* x, void* out, int out_f32, float* gf, float* uf, const Axis1Geom& g,
+                             int64_t grid, hipStream_t stream) {
+  switch (axis1_ng(g.C)) {
     case 2: return axis1_dispatch_gu<K, 2>(c0, s0, c1, s1, x, out, out_f32, gf, uf, g, grid, stream);
     case 5: return axis1_dispatch_gu<K, 5>(c0, s0, c1, s1, x, out, out_f32, gf, uf, g, grid, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+template <int K>
+hipError_t axis1_main(const uint32_t* c0, const uint16_t* s0, const uint32_t* c1,
+                      const uint16_t* s1, const uint16_t* x, void* out, int out_f32, float* gf,
+                      float* uf, int64_t R, int64_t C, int M, void* workspace, hipStream_t stream) {
+  const bool gu = c1 != nullptr;
+  const int64_t grid = axis1_grid(R, gu);
+  const int64_t nch = axis1_nchunks(C);
+  if (nch == 1) {
+    Axis1Geom g;
+    if (!axis1_geom(R, C, M, K, gu, grid, g)) return hipErrorInvalidValue;
+    return axis1_launch_geom<K>(c0, s0, c1, s1, x, out, out_f32, gf, uf, g, grid, stream);
+  }
+  // column chunks into f32 partials [chunk][gate/up][M][R], then the fold
+  if (!workspace) return hipErrorInvalidValue;
+  float* part = reinterpret_cast<float*>(workspace);
+  const int64_t MR = (int64_t)M * R, nb = C / 256, per_chunk = (gu ? 2 : 1) * MR;
+  constexpr int WPB = words_per_block(K);
+  for (int64_t j = 0; j < nch; ++j) {
+    const int64_t b0 = axis1_chunk_first(nb, nch, j), b1 = axis1_chunk_first(nb, nch, j + 1);
+    Axis1Geom g;
+    if (!axis1_geom(R, (b1 - b0) * 256, M, K, gu, grid, g)) return hipErrorInvalidValue;
+    g.ldx = C;
+    g.row_bytes = C * K / 8;
+    float* pj = part + j * per_chunk;
+    const uint32_t* cc0 = c0 + b0 * WPB;
+    const uint32_t* cc1 = gu ? c1 + b0 * WPB : nullptr;
+    const uint16_t* xc = x + b0 * 256;
+    const hipError_t e = gu ? axis1_launch_geom<K>(cc0, s0, cc1, s1, xc, nullptr, 0, pj, pj + MR, g, grid, stream)
+                            : axis1_launch_geom<K>(cc0, s0, nullptr, nullptr, xc, pj, 1, nullptr, nullptr, g, grid,
+                                                   stream);
+    if (e != hipSuccess) return e;
+  }
+  const unsigned blocks = (unsigned)((MR + 255) / 256);
+  if (gu)
+    hipLaunchKernelGGL(axis1_chunk_fold_kernel<true>, dim3(blocks), dim3(256), 0, stream, part, (int)nch, MR, out,
+                       0, gf, uf);
+  else
+    hipLaunchKernelGGL(axis1_chunk_fold_kernel<false>, dim3(blocks), dim3(256), 0, stream, part, (int)nch, MR, out,
+                       out_f32, nullptr, nullptr);
+  return hipGetLastError();
 }
 
 template <int K>
@@ -627,7 +713,10 @@ hipError_t axis1_group_main(const uint32_t* const* codes, const uint16_t* const*
 
 }  // namespace
 
-size_t axis1_workspace_bytes(int64_t, int64_t, int, int) { return 0; }
+size_t axis1_workspace_bytes(int64_t R, int64_t C, int M, int, bool gateup) {
+  const int64_t n = axis1_nchunks(C);
+  return n == 1 ? 0 : (size_t)n * (gateup ? 2 : 1) * (size_t)M * (size_t)R * sizeof(float);
+}
 
 int axis1_max_group() { return kMaxGroup; }
 
@@ -652,18 +741,31 @@ hipError_t launch_axis1_group(const uint32_t* const* codes, const uint16_t* cons
 }
 
 bool axis1_supported(int64_t R, int64_t C, int M, int k, bool gateup) {
-  Axis1Geom g;
-  return axis1_geom(R, C, M, k, gateup, axis1_grid(R, gateup), g);
+  if (C % 256 != 0 || C < 256) return false;
+  const int64_t nb = C / 256, n = axis1_nchunks(C);
+  for (int64_t j = 0; j < n; ++j) {            // every chunk's geometry fits
+    const int64_t w = (axis1_chunk_first(nb, n, j + 1) - axis1_chunk_first(nb, n, j)) * 256;
+    Axis1Geom g;
+    if (!axis1_geom(R, w, M, k, gateup, axis1_grid(R, gateup), g)) return false;
+    if (n == 1) break;
+  }
+  return true;
 }
 
 hipError_t launch_axis1(const uint32_t* codes0, const uint16_t* scales0, const uint32_t* codes1,
                         const uint16_t* scales1, const uint16_t* x, void* out, int out_f32,
                         float* gate_f32, float* up_f32, int64_t R, int64_t C, int M, int k,
-                        void*, hipStream_t stream) {
+                        void* workspace, hipStream_t stream) {
   switch (k) {
-    case 2: return axis1_main<2>(codes0, scales0, codes1, scales1, x, out, out_f32, gate_f32, up_f32, R, C, M, stream);
-    case 3: return axis1_main<3>(codes0, scales0, codes1, scales1, x, out, out_f32, gate_f32, up_f32, R, C, M, stream);
-    case 4: return axis1_main<4>(codes0, scales0, codes1, scales1, x, out, out_f32, gate_f32, up_f32, R, C, M, stream);
+    case 2:
+      return axis1_main<2>(codes0, scales0, codes1, scales1, x, out, out_f32, gate_f32, up_f32, R, C, M, workspace,
+                           stream);
+    case 3:
+      return axis1_main<3>(codes0, scales0, codes1, scales1, x, out, out_f32, gate_f32, up_f32, R, C, M, workspace,
+                           stream);
+    case 4:
+      return axis1_main<4>(codes0, scales0, codes1, scales1, x, out, out_f32, gate_f32, up_f32, R, C, M, workspace,
+                           stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -12,6 +12,8 @@ namespace trellis {
 // axis 1 (gate/up when codes1 != nullptr).  The persistent kernel keeps a
 // ring of 16-row code tiles in LDS and x in registers; axis1_supported says
 // whether a shape fits (LDS and register budget), checked on the host.
+// Rows wider than 5120 columns run as column chunks into f32 partials in the
+// workspace (axis1_workspace_bytes), folded by a second kernel.
 constexpr size_t kAxis1MaxLdsBytes = 160 * 1024;
 bool axis1_supported(int64_t R, int64_t C, int M, int k, bool gateup);
 // grouped plain axis-1 call: n <= axis1_max_group() matrices of the same C
@@ -21,7 +23,7 @@ bool axis1_group_supported(const int64_t* R, int n, int64_t C, int M, int k);
 hipError_t launch_axis1_group(const uint32_t* const* codes, const uint16_t* const* scales, void* const* outs,
                               const int64_t* R, int n, const uint16_t* x, int out_f32, int64_t C, int M, int k,
                               hipStream_t stream);
-size_t axis1_workspace_bytes(int64_t R, int64_t C, int M, int k);
+size_t axis1_workspace_bytes(int64_t R, int64_t C, int M, int k, bool gateup);
 hipError_t launch_axis1(const uint32_t* codes0, const uint16_t* scales0, const uint32_t* codes1,
                         const uint16_t* scales1, const uint16_t* x, void* out, int out_f32,
                         float* gate_f32, float* up_f32, int64_t R, int64_t C, int M, int k,
@@ -51,8 +53,10 @@ int device_cus();
 // [C, R k / 32] (the stored transpose), scales [C].
 bool prefill_fused_supported(int64_t R, int64_t C, int64_t M, int k);
 size_t prefill_fused_workspace_bytes(int64_t R, int64_t C, int64_t M, int axis0 = 0);
+// interleave (axis 0, k = 3, R % 512 == 0): codes in the block-interleaved
+// layout [R/512, C, 48].
 hipError_t launch_prefill_fused(const uint32_t* codes, const uint16_t* scales, const uint16_t* x,
                                 uint16_t* out, int64_t R, int64_t C, int64_t M, int k,
-                                void* workspace, hipStream_t stream, int axis0 = 0);
+                                void* workspace, hipStream_t stream, int axis0 = 0, int interleave = 0);
 
 }  // namespace trellis

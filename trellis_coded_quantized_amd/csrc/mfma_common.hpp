@@ -1,6 +1,6 @@
 // mfma_common.hpp -- register-level helpers shared by the MFMA matvec
 // kernels: the 1MAD word in one v_mad_u64_u32, exact f16 code pairs built
-// from the byte sum, and MFMA operand types.
+// from the byte sums, and MFMA operand types.
 #pragma once
 
 #include "trellis_device.hpp"
@@ -23,19 +23,23 @@ __device__ __forceinline__ uint32_t onemad_word_mad64(uint32_t s, uint32_t mul, 
   return (uint32_t)r;
 }
 
-// f16 bits 0x6402 + b encode 1026 + b exactly for a byte sum b in [0, 1020]
-// (binade [1024, 2048) has unit spacing), i.e. y + 1536 with y = b - 510.
-constexpr uint32_t kHalfMagic = 0x6402u;
+// The exact codes y = b - 510 of two 1MAD words as a pair of f16 integers
+// (normal numbers for y != 0; every integer up to 2048 is exact in f16).
+// The byte sums b land in f16 bits directly: v_sad_hi_u8 / v_sad_u8 add them
+// to the pattern 0x6402 in each half, which encodes 1026 + b in the binade
+// [1024, 2048) of unit spacing (b <= 1020 keeps the mantissa below 1024, so
+// no half carries into the other), and one packed f16 add of -1536 leaves
+// y exactly.  Normal operands matter for the MFMA: it aligns its products
+// to the operands' exponents, and a subnormal operand always counts with
+// the smallest normal exponent, so products of subnormal codes with small
+// activations would lose their low bits; integer codes keep each product
+// aligned to its own magnitude.
+constexpr uint32_t kHalfMagic2 = 0x64026402u;   // f16 1026 in both halves
+constexpr uint32_t kNeg1536Pair = 0xE600E600u;  // f16 -1536 in both halves
 
-// Pack the exact codes y(lo), y(hi) of two 1MAD words as an f16 pair:
-// two byte sums land directly in f16 bits, then one packed subtract of 1536
-// (exact: the difference is an integer of magnitude <= 510).
-__device__ __forceinline__ uint32_t code_pair_f16(uint32_t word_lo, uint32_t word_hi,
-                                                  uint32_t magic) {
-  const uint32_t hi = __builtin_amdgcn_sad_u8(word_hi, 0u, magic);
-  const uint32_t both = __builtin_amdgcn_sad_u8(word_lo, 0u, (hi << 16) | magic);
-  half2v h = __builtin_bit_cast(half2v, both);
-  h = h + half2v{(_Float16)-1536.0f, (_Float16)-1536.0f};
+__device__ __forceinline__ uint32_t code_pair_y(uint32_t word_lo, uint32_t word_hi) {
+  const uint32_t both = __builtin_amdgcn_sad_u8(word_lo, 0u, __builtin_amdgcn_sad_hi_u8(word_hi, 0u, kHalfMagic2));
+  const half2v h = __builtin_bit_cast(half2v, both) + __builtin_bit_cast(half2v, kNeg1536Pair);
   return __builtin_bit_cast(uint32_t, h);
 }
 

@@ -145,6 +145,7 @@ struct PrefillPlan {
   int nfull, per;    // rounds: whole tiles; per XCD
   int nsplit, S, seg;
   int U, G;          // stream: steps per workgroup, workgroups
+  int il;            // axis 0: codes in the block-interleaved k = 3 layout [R/512, C, 48]
 };
 
 // Shapes that follow from the x rows BM of a workgroup tile.
@@ -217,6 +218,12 @@ __global__ __launch_bounds__(256, XTile<BM>::kOcc) void prefill_fused_kernel(
   const int row_bytes = ((A0 ? R : C) / kT) * WPB * 4;
   const __amdgpu_buffer_rsrc_t cr =
       __builtin_amdgcn_make_buffer_rsrc((void*)codes, (short)0, (A0 ? C : R) * row_bytes, kRsrcWord3);
+  // axis 0: bytes between stored rows within the tile's block, and the
+  // block's first byte (row-major: rows of R / 256 blocks; interleaved: block
+  // pairs [R / 512][C][2 blocks], so a block's rows are 2 blocks apart)
+  const int rstride = (A0 && plan.il) ? 2 * WPB * 4 : row_bytes;
+  const int nblk0 = n0 / kT;
+  const int bbase = (A0 && plan.il) ? ((nblk0 >> 1) * C * 2 + (nblk0 & 1)) * WPB * 4 : nblk0 * WPB * 4;
   const int cvo = grow * row_bytes;
   float sc = 0.f;
   if constexpr (!A0) sc = half_bits_to_f32(scales[grow]);
@@ -234,7 +241,7 @@ __global__ __launch_bounds__(256, XTile<BM>::kOcc) void prefill_fused_kernel(
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
       const int wj = (w0 + j >= WPB) ? w0 + j - WPB : w0 + j;
-      avo[j] = (uint32_t)(sr * row_bytes + (n0 / kT) * WPB * 4 + wj * 4);
+      avo[j] = (uint32_t)(sr * rstride + bbase + wj * 4);
     }
   }
 
@@ -262,7 +269,7 @@ __global__ __launch_bounds__(256, XTile<BM>::kOcc) void prefill_fused_kernel(
   auto load_w = [&](uint32_t (&dst)[NL], uint32_t& sdst, int t) {
     t = min(t, nsteps - 1);
     if constexpr (A0) {
-      const int so = t * kBK * row_bytes;        // stored row 32 t
+      const int so = t * kBK * rstride;          // stored row 32 t
 #pragma unroll
       for (int j = 0; j < NL; ++j) dst[j] = __builtin_amdgcn_raw_buffer_load_b32(cr, (int)avo[j], so, 0);
       sdst = scales[t * kBK + sr];
@@ -790,8 +797,10 @@ size_t prefill_fused_workspace_bytes(int64_t R, int64_t C, int64_t M, int axis0)
 
 hipError_t launch_prefill_fused(const uint32_t* codes, const uint16_t* scales, const uint16_t* x,
                                 uint16_t* out, int64_t R, int64_t C, int64_t M, int k,
-                                void* workspace, hipStream_t stream, int axis0) {
-  const PrefillPlan p = make_plan(R, C, M);
+                                void* workspace, hipStream_t stream, int axis0, int interleave) {
+  if (interleave && (!axis0 || k != 3 || R % 512 != 0)) return hipErrorInvalidValue;
+  PrefillPlan p = make_plan(R, C, M);
+  p.il = interleave;
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
   uint16_t* xf = reinterpret_cast<uint16_t*>(ws);
   float* part = reinterpret_cast<float*>(ws + ((size_t)prefill_xf_bytes(C, M) + 255) / 256 * 256);

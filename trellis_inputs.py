@@ -44,6 +44,33 @@ def activations(rng: np.random.Generator, M: int, n: int) -> np.ndarray:
     return to_bf16_bits(rng.standard_normal((M, n), dtype=np.float32))
 
 
+def wide_activations(rng: np.random.Generator, M: int, n: int, zero: slice = None,
+                     outliers: int = 3) -> np.ndarray:
+    """bf16 bits [M, n] spread over a wide range: N(0, 1) * 2^U(-20, 20) per
+    element, `outliers` entries per row at +-1e4, and the columns in `zero`
+    (a slice) all zero."""
+    v = rng.standard_normal((M, n)) * np.exp2(rng.uniform(-20.0, 20.0, (M, n)))
+    for m in range(M):
+        idx = rng.choice(n, size=min(outliers, n), replace=False)
+        v[m, idx] = rng.choice([-1e4, 1e4], size=idx.size)
+    if zero is not None:
+        v[:, zero] = 0.0
+    return to_bf16_bits(v.astype(np.float32))
+
+
+def extreme_scales(rng: np.random.Generator, rows: int) -> np.ndarray:
+    """fp16 bits [rows]: mostly U[0.005, 0.02], with every 7th row at one of
+    the fp16 extremes in turn -- the smallest normal 2^-14, a subnormal 2^-20,
+    the largest finite 65504, 1000 -- each but 65504 multiplied by 1 or 1.5
+    at random."""
+    s = rng.uniform(0.005, 0.02, rows)
+    ends = [2.0 ** -14, 2.0 ** -20, 65504.0, 1000.0]
+    for j, r in enumerate(range(0, rows, 7)):
+        e = ends[j % len(ends)]
+        s[r] = e * (1.5 if (e < 60000.0 and rng.integers(0, 2)) else 1.0)
+    return s.astype(np.float16).view(np.uint16)
+
+
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
