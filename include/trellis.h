@@ -144,6 +144,23 @@ int trellis_matvec_axis0(const uint32_t* codes, const uint16_t* scales, const ui
                          int L, int T, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * trellis_matvec_axis0_noalloc -- trellis_matvec_axis0 without a workspace
+ * argument, for callers that cannot allocate device memory (code under
+ * stream capture, tight serving loops, harnesses that forbid hipMalloc).
+ * The split-K partials go to a static device array of 4 MiB that the
+ * library holds on each device until the process ends; nothing is
+ * allocated by the call.  Shapes whose partials (trellis_matvec_axis0_
+ * workspace_bytes) exceed 4 MiB are rejected with TRELLIS_EUNSUPPORTED.
+ * Every call on one device shares that device's array, so calls that
+ * overlap in time on one device (other streams, other threads) race; calls
+ * in one stream's order do not.  Outputs equal trellis_matvec_axis0's bit
+ * for bit.  Arguments and errors otherwise as for trellis_matvec_axis0.
+ */
+int trellis_matvec_axis0_noalloc(const uint32_t* codes, const uint16_t* scales, const uint16_t* x,
+                                 void* out, int out_dtype, int64_t R_in, int64_t C_out, int M, int k,
+                                 int L, int T, void* stream);
+
+/*
  * trellis_mlp_decode -- the MLP of a decoder layer for M <= 4 rows:
  *   hidden = silu(gate(x)) * up(x)        (trellis_gateup_swiglu, bf16)
  *   out    = down(hidden)                 (trellis_matvec_axis0, bf16)

@@ -229,3 +229,16 @@ def test_axis1_group_rejects_on_host():
         st = call(**kw)
         assert st == status and needle in lib.trellis_last_error().decode(), (kw, st, lib.trellis_last_error())
 
+
+
+def test_axis0_noalloc_rejects_on_host():
+    lib = tq.load_library()
+    # partials of 327680 outputs x 4 vectors need more than the 4 MiB static scratch
+    assert lib.trellis_matvec_axis0_noalloc(FAKE, FAKE, FAKE, FAKE, tq.OUT_F32, 32, 327680, 4, 3, 12, 256,
+                                            None) == tq.EUNSUPPORTED
+    assert "static scratch" in lib.trellis_last_error().decode()
+    assert lib.trellis_matvec_axis0_noalloc(None, FAKE, FAKE, FAKE, tq.OUT_F32, 32, 512, 4, 3, 12, 256,
+                                            None) == tq.EINVAL
+    assert lib.trellis_matvec_axis0_noalloc(FAKE, FAKE, FAKE, FAKE, tq.OUT_F32, 32, 512, 5, 3, 12, 256,
+                                            None) == tq.EINVAL
+    assert lib.trellis_matvec_axis0_noalloc(FAKE, FAKE, FAKE, FAKE, 7, 32, 512, 4, 3, 12, 256, None) == tq.EINVAL

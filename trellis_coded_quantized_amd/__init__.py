@@ -31,7 +31,7 @@ GROUP_MAX = 4
 EXPORTS = (
     "trellis_matvec_axis1_workspace_bytes", "trellis_matvec_axis1", "trellis_matvec_axis1_group",
     "trellis_gateup_swiglu_workspace_bytes", "trellis_gateup_swiglu",
-    "trellis_matvec_axis0_workspace_bytes", "trellis_matvec_axis0",
+    "trellis_matvec_axis0_workspace_bytes", "trellis_matvec_axis0", "trellis_matvec_axis0_noalloc",
     "trellis_mlp_decode_workspace_bytes", "trellis_mlp_decode",
     "trellis_matvec_axis0_il", "trellis_expand_bf16_il",
     "trellis_expand_bf16", "trellis_prefill_workspace_bytes", "trellis_prefill",
@@ -71,6 +71,8 @@ def load_library():
         "trellis_matvec_axis0_workspace_bytes": (_sz, [_i64, _i64, _int, _int, _int, _int]),
         "trellis_matvec_axis0": (_int, [_vp, _vp, _vp, _vp, _int, _i64, _i64, _int, _int, _int, _int,
                                         _vp, _sz, _vp]),
+        "trellis_matvec_axis0_noalloc": (_int, [_vp, _vp, _vp, _vp, _int, _i64, _i64, _int, _int, _int, _int,
+                                                _vp]),
         "trellis_mlp_decode_workspace_bytes": (_sz, [_i64, _i64, _i64, _int, _int, _int, _int, _int]),
         "trellis_mlp_decode": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int,
                                       _int, _int, _int, _int, _vp, _sz, _vp]),

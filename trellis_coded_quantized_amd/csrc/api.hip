@@ -361,6 +361,31 @@ int trellis_matvec_axis0(const uint32_t* codes, const uint16_t* scales, const ui
                                               R_in, C_out, M, k, workspace, (hipStream_t)stream));
 }
 
+int trellis_matvec_axis0_noalloc(const uint32_t* codes, const uint16_t* scales, const uint16_t* x,
+                                 void* out, int out_dtype, int64_t R_in, int64_t C_out, int M, int k,
+                                 int L, int T, void* stream) {
+  const char* fn = "trellis_matvec_axis0_noalloc";
+  TRY(check_geometry(fn, R_in, C_out, k, L, T));
+  TRY(check_m(fn, M, TRELLIS_MATVEC_MAX_M));
+  if (out_dtype != TRELLIS_OUT_BF16 && out_dtype != TRELLIS_OUT_F32)
+    return fail(TRELLIS_EINVAL, "%s: out_dtype=%d unknown", fn, out_dtype);
+  TRY(check_ptr(fn, "codes", codes, 16));
+  TRY(check_ptr(fn, "scales", scales, 2));
+  TRY(check_ptr(fn, "x", x, 16));
+  TRY(check_ptr(fn, "out", out, 16));
+  if (!trellis::axis0_supported(R_in, C_out, M, k))
+    return fail(TRELLIS_EUNSUPPORTED, "%s: shape R=%lld C=%lld M=%d k=%d does not fit the kernel's LDS plan", fn,
+                (long long)R_in, (long long)C_out, M, k);
+  const size_t need = trellis::axis0_workspace_bytes(R_in, C_out, M, k);
+  if (need > trellis::kAxis0ScratchBytes)
+    return fail(TRELLIS_EUNSUPPORTED, "%s: the split partials need %zu bytes, beyond the %zu-byte static scratch "
+                "(use trellis_matvec_axis0 with a workspace)", fn, need, trellis::kAxis0ScratchBytes);
+  void* scratch = nullptr;
+  TRY(hip_status(fn, trellis::axis0_scratch(&scratch)));
+  return hip_status(fn, trellis::launch_axis0(codes, scales, x, out, out_dtype == TRELLIS_OUT_F32, R_in, C_out, M,
+                                              k, scratch, (hipStream_t)stream));
+}
+
 size_t trellis_mlp_decode_workspace_bytes(int64_t R, int64_t C, int64_t C_out, int M, int k_gu,
                                           int k_down, int L, int T) {
   if (check_geometry("trellis_mlp_decode_workspace_bytes", R, C, k_gu, L, T) != TRELLIS_OK) return 0;

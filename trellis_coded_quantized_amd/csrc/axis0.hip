@@ -25,6 +25,8 @@
 // ring (global_load_lds copies, explicit vmcnt waits, no barrier in the
 // loop).  The waves' D tiles meet in LDS at the end; the workgroup writes its
 // f32 partial [s][m][c], scaled back by 2^-e_n; a fold kernel adds the splits.
+#include <mutex>
+
 #include "copy_ring.hpp"
 #include "internal.hpp"
 #include "mfma_common.hpp"
@@ -474,7 +476,33 @@ hipError_t axis0_launch(const uint32_t* codes, const uint16_t* scales, const uin
   return hipGetLastError();
 }
 
+// Static scratch of the allocation-free axis-0 call: the split-K partials
+// live here instead of in a caller's workspace.  Each device holds its own
+// copy of the array until the process ends; host code reaches it only
+// through the per-device address from hipGetSymbolAddress (the name itself
+// is a host-side stand-in, not a device address).
+static __device__ __align__(256) uint8_t scratch[kAxis0ScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
 }  // namespace
+
+hipError_t axis0_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {                  // once per device, with that device current
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 bool axis0_supported(int64_t R, int64_t C, int M, int k) {
   Axis0Geom g;

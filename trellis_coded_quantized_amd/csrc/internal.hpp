@@ -32,6 +32,12 @@ hipError_t launch_axis1(const uint32_t* codes0, const uint16_t* scales0, const u
 // axis 0 (split-K over stored rows, MFMA on 32-row blocks, then a fold)
 bool axis0_supported(int64_t R, int64_t C, int M, int k);
 size_t axis0_workspace_bytes(int64_t R, int64_t C, int M, int k);
+// The static device scratch that stands in for the axis-0 workspace in the
+// allocation-free call: kAxis0ScratchBytes per device, its address resolved
+// once per device (the current one) and cached.
+constexpr size_t kAxis0ScratchBytes = (size_t)4 << 20;
+constexpr int kMaxDevices = 64;
+hipError_t axis0_scratch(void** ptr);
 // interleave: codes in the block-interleaved k = 3 layout [C/512, R, 48]
 hipError_t launch_axis0(const uint32_t* codes, const uint16_t* scales, const uint16_t* x,
                         void* out, int out_f32, int64_t R, int64_t C, int M, int k,
