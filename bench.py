@@ -7,27 +7,37 @@ value is packed-code bytes per second over the whole step (inputs resident
 in HBM; code buffers rotate over >= 1 GiB of replicas so the 256 MB
 Infinity Cache cannot serve repeats).  Other workloads (--workload) print
 the same JSON line for their own metric: the 512 x 2048 reduce matvec, the
-17408 x 5120 k = 3 down-projection scatter, the k = 4 decoder-layer chain,
-the MLP (gate/up + SwiGLU, then the down projection, in one call), the
-axis-0 (down projection) prefill through expansion and GEMM,
-and the 17408 x 5120 prefill at M in {32, 512, 2048} (fused or expand +
-GEMM), plus a plain device copy used as the HBM reference point.
+17408 x 5120 k = 3 down-projection scatter (row-major or interleaved), the
+k = 4 decoder-layer chain, the MLP (gate/up + SwiGLU, then the down
+projection, in one call), the axis-1 and axis-0 prefills (fused or
+expansion + GEMM), the two measurement probes (decode_free, decode_only)
+and a plain device copy used as the HBM reference point.
 
 Steps run as HIP graphs (one graph per replica offset, captured after an
 eager warm-up) so the Python call overhead of the binding stays out of the
 measurement, as it would in a serving loop; --eager times the plain calls.
-The prefill expand + GEMM path always runs eagerly (the library GEMM is not
-captured).
+Expansion + GEMM runs eagerly, after one trellis_prefill_tune call in
+set-up picks the GEMM.
 
 The JSON line carries:
   roofline      the dominant kernel's algorithmic bytes (or flops) per launch
                 over its mean launch time (HIP events on the launch stream,
-                every step of the timed region), against the MI355X peak;
-                traffic = HBM bytes per launch from the committed rocprofv3
-                FETCH_SIZE / WRITE_SIZE summary under profiles/, or null when
-                the kernel sources changed since those counters were taken;
+                every step of the timed region), against the MI355X peak of
+                its bound (matvecs: HBM 8 TB/s; prefill: bf16 MFMA 2.5
+                PFLOP/s).  Matvecs add two ALU ceilings of their decode: the
+                VALU slot model (alu_model_*) and the rate of the
+                register-only decode probe measured in the same run
+                (alu_*).  traffic = HBM bytes per launch from the committed
+                rocprofv3 FETCH_SIZE / WRITE_SIZE summary under profiles/, or
+                null when the kernel sources changed since those counters
+                were taken;
   cpu_baseline  the CPU oracle timed on a bounded sample of the same
-                workload on this host (a baseline, not a target).
+                workload on this host (a baseline, not a target), with the
+                host's CPU model.
+The default (gate/up) line adds bound_location (the decode-free kernel and
+the decode-only probe on the same weights) and prefill, the metric's second
+half: 17408 x 5120, k = 2, M = 2048, fused and expansion + GEMM, each with
+its own MFMA roofline, and the oracle's CPU baseline for it.
 """
 import argparse
 import hashlib
@@ -45,16 +55,18 @@ METRIC = "decode matvec GB/s of packed codes (% HBM peak) at M=1..4; prefill TFL
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 # VALU issue slots of the chip: 256 CUs x 4 SIMDs x 16 lanes at 2.4 GHz.  The
-# decode of one weight takes 4 of them on gfx950 (window extract 1, the 1MAD
-# multiply-add v_mad_u64_u32 2 (half rate), byte sum 1); the products with x
-# run on MFMA.  The matvec roofline is the lower of this and HBM.
+# decode of one weight takes 4.5 of them on gfx950 (window extract 1, the 1MAD
+# multiply-add v_mad_u64_u32 2 (half rate), the byte sums of a weight pair to
+# f16 integer codes 3 per pair); the products with x run on MFMA.  This slot
+# model is one ALU ceiling; the other is the rate the register-only decode
+# probe measures on the box in the same run (trellis_probe_decode_only).
 VALU_LANE_SLOTS_PER_S = 256 * 4 * 16 * 2.4e9
-DECODE_SLOTS_PER_WEIGHT = 4
+DECODE_SLOTS_PER_WEIGHT = 4.5
 
 
-def decode_alu_peak_gbs(k):
+def decode_alu_model_gbs(code_bytes_per_weight):
     """Packed-code GB/s at which the decode alone fills every VALU issue slot."""
-    return VALU_LANE_SLOTS_PER_S / DECODE_SLOTS_PER_WEIGHT * k / 8 / 1e9
+    return VALU_LANE_SLOTS_PER_S / DECODE_SLOTS_PER_WEIGHT * code_bytes_per_weight / 1e9
 L, T = 12, 256
 ROTATE_BYTES = 1 << 30
 CSRC = os.path.join(ROOT, "trellis_coded_quantized_amd", "csrc")
@@ -137,7 +149,7 @@ PREFILL_SOURCES = ("prefill.hip", "mfma_common.hpp", "trellis_device.hpp")
 
 
 class GateUp(Workload):
-    bound = "alu"
+    bound = "hbm"
 
     def __init__(self, args, np, torch, dev):
         import trellis_coded_quantized_amd as tq
@@ -147,7 +159,7 @@ class GateUp(Workload):
         self.g, self.u = g, u = w.mats
         codes, half, bf16 = _dev_tensors(np, torch, dev)
         self.code_bytes = g.codes.nbytes + u.codes.nbytes
-        self.alu_k = g.k
+        self.bytes_per_weight = g.k / 8
         self.nrep = _nrep(self.code_bytes)
         self.gcs = [codes(g.codes)]
         self.ucs = [codes(u.codes)]
@@ -194,12 +206,12 @@ class GateUp(Workload):
 class Matvec(Workload):
     """Calls of the axis-1 / axis-0 matvec entry points, one per matrix, per M."""
 
-    bound = "alu"
+    bound = "hbm"
 
     def __init__(self, w, Ms, label, profile, sources, args, np, torch, dev):
         import trellis_coded_quantized_amd as tq
         self.np, self.tq, self.w, self.Ms = np, tq, w, Ms
-        self.alu_k = min(m.k for m in w.mats)
+        self.bytes_per_weight = sum(m.codes.nbytes for m in w.mats) / sum(m.R * m.C for m in w.mats)
         codes, half, bf16 = _dev_tensors(np, torch, dev)
         self.code_bytes = sum(m.codes.nbytes for m in w.mats)
         self.nrep = _nrep(self.code_bytes)
@@ -265,7 +277,7 @@ class Matvec(Workload):
 class Mlp(Workload):
     """The decoder-layer MLP for M = 1..4: gate/up + SwiGLU (17408 x 5120, k = 2), then the
     down projection stored transposed (17408 x 5120, k = 3), one trellis_mlp_decode call each."""
-    bound = "alu"
+    bound = "hbm"
 
     def __init__(self, args, np, torch, dev):
         import trellis_coded_quantized_amd as tq
@@ -278,8 +290,7 @@ class Mlp(Workload):
         codes, half, bf16 = _dev_tensors(np, torch, dev)
         self.code_bytes = g.codes.nbytes + u.codes.nbytes + d.codes.nbytes
         weights = 2 * g.R * g.C + d.R * d.C
-        self.alu_peak_gbs = VALU_LANE_SLOTS_PER_S / DECODE_SLOTS_PER_WEIGHT * (self.code_bytes / weights) / 1e9
-        self.alu_k = None
+        self.bytes_per_weight = self.code_bytes / weights
         self.nrep = _nrep(self.code_bytes)
         self.reps = [[codes(g.codes), codes(u.codes), codes(d.codes)]]
         for _ in range(self.nrep - 1):
@@ -356,6 +367,8 @@ class Prefill(Workload):
         nbytes = wsb(self.algo)
         self.ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
         self.graph = _runs_fused(tq, self.algo, wsb)
+        if not self.graph:                     # pick the fastest hipBLASLt candidate once, in set-up
+            tq.prefill(self.dc, self.ds, self.dx, m.k, out=self.out, workspace=self.ws, tune=True)
         self.kernels_per_step = 1 if self.graph else 2
         self.units_per_step = 2.0 * M * m.R * m.C
         self.name = w.name
@@ -410,6 +423,8 @@ class PrefillAxis0(Workload):
         nbytes = wsb(self.algo)
         self.ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
         self.graph = _runs_fused(tq, self.algo, wsb)
+        if not self.graph:                     # pick the fastest hipBLASLt candidate once, in set-up
+            tq.prefill_axis0(self.dc, self.ds, self.dx, m.k, out=self.out, workspace=self.ws, tune=True)
         self.kernels_per_step = 1 if self.graph else 2
         self.units_per_step = 2.0 * M * m.R * m.C
         self.name = f"prefill_axis0_{m.R}x{m.C}_k{m.k}_m{M}"
@@ -439,6 +454,51 @@ class PrefillAxis0(Workload):
         f = 2.0 * M * n * m.R
         return {"value": f / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
                 "sample": f"{n} of {m.C} output columns at M={M}: {f:.3e} flop in {dt:.2f} s"}
+
+
+class DecodeFree(GateUp):
+    """The gate/up workload through the decode-free kernel (the pages' variant 4
+    timing floor): the same copies, MFMAs, prologue and epilogue, no decode."""
+
+    def __init__(self, args, np, torch, dev):
+        super().__init__(args, np, torch, dev)
+        self.name = self.config["workload"] = "decode_free_gateup_17408x5120_k2"
+        self.kernel = "axis1_kernel without the decode (gate/up), one launch per M"
+        self.profile = None
+
+    def step(self, s):
+        for j, M in enumerate(self.Ms):
+            i = (s * len(self.Ms) + j) % self.nrep
+            self.tq.probe_gateup_decode_free(self.gcs[i], self.gs, self.ucs[i], self.us, self.x[:M], self.g.k,
+                                             out=self.outs[M])
+
+    def cpu_baseline(self, seconds):
+        return None
+
+
+class DecodeOnly(Workload):
+    """The register-only decode probe: the matvec loop's decode and MFMAs with no
+    memory traffic, one workgroup of 8 waves per compute unit.  Its rate is the
+    ALU ceiling of the matvec kernels, reported as packed-code GB/s at k = 2."""
+    unit, bound, dtype = "GB/s", "alu", "u32"
+    ITERS = 4096
+
+    def __init__(self, args, np, torch, dev):
+        import trellis_coded_quantized_amd as tq
+        self.np, self.tq, self.k = np, tq, 2
+        self.blocks = torch.cuda.get_device_properties(dev).multi_processor_count
+        rng = np.random.default_rng(77)
+        n = self.blocks * tq.PROBE_THREADS
+        self.runs = torch.from_numpy(rng.integers(0, 2 ** 32, (n, self.k + 1), dtype=np.uint32).view(np.int32)).to(dev)
+        self.weights_per_step = float(n) * self.ITERS * 32
+        self.units_per_step = self.weights_per_step * self.k / 8      # packed-code bytes at k = 2
+        self.name = "decode_only_probe"
+        self.kernel = "decode_only_kernel (register-only decode + MFMA)"
+        self.config = {"workload": self.name, "blocks": self.blocks, "threads_per_block": tq.PROBE_THREADS,
+                       "iters": self.ITERS, "k": self.k, "weights_per_launch": self.weights_per_step}
+
+    def step(self, s):
+        self.tq.probe_decode_only(self.runs, self.k, self.ITERS)
 
 
 class Copy(Workload):
@@ -524,7 +584,114 @@ def workload_axis1_m1(args, np, torch, dev):
 WORKLOADS = {"copy": Copy, "gateup": GateUp, "prefill": Prefill, "axis0": workload_axis0, "mlp": Mlp,
              "prefill_axis0": PrefillAxis0, "axis0_il": workload_axis0_il,
              "layer_chain": workload_layer_chain, "layer_chain_grouped": workload_layer_chain_grouped,
-             "axis1_m1": workload_axis1_m1}
+             "axis1_m1": workload_axis1_m1, "decode_free": DecodeFree, "decode_only": DecodeOnly}
+
+
+MATVEC_WORKLOADS = ("gateup", "axis0", "axis0_il", "layer_chain", "layer_chain_grouped", "mlp", "axis1_m1",
+                    "decode_free")
+
+
+def time_workload(wl, steps, warmup, eager, torch, label):
+    """Warm up, capture one graph per replica offset (unless eager or the
+    workload cannot be captured), then time `steps` steps between device
+    synchronisations.  Returns (ms per step, mean launch ms from HIP events on
+    the launch stream, mode)."""
+    print(f"[bench] {label}: warmup {warmup}", file=sys.stderr, flush=True)
+    for s in range(warmup):
+        wl.step(s)
+    torch.cuda.synchronize()
+    graphs = None
+    if wl.graph and not eager:
+        graphs = []
+        for s in range(wl.period):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                wl.step(s)
+            graphs.append(g)
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
+    mode = "graph" if graphs else "eager"
+    print(f"[bench] {label}: timing {steps} steps ({mode})", file=sys.stderr, flush=True)
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        a, b = events[s]
+        a.record()
+        if graphs:
+            graphs[s % len(graphs)].replay()
+        else:
+            wl.step(s)
+        b.record()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / max(steps, 1)
+    step_ms = sum(a.elapsed_time(b) for a, b in events) / max(steps, 1)
+    return ms_step, step_ms / wl.kernels_per_step, mode
+
+
+def roofline_of(wl, launch_ms, probe_weights_per_s=None):
+    """The dominant kernel's achieved rate against the MI355X peak of its bound;
+    matvecs also against the two ALU ceilings of their decode."""
+    scale = 1e9 if wl.unit == "GB/s" else 1e12
+    achieved = wl.units_per_step / wl.kernels_per_step / (launch_ms * 1e-3) / scale
+    peak = {"hbm": HBM_PEAK_GBS, "mfma": BF16_PEAK_TFLOPS}.get(wl.bound)
+    traffic = committed_traffic(wl.profile, wl.profile_sources) if wl.profile else None
+    r = {"bound": wl.bound, "achieved": achieved, "peak": peak, "unit": wl.unit,
+         "frac": achieved / peak if peak else None, "traffic": traffic, "kernel": wl.kernel,
+         "mean_launch_us": launch_ms * 1e3}
+    bpw = getattr(wl, "bytes_per_weight", None)
+    if bpw:
+        model = decode_alu_model_gbs(bpw)
+        r.update({"alu_model_peak": model, "alu_model_frac": achieved / model,
+                  "alu_model_basis": f"{VALU_LANE_SLOTS_PER_S:.4g} VALU lane-slots/s / {DECODE_SLOTS_PER_WEIGHT} "
+                                     f"slots per weight x {bpw:.4g} code bytes per weight"})
+        if probe_weights_per_s:
+            probe = probe_weights_per_s * bpw / 1e9
+            r.update({"alu_peak": probe, "alu_frac": achieved / probe,
+                      "alu_basis": "decode_only_kernel rate measured in this run x code bytes per weight"})
+    return r
+
+
+def cpu_info():
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "host_cpus": os.cpu_count()}
+
+
+def probe_rate(np, torch, dev, args):
+    """Decoded weights per second of the register-only decode probe."""
+    wl = DecodeOnly(args, np, torch, dev)
+    _, launch_ms, _ = time_workload(wl, 10, 2, True, torch, "decode_only probe")
+    return wl.weights_per_step / (launch_ms * 1e-3), wl
+
+
+def prefill_leg(np, torch, dev, args, cpu_seconds):
+    """The prefill half of the metric: 17408 x 5120, k = 2, M = 2048, fused and
+    expansion + tuned GEMM, each against the bf16 MFMA peak."""
+    legs = {}
+    cpu = None
+    for algo in ("fused", "expand_gemm"):
+        a = argparse.Namespace(m=2048, algo=algo)
+        wl = Prefill(a, np, torch, dev)
+        ms_step, launch_ms, mode = time_workload(wl, 20, 3, False, torch, f"prefill {algo}")
+        legs[algo] = {"value": wl.units_per_step / (ms_step * 1e-3) / 1e12, "unit": "TFLOP/s",
+                      "ms_per_call": ms_step, "mode": mode, "roofline": roofline_of(wl, launch_ms)}
+        if cpu is None and cpu_seconds > 0:
+            print("[bench] prefill cpu baseline (oracle)", file=sys.stderr, flush=True)
+            cpu = wl.cpu_baseline(cpu_seconds)
+            cpu.update(cpu_info())
+        del wl
+        torch.cuda.empty_cache()
+    return {"workload": "prefill_17408x5120_k2_m2048", "M": 2048, "R": 17408, "C": 5120, "k": 2,
+            "flop_per_call": 2.0 * 2048 * 17408 * 5120, **legs, "cpu_baseline": cpu}
 
 
 def main():
@@ -537,6 +704,8 @@ def main():
     ap.add_argument("--algo", default="fused", choices=["fused", "expand_gemm", "auto"])
     ap.add_argument("--eager", action="store_true", help="time plain calls instead of graph replays")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="gateup only: skip the prefill leg and the bound-location probes")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -551,67 +720,40 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     wl = WORKLOADS[args.workload](args, np, torch, dev)
-    print(f"[bench] {args.workload}: warmup {args.warmup}", file=sys.stderr, flush=True)
-    for s in range(args.warmup):
-        wl.step(s)
-    torch.cuda.synchronize()
-    graphs = None
-    if wl.graph and not args.eager:
-        graphs = []
-        for s in range(wl.period):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                wl.step(s)
-            graphs.append(g)
-        for g in graphs:
-            g.replay()
-        torch.cuda.synchronize()
-    mode = "graph" if graphs else "eager"
-    print(f"[bench] timing {args.steps} steps ({mode})", file=sys.stderr, flush=True)
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        a, b = events[s]
-        a.record()
-        if graphs:
-            graphs[s % len(graphs)].replay()
-        else:
-            wl.step(s)
-        b.record()
-    torch.cuda.synchronize()
-    ms_step = (time.perf_counter() - t0) * 1e3 / max(args.steps, 1)
-    step_ms = sum(a.elapsed_time(b) for a, b in events) / max(args.steps, 1)
-    launch_ms = step_ms / wl.kernels_per_step
-    scale = 1e9 if wl.unit == "GB/s" else 1e12
-    per_launch_units = wl.units_per_step / wl.kernels_per_step
-    achieved = per_launch_units / (launch_ms * 1e-3) / scale
-    peak = {"hbm": HBM_PEAK_GBS, "mfma": BF16_PEAK_TFLOPS}.get(wl.bound)
-    if wl.bound == "alu":
-        alu = getattr(wl, "alu_peak_gbs", None) or decode_alu_peak_gbs(wl.alu_k)
-        peak = min(alu, HBM_PEAK_GBS)
-    traffic = committed_traffic(wl.profile, wl.profile_sources) if wl.profile else None
+    ms_step, launch_ms, mode = time_workload(wl, args.steps, args.warmup, args.eager, torch, args.workload)
+    rate = None
+    if args.workload in MATVEC_WORKLOADS:
+        rate, _ = probe_rate(np, torch, dev, args)
+    roof = roofline_of(wl, launch_ms, rate)
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         cpu = wl.cpu_baseline(args.cpu_seconds)
+        if cpu is not None:
+            cpu.update(cpu_info())
+    scale = 1e9 if wl.unit == "GB/s" else 1e12
     line = {
         "metric": METRIC, "value": wl.units_per_step / (ms_step * 1e-3) / scale, "unit": wl.unit, "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
-        "data": DATA, "config": dict(wl.config, mode=mode),
-        "roofline": {"bound": wl.bound, "achieved": achieved, "peak": peak,
-                     "unit": wl.unit, "frac": achieved / peak,
-                     "traffic": traffic, "kernel": wl.kernel, "mean_launch_us": launch_ms * 1e3},
-        "cpu_baseline": cpu,
+        "data": DATA, "config": dict(wl.config, mode=mode), "roofline": roof, "cpu_baseline": cpu,
     }
-    if wl.bound == "alu":
-        line["roofline"].update({
-            "peak_basis": f"decode VALU bound: {VALU_LANE_SLOTS_PER_S:.4g} lane-slots/s / "
-                          f"{DECODE_SLOTS_PER_WEIGHT} slots per weight x k/8 bytes "
-                          + (f"(k={wl.alu_k})" if wl.alu_k else "(k weighted over the matrices)"),
-            "hbm_peak": HBM_PEAK_GBS, "hbm_frac": achieved / HBM_PEAK_GBS})
+    if args.workload == "gateup" and not args.no_extras:
+        df = DecodeFree.__new__(DecodeFree)          # the same buffers through the decode-free kernel
+        df.__dict__.update(wl.__dict__)
+        df.name = "decode_free_gateup_17408x5120_k2"
+        df.kernel = "axis1_kernel without the decode (gate/up)"
+        _, df_launch, _ = time_workload(df, args.steps, args.warmup, args.eager, torch, "decode_free")
+        line["bound_location"] = {
+            "kernel_launch_us": launch_ms * 1e3,
+            "decode_free_launch_us": df_launch * 1e3,
+            "decode_free_gbs": wl.code_bytes / (df_launch * 1e-3) / 1e9,
+            "decode_only_weights_per_s": rate,
+            "decode_only_launch_us_same_weights": 2 * 17408 * 5120 / rate * 1e6,
+            "note": "decode-free = the kernel's copies, MFMAs, prologue and epilogue; decode-only = its decode "
+                    "alone on the same weight count (register-only probe)",
+        }
+        line["prefill"] = prefill_leg(np, torch, dev, args, 0.0 if args.no_cpu_baseline else 10.0)
     print(json.dumps(line), flush=True)
 
 

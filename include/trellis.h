@@ -330,6 +330,31 @@ int trellis_prefill_axis0_tune(const uint32_t* codes, const uint16_t* scales, co
 int trellis_decode_states(const uint32_t* codes, int64_t R, int64_t C, int k, int L, int T,
                           uint16_t* states, int16_t* y, float* value, void* stream);
 
+/*
+ * Measurement probes: where the matvec kernels' time goes (the pages' decode
+ * variant 4, "no decode, timing floor only", trellis-linear.ts HEADER, page
+ * 55, and a decode without memory).  Not part of the layer's contract.
+ *
+ * trellis_probe_decode_only -- the matvec loop's decode and MFMAs with no
+ * memory traffic.  Thread g of blocks * 512 threads decodes the 32-position
+ * run held in runs[g][0 .. k] (k words and the word after them) `iters`
+ * times, adding 1 to every word after each pass, and feeds each pass's codes
+ * to the matvec kernels' MFMA against an all-ones operand.  wave_sums[w]
+ * (blocks * 8 floats) receives 16 times the sum of the codes wave w decoded
+ * (exact while each sum stays below 2^24).  Decoded weights per call:
+ * blocks * 512 * iters * 32.  runs uint32 [blocks * 512][k + 1].
+ *
+ * trellis_probe_gateup_decode_free -- trellis_gateup_swiglu's kernel with
+ * the raw code words in place of the decoded codes: the same copies,
+ * MFMAs, prologue and epilogue, no decode.  out (bf16 [M, R]) receives
+ * meaningless values.  One launch only (C <= 5120).
+ */
+int trellis_probe_decode_only(const uint32_t* runs, float* wave_sums, int blocks, int iters, int k,
+                              void* stream);
+int trellis_probe_gateup_decode_free(const uint32_t* gcodes, const uint16_t* gscales, const uint32_t* ucodes,
+                                     const uint16_t* uscales, const uint16_t* x, uint16_t* out, int64_t R,
+                                     int64_t C, int M, int k, int L, int T, void* stream);
+
 /* Description of the last non-OK status on this thread ("" if none). */
 const char* trellis_last_error(void);
 

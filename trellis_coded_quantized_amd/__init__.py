@@ -37,6 +37,7 @@ EXPORTS = (
     "trellis_expand_bf16", "trellis_prefill_workspace_bytes", "trellis_prefill",
     "trellis_prefill_axis0_workspace_bytes", "trellis_prefill_axis0", "trellis_prefill_axis0_il",
     "trellis_prefill_tune", "trellis_prefill_axis0_tune",
+    "trellis_probe_decode_only", "trellis_probe_gateup_decode_free",
     "trellis_decode_states", "trellis_last_error", "trellis_version",
 )
 
@@ -91,6 +92,9 @@ def load_library():
         "trellis_prefill_tune": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int, _vp, _sz, _vp]),
         "trellis_prefill_axis0_tune": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int, _vp, _sz,
                                               _vp]),
+        "trellis_probe_decode_only": (_int, [_vp, _vp, _int, _int, _int, _vp]),
+        "trellis_probe_gateup_decode_free": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _int, _int, _int,
+                                                    _int, _vp]),
         "trellis_decode_states": (_int, [_vp, _i64, _i64, _int, _int, _int, _vp, _vp, _vp, _vp]),
         "trellis_last_error": (ctypes.c_char_p, []),
         "trellis_version": (ctypes.c_char_p, []),
@@ -418,3 +422,31 @@ def decode_states(codes, k, L=12, T=256):
     _check(load_library().trellis_decode_states(_ptr(codes), R, C, k, L, T, _ptr(st), _ptr(ys),
                                                 _ptr(vals), _stream(dev)))
     return st, ys, vals
+
+
+PROBE_THREADS = 512
+
+
+def probe_decode_only(runs, k, iters, blocks=None):
+    """Measurement probe: decode the runs held in `runs` (int32/uint32
+    [blocks * 512, k + 1]) `iters` times each; returns the per-wave sums
+    (f32 [blocks * 8], 16 times the sum of the codes each wave decoded)."""
+    _need(runs, "runs", _CODES, 2)
+    n, words = runs.shape
+    if words != k + 1 or n % PROBE_THREADS:
+        raise ValueError(f"runs must be [blocks * {PROBE_THREADS}, k + 1], got {tuple(runs.shape)}")
+    blocks = n // PROBE_THREADS if blocks is None else blocks
+    out = torch.empty(blocks * PROBE_THREADS // 64, dtype=torch.float32, device=runs.device)
+    _check(load_library().trellis_probe_decode_only(_ptr(runs), _ptr(out), blocks, iters, k, _stream(runs.device)))
+    return out
+
+
+def probe_gateup_decode_free(gcodes, gscales, ucodes, uscales, x, k, L=12, T=256, out=None):
+    """Measurement probe: the gate/up kernel with no decode (timing floor; the
+    output values are meaningless)."""
+    R, C = _geometry(gcodes, k)
+    M = x.shape[0]
+    out = _out(out, "out", (M, R), (torch.bfloat16,), x.device)
+    _check(load_library().trellis_probe_gateup_decode_free(_ptr(gcodes), _ptr(gscales), _ptr(ucodes), _ptr(uscales),
+                                                           _ptr(x), _ptr(out), R, C, M, k, L, T, _stream(x.device)))
+    return out

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtrellis.so")
-SOURCES = ["api.hip", "axis1.hip", "axis0.hip", "expand.hip", "prefill.hip"]
+SOURCES = ["api.hip", "axis1.hip", "axis0.hip", "expand.hip", "prefill.hip", "probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 CFLAGS = [

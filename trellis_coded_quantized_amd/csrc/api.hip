@@ -631,6 +631,35 @@ int trellis_prefill_axis0_tune(const uint32_t* codes, const uint16_t* scales, co
                            (hipStream_t)stream);
 }
 
+int trellis_probe_decode_only(const uint32_t* runs, float* wave_sums, int blocks, int iters, int k,
+                              void* stream) {
+  const char* fn = "trellis_probe_decode_only";
+  if (k != 2 && k != 3 && k != 4) return fail(TRELLIS_EUNSUPPORTED, "%s: k=%d not in {2,3,4}", fn, k);
+  if (blocks < 1 || blocks > 65535) return fail(TRELLIS_EINVAL, "%s: blocks=%d outside 1..65535", fn, blocks);
+  if (iters < 1) return fail(TRELLIS_EINVAL, "%s: iters=%d < 1", fn, iters);
+  TRY(check_ptr(fn, "runs", runs, 4));
+  TRY(check_ptr(fn, "wave_sums", wave_sums, 4));
+  return hip_status(fn, trellis::launch_decode_only(runs, wave_sums, blocks, iters, k, (hipStream_t)stream));
+}
+
+int trellis_probe_gateup_decode_free(const uint32_t* gcodes, const uint16_t* gscales, const uint32_t* ucodes,
+                                     const uint16_t* uscales, const uint16_t* x, uint16_t* out, int64_t R,
+                                     int64_t C, int M, int k, int L, int T, void* stream) {
+  const char* fn = "trellis_probe_gateup_decode_free";
+  TRY(check_geometry(fn, R, C, k, L, T));
+  TRY(check_m(fn, M, TRELLIS_MATVEC_MAX_M));
+  TRY(check_ptr(fn, "gcodes", gcodes, 16));
+  TRY(check_ptr(fn, "gscales", gscales, 2));
+  TRY(check_ptr(fn, "ucodes", ucodes, 16));
+  TRY(check_ptr(fn, "uscales", uscales, 2));
+  TRY(check_ptr(fn, "x", x, 16));
+  TRY(check_ptr(fn, "out", out, 16));
+  if (trellis::axis1_workspace_bytes(R, C, M, k, true) != 0 || !trellis::axis1_supported(R, C, M, k, true))
+    return fail(TRELLIS_EUNSUPPORTED, "%s: one launch only (C <= 5120), C=%lld", fn, (long long)C);
+  return hip_status(fn, trellis::launch_gateup_decode_free(gcodes, gscales, ucodes, uscales, x, out, R, C, M, k,
+                                                           (hipStream_t)stream));
+}
+
 int trellis_decode_states(const uint32_t* codes, int64_t R, int64_t C, int k, int L, int T,
                           uint16_t* states, int16_t* y, float* value, void* stream) {
   const char* fn = "trellis_decode_states";

@@ -34,7 +34,6 @@
 namespace trellis {
 namespace {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;

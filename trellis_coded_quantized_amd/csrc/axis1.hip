@@ -41,7 +41,6 @@
 namespace trellis {
 namespace {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
@@ -93,32 +92,6 @@ __device__ __forceinline__ uint16_t swiglu_bf16(float gate, float up) {
   const float sig = round_bf16(gT >= 0.0f ? 1.0f / (1.0f + t) : t / (1.0f + t));
   const float silu = round_bf16(gT * sig);
   return f32_to_bf16_bits(silu * uT);
-}
-
-// The 32 codes of one run as four MFMA A operands of 8 f16 subnormals
-// (A[u] element e = code y of position 8u + e of the run).
-template <int K>
-__device__ __forceinline__ void decode_run_sub(const uint32_t (&w)[K + 1], uint32_t mul, uint64_t add64,
-                                               u32x4 (&A)[4]) {
-  uint32_t a[2 * K];                           // a[j] holds bits 16j .. 16j+31 of the run
-#pragma unroll
-  for (int m = 0; m < K; ++m) {
-    a[2 * m] = w[m];
-    a[2 * m + 1] = __builtin_amdgcn_alignbit(w[m + 1], w[m], 16);
-  }
-  // three phases, so no 1MAD result is consumed right after it is produced:
-  // all 32 windows, all 32 1MAD words, then the 16 code pairs
-  uint32_t st[32];
-#pragma unroll
-  for (int p = 0; p < 32; ++p) {
-    const int b = (31 - p) * K;                 // window start of position p
-    st[p] = __builtin_amdgcn_ubfe(a[b >> 4], b & 15, kL);
-  }
-  uint32_t xw[32];
-#pragma unroll
-  for (int p = 0; p < 32; ++p) xw[p] = onemad_word_mad64(st[p], mul, add64);
-#pragma unroll
-  for (int v = 0; v < 16; ++v) A[v >> 2][v & 3] = code_pair_y(xw[2 * v], xw[2 * v + 1]);
 }
 
 // The code words of five run groups of one tile row, read from the ring and
@@ -197,7 +170,11 @@ __device__ __forceinline__ void lds_read_runs5(const uint32_t (&aw)[5], const ui
 
 // GROUP: the launch spans the row groups of several matrices (a grouped
 // call); the plain and gate/up instantiations compile the lookup out.
-template <int K, bool GATEUP, int NG, bool GROUP = false>
+// DECODE = false is the decode-free timing floor: the raw code words go to
+// the MFMA in place of the decoded codes (meaningless outputs), so a launch
+// costs the copies, the MFMAs, the prologue and the epilogue without the
+// decode.
+template <int K, bool GATEUP, int NG, bool GROUP = false, bool DECODE = true>
 __global__ __launch_bounds__(kThreads) void axis1_kernel(
     const uint32_t* __restrict__ codes0, const uint16_t* __restrict__ scales0,
     const uint32_t* __restrict__ codes1, const uint16_t* __restrict__ scales1,
@@ -422,7 +399,12 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
     for (int u = 0; u < 4; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
     auto consume = [&](const uint32_t (&W)[K + 1], const half8 (&Bg)[4]) {
       u32x4 A[4];
-      decode_run_sub<K>(W, mul, add64, A);
+      if constexpr (DECODE) {
+        decode_run_codes<K>(W, mul, add64, A);
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) A[u] = u32x4{W[u % (K + 1)], W[(u + 1) % (K + 1)], W[(u + 2) % (K + 1)], W[0]};
+      }
 #pragma unroll
       for (int u = 0; u < 4; ++u)
         acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, A[u]), Bg[u], acc[u], 0, 0, 0);
@@ -601,7 +583,7 @@ int64_t axis1_grid(int64_t R, bool gateup, int64_t nrg_total = 0) {
   return nrg < cus ? nrg : cus;
 }
 
-template <int K, bool GU, int NG, bool GROUP = false>
+template <int K, bool GU, int NG, bool GROUP = false, bool DECODE = true>
 hipError_t axis1_launch_one(const uint32_t* c0, const uint16_t* s0, const uint32_t* c1,
                             const uint16_t* s1, const uint16_t* x, void* out, int out_f32,
                             float* gf, float* uf, const Axis1Geom& g, int64_t grid, hipStream_t stream) {
@@ -610,13 +592,13 @@ hipError_t axis1_launch_one(const uint32_t* c0, const uint16_t* s0, const uint32
   if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
   const uint64_t bit = 1ull << (dev & 63);
   if (!(lds_attr & bit)) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&axis1_kernel<K, GU, NG, GROUP>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&axis1_kernel<K, GU, NG, GROUP, DECODE>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kAxis1MaxLdsBytes);
     if (e != hipSuccess) return e;
     lds_attr |= bit;
   }
-  hipLaunchKernelGGL((axis1_kernel<K, GU, NG, GROUP>), dim3((unsigned)grid), dim3(kThreads), g.total, stream,
-                     c0, s0, c1, s1, x, out, out_f32, gf, uf, g);
+  hipLaunchKernelGGL((axis1_kernel<K, GU, NG, GROUP, DECODE>), dim3((unsigned)grid), dim3(kThreads), g.total,
+                     stream, c0, s0, c1, s1, x, out, out_f32, gf, uf, g);
   return hipGetLastError();
 }
 
@@ -711,7 +693,35 @@ hipError_t axis1_group_main(const uint32_t* const* codes, const uint16_t* const*
   }
 }
 
+template <int K>
+hipError_t axis1_decode_free_main(const uint32_t* c0, const uint16_t* s0, const uint32_t* c1, const uint16_t* s1,
+                                  const uint16_t* x, uint16_t* out, int64_t R, int64_t C, int M, hipStream_t stream) {
+  const int64_t grid = axis1_grid(R, true);
+  Axis1Geom g;
+  if (!axis1_geom(R, C, M, K, true, grid, g)) return hipErrorInvalidValue;
+  switch (axis1_ng(C)) {
+    case 2:
+      return axis1_launch_one<K, true, 2, false, false>(c0, s0, c1, s1, x, out, 0, nullptr, nullptr, g, grid,
+                                                        stream);
+    case 5:
+      return axis1_launch_one<K, true, 5, false, false>(c0, s0, c1, s1, x, out, 0, nullptr, nullptr, g, grid,
+                                                        stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_gateup_decode_free(const uint32_t* c0, const uint16_t* s0, const uint32_t* c1, const uint16_t* s1,
+                                     const uint16_t* x, uint16_t* out, int64_t R, int64_t C, int M, int k,
+                                     hipStream_t stream) {
+  switch (k) {
+    case 2: return axis1_decode_free_main<2>(c0, s0, c1, s1, x, out, R, C, M, stream);
+    case 3: return axis1_decode_free_main<3>(c0, s0, c1, s1, x, out, R, C, M, stream);
+    case 4: return axis1_decode_free_main<4>(c0, s0, c1, s1, x, out, R, C, M, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 size_t axis1_workspace_bytes(int64_t R, int64_t C, int M, int, bool gateup) {
   const int64_t n = axis1_nchunks(C);

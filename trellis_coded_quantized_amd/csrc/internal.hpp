@@ -29,6 +29,16 @@ hipError_t launch_axis1(const uint32_t* codes0, const uint16_t* scales0, const u
                         float* gate_f32, float* up_f32, int64_t R, int64_t C, int M, int k,
                         void* workspace, hipStream_t stream);
 
+// measurement probes: the gate/up kernel without the decode (timing floor,
+// one launch, C <= 5120), and the register-only decode of `iters` runs per
+// thread (the instruction mix of the matvec loop without memory)
+hipError_t launch_gateup_decode_free(const uint32_t* c0, const uint16_t* s0, const uint32_t* c1, const uint16_t* s1,
+                                     const uint16_t* x, uint16_t* out, int64_t R, int64_t C, int M, int k,
+                                     hipStream_t stream);
+constexpr int kProbeThreads = 512;
+hipError_t launch_decode_only(const uint32_t* runs, float* wave_sums, int blocks, int iters, int k,
+                              hipStream_t stream);
+
 // axis 0 (split-K over stored rows, MFMA on 32-row blocks, then a fold)
 bool axis0_supported(int64_t R, int64_t C, int M, int k);
 size_t axis0_workspace_bytes(int64_t R, int64_t C, int M, int k);

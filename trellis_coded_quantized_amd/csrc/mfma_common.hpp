@@ -8,6 +8,7 @@
 namespace trellis {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -41,6 +42,34 @@ __device__ __forceinline__ uint32_t code_pair_y(uint32_t word_lo, uint32_t word_
   const uint32_t both = __builtin_amdgcn_sad_u8(word_lo, 0u, __builtin_amdgcn_sad_hi_u8(word_hi, 0u, kHalfMagic2));
   const half2v h = __builtin_bit_cast(half2v, both) + __builtin_bit_cast(half2v, kNeg1536Pair);
   return __builtin_bit_cast(uint32_t, h);
+}
+
+// The 32 codes of one 32-position run (words w[0 .. K-1] and the word after
+// it, wrapped in its block) as four MFMA A operands of 8 f16 integers: A[u]
+// element e is the code y of run position 8u + e, whose state is the 12-bit
+// window at bit (31 - 8u - e) K of the run.
+template <int K>
+__device__ __forceinline__ void decode_run_codes(const uint32_t (&w)[K + 1], uint32_t mul, uint64_t add64,
+                                               u32x4 (&A)[4]) {
+  uint32_t a[2 * K];                           // a[j] holds bits 16j .. 16j+31 of the run
+#pragma unroll
+  for (int m = 0; m < K; ++m) {
+    a[2 * m] = w[m];
+    a[2 * m + 1] = __builtin_amdgcn_alignbit(w[m + 1], w[m], 16);
+  }
+  // three phases, so no 1MAD result is consumed right after it is produced:
+  // all 32 windows, all 32 1MAD words, then the 16 code pairs
+  uint32_t st[32];
+#pragma unroll
+  for (int p = 0; p < 32; ++p) {
+    const int b = (31 - p) * K;                 // window start of position p
+    st[p] = __builtin_amdgcn_ubfe(a[b >> 4], b & 15, kL);
+  }
+  uint32_t xw[32];
+#pragma unroll
+  for (int p = 0; p < 32; ++p) xw[p] = onemad_word_mad64(st[p], mul, add64);
+#pragma unroll
+  for (int v = 0; v < 16; ++v) A[v >> 2][v & 3] = code_pair_y(xw[2 * v], xw[2 * v + 1]);
 }
 
 }  // namespace trellis
