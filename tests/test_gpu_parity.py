@@ -456,3 +456,35 @@ def test_prefill_axis0_down_17408x5120_k3(axis0_workload, algo, M):
     want, cond = oracle.prefill_axis0_sums(m.codes, m.scales, x, M, m.R, m.C, m.k, L, T, ms, cols, with_abs=True)
     sub = h_u16(got[torch.as_tensor(ms, device=DEV)][:, torch.as_tensor(cols, device=DEV)])
     tol.assert_bf16_close(sub, want, cond, f"prefill axis0 down M={M}")
+
+
+# ------------------------------------------------------------------ bf16-weight matvec contract (variants 0-3)
+
+@pytest.mark.parametrize("algo", ALGOS)
+def test_bf16_weight_matvec_17408x5120_k2_m1_to_4(prefill_workload, algo):
+    # the pages' decode variants 0-3 round every weight to bf16 before the products (trellis-linear.ts file
+    # header, HEADER TRELLIS_ROUND); trellis_prefill computes that contract for any M.  Every output of the
+    # gate/up shape at M = 1..4 against the oracle's bf16-weight sums.
+    w = prefill_workload
+    m = w.mats[0]
+    x = w.x[0][:4]
+    want, cond = oracle.prefill_sums(m.codes, m.scales, x, 4, m.R, m.C, m.k, L, T, np.arange(4), np.arange(m.R),
+                                     with_abs=True)
+    dc, ds = d_codes(m.codes), d_half(m.scales)
+    for M in (1, 2, 3, 4):
+        got = h_u16(tq.prefill(dc, ds, d_bf16(x[:M]), m.k, algo=algo))
+        tol.assert_bf16_close(got, want[:M], cond[:M], f"bf16-weight matvec algo={algo} M={M}")
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+def test_bf16_weight_matvec_axis0_17408x5120_k3_m1_to_4(axis0_workload, algo):
+    # the same contract for the down projection stored transposed (axis 0), every output
+    w, _ = axis0_workload
+    m = w.mats[0]
+    x = w.x[0][:4]
+    want, cond = oracle.prefill_axis0_sums(m.codes, m.scales, x, 4, m.R, m.C, m.k, L, T, np.arange(4),
+                                           np.arange(m.C), with_abs=True)
+    dc, ds = d_codes(m.codes), d_half(m.scales)
+    for M in (1, 2, 3, 4):
+        got = h_u16(tq.prefill_axis0(dc, ds, d_bf16(x[:M]), m.k, algo=algo))
+        tol.assert_bf16_close(got, want[:M], cond[:M], f"bf16-weight axis0 matvec algo={algo} M={M}")

@@ -12,7 +12,7 @@
 #include <mutex>
 #include <tuple>
 
-#include "../../include/trellis.h"
+#include "trellis.h"
 #include "internal.hpp"
 
 namespace trellis {

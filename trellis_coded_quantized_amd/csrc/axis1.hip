@@ -45,7 +45,8 @@ namespace {
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxSlots = 4;           // tile ring depth per wave
-constexpr int kMaxDma = 7;             // copies per wave per tile (C <= 5120, k <= 4: 16 rows x 25 granules)
+constexpr int kMaxDma = 8;             // copies per wave per tile (C <= 5120, k <= 4: 2 x 8 rows x 25 granules)
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer resource, 32-bit data format
 constexpr int kXPer = 5;               // x granules per lane of a wave's slice (M * C <= 4 * 5120)
 constexpr uint32_t kPartBytes = kWaves * 4 * 16 * 4;   // one row group's partial tiles: f32 [wave][n][16 rows]
 constexpr int kMaxGroup = 4;           // matrices of one grouped call
@@ -66,7 +67,7 @@ struct Axis1Geom {
   int M;
   int per;              // runs of 32 columns per wave (C / 256)
   int gsw;              // granules per tile row of a wave's window (its blocks + one pad granule)
-  int nwd;              // copies per wave per tile: ceil(16 gsw / 64)
+  int nwd;              // copy slots per wave per tile (ceil(rows gsw / 64) per matrix)
   uint32_t gsw_magic;   // ceil(2^24 / gsw): p / gsw == (p * gsw_magic) >> 24 for p < 4096
   int nslots, xslots, nmine_max;
   uint32_t slot_bytes, part_off, total;
@@ -226,20 +227,36 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
   const int b0 = rb >> 3, b1 = (re - 1) >> 3;
   const int gwr = (b1 - b0 + 1) * (BLK / 16);  // granules of the window per row (< gsw)
 
-  // copy descriptors: window granule p = 64 j + lane is granule p % gsw of
-  // tile row p / gsw (granules past the wave's blocks are skipped).
-  // dd = active bit | tile row << 16 | byte offset of the granule in its row.
+  // copy descriptors.  A tile is ROWS rows of each matrix it reads (16 of
+  // one, or 8 gate + 8 up).  Copy j moves granules p = 64 jh + lane of its
+  // matrix's rows: plain, jh = j; gate/up, copies [0, nh) read the gate rows
+  // and [nh, 2 nh) the up rows, jh = j mod nh, so every copy reads a single
+  // matrix.  Granule p is granule p % gsw of row p / gsw (granules past the
+  // wave's blocks are pad and not copied).  dd = active bit | byte offset of
+  // the granule from the tile's first row, computed once: a copy then needs
+  // no vector arithmetic, only the tile's buffer resource.
+  const int nh = GATEUP ? nwd / 2 : nwd;
+  const uint32_t row_bytes = (uint32_t)g.row_bytes;
   uint32_t dd[kMaxDma];
 #pragma unroll
   for (int j = 0; j < kMaxDma; ++j) {
-    const uint32_t p = (uint32_t)(j * 64 + lane);
+    const int jh = (GATEUP && j >= nh) ? j - nh : j;
+    const uint32_t p = (uint32_t)(jh * 64 + lane);
     const uint32_t r = (uint32_t)(((uint64_t)p * g.gsw_magic) >> 24), jj = p - r * (uint32_t)gsw;
-    dd[j] = (j < nwd && p < 16u * (uint32_t)gsw && jj < (uint32_t)gwr)
-                ? (1u << 31) | (r << 16) | ((uint32_t)b0 * BLK + jj * 16u) : 0u;
+    dd[j] = (j < nwd && p < (uint32_t)(ROWS * gsw) && jj < (uint32_t)gwr)
+                ? (1u << 31) | (r * row_bytes + (uint32_t)b0 * BLK + jj * 16u) : 0u;
   }
+  // copies this wave issues per tile: the slots with an active lane (a wave
+  // whose window is a single block can leave the last slot of a matrix
+  // empty); its vmcnt arithmetic counts these
+  uint32_t act = 0u;                           // wave-uniform: slot j has an active lane
+#pragma unroll
+  for (int j = 0; j < kMaxDma; ++j)
+    if (j < nwd && __builtin_amdgcn_ballot_w64((dd[j] >> 31) != 0u) != 0) act |= 1u << j;
+  const int ncp = __builtin_popcount(act);
   const uint8_t* cb0 = reinterpret_cast<const uint8_t*>(codes0);
   const uint8_t* cb1 = reinterpret_cast<const uint8_t*>(GATEUP ? codes1 : codes0);
-  const uint32_t row_bytes = (uint32_t)g.row_bytes;
+  const uint32_t up_lds = (uint32_t)(ROWS * gsw * 16);   // LDS byte offset of the up rows in a tile
   auto issue_tile = [&](int t) {
     int gi;
     int64_t rg;
@@ -247,25 +264,26 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
     const int64_t Rm = pick(R, g.gR, gi);
     const uint8_t* cbm = GATEUP ? cb0 : reinterpret_cast<const uint8_t*>(pick(codes0, g.gcodes, gi));
     uint8_t* slot = ring + (size_t)(t % NS) * g.slot_bytes;
-    const bool full = rg * ROWS + ROWS <= Rm;  // ragged last row group: rows past Rm read row Rm - 1
-    const int64_t gbase = rg * ROWS * g.row_bytes;
+    // the tile's rows of each matrix as one buffer: rows past the matrix
+    // (a ragged last row group) fall outside it and read as zeros
+    const int64_t r0 = rg * ROWS;
+    const int nbytes = (int)((Rm - r0 < ROWS ? Rm - r0 : ROWS) * (int64_t)row_bytes);
+    const __amdgpu_buffer_rsrc_t rs0 =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(cbm + r0 * g.row_bytes), (short)0, nbytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rs1 =
+        GATEUP ? __builtin_amdgcn_make_buffer_rsrc((void*)(cb1 + r0 * g.row_bytes), (short)0, nbytes, kRsrcWord3)
+               : rs0;
 #pragma unroll
     for (int j = 0; j < kMaxDma; ++j) {
-      if (j < nwd) {                           // every issued copy has an active lane
+      if (act & (1u << j)) {                   // slots with no active lane are not issued
         const uint32_t d = dd[j];
         if (d >> 31) {
-          const uint32_t r = (d >> 16) & 15u;
-          const uint32_t rr = GATEUP ? (r & 7u) : r;
-          const uint8_t* base = (GATEUP && r >= 8u) ? cb1 : cbm;
-          const uint8_t* src;
-          if (full) {
-            src = base + gbase + (rr * row_bytes + (d & 0xFFFFu));
-          } else {
-            int64_t row = rg * ROWS + rr;
-            row = row < Rm ? row : Rm - 1;
-            src = base + row * g.row_bytes + (d & 0xFFFFu);
-          }
-          __builtin_amdgcn_global_load_lds(src, slot + (size_t)j * 1024, 16, 0, 0);
+          const bool up = GATEUP && j >= nh;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              up ? rs1 : rs0,
+              (__attribute__((address_space(3))) void*)(slot + (up ? up_lds + (uint32_t)(j - nh) * 1024u
+                                                                   : (uint32_t)j * 1024u)),
+              16, (int)(d & 0x7FFFFFFFu), 0, 0, 0);
         }
       }
     }
@@ -290,7 +308,7 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
   int next = 0;                                // next tile to copy; tiles go out in order
   const int t0 = min(nmine, min(2, NS - g.xslots));
   for (; next < t0; ++next) issue_tile(next);
-  wait_vmcnt(nwd * t0);                        // the x slice has landed
+  wait_vmcnt(ncp * t0);                        // the x slice has landed
 
   // ---- 2. exponent of the slice per vector: its largest |x[n]| * 2^e lands
   // in [2^14, 2^15); then x' = f16(x 2^e) in place
@@ -392,7 +410,7 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
     // other to finish alone
     if ((t + (wave >> 2)) & 1) __builtin_amdgcn_s_setprio(1);
     else __builtin_amdgcn_s_setprio(0);
-    wait_vmcnt(nwd * (next - 1 - t));          // tile t has landed (tiles after it may be in flight)
+    wait_vmcnt(ncp * (next - 1 - t));          // tile t has landed (tiles after it may be in flight)
     const uint8_t* trow = ring + (size_t)(t % NS) * g.slot_bytes + (size_t)i * gsw * 16;
     f32x4 acc[4];
 #pragma unroll
@@ -548,19 +566,9 @@ bool axis1_geom(int64_t R, int64_t C, int M, int k, bool gateup, int64_t grid, A
     nb = b > nb ? b : nb;
   }
   g.gsw = nb * blk / 16 + 1;
-  g.nwd = (16 * g.gsw + 63) / 64;
+  const int nh = (rows * g.gsw + 63) / 64;     // copies per matrix of a tile
+  g.nwd = gateup ? 2 * nh : nh;
   if (g.nwd > kMaxDma) return false;
-  // the kernel's vmcnt arithmetic counts nwd copies per tile per wave: each
-  // of them must have at least one active lane (a real granule of the window)
-  for (int w = 0; w < kWaves; ++w) {
-    const int rb = w * g.per, re = rb + g.per;
-    const int gwr = (((re - 1) >> 3) - (rb >> 3) + 1) * blk / 16;
-    for (int j = 0; j < g.nwd; ++j) {
-      bool any = false;
-      for (int p = j * 64; p < j * 64 + 64 && p < 16 * g.gsw && !any; ++p) any = p % g.gsw < gwr;
-      if (!any) return false;
-    }
-  }
   g.gsw_magic = (uint32_t)(((1u << 24) + g.gsw - 1) / g.gsw);
   g.nmine_max = (int)((g.nrg + grid - 1) / grid);
   g.slot_bytes = (uint32_t)((16 * g.gsw * 16 + 255) / 256 * 256);
