@@ -9,11 +9,13 @@ terms cancel to almost zero: each rounding contributes up to 2^-24 of the
 running magnitude, which is set by the terms, not by the result.  The floor
 therefore measures such outputs against their own terms: with COND = 2^-6
 the error allowed near cancellation is 1e-5 / 64 * a_i, about 2.6 units of
-f32 roundoff (2^-24 a_i) -- below the worst case of even a two-level
-summation tree, so a kernel that loses more than a couple of roundings'
-worth of its terms fails.  (For N(0, 1) activations over 5120 inputs, a_i is
-about 45 times the typical |o_i|, so the floor sits near 0.7 times the rms
-output; for a sum dominated by one large term it equals |o_i|.)
+f32 roundoff (2^-24 a_i).  For scale: on the same inputs, f32 sums taken in
+the order of the pages' REDUCE kernel (per-lane partial sums, then a
+SIMD-group tree) lose up to 1.2 such units and a plain sequential f32 sum
+up to 10.3, so the bound admits a well-ordered f32 reduction and rejects a
+careless one.  (For N(0, 1) activations over 5120 inputs, a_i is about 45
+times the typical |o_i|, so the floor sits near 0.7 times the rms output;
+for a sum dominated by one large term it equals |o_i|.)
 
 bf16 outputs: the stored value must lie within one bf16 ulp of the bf16
 rounding of some value inside the f32 band above, i.e. its ordered bit key
