@@ -50,11 +50,24 @@ constexpr int kRsrcWord3 = 0x00020000;  // raw buffer resource, 32-bit data form
 constexpr int kXPer = 5;               // x granules per lane of a wave's slice (M * C <= 4 * 5120)
 constexpr uint32_t kPartBytes = kWaves * 4 * 16 * 4;   // one row group's partial tiles: f32 [wave][n][16 rows]
 constexpr int kMaxGroup = 4;           // matrices of one grouped call
+constexpr uint32_t kProgBytes = 64;    // row groups each wave has finished: u32 [wave]
 
 // Geometry shared by the host (LDS sizing) and the kernel.
 struct Axis1Geom {
-  int64_t R, C, nrg, row_bytes;
+  // the fields the first copies need come first, so they share the first
+  // lines of the kernel argument segment
+  int64_t R, row_bytes;
   int64_t ldx;          // elements between rows of x (C, or the full width for a column chunk)
+  int M;
+  int per;              // runs of 32 columns per wave (C / 256)
+  int gsw;              // granules per tile row of a wave's window (its blocks + one pad granule)
+  int nwd;              // copy slots per wave per tile (ceil(rows gsw / 64) per matrix)
+  uint32_t gsw_magic;   // ceil(2^24 / gsw): p / gsw == (p * gsw_magic) >> 24 for p < 4096
+  int nslots, xslots;
+  int nfull, nrem;      // row groups per workgroup: nfull, plus one for workgroups b < nrem
+  uint32_t slot_bytes, part_off, prog_off, total;
+  int nmine_max;
+  int64_t C, nrg;
   // Grouped call (plain axis 1 only): ngroup matrices of the same C and k
   // over the same x.  Matrix j owns the launch's row groups [gend[j - 1],
   // gend[j]) (gend[-1] = 0) and has gR[j] rows; matrix 0 is the kernel's
@@ -64,13 +77,6 @@ struct Axis1Geom {
   const uint32_t* gcodes[kMaxGroup];
   const uint16_t* gscales[kMaxGroup];
   void* gout[kMaxGroup];
-  int M;
-  int per;              // runs of 32 columns per wave (C / 256)
-  int gsw;              // granules per tile row of a wave's window (its blocks + one pad granule)
-  int nwd;              // copy slots per wave per tile (ceil(rows gsw / 64) per matrix)
-  uint32_t gsw_magic;   // ceil(2^24 / gsw): p / gsw == (p * gsw_magic) >> 24 for p < 4096
-  int nslots, xslots, nmine_max;
-  uint32_t slot_bytes, part_off, total;
 };
 
 __device__ __forceinline__ uint32_t max_abs8(const uint4& v) {
@@ -185,15 +191,22 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
   constexpr int BLK = WPB * 4;                 // bytes per packed block
   constexpr int ROWS = GATEUP ? 8 : 16;        // output rows per row group
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  // the pointers the first copies need are read with the geometry at entry
+  // (one wait for all of them instead of one per use)
+  asm volatile("" : : "s"(codes0), "s"(codes1), "s"(x), "s"(g.R), "s"(g.row_bytes), "s"(g.ldx), "s"(g.M), "s"(g.per));
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int i = lane & 15, q = lane >> 4;
   const int M = g.M;
   const int64_t R = g.R;
   const int NS = g.nslots, nwd = g.nwd, gsw = g.gsw;
-  const int nmine = (int)((g.nrg - 1 - (int64_t)blockIdx.x) / gridDim.x + 1);   // grid <= nrg
+  const int nmine = g.nfull + ((int)blockIdx.x < g.nrem ? 1 : 0);             // grid <= nrg
   uint8_t* ring = smem + (size_t)wave * NS * g.slot_bytes;                      // this wave's slots
   float* part = reinterpret_cast<float*>(smem + g.part_off);
+  // progress of the two waves of a SIMD (w and w ^ 4): the one ahead yields
+  const uint32_t prog_mine = lds_addr(smem + g.prog_off) + (uint32_t)wave * 4u;
+  const uint32_t prog_other = lds_addr(smem + g.prog_off) + (uint32_t)(wave ^ 4) * 4u;
+  lds_write_b32(prog_mine, 0u);
 
   // Grouped calls: the matrix gi of row group rg and its row group lrg in
   // that matrix (compile-time indices only, so the table stays in SGPRs).
@@ -226,6 +239,21 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
   const int rb = wave * per, re = rb + per;
   const int b0 = rb >> 3, b1 = (re - 1) >> 3;
   const int gwr = (b1 - b0 + 1) * (BLK / 16);  // granules of the window per row (< gsw)
+
+  // ---- 1. the wave's slice of x (M vectors) goes out first, into its last
+  // ring slots (the first tiles follow once their descriptors are ready)
+  const int gx = per * 4;                      // 16-byte granules of one vector's slice
+  const int nxg = M * gx;
+  const int nxw = (nxg + 63) / 64;
+  uint8_t* xsl = ring + (size_t)(NS - g.xslots) * g.slot_bytes;                  // [n][slice], then x'
+  for (int j = 0; j < nxw; ++j) {              // every issued copy has an active lane
+    const int p = j * 64 + lane;
+    if (p < nxg) {
+      const int n = (p >= gx) + (p >= 2 * gx) + (p >= 3 * gx), jj = p - n * gx;
+      __builtin_amdgcn_global_load_lds(x + (int64_t)n * g.ldx + (int64_t)rb * 32 + jj * 8, xsl + (size_t)j * 1024,
+                                       16, 0, 0);
+    }
+  }
 
   // copy descriptors.  A tile is ROWS rows of each matrix it reads (16 of
   // one, or 8 gate + 8 up).  Copy j moves granules p = 64 jh + lane of its
@@ -289,20 +317,6 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
     }
   };
 
-  // ---- 1. the wave's slice of x (M vectors) lands in its last ring slots
-  // while the first tiles go out
-  const int gx = per * 4;                      // 16-byte granules of one vector's slice
-  const int nxg = M * gx;
-  const int nxw = (nxg + 63) / 64;
-  uint8_t* xsl = ring + (size_t)(NS - g.xslots) * g.slot_bytes;                  // [n][slice], then x'
-  for (int j = 0; j < nxw; ++j) {              // every issued copy has an active lane
-    const int p = j * 64 + lane;
-    if (p < nxg) {
-      const int n = (p >= gx) + (p >= 2 * gx) + (p >= 3 * gx), jj = p - n * gx;
-      __builtin_amdgcn_global_load_lds(x + (int64_t)n * g.ldx + (int64_t)rb * 32 + jj * 8, xsl + (size_t)j * 1024,
-                                       16, 0, 0);
-    }
-  }
   // the ring fills a little at a time (a burst of copies would stall the
   // issuing wave): up to two tiles now, in slots the x slice does not use
   int next = 0;                                // next tile to copy; tiles go out in order
@@ -375,6 +389,7 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
   half8 B[NG][4];
   int wo[NG], so[NG];
   const int ngw = (per + 3) >> 2;              // groups of four runs (<= NG)
+  uint32_t ba[NG];
 #pragma unroll
   for (int gg = 0; gg < NG; ++gg) {
     const int run = rb + 4 * gg + q;
@@ -384,11 +399,15 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
     const int blk = (runc >> 3) - b0;          // block within the window
     wo[gg] = blk * WPB + w0;
     so[gg] = blk * WPB + (w0 + K == WPB ? 0 : w0 + K);   // word after the run, wrapping in the block
-    const uint8_t* bp = xsl + ((size_t)(i < M ? i : 0) * gx * 8 + (size_t)(runc - rb) * 32) * 2;
-    lds_u32x4 bv[4];
-    lds_read_b128x4(lds_addr(bp), bv);         // in-slice address for every lane
+    ba[gg] = lds_addr(xsl + ((size_t)(i < M ? i : 0) * gx * 8 + (size_t)(runc - rb) * 32) * 2);
+  }
+  {
+    lds_u32x4 bv[NG][4];
+    lds_read_b128x4n<NG>(ba, bv);              // in-slice address for every lane
 #pragma unroll
-    for (int u = 0; u < 4; ++u) B[gg][u] = __builtin_bit_cast(half8, bv[u]);
+    for (int gg = 0; gg < NG; ++gg)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) B[gg][u] = __builtin_bit_cast(half8, bv[gg][u]);
   }
 #pragma unroll
   for (int gg = 0; gg < NG; ++gg) {
@@ -405,11 +424,15 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
   const uint32_t mul = kMul;
   const uint64_t add64 = kAdd;
   for (int t = 0; t < nmine; ++t) {
-    // the two waves of a SIMD (w, w + 4) take turns at the higher issue
-    // priority, one row group each, so neither runs ahead and leaves the
-    // other to finish alone
-    if ((t + (wave >> 2)) & 1) __builtin_amdgcn_s_setprio(1);
-    else __builtin_amdgcn_s_setprio(0);
+    // the two waves of a SIMD (w, w ^ 4) share its VALU: the one that has
+    // finished more row groups drops to the lower issue priority, so neither
+    // runs ahead and leaves the other to finish alone (the hardware breaks
+    // ties by age, so on a tie the younger wave takes the higher priority)
+    {
+      const uint32_t other = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_read_b32(prog_other));
+      if ((uint32_t)t < other || ((uint32_t)t == other && wave >= 4)) __builtin_amdgcn_s_setprio(1);
+      else __builtin_amdgcn_s_setprio(0);
+    }
     wait_vmcnt(ncp * (next - 1 - t));          // tile t has landed (tiles after it may be in flight)
     const uint8_t* trow = ring + (size_t)(t % NS) * g.slot_bytes + (size_t)i * gsw * 16;
     f32x4 acc[4];
@@ -449,6 +472,7 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
 #pragma unroll
     for (int e = 0; e < 4; ++e) pv[e] = ldexpf(sum[e], -my_e);
     if (i < M) *reinterpret_cast<f32x4*>(part + ((size_t)(t * kWaves + wave) * 4 + i) * 16 + 4 * q) = pv;
+    lds_write_b32(prog_mine, (uint32_t)t + 1u);
     // refill: tiles up to t + NS may use the ring now (slot t is free, and
     // after this row group the x slots too), at most two per row group
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -571,16 +595,20 @@ bool axis1_geom(int64_t R, int64_t C, int M, int k, bool gateup, int64_t grid, A
   if (g.nwd > kMaxDma) return false;
   g.gsw_magic = (uint32_t)(((1u << 24) + g.gsw - 1) / g.gsw);
   g.nmine_max = (int)((g.nrg + grid - 1) / grid);
+  g.nfull = (int)(g.nrg / grid);
+  g.nrem = (int)(g.nrg % grid);
   g.slot_bytes = (uint32_t)((16 * g.gsw * 16 + 255) / 256 * 256);
   const uint64_t parts = (uint64_t)g.nmine_max * kPartBytes;
   if (parts >= kAxis1MaxLdsBytes) return false;
-  const uint64_t nsl = (kAxis1MaxLdsBytes - parts) / ((uint64_t)kWaves * g.slot_bytes);
+  if (parts + kProgBytes >= kAxis1MaxLdsBytes) return false;
+  const uint64_t nsl = (kAxis1MaxLdsBytes - parts - kProgBytes) / ((uint64_t)kWaves * g.slot_bytes);
   g.nslots = (int)(nsl < (uint64_t)kMaxSlots ? nsl : kMaxSlots);
   const uint64_t xbytes = (uint64_t)M * g.per * 64;   // one wave's x slice
   g.xslots = (int)((xbytes + g.slot_bytes - 1) / g.slot_bytes);
   if (g.nslots < 2 || g.nslots < g.xslots + 1) return false;
   g.part_off = (uint32_t)kWaves * g.nslots * g.slot_bytes;
-  g.total = (uint32_t)(g.part_off + parts);
+  g.prog_off = (uint32_t)(g.part_off + parts);
+  g.total = g.prog_off + kProgBytes;
   return g.total <= kAxis1MaxLdsBytes;
 }
 

@@ -54,6 +54,16 @@ __device__ __forceinline__ void lds_write_b128(uint32_t a, lds_u32x4 v) {
   asm volatile("ds_write_b128 %0, %1" : : "v"(a), "v"(v) : "memory");
 }
 
+__device__ __forceinline__ void lds_write_b32(uint32_t a, uint32_t v) {
+  asm volatile("ds_write_b32 %0, %1" : : "v"(a), "v"(v) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_read_b32(uint32_t a) {
+  uint32_t r;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(r) : "v"(a) : "memory");
+  return r;
+}
+
 __device__ __forceinline__ lds_u32x4 lds_read_b128(uint32_t a) {
   lds_u32x4 r;
   asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(r) : "v"(a) : "memory");
@@ -71,6 +81,43 @@ __device__ __forceinline__ void lds_read_b128x4(uint32_t a, lds_u32x4 (&o)[4]) {
       : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])
       : "v"(a)
       : "memory");
+}
+
+// four consecutive 16-byte reads at each of N addresses (N = 2 or 5), one wait
+template <int N>
+__device__ __forceinline__ void lds_read_b128x4n(const uint32_t (&a)[N], lds_u32x4 (&o)[N][4]) {
+  static_assert(N == 2 || N == 5, "two or five groups");
+  if constexpr (N == 2) {
+    asm volatile(
+        "ds_read_b128 %0, %8\n\tds_read_b128 %1, %8 offset:16\n\t"
+        "ds_read_b128 %2, %8 offset:32\n\tds_read_b128 %3, %8 offset:48\n\t"
+        "ds_read_b128 %4, %9\n\tds_read_b128 %5, %9 offset:16\n\t"
+        "ds_read_b128 %6, %9 offset:32\n\tds_read_b128 %7, %9 offset:48\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(o[0][0]), "=&v"(o[0][1]), "=&v"(o[0][2]), "=&v"(o[0][3]), "=&v"(o[1][0]), "=&v"(o[1][1]),
+          "=&v"(o[1][2]), "=&v"(o[1][3])
+        : "v"(a[0]), "v"(a[1])
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b128 %0, %20\n\tds_read_b128 %1, %20 offset:16\n\t"
+        "ds_read_b128 %2, %20 offset:32\n\tds_read_b128 %3, %20 offset:48\n\t"
+        "ds_read_b128 %4, %21\n\tds_read_b128 %5, %21 offset:16\n\t"
+        "ds_read_b128 %6, %21 offset:32\n\tds_read_b128 %7, %21 offset:48\n\t"
+        "ds_read_b128 %8, %22\n\tds_read_b128 %9, %22 offset:16\n\t"
+        "ds_read_b128 %10, %22 offset:32\n\tds_read_b128 %11, %22 offset:48\n\t"
+        "ds_read_b128 %12, %23\n\tds_read_b128 %13, %23 offset:16\n\t"
+        "ds_read_b128 %14, %23 offset:32\n\tds_read_b128 %15, %23 offset:48\n\t"
+        "ds_read_b128 %16, %24\n\tds_read_b128 %17, %24 offset:16\n\t"
+        "ds_read_b128 %18, %24 offset:32\n\tds_read_b128 %19, %24 offset:48\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(o[0][0]), "=&v"(o[0][1]), "=&v"(o[0][2]), "=&v"(o[0][3]), "=&v"(o[1][0]), "=&v"(o[1][1]),
+          "=&v"(o[1][2]), "=&v"(o[1][3]), "=&v"(o[2][0]), "=&v"(o[2][1]), "=&v"(o[2][2]), "=&v"(o[2][3]),
+          "=&v"(o[3][0]), "=&v"(o[3][1]), "=&v"(o[3][2]), "=&v"(o[3][3]), "=&v"(o[4][0]), "=&v"(o[4][1]),
+          "=&v"(o[4][2]), "=&v"(o[4][3])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4])
+        : "memory");
+  }
 }
 
 // five 16-byte reads at independent addresses
