@@ -46,6 +46,9 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxSlots = 4;           // tile ring depth per wave
 constexpr int kMaxDma = 8;             // copies per wave per tile (C <= 5120, k <= 4: 2 x 8 rows x 25 granules)
+// copies per wave per tile for a given k (k = 2: windows of at most four
+// 64-byte blocks, 16 rows x 17 granules)
+__host__ __device__ constexpr int max_dma(int k) { return k == 2 ? 6 : kMaxDma; }
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer resource, 32-bit data format
 constexpr int kXPer = 5;               // x granules per lane of a wave's slice (M * C <= 4 * 5120)
 constexpr uint32_t kPartBytes = kWaves * 4 * 16 * 4;   // one row group's partial tiles: f32 [wave][n][16 rows]
@@ -256,35 +259,30 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
   }
 
   // copy descriptors.  A tile is ROWS rows of each matrix it reads (16 of
-  // one, or 8 gate + 8 up).  Copy j moves granules p = 64 jh + lane of its
-  // matrix's rows: plain, jh = j; gate/up, copies [0, nh) read the gate rows
-  // and [nh, 2 nh) the up rows, jh = j mod nh, so every copy reads a single
-  // matrix.  Granule p is granule p % gsw of row p / gsw (granules past the
-  // wave's blocks are pad and not copied).  dd = active bit | byte offset of
-  // the granule from the tile's first row, computed once: a copy then needs
-  // no vector arithmetic, only the tile's buffer resource.
+  // one, or 8 gate rows then 8 up rows), row r of the tile r * gsw granules
+  // into the slot.  Copy j moves granules p = 64 (j mod nh) + lane of its
+  // matrix's rows; granule p is granule p % gsw of row p / gsw.  Lanes whose
+  // granule is a row's pad granule copy the row's first block into that pad
+  // (which nothing reads), so only the last copy of each matrix masks lanes:
+  // those past its ROWS rows, whose LDS would belong to the next rows or
+  // slot.  dd = the lane's byte offset from the tile's first row, computed
+  // once.
   const int nh = GATEUP ? nwd / 2 : nwd;
   const uint32_t row_bytes = (uint32_t)g.row_bytes;
-  uint32_t dd[kMaxDma];
+  constexpr int NDMA = max_dma(K);
+  uint32_t dd[NDMA];
 #pragma unroll
-  for (int j = 0; j < kMaxDma; ++j) {
+  for (int j = 0; j < NDMA; ++j) {
     const int jh = (GATEUP && j >= nh) ? j - nh : j;
     const uint32_t p = (uint32_t)(jh * 64 + lane);
     const uint32_t r = (uint32_t)(((uint64_t)p * g.gsw_magic) >> 24), jj = p - r * (uint32_t)gsw;
-    dd[j] = (j < nwd && p < (uint32_t)(ROWS * gsw) && jj < (uint32_t)gwr)
-                ? (1u << 31) | (r * row_bytes + (uint32_t)b0 * BLK + jj * 16u) : 0u;
+    dd[j] = (uint32_t)b0 * BLK + ((p < (uint32_t)(ROWS * gsw) && jj < (uint32_t)gwr) ? r * row_bytes + jj * 16u : 0u);
   }
-  // copies this wave issues per tile: the slots with an active lane (a wave
-  // whose window is a single block can leave the last slot of a matrix
-  // empty); its vmcnt arithmetic counts these
-  uint32_t act = 0u;                           // wave-uniform: slot j has an active lane
-#pragma unroll
-  for (int j = 0; j < kMaxDma; ++j)
-    if (j < nwd && __builtin_amdgcn_ballot_w64((dd[j] >> 31) != 0u) != 0) act |= 1u << j;
-  const int ncp = __builtin_popcount(act);
+  const bool tail_ok = (uint32_t)((nh - 1) * 64 + lane) < (uint32_t)(ROWS * gsw);   // lane of a last copy in use
+  const uint32_t up_lds = (uint32_t)(ROWS * gsw * 16);   // LDS byte offset of the up rows in a tile
+  const int ncp = nwd;                         // copies per tile (wave-uniform)
   const uint8_t* cb0 = reinterpret_cast<const uint8_t*>(codes0);
   const uint8_t* cb1 = reinterpret_cast<const uint8_t*>(GATEUP ? codes1 : codes0);
-  const uint32_t up_lds = (uint32_t)(ROWS * gsw * 16);   // LDS byte offset of the up rows in a tile
   auto issue_tile = [&](int t) {
     int gi;
     int64_t rg;
@@ -302,17 +300,15 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
         GATEUP ? __builtin_amdgcn_make_buffer_rsrc((void*)(cb1 + r0 * g.row_bytes), (short)0, nbytes, kRsrcWord3)
                : rs0;
 #pragma unroll
-    for (int j = 0; j < kMaxDma; ++j) {
-      if (act & (1u << j)) {                   // slots with no active lane are not issued
-        const uint32_t d = dd[j];
-        if (d >> 31) {
-          const bool up = GATEUP && j >= nh;
+    for (int j = 0; j < NDMA; ++j) {
+      if (j < nwd) {
+        const bool up = GATEUP && j >= nh;
+        const int jh = up ? j - nh : j;
+        if (jh < nh - 1 || tail_ok)
           __builtin_amdgcn_raw_ptr_buffer_load_lds(
               up ? rs1 : rs0,
-              (__attribute__((address_space(3))) void*)(slot + (up ? up_lds + (uint32_t)(j - nh) * 1024u
-                                                                   : (uint32_t)j * 1024u)),
-              16, (int)(d & 0x7FFFFFFFu), 0, 0, 0);
-        }
+              (__attribute__((address_space(3))) void*)(slot + (up ? up_lds : 0u) + (uint32_t)jh * 1024u), 16,
+              (int)dd[j], 0, 0, 0);
       }
     }
   };
@@ -345,6 +341,7 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
   uint32_t mx0 = 0u, mx1 = 0u, mx2 = 0u, mx3 = 0u;
 #pragma unroll
   for (int u = 0; u < kXPer; ++u) {
+    if (u >= nxw) break;                       // granules of the M vectors only (wave-uniform)
     const int p = lane + 64 * u;
     const uint32_t a = max_abs8(xr[u]);        // zero past the slice
     const int n = (p >= gx) + (p >= 2 * gx) + (p >= 3 * gx);
@@ -369,6 +366,7 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
   const int e0 = exponent(mx0), e1 = exponent(mx1), e2 = exponent(mx2), e3 = exponent(mx3);
 #pragma unroll
   for (int u = 0; u < kXPer; ++u) {
+    if (u >= nxw) break;
     const int p = lane + 64 * u;
     const int n = (p >= gx) + (p >= 2 * gx) + (p >= 3 * gx);
     const int en = n == 0 ? e0 : n == 1 ? e1 : n == 2 ? e2 : e3;
@@ -385,7 +383,10 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
 
   // ---- 3. B operand in registers: lane (n, q) of group gg holds
   // x'[n, run * 32 + 8u .. +7] for run = rb + 4 gg + q (zero past the M
-  // vectors or past the slice, whose A lanes then decode run rb).
+  // vectors or past the slice, whose A lanes then decode run rb): those
+  // lanes read 64 zero bytes written after the slice's x'.
+  const uint32_t zero_lds = lds_addr(xsl) + (uint32_t)nxg * 16u;
+  if (lane < 4) lds_write_b128(zero_lds + (uint32_t)lane * 16u, lds_u32x4{0u, 0u, 0u, 0u});
   half8 B[NG][4];
   int wo[NG], so[NG];
   const int ngw = (per + 3) >> 2;              // groups of four runs (<= NG)
@@ -399,7 +400,7 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
     const int blk = (runc >> 3) - b0;          // block within the window
     wo[gg] = blk * WPB + w0;
     so[gg] = blk * WPB + (w0 + K == WPB ? 0 : w0 + K);   // word after the run, wrapping in the block
-    ba[gg] = lds_addr(xsl + ((size_t)(i < M ? i : 0) * gx * 8 + (size_t)(runc - rb) * 32) * 2);
+    ba[gg] = (valid && i < M) ? lds_addr(xsl + ((size_t)i * gx * 8 + (size_t)(runc - rb) * 32) * 2) : zero_lds;
   }
   {
     lds_u32x4 bv[NG][4];
@@ -408,13 +409,6 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
     for (int gg = 0; gg < NG; ++gg)
 #pragma unroll
       for (int u = 0; u < 4; ++u) B[gg][u] = __builtin_bit_cast(half8, bv[gg][u]);
-  }
-#pragma unroll
-  for (int gg = 0; gg < NG; ++gg) {
-    const bool keep = (rb + 4 * gg + q < re) && i < M;
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (!keep) B[gg][u] = half8{0, 0, 0, 0, 0, 0, 0, 0};
   }
   const int my_e = i == 0 ? e0 : i == 1 ? e1 : i == 2 ? e2 : e3;     // scale of column n = i
 
@@ -592,7 +586,7 @@ bool axis1_geom(int64_t R, int64_t C, int M, int k, bool gateup, int64_t grid, A
   g.gsw = nb * blk / 16 + 1;
   const int nh = (rows * g.gsw + 63) / 64;     // copies per matrix of a tile
   g.nwd = gateup ? 2 * nh : nh;
-  if (g.nwd > kMaxDma) return false;
+  if (g.nwd > max_dma(k)) return false;
   g.gsw_magic = (uint32_t)(((1u << 24) + g.gsw - 1) / g.gsw);
   g.nmine_max = (int)((g.nrg + grid - 1) / grid);
   g.nfull = (int)(g.nrg / grid);
@@ -603,7 +597,7 @@ bool axis1_geom(int64_t R, int64_t C, int M, int k, bool gateup, int64_t grid, A
   if (parts + kProgBytes >= kAxis1MaxLdsBytes) return false;
   const uint64_t nsl = (kAxis1MaxLdsBytes - parts - kProgBytes) / ((uint64_t)kWaves * g.slot_bytes);
   g.nslots = (int)(nsl < (uint64_t)kMaxSlots ? nsl : kMaxSlots);
-  const uint64_t xbytes = (uint64_t)M * g.per * 64;   // one wave's x slice
+  const uint64_t xbytes = (uint64_t)M * g.per * 64 + 64;   // one wave's x slice and 64 zero bytes
   g.xslots = (int)((xbytes + g.slot_bytes - 1) / g.slot_bytes);
   if (g.nslots < 2 || g.nslots < g.xslots + 1) return false;
   g.part_off = (uint32_t)kWaves * g.nslots * g.slot_bytes;
