@@ -22,7 +22,7 @@
 //   D: f32 sums of signed products (no offset to cancel).
 // Work: workgroup (column group g of 256 columns, row split s) with 8 waves;
 // wave w takes the split's 32-row blocks w, w + 8, ... through its own LDS
-// ring (global_load_lds copies, explicit vmcnt waits, no barrier in the
+// ring (buffer_load ... lds copies, explicit vmcnt waits, no barrier in the
 // loop).  The waves' D tiles meet in LDS at the end; the workgroup writes its
 // f32 partial [s][m][c], scaled back by 2^-e_n; a fold kernel adds the splits.
 #include <mutex>
@@ -44,6 +44,13 @@ constexpr int kMaxSlots = 3;
 constexpr int kMaxDma = 5;                // copies per wave per 32-row tile (k = 4: 32 rows x 9 granules)
 constexpr int kMaxRowsPerSplit = 2048;
 constexpr size_t kLdsBudget = 160 * 1024;
+constexpr uint32_t kProgBytes = 64;       // blocks each wave has finished: u32 [wave]
+// Pad granules after every 8 tile rows.  Lane group q reads tile rows 8q ..
+// 8q+7; with rows gsr granules apart alone (a multiple of 4 dwords), rows 8
+// apart fall in the same LDS banks and the four groups' reads would conflict
+// four ways.  Two extra granules shift group q by 8q dwords: the words one
+// read instruction touches (at most 8 per group) then lie in disjoint banks.
+constexpr int kQuadPad = 2;
 
 struct Axis0Geom {
   int64_t R, C;
@@ -51,11 +58,13 @@ struct Axis0Geom {
   int64_t row_bytes;       // stride between stored rows (2 blocks when interleaved)
   int interleave;          // codes in the block-interleaved layout [C/512, R, 2 wpb]
   int gsr;                // granules per tile row in LDS (the group's block + one pad granule)
+  int gq;                 // granules per 8 tile rows: 8 gsr + kQuadPad
   int nwd;                // copies per wave per tile
   int nslots;
   int scales16;           // scales 16-byte aligned: 16-byte loads in the prologue
   int x16;                // every row of x 16-byte aligned (x aligned, R % 8 == 0)
-  uint32_t slot_bytes, xt_off, scr_off, total;
+  uint32_t slot_bytes, xt_off, scr_off, prog_off, total;
+  uint32_t scr_wave;      // bytes per wave in the scratch area: its x / scale staging, then its D tiles
 };
 
 // Row pairs of one chunk word: ds_read2_b32 of tile rows (0,1), (2,3), (4,5),
@@ -117,6 +126,11 @@ __global__ __launch_bounds__(kThreads) void axis0_kernel(const uint32_t* __restr
   constexpr int BLK = WPB * 4;                 // bytes of one block of a row
   constexpr int GSR = BLK / 16 + 1;            // granules per tile row in LDS (one pad granule)
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  // the arguments the prologue needs are read together at entry (one wait
+  // instead of one per first use)
+  asm volatile("" : : "s"(codes), "s"(scales), "s"(x), "s"(g.R), "s"(g.M), "s"(g.ncg), "s"(g.S), "s"(g.rps),
+               "s"(g.row_bytes), "s"(g.interleave), "s"(g.nwd), "s"(g.nslots), "s"(g.scales16), "s"(g.x16),
+               "s"(g.slot_bytes), "s"(g.xt_off), "s"(g.scr_off), "s"(g.prog_off), "s"(g.scr_wave));
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int i = lane & 15, q = lane >> 4;
@@ -138,75 +152,91 @@ __global__ __launch_bounds__(kThreads) void axis0_kernel(const uint32_t* __restr
   const int nblk = (nr + 31) >> 5;
   const int NS = g.nslots, nwd = g.nwd;
   constexpr int gsr = GSR;
+  constexpr int GQ = 8 * GSR + kQuadPad;       // granules per 8 tile rows
   uint8_t* ring = smem + (size_t)wave * NS * g.slot_bytes;
   uint16_t* xt = reinterpret_cast<uint16_t*>(smem + g.xt_off);        // f16 [8][rps]: hi n, lo n
-  float* scr = reinterpret_cast<float*>(smem + g.scr_off);            // the waves' D tiles at the end
+  uint8_t* scr = smem + g.scr_off + (size_t)wave * g.scr_wave;        // this wave's staging, then its D tiles
+  // progress of the two waves of a SIMD (w and w ^ 4): the one ahead yields
+  const uint32_t prog_mine = lds_addr(smem + g.prog_off) + (uint32_t)wave * 4u;
+  const uint32_t prog_other = lds_addr(smem + g.prog_off) + (uint32_t)(wave ^ 4) * 4u;
+  lds_write_b32(prog_mine, 0u);
 
-  // ---- 2. copy descriptors: tile granule p = 64 j + lane is granule p % gsr
-  // of tile row p / gsr (the last granule of a row is pad).  Then the first tiles.
+  // ---- 1. x~ staging: lane (t, g) of the wave will hold rows 8g .. 8g+7 of
+  // its t-th block.  When x and scales are 16-byte aligned and the wave's
+  // rows are whole, the copy engine brings its x and scale granules into the
+  // wave's scratch first, ahead of the first tiles, so only they are waited
+  // for; otherwise plain loads (which then wait behind the tiles).
   const int nmy = nblk > wave ? (nblk - 1 - wave) / kWaves + 1 : 0;   // this wave's 32-row blocks
-  uint32_t dd[kMaxDma];
+  const int tb = lane >> 2, g8 = lane & 3;
+  const bool hold = tb < nmy;
+  const int rl = (wave + kWaves * tb) * 32 + 8 * g8;   // first row of the lane's eight, in the split
+  const bool fast = g.x16 && g.scales16 && nmy > 0 && (wave + kWaves * (nmy - 1)) * 32 + 32 <= nr;
+  uint8_t* stg = scr;                          // 1 KB each: x[0 .. M-1], then the scales
+  if (fast) {
+#pragma unroll
+    for (int c = 0; c < 5; ++c) {
+      if (c < M || c == 4) {                   // lane 0 holds rows of the wave's first block: active
+        const uint16_t* src = c < 4 ? x + (int64_t)c * R + r0 + rl : scales + r0 + rl;
+        if (hold) __builtin_amdgcn_global_load_lds(src, stg + (c < 4 ? c : M) * 1024, 16, 0, 0);
+      }
+    }
+  }
+
+  // ---- 2. copy descriptors: tile granule p = 64 j + lane lies in group p / gq
+  // of 8 rows; within it, granule c = rem % gsr of row rem / gsr (rem = p % gq;
+  // the last granule of a row and the group's last kQuadPad granules are
+  // pad).  Then the first tiles.
+  uint32_t dd[kMaxDma];                       // active bit | byte offset from the tile's first row
 #pragma unroll
   for (int j = 0; j < kMaxDma; ++j) {
     const int p = j * 64 + lane;
-    const int rr = p / gsr, gg = p - rr * gsr;
-    dd[j] = (j < nwd && p < 32 * gsr && gg < gsr - 1) ? (1u << 31) | ((uint32_t)rr << 16) | (uint32_t)(gg * 16) : 0u;
+    const int g8 = p / GQ, rem = p - g8 * GQ;
+    const int rr = 8 * g8 + rem / gsr, gg = rem % gsr;
+    dd[j] = (j < nwd && g8 < 4 && rem < 8 * gsr && gg < gsr - 1)
+                ? (1u << 31) | ((uint32_t)rr * (uint32_t)g.row_bytes + (uint32_t)(gg * 16)) : 0u;
   }
   // this column group's block of row 0; rows follow at g.row_bytes
   const uint8_t* cb = reinterpret_cast<const uint8_t*>(codes) +
                       (g.interleave ? ((int64_t)(cgi >> 1) * R * 2 + (cgi & 1)) * BLK : (int64_t)cgi * BLK);
+  // The tiles go through a buffer resource per tile (rows past R fall outside
+  // it and read as zeros; their x~ is zero): buffer copies count only against
+  // vmcnt, so the LDS reads of the loop, which wait for lgkmcnt(0), do not
+  // wait for the tiles still in flight (global-address copies would count
+  // against both).
   auto issue_tile = [&](int t) {             // t-th block of this wave
     const int64_t rowb = r0 + (int64_t)(wave + kWaves * t) * 32;
+    const int64_t left = R - rowb;
+    const int nbytes = (int)((left < 32 ? left : 32) * g.row_bytes);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(cb + rowb * g.row_bytes), (short)0, nbytes, kRawBufferWord3);
     uint8_t* slot = ring + (size_t)(t % NS) * g.slot_bytes;
 #pragma unroll
     for (int j = 0; j < kMaxDma; ++j) {
       if (j < nwd) {                           // every issued copy has an active lane
         const uint32_t d = dd[j];
-        if (d >> 31) {
-          int64_t row = rowb + ((d >> 16) & 31u);
-          row = row < R ? row : R - 1;         // rows past R read row R - 1 (their x~ is zero)
-          __builtin_amdgcn_global_load_lds(cb + row * g.row_bytes + (d & 0xFFFFu), slot + (size_t)j * 1024,
-                                           16, 0, 0);
-        }
+        if (d >> 31)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(slot + (size_t)j * 1024),
+                                                   16, (int)(d & 0x7FFFFFFFu), 0, 0, 0);
       }
     }
   };
 
-  // ---- 3. x~[n, r] = scale[r] * x[n, r] (exact in f32) for this wave's rows:
-  // lane (t, g) of the wave holds rows 8g .. 8g+7 of its t-th block, loaded
-  // 16 bytes at a time.  The wave's largest |x~[n]| * 2^e lands in
+  // ---- 3. x~[n, r] = scale[r] * x[n, r] (exact in f32) for this wave's rows,
+  // eight per lane as staged above.  The wave's largest |x~[n]| * 2^e lands in
   // [2^14, 2^15); x~ 2^e is split into f16 hi and lo halves in xt, and the
   // wave's partial sums are scaled back by 2^-e at the end.
-  const int tb = lane >> 2, g8 = lane & 3;
-  const bool hold = tb < nmy;
-  const int rl = (wave + kWaves * tb) * 32 + 8 * g8;   // first row of the lane's eight, in the split
   float xv[4][8];
   uint32_t mx0 = 0u, mx1 = 0u, mx2 = 0u, mx3 = 0u;
   {
-    // when x and scales are 16-byte aligned and the wave's rows are whole, the
-    // copy engine brings its x and scale granules into ring slots 1-2 ahead of
-    // tile 0, so only they are waited for; otherwise plain loads (which then
-    // wait behind tile 0)
-    const bool fast = g.x16 && g.scales16 && NS >= 3 && nmy > 0 && (wave + kWaves * (nmy - 1)) * 32 + 32 <= nr;
-    uint8_t* stg = ring + g.slot_bytes;        // 5 x 1 KB: x[0..3], scales
-    if (fast) {
-#pragma unroll
-      for (int c = 0; c < 5; ++c) {
-        if (c < M || c == 4) {                 // lane 0 holds rows of the wave's first block: active
-          const uint16_t* src = c < 4 ? x + (int64_t)c * R + r0 + rl : scales + r0 + rl;
-          if (hold) __builtin_amdgcn_global_load_lds(src, stg + c * 1024, 16, 0, 0);
-        }
-      }
-    }
     int next0 = 0;
-    if (nmy > 0) issue_tile(next0++);          // tile 0 streams while x is prepared
+    for (; next0 < min(nmy, 1); ++next0) issue_tile(next0);   // tile 0 streams while x is prepared (more tiles would delay it)
     uint4 xb[4];
     uint16_t sb[8];
     if (fast) {
       wait_vmcnt(nwd * next0);                 // the x and scale copies have landed
       uint32_t sa[5];
 #pragma unroll
-      for (int c = 0; c < 5; ++c) sa[c] = lds_addr(stg) + (uint32_t)(c * 1024 + lane * 16);
+      for (int c = 0; c < 5; ++c) sa[c] = lds_addr(stg) + (uint32_t)((c < 4 ? (c < M ? c : 0) : M) * 1024 + lane * 16);
       lds_u32x4 sv[5];
       lds_read_b128x5(sa, sv);                 // lanes without copies read stale bytes, masked here
 #pragma unroll
@@ -275,8 +305,8 @@ __global__ __launch_bounds__(kThreads) void axis0_kernel(const uint32_t* __restr
     }
   }
 
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);     // the staging reads above stay before slots 1-2 refill
-  int next = nmy > 0 ? 1 : 0;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  int next = min(nmy, 1);
   for (; next < min(nmy, NS); ++next) issue_tile(next);
 
   // ---- 4. per-lane decode geometry for the four chunks: the 32-bit window
@@ -307,15 +337,18 @@ __global__ __launch_bounds__(kThreads) void axis0_kernel(const uint32_t* __restr
   const uint32_t mul = kMul;
   const uint64_t add64 = kAdd;
   for (int t = 0; t < nmy; ++t) {
-    // the two waves of a SIMD (w, w + 4) take turns at the higher issue
-    // priority, one block each, so neither runs ahead and leaves the other
-    // to finish alone
-    if ((t + (wave >> 2)) & 1) __builtin_amdgcn_s_setprio(1);
-    else __builtin_amdgcn_s_setprio(0);
+    // the two waves of a SIMD (w, w ^ 4) share its VALU: the one that has
+    // finished more blocks drops to the lower issue priority (on a tie the
+    // younger wave takes the higher one: the hardware favours the older)
+    {
+      const uint32_t other = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_read_b32(prog_other));
+      if ((uint32_t)t < other || ((uint32_t)t == other && wave >= 4)) __builtin_amdgcn_s_setprio(1);
+      else __builtin_amdgcn_s_setprio(0);
+    }
     wait_vmcnt(nwd * (next - 1 - t));          // tile t has landed
     const int blk = wave + kWaves * t;
     half8 Bv;
-    const uint8_t* tile = ring + (size_t)(t % NS) * g.slot_bytes + (size_t)(8 * q) * gsr * 16;
+    const uint8_t* tile = ring + (size_t)(t % NS) * g.slot_bytes + (size_t)q * GQ * 16;
     // 8 rows x 4 columns: windows, then 1MAD words, then row-paired codes
     auto decode_chunk = [&](int ch, const uint32_t (&W)[8][2]) {
       uint32_t st[8][4];
@@ -351,13 +384,14 @@ __global__ __launch_bounds__(kThreads) void axis0_kernel(const uint32_t* __restr
       decode_chunk(ch, W[0]);
       decode_chunk(ch + 1, W[1]);
     }
+    lds_write_b32(prog_mine, (uint32_t)t + 1u);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);   // this tile's reads stay before its slot is refilled
     if (next < nmy && next <= t + NS) issue_tile(next++);
   }
 
   // ---- 5. hi + lo into LDS; the waves' tiles are added in a
   // fixed order and scaled by 1 / d * 2^-e_n into the partial of this split
-  float* red = scr;                            // f32 [wave][M][kCols]
+  float* red = reinterpret_cast<float*>(scr);  // f32 [M][kCols] of this wave, scr_wave bytes apart
 #pragma unroll
   for (int ch = 0; ch < kChunks; ++ch)
 #pragma unroll
@@ -373,7 +407,7 @@ __global__ __launch_bounds__(kThreads) void axis0_kernel(const uint32_t* __restr
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int col = ch * 64 + 4 * (4 * q + e) + j;   // MFMA row 4q + e of chunk ch, MFMA j
-          red[(wave * M + i) * kCols + col] = ldexpf(tot[e], -my_e);   // exact: common units
+          red[i * kCols + col] = ldexpf(tot[e], -my_e);   // exact: common units
         }
       }
     }
@@ -382,7 +416,8 @@ __global__ __launch_bounds__(kThreads) void axis0_kernel(const uint32_t* __restr
     const int n = idx / kCols, col = idx - n * kCols;
     float v = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) v += red[(w * M + n) * kCols + col];
+    for (int w = 0; w < kWaves; ++w)
+      v += reinterpret_cast<const float*>(smem + g.scr_off + (size_t)w * g.scr_wave)[n * kCols + col];
     partial[((int64_t)s * M + n) * C + (int64_t)cgi * kCols + col] = v * kRcp;
   }
 }
@@ -436,12 +471,15 @@ bool axis0_geom(int64_t R, int64_t C, int M, int k, Axis0Geom& g) {
   g.row_bytes = C * k / 8;
   g.interleave = 0;
   g.gsr = blk / 16 + 1;
-  g.nwd = (32 * g.gsr + 63) / 64;
+  g.gq = 8 * g.gsr + kQuadPad;
+  g.nwd = (4 * g.gq + 63) / 64;
   if (g.nwd > kMaxDma) return false;
-  g.slot_bytes = (uint32_t)((32 * g.gsr * 16 + 255) / 256 * 256);
+  g.slot_bytes = (uint32_t)((4 * g.gq * 16 + 255) / 256 * 256);
   const size_t xt = (size_t)8 * g.rps * 2;
-  const size_t scr = (size_t)kWaves * M * kCols * 4;
-  const size_t fixed = ((xt + 255) / 256 + (scr + 255) / 256) * 256;
+  // per wave: its x and scale staging ((M + 1) KB), later its D tiles (M KB)
+  g.scr_wave = (uint32_t)((size_t)(M + 1) * 1024);
+  const size_t scr = (size_t)kWaves * g.scr_wave;
+  const size_t fixed = ((xt + 255) / 256 + (scr + 255) / 256) * 256 + kProgBytes;
   if (fixed >= kLdsBudget) return false;
   size_t ns = (kLdsBudget - fixed) / ((size_t)kWaves * g.slot_bytes);
   if (ns > (size_t)kMaxSlots) ns = kMaxSlots;
@@ -449,7 +487,8 @@ bool axis0_geom(int64_t R, int64_t C, int M, int k, Axis0Geom& g) {
   g.nslots = (int)ns;
   g.xt_off = (uint32_t)kWaves * g.nslots * g.slot_bytes;
   g.scr_off = g.xt_off + (uint32_t)((xt + 255) / 256 * 256);
-  g.total = g.scr_off + (uint32_t)((scr + 255) / 256 * 256);
+  g.prog_off = g.scr_off + (uint32_t)((scr + 255) / 256 * 256);
+  g.total = g.prog_off + kProgBytes;
   g.scales16 = 0;
   g.x16 = 0;
   return g.total <= kLdsBudget;

@@ -49,7 +49,6 @@ constexpr int kMaxDma = 8;             // copies per wave per tile (C <= 5120, k
 // copies per wave per tile for a given k (k = 2: windows of at most four
 // 64-byte blocks, 16 rows x 17 granules)
 __host__ __device__ constexpr int max_dma(int k) { return k == 2 ? 6 : kMaxDma; }
-constexpr int kRsrcWord3 = 0x00020000;  // raw buffer resource, 32-bit data format
 constexpr int kXPer = 5;               // x granules per lane of a wave's slice (M * C <= 4 * 5120)
 constexpr uint32_t kPartBytes = kWaves * 4 * 16 * 4;   // one row group's partial tiles: f32 [wave][n][16 rows]
 constexpr int kMaxGroup = 4;           // matrices of one grouped call
@@ -295,9 +294,9 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
     const int64_t r0 = rg * ROWS;
     const int nbytes = (int)((Rm - r0 < ROWS ? Rm - r0 : ROWS) * (int64_t)row_bytes);
     const __amdgpu_buffer_rsrc_t rs0 =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(cbm + r0 * g.row_bytes), (short)0, nbytes, kRsrcWord3);
+        __builtin_amdgcn_make_buffer_rsrc((void*)(cbm + r0 * g.row_bytes), (short)0, nbytes, kRawBufferWord3);
     const __amdgpu_buffer_rsrc_t rs1 =
-        GATEUP ? __builtin_amdgcn_make_buffer_rsrc((void*)(cb1 + r0 * g.row_bytes), (short)0, nbytes, kRsrcWord3)
+        GATEUP ? __builtin_amdgcn_make_buffer_rsrc((void*)(cb1 + r0 * g.row_bytes), (short)0, nbytes, kRawBufferWord3)
                : rs0;
 #pragma unroll
     for (int j = 0; j < NDMA; ++j) {

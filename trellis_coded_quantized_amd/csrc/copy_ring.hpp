@@ -10,6 +10,11 @@
 
 namespace trellis {
 
+// Word 3 of a raw buffer resource (32-bit data format, no swizzle): the
+// copies address a tile through such a resource, with its size in bytes as
+// the record count, so reads past it return zeros.
+constexpr int kRawBufferWord3 = 0x00020000;
+
 // s_waitcnt vmcnt(n) with expcnt / lgkmcnt left alone (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void waitcnt_vm() {
