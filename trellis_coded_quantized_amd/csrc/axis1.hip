@@ -67,6 +67,9 @@ struct Axis1Geom {
   uint32_t gsw_magic;   // ceil(2^24 / gsw): p / gsw == (p * gsw_magic) >> 24 for p < 4096
   int nslots, xslots;
   int nfull, nrem;      // row groups per workgroup: nfull, plus one for workgroups b < nrem
+  // half = 1: the last nrem row groups run as 2 nrem halves (ROWS / 2 output
+  // rows each), one on each workgroup b < 2 nrem, after its nfull whole ones
+  int half;
   uint32_t slot_bytes, part_off, prog_off, total;
   int nmine_max;
   int64_t C, nrg;
@@ -202,7 +205,10 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
   const int M = g.M;
   const int64_t R = g.R;
   const int NS = g.nslots, nwd = g.nwd, gsw = g.gsw;
-  const int nmine = g.nfull + ((int)blockIdx.x < g.nrem ? 1 : 0);             // grid <= nrg
+  const int bid = (int)blockIdx.x;
+  const bool hit = g.half && bid < 2 * g.nrem;                                  // this workgroup has a half row group
+  const int nmine = g.nfull + ((g.half ? hit : bid < g.nrem) ? 1 : 0);          // row groups (the half last)
+  const int nwhole = hit ? g.nfull : nmine;
   uint8_t* ring = smem + (size_t)wave * NS * g.slot_bytes;                      // this wave's slots
   float* part = reinterpret_cast<float*>(smem + g.part_off);
   // progress of the two waves of a SIMD (w and w ^ 4): the one ahead yields
@@ -233,6 +239,10 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
         if (gi == j) p = tab[j];
     }
     return p;
+  };
+  // row group of item t: whole ones bid + t grid, the half nfull grid + bid / 2
+  auto item_rg = [&](int t) -> int64_t {
+    return (hit && t == g.nfull) ? (int64_t)g.nfull * gridDim.x + (bid >> 1) : (int64_t)bid + (int64_t)t * gridDim.x;
   };
 
   // ---- this wave's slice: runs [rb, re) of 32 columns, held in packed
@@ -285,14 +295,18 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
   auto issue_tile = [&](int t) {
     int gi;
     int64_t rg;
-    locate((int64_t)blockIdx.x + (int64_t)t * gridDim.x, gi, rg);
+    locate(item_rg(t), gi, rg);
     const int64_t Rm = pick(R, g.gR, gi);
     const uint8_t* cbm = GATEUP ? cb0 : reinterpret_cast<const uint8_t*>(pick(codes0, g.gcodes, gi));
     uint8_t* slot = ring + (size_t)(t % NS) * g.slot_bytes;
     // the tile's rows of each matrix as one buffer: rows past the matrix
-    // (a ragged last row group) fall outside it and read as zeros
-    const int64_t r0 = rg * ROWS;
-    const int nbytes = (int)((Rm - r0 < ROWS ? Rm - r0 : ROWS) * (int64_t)row_bytes);
+    // (a ragged last row group) or past a half's ROWS / 2 rows fall outside
+    // it and read as zeros
+    const bool hf = hit && t == g.nfull;
+    const int64_t r0 = rg * ROWS + (hf ? (bid & 1) * (ROWS / 2) : 0);
+    const int64_t nrow = hf ? ROWS / 2 : ROWS;
+    const int64_t left = Rm - r0;
+    const int nbytes = (int)((left < nrow ? (left > 0 ? left : 0) : nrow) * (int64_t)row_bytes);
     const __amdgpu_buffer_rsrc_t rs0 =
         __builtin_amdgcn_make_buffer_rsrc((void*)(cbm + r0 * g.row_bytes), (short)0, nbytes, kRawBufferWord3);
     const __amdgpu_buffer_rsrc_t rs1 =
@@ -416,7 +430,7 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
 
   const uint32_t mul = kMul;
   const uint64_t add64 = kAdd;
-  for (int t = 0; t < nmine; ++t) {
+  for (int t = 0; t < nwhole; ++t) {
     // the two waves of a SIMD (w, w ^ 4) share its VALU: the one that has
     // finished more row groups drops to the lower issue priority, so neither
     // runs ahead and leaves the other to finish alone (the hardware breaks
@@ -473,29 +487,96 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
     for (; next <= upto; ++next) issue_tile(next);
   }
 
+  // ---- 4b. the half row group (always the last item): ROWS / 2 output
+  // rows.  MFMA row i < 8 carries output row i & 7 (gate/up: gate rows 0-3,
+  // up rows 4-7) at run positions 0-15, row 8 + i the same output row at
+  // positions 16-31; B columns 0-3 hold x' of positions 0-15 (the lane's
+  // own B[gg][0..1]) and columns 4-7 x' of positions 16-31 (B[gg][2..3] of
+  // lane n - 4, one DPP row shift).  D rows 0-7 x columns 0-3 and rows 8-15
+  // x columns 4-7 are the two halves of each sum; the epilogue adds them.
+  if (hit) {
+    const int t = g.nfull;
+    wait_vmcnt(0);
+    const int hr = GATEUP ? ((i & 7) < 4 ? (i & 3) : 8 + (i & 3)) : (i & 7);   // tile row of the lane
+    const uint32_t tbh = lds_addr(ring + (size_t)(t % NS) * g.slot_bytes + (size_t)hr * gsw * 16);
+    uint32_t aw[5], as[5];
+#pragma unroll
+    for (int gg = 0; gg < 5; ++gg) {
+      aw[gg] = tbh + (uint32_t)wo[gg < NG ? gg : 0] * 4u;
+      as[gg] = tbh + (uint32_t)so[gg < NG ? gg : 0] * 4u;
+    }
+    uint32_t W[5][K + 1];
+    lds_read_runs5<K>(aw, as, W);
+    f32x4 hacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) {
+      if (gg < ngw) {
+        u32x4 A2[2];
+        if constexpr (DECODE) {
+          decode_half_codes<K>(W[gg], i >= 8, mul, add64, A2);
+        } else {
+#pragma unroll
+          for (int u = 0; u < 2; ++u) A2[u] = u32x4{W[gg][u % (K + 1)], W[gg][(u + 1) % (K + 1)], W[gg][0], W[gg][K]};
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const u32x4 own = __builtin_bit_cast(u32x4, B[gg][u]);
+          const u32x4 hi = __builtin_bit_cast(u32x4, B[gg][u + 2]);
+          // lanes 4-7 of each row take lane n - 4's upper x' (row_shr:4,
+          // bank 1 only); every other lane keeps its own B, which is zero for
+          // n >= M (so for n >= 4)
+          u32x4 bh;
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            bh[c] = (uint32_t)__builtin_amdgcn_update_dpp((int)own[c], (int)hi[c], 0x114, 0xF, 0x2, false);
+          hacc[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, A2[u]),
+                                                           __builtin_bit_cast(half8, bh), hacc[u], 0, 0, 0);
+        }
+      }
+    }
+    // lane (n, q) holds D rows 4q .. 4q+3 of column n: n < 4, q < 2 the
+    // first halves of vector n, 4 <= n < 8, q >= 2 the second halves of
+    // vector n - 4; both go to the partial tile of that vector, rows 4q ..
+    const f32x4 hsum = hacc[0] + hacc[1];
+    const int m = i & 3;
+    const int me = m == 0 ? e0 : m == 1 ? e1 : m == 2 ? e2 : e3;
+    f32x4 hv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) hv[e] = ldexpf(hsum[e], -me);
+    if (m < M && ((i < 4 && q < 2) || (i >= 4 && i < 8 && q >= 2)))
+      *reinterpret_cast<f32x4*>(part + ((size_t)(t * kWaves + wave) * 4 + m) * 16 + 4 * q) = hv;
+  }
+
   // ---- 5. one barrier, then every output: the eight slices' partials in a
   // fixed order, times scale / d, and the epilogue
   lds_barrier();
-  const int per_t = M * ROWS;
-  for (int idx = tid; idx < nmine * per_t; idx += kThreads) {
-    const int t = idx / per_t, r = idx - t * per_t;
-    const int m = r / ROWS, row = r - m * ROWS;
+  // thread idx takes output row idx % ROWS of vector (idx / ROWS) % 4 of
+  // item idx / (4 ROWS) (shifts only; vectors past M skip)
+  constexpr int kRowsLog = GATEUP ? 3 : 4;
+  for (int idx = tid; idx < nmine * 4 * ROWS; idx += kThreads) {
+    const int t = idx >> (kRowsLog + 2), m = (idx >> kRowsLog) & 3, row = idx & (ROWS - 1);
+    if (m >= M) continue;
     int gi;
     int64_t lrg;
-    locate((int64_t)blockIdx.x + (int64_t)t * gridDim.x, gi, lrg);
+    locate(item_rg(t), gi, lrg);
+    const bool hf = hit && t == g.nfull;
+    if (hf && row >= ROWS / 2) continue;
     const int64_t Rm = pick(R, g.gR, gi);
-    const int64_t orow = lrg * ROWS + row;
+    const int64_t orow = lrg * ROWS + (hf ? (bid & 1) * (ROWS / 2) : 0) + row;
     if (orow >= Rm) continue;
     const int64_t o = (int64_t)m * Rm + orow;
-    const float* pp = part + ((size_t)t * kWaves * 4 + m) * 16 + row;
+    const float* pp = part + ((size_t)t * kWaves * 4 + m) * 16;
+    // partial-tile rows of this output: whole row groups row (gate/up: gate
+    // row, up row + 8); a half its two position halves, rows row and row + 8
+    // (gate/up: gate row and row + 8, up 4 + row and 12 + row)
     float d0 = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) d0 += pp[w * 64];
+    for (int w = 0; w < kWaves; ++w) d0 += hf ? pp[w * 64 + row] + pp[w * 64 + row + 8] : pp[w * 64 + row];
     const float v0 = d0 * (half_bits_to_f32(pick(scales0, g.gscales, gi)[orow]) * kRcp);
     if constexpr (GATEUP) {
       float d1 = 0.f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) d1 += pp[w * 64 + 8];
+      for (int w = 0; w < kWaves; ++w) d1 += hf ? pp[w * 64 + 4 + row] + pp[w * 64 + 12 + row] : pp[w * 64 + 8 + row];
       const float v1 = d1 * (half_bits_to_f32(scales1[orow]) * kRcp);
       if (gate_f32) gate_f32[o] = v0;
       if (up_f32) up_f32[o] = v1;
@@ -590,6 +671,12 @@ bool axis1_geom(int64_t R, int64_t C, int M, int k, bool gateup, int64_t grid, A
   g.nmine_max = (int)((g.nrg + grid - 1) / grid);
   g.nfull = (int)(g.nrg / grid);
   g.nrem = (int)(g.nrg % grid);
+  // the last round in halves when its row groups fill at most half the grid.
+  // A half computes its outputs bit for bit as the whole row group would:
+  // its two MFMAs per run group see, per output element, the same operands
+  // as the whole row group's MFMAs 0/1 and 2/3, and the epilogue adds the
+  // two position halves in the same order.
+  g.half = (g.nrem > 0 && 2 * (int64_t)g.nrem <= grid) ? 1 : 0;
   g.slot_bytes = (uint32_t)((16 * g.gsw * 16 + 255) / 256 * 256);
   const uint64_t parts = (uint64_t)g.nmine_max * kPartBytes;
   if (parts >= kAxis1MaxLdsBytes) return false;
@@ -605,11 +692,15 @@ bool axis1_geom(int64_t R, int64_t C, int M, int k, bool gateup, int64_t grid, A
   return g.total <= kAxis1MaxLdsBytes;
 }
 
+// One workgroup per CU, or per row group when there are fewer; a plain or
+// gate/up call with at most half as many row groups as CUs runs each of
+// them as two halves on twice as many workgroups.
 int64_t axis1_grid(int64_t R, bool gateup, int64_t nrg_total = 0) {
   const int64_t rows = gateup ? 8 : 16;
   const int64_t nrg = nrg_total > 0 ? nrg_total : (R + rows - 1) / rows;
   const int64_t cus = device_cus();
-  return nrg < cus ? nrg : cus;
+  if (nrg >= cus) return cus;
+  return (nrg_total == 0 && 2 * nrg <= cus) ? 2 * nrg : nrg;
 }
 
 template <int K, bool GU, int NG, bool GROUP = false, bool DECODE = true>

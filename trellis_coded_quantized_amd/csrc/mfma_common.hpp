@@ -72,4 +72,34 @@ __device__ __forceinline__ void decode_run_codes(const uint32_t (&w)[K + 1], uin
   for (int v = 0; v < 16; ++v) A[v >> 2][v & 3] = code_pair_y(xw[2 * v], xw[2 * v + 1]);
 }
 
+// Half a run: the 16 codes of positions 0..15 (upper = false) or 16..31
+// (upper = true) of the run, as two MFMA A operands (A[u] element e is
+// position 16 upper + 8u + e).  The windows of the upper half start 16 K
+// bits lower in the run than those of the lower half, so both halves read
+// the same compile-time offsets from a lane-selected set of 16-bit chunks.
+template <int K>
+__device__ __forceinline__ void decode_half_codes(const uint32_t (&w)[K + 1], bool upper, uint32_t mul,
+                                                  uint64_t add64, u32x4 (&A)[2]) {
+  uint32_t a[2 * K];                           // a[j] holds bits 16j .. 16j+31 of the run
+#pragma unroll
+  for (int m = 0; m < K; ++m) {
+    a[2 * m] = w[m];
+    a[2 * m + 1] = __builtin_amdgcn_alignbit(w[m + 1], w[m], 16);
+  }
+  uint32_t h[K];                               // chunks K .. 2K-1 (lower half) or 0 .. K-1 (upper)
+#pragma unroll
+  for (int j = 0; j < K; ++j) h[j] = upper ? a[j] : a[j + K];
+  uint32_t st[16];
+#pragma unroll
+  for (int p = 0; p < 16; ++p) {
+    const int b = (15 - p) * K;                 // window start of half position p, from the chunk base
+    st[p] = __builtin_amdgcn_ubfe(h[b >> 4], b & 15, kL);
+  }
+  uint32_t xw[16];
+#pragma unroll
+  for (int p = 0; p < 16; ++p) xw[p] = onemad_word_mad64(st[p], mul, add64);
+#pragma unroll
+  for (int v = 0; v < 8; ++v) A[v >> 2][v & 3] = code_pair_y(xw[2 * v], xw[2 * v + 1]);
+}
+
 }  // namespace trellis
