@@ -334,39 +334,55 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
   wait_vmcnt(ncp * t0);                        // the x slice has landed
 
   // ---- 2. exponent of the slice per vector: its largest |x[n]| * 2^e lands
-  // in [2^14, 2^15); then x' = f16(x 2^e) in place
-  // every lane holds at most kXPer granules of the slice (M * C / 8 / 64 <= 5 * 64 granules per wave)
+  // in [2^14, 2^15); then x' = f16(x 2^e) in place.  Each vector's granules
+  // belong to one group of G = 64 / M' lanes (M' = M rounded up to a power
+  // of two): lane (n, j) = (lane / G, lane % G) takes granules j, j + G, ...
+  // of vector n, so the maximum is one short DPP reduction over the group
+  // and each lane scales by its own vector's exponent.
   static_assert(kXPer == 5, "x granules are read five at a time");
+  const int lgG = M == 1 ? 6 : (M == 2 ? 5 : 4);
+  const int G = 1 << lgG;
+  const int xn = lane >> lgG, xj = lane & (G - 1);
+  const int nxu = (gx + G - 1) >> lgG;         // granules per lane (<= kXPer: gx <= 80)
   uint4 xr[kXPer];
+  uint32_t xa[kXPer];
+  bool xok[kXPer];
   {
-    uint32_t xa[kXPer];
 #pragma unroll
-    for (int u = 0; u < kXPer; ++u) {          // granules past the slice re-read its last one
-      const int p = lane + 64 * u;
-      xa[u] = lds_addr(xsl) + (uint32_t)(p < nxg ? p : nxg - 1) * 16u;
+    for (int u = 0; u < kXPer; ++u) {          // granules past the slice read granule 0 and are zeroed
+      const int jj = u * G + xj;
+      xok[u] = xn < M && u < nxu && jj < gx;
+      xa[u] = lds_addr(xsl) + (uint32_t)(xok[u] ? xn * gx + jj : 0) * 16u;
     }
     lds_u32x4 xv[kXPer];
     lds_read_b128x5(xa, xv);
 #pragma unroll
     for (int u = 0; u < kXPer; ++u)
-      xr[u] = lane + 64 * u < nxg ? make_uint4(xv[u][0], xv[u][1], xv[u][2], xv[u][3]) : make_uint4(0u, 0u, 0u, 0u);
+      xr[u] = xok[u] ? make_uint4(xv[u][0], xv[u][1], xv[u][2], xv[u][3]) : make_uint4(0u, 0u, 0u, 0u);
   }
-  uint32_t mx0 = 0u, mx1 = 0u, mx2 = 0u, mx3 = 0u;
+  uint32_t mx = 0u;
 #pragma unroll
   for (int u = 0; u < kXPer; ++u) {
-    if (u >= nxw) break;                       // granules of the M vectors only (wave-uniform)
-    const int p = lane + 64 * u;
-    const uint32_t a = max_abs8(xr[u]);        // zero past the slice
-    const int n = (p >= gx) + (p >= 2 * gx) + (p >= 3 * gx);
-    mx0 = n == 0 ? max(mx0, a) : mx0;
-    mx1 = n == 1 ? max(mx1, a) : mx1;
-    mx2 = n == 2 ? max(mx2, a) : mx2;
-    mx3 = n == 3 ? max(mx3, a) : mx3;
+    if (u >= nxu) break;                       // wave-uniform
+    mx = max(mx, max_abs8(xr[u]));             // zero past the slice
   }
-  mx0 = wave_max_u32(mx0);
-  mx1 = wave_max_u32(mx1);
-  mx2 = wave_max_u32(mx2);
-  mx3 = wave_max_u32(mx3);
+  // maximum over the lane's group: within rows of 16 by rotation (every
+  // lane of a row ends with the row's maximum), then across rows
+  mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0x121, 0xF, 0xF, false));   // row_ror:1
+  mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0x122, 0xF, 0xF, false));   // row_ror:2
+  mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0x124, 0xF, 0xF, false));   // row_ror:4
+  mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0x128, 0xF, 0xF, false));   // row_ror:8
+  if (lgG >= 5) {                              // rows 1 and 3 take the maxima of rows 0-1 and 2-3
+    mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0x142, 0xA, 0xF, false));   // row_bcast:15
+    if (lgG == 6) {                            // rows 2 and 3 take the maximum of rows 0-1: row 3 has all
+      mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0x143, 0xC, 0xF, false));   // row_bcast:31
+      mx = (uint32_t)__builtin_amdgcn_readlane((int)mx, 63);
+    } else {
+      const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)mx, 31);
+      const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)mx, 63);
+      mx = lane < 32 ? lo : hi;
+    }
+  }
   auto exponent = [](uint32_t v) {
     int e = 0;
     if (v != 0u && v < 0x7F80u) {              // finite, non-zero maximum
@@ -376,22 +392,24 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
     }
     return e;
   };
-  const int e0 = exponent(mx0), e1 = exponent(mx1), e2 = exponent(mx2), e3 = exponent(mx3);
+  const int xe = exponent(mx);                 // the exponent of this lane's vector
+  // per-vector exponents for the epilogue's scaling (vectors past M: 0)
+  const int e0 = __builtin_amdgcn_readlane(xe, 0);
+  const int e1 = M > 1 ? __builtin_amdgcn_readlane(xe, 1 * (M == 2 ? 32 : 16)) : 0;
+  const int e2 = M > 2 ? __builtin_amdgcn_readlane(xe, 32) : 0;
+  const int e3 = M > 3 ? __builtin_amdgcn_readlane(xe, 48) : 0;
 #pragma unroll
   for (int u = 0; u < kXPer; ++u) {
-    if (u >= nxw) break;
-    const int p = lane + 64 * u;
-    const int n = (p >= gx) + (p >= 2 * gx) + (p >= 3 * gx);
-    const int en = n == 0 ? e0 : n == 1 ? e1 : n == 2 ? e2 : e3;
+    if (u >= nxu) break;
     const uint32_t u4[4] = {xr[u].x, xr[u].y, xr[u].z, xr[u].w};
     uint32_t o[4];
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-      const _Float16 lo = (_Float16)ldexpf(bf16_bits_to_f32(u4[h] & 0xFFFFu), en);
-      const _Float16 hi = (_Float16)ldexpf(bf16_bits_to_f32(u4[h] >> 16), en);
+      const _Float16 lo = (_Float16)ldexpf(bf16_bits_to_f32(u4[h] & 0xFFFFu), xe);
+      const _Float16 hi = (_Float16)ldexpf(bf16_bits_to_f32(u4[h] >> 16), xe);
       o[h] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
     }
-    if (p < nxg) lds_write_b128(lds_addr(xsl) + (uint32_t)p * 16u, lds_u32x4{o[0], o[1], o[2], o[3]});
+    if (xok[u]) lds_write_b128(xa[u], lds_u32x4{o[0], o[1], o[2], o[3]});
   }
 
   // ---- 3. B operand in registers: lane (n, q) of group gg holds
