@@ -591,38 +591,50 @@ MATVEC_WORKLOADS = ("gateup", "axis0", "axis0_il", "layer_chain", "layer_chain_g
                     "decode_free")
 
 
+def steps_per_graph(steps, cap=5):
+    """Steps captured in one graph: the largest divisor of `steps` up to cap,
+    so that exactly `steps` steps are timed."""
+    return max(d for d in range(1, min(cap, max(steps, 1)) + 1) if steps % d == 0)
+
+
 def time_workload(wl, steps, warmup, eager, torch, label):
-    """Warm up, capture one graph per replica offset (unless eager or the
-    workload cannot be captured), then time `steps` steps between device
-    synchronisations.  Returns (ms per step, mean launch ms from HIP events on
-    the launch stream, mode)."""
+    """Warm up, capture graphs of G consecutive steps (G divides `steps`;
+    the graphs cycle through every replica offset) unless eager or the
+    workload cannot be captured, then time exactly `steps` steps between
+    device synchronisations.  Several steps per graph keep the per-replay
+    launch cost (and torch's per-replay fill kernel) off each step, as a
+    model's layer graph would.  Returns (ms per step, mean launch ms from HIP
+    events on the launch stream, mode)."""
     print(f"[bench] {label}: warmup {warmup}", file=sys.stderr, flush=True)
     for s in range(warmup):
         wl.step(s)
     torch.cuda.synchronize()
     graphs = None
+    G = steps_per_graph(steps)
     if wl.graph and not eager:
         graphs = []
-        for s in range(wl.period):
+        for r in range(wl.period):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                wl.step(s)
+                for s in range(G):
+                    wl.step(r * G + s)
             graphs.append(g)
         for g in graphs:
             g.replay()
         torch.cuda.synchronize()
-    mode = "graph" if graphs else "eager"
+    mode = f"graph ({G} steps per replay)" if graphs else "eager"
     print(f"[bench] {label}: timing {steps} steps ({mode})", file=sys.stderr, flush=True)
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    nrec = steps // G if graphs else steps
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nrec)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(steps):
-        a, b = events[s]
+    for i in range(nrec):
+        a, b = events[i]
         a.record()
         if graphs:
-            graphs[s % len(graphs)].replay()
+            graphs[i % len(graphs)].replay()
         else:
-            wl.step(s)
+            wl.step(i)
         b.record()
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t0) * 1e3 / max(steps, 1)
