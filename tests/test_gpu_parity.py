@@ -137,6 +137,30 @@ def test_gateup_wide_rows_column_chunks(R, C, M, k):
     check_gateup(g, u, x, R, C, M, k, f"gateup R={R} C={C} M={M} k={k}")
 
 
+@pytest.mark.parametrize("R", [33, 160])
+def test_axis1_and_gateup_scales_at_odd_offset(R):
+    # scales that start 2 bytes into an allocation (not 4-byte aligned) are
+    # read from global memory instead of the LDS copy; the outputs must not
+    # change at all
+    rng = np.random.default_rng(4000 + R)
+    C, k, M = 1280, 3, 4
+    codes, scales = rand_matrix(rng, R, C, k)
+    ucodes, uscales = rand_matrix(rng, R, C, k)
+    x = d_bf16(ti.activations(rng, M, C))
+    dc, uc = d_codes(codes), d_codes(ucodes)
+    big = torch.empty(2 * R + 2, dtype=torch.float16, device=DEV)
+    s_odd, u_odd = big[1:R + 1], big[R + 1:2 * R + 1]
+    s_odd.copy_(d_half(scales))
+    u_odd.copy_(d_half(uscales))
+    assert s_odd.data_ptr() % 4 == 2
+    a = tq.matvec_axis1(dc, d_half(scales), x, k, out_dtype=torch.float32)
+    b = tq.matvec_axis1(dc, s_odd, x, k, out_dtype=torch.float32)
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    ga = tq.gateup_swiglu(dc, d_half(scales), uc, d_half(uscales), x, k)
+    gb = tq.gateup_swiglu(dc, s_odd, uc, u_odd, x, k)
+    assert torch.equal(ga.view(torch.int16), gb.view(torch.int16))
+
+
 def test_axis1_zero_input_is_exact_zero():
     rng = np.random.default_rng(3)
     codes, scales = rand_matrix(rng, 33, 512, 3)

@@ -53,6 +53,7 @@ constexpr int kXPer = 5;               // x granules per lane of a wave's slice 
 constexpr uint32_t kPartBytes = kWaves * 4 * 16 * 4;   // one row group's partial tiles: f32 [wave][n][16 rows]
 constexpr int kMaxGroup = 4;           // matrices of one grouped call
 constexpr uint32_t kProgBytes = 64;    // row groups each wave has finished: u32 [wave]
+constexpr uint32_t kScaleBytes = 32;   // one row group's fp16 scales: 16 rows, or 8 gate then 8 up rows
 
 // Geometry shared by the host (LDS sizing) and the kernel.
 struct Axis1Geom {
@@ -70,7 +71,7 @@ struct Axis1Geom {
   // half = 1: the last nrem row groups run as 2 nrem halves (ROWS / 2 output
   // rows each), one on each workgroup b < 2 nrem, after its nfull whole ones
   int half;
-  uint32_t slot_bytes, part_off, prog_off, total;
+  uint32_t slot_bytes, part_off, prog_off, sc_off, total;
   int nmine_max;
   int64_t C, nrg;
   // Grouped call (plain axis 1 only): ngroup matrices of the same C and k
@@ -198,7 +199,9 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   // the pointers the first copies need are read with the geometry at entry
   // (one wait for all of them instead of one per use)
-  asm volatile("" : : "s"(codes0), "s"(codes1), "s"(x), "s"(g.R), "s"(g.row_bytes), "s"(g.ldx), "s"(g.M), "s"(g.per));
+  int gdim = (int)gridDim.x;
+  asm volatile("" : "+s"(gdim) : "s"(codes0), "s"(codes1), "s"(x), "s"(g.R), "s"(g.row_bytes), "s"(g.ldx), "s"(g.M),
+               "s"(g.per));
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int i = lane & 15, q = lane >> 4;
@@ -242,8 +245,34 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
   };
   // row group of item t: whole ones bid + t grid, the half nfull grid + bid / 2
   auto item_rg = [&](int t) -> int64_t {
-    return (hit && t == g.nfull) ? (int64_t)g.nfull * gridDim.x + (bid >> 1) : (int64_t)bid + (int64_t)t * gridDim.x;
+    return (hit && t == g.nfull) ? (int64_t)g.nfull * gdim + (bid >> 1) : (int64_t)bid + (int64_t)t * gdim;
   };
+
+  // ---- 0. the scales of the workgroup's rows go to LDS ahead of everything
+  // else, so the epilogue reads them there: dword v holds rows 2 (v % 8) and
+  // 2 (v % 8) + 1 of item v / 8 (gate/up: dwords 0-3 the gate rows, 4-7 the
+  // up rows).  A pair that reaches past the matrix is not copied (a ragged
+  // last row group; an odd R leaves its last row to the epilogue's global
+  // read), nor are scales whose pointer is not 4-byte aligned.
+  bool sc_ok = ((reinterpret_cast<uintptr_t>(scales0) | (GATEUP ? reinterpret_cast<uintptr_t>(scales1) : 0u)) & 3u) == 0;
+  if constexpr (GROUP) {
+#pragma unroll
+    for (int j = 1; j < kMaxGroup; ++j)
+      if (j < g.ngroup) sc_ok = sc_ok && (reinterpret_cast<uintptr_t>(g.gscales[j]) & 3u) == 0;
+  }
+  if (sc_ok) {
+    for (int v0 = wave * 64; v0 < nmine * 8; v0 += kThreads) {   // wave-uniform
+      const int v = v0 + lane, t = min(v >> 3, nmine - 1), d = v & 7;
+      int gi;
+      int64_t lrg;
+      locate(item_rg(t), gi, lrg);
+      const int64_t Rm = pick(R, g.gR, gi);
+      const int64_t row = GATEUP ? lrg * ROWS + 2 * (d & 3) : lrg * ROWS + 2 * d;
+      const uint16_t* sp = GATEUP ? (d < 4 ? scales0 : scales1) : pick(scales0, g.gscales, gi);
+      if (v < nmine * 8 && row + 1 < Rm)
+        __builtin_amdgcn_global_load_lds(sp + row, smem + g.sc_off + (uint32_t)v0 * 4u, 4, 0, 0);
+    }
+  }
 
   // ---- this wave's slice: runs [rb, re) of 32 columns, held in packed
   // blocks [b0, b1]; a tile row of the wave's window is those blocks
@@ -586,16 +615,33 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
     const float* pp = part + ((size_t)t * kWaves * 4 + m) * 16;
     // partial-tile rows of this output: whole row groups row (gate/up: gate
     // row, up row + 8); a half its two position halves, rows row and row + 8
-    // (gate/up: gate row and row + 8, up 4 + row and 12 + row)
+    // (gate/up: gate row and row + 8, up 4 + row and 12 + row).  Both reads
+    // are made either way (the second repeats the first for a whole row
+    // group), so the sum needs no branch.
+    const int b0h = hf ? row + 8 : row;
     float d0 = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) d0 += hf ? pp[w * 64 + row] + pp[w * 64 + row + 8] : pp[w * 64 + row];
-    const float v0 = d0 * (half_bits_to_f32(pick(scales0, g.gscales, gi)[orow]) * kRcp);
+    for (int w = 0; w < kWaves; ++w) {
+      const float lo = pp[w * 64 + row], hi = pp[w * 64 + b0h];
+      d0 += hf ? lo + hi : lo;
+    }
+    // the row's scale from LDS (scale row srow of item t), or from global
+    // memory where its pair was not copied
+    const int srow = (int)(orow - lrg * ROWS);
+    const bool sl = sc_ok && (orow | 1) < Rm;
+    const uint8_t* sct = smem + g.sc_off + (size_t)t * kScaleBytes;
+    const uint16_t sg = sl ? *reinterpret_cast<const uint16_t*>(sct + srow * 2) : pick(scales0, g.gscales, gi)[orow];
+    const float v0 = d0 * (half_bits_to_f32(sg) * kRcp);
     if constexpr (GATEUP) {
+      const int a1 = hf ? 4 + row : 8 + row, b1 = hf ? 12 + row : 8 + row;
       float d1 = 0.f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) d1 += hf ? pp[w * 64 + 4 + row] + pp[w * 64 + 12 + row] : pp[w * 64 + 8 + row];
-      const float v1 = d1 * (half_bits_to_f32(scales1[orow]) * kRcp);
+      for (int w = 0; w < kWaves; ++w) {
+        const float lo = pp[w * 64 + a1], hi = pp[w * 64 + b1];
+        d1 += hf ? lo + hi : lo;
+      }
+      const uint16_t su = sl ? *reinterpret_cast<const uint16_t*>(sct + 16 + srow * 2) : scales1[orow];
+      const float v1 = d1 * (half_bits_to_f32(su) * kRcp);
       if (gate_f32) gate_f32[o] = v0;
       if (up_f32) up_f32[o] = v1;
       if (out) reinterpret_cast<uint16_t*>(out)[o] = swiglu_bf16(v0, v1);   // no out: a column chunk
@@ -698,15 +744,17 @@ bool axis1_geom(int64_t R, int64_t C, int M, int k, bool gateup, int64_t grid, A
   g.slot_bytes = (uint32_t)((16 * g.gsw * 16 + 255) / 256 * 256);
   const uint64_t parts = (uint64_t)g.nmine_max * kPartBytes;
   if (parts >= kAxis1MaxLdsBytes) return false;
-  if (parts + kProgBytes >= kAxis1MaxLdsBytes) return false;
-  const uint64_t nsl = (kAxis1MaxLdsBytes - parts - kProgBytes) / ((uint64_t)kWaves * g.slot_bytes);
+  const uint64_t fixed = parts + kProgBytes + (uint64_t)g.nmine_max * kScaleBytes;
+  if (fixed >= kAxis1MaxLdsBytes) return false;
+  const uint64_t nsl = (kAxis1MaxLdsBytes - fixed) / ((uint64_t)kWaves * g.slot_bytes);
   g.nslots = (int)(nsl < (uint64_t)kMaxSlots ? nsl : kMaxSlots);
   const uint64_t xbytes = (uint64_t)M * g.per * 64 + 64;   // one wave's x slice and 64 zero bytes
   g.xslots = (int)((xbytes + g.slot_bytes - 1) / g.slot_bytes);
   if (g.nslots < 2 || g.nslots < g.xslots + 1) return false;
   g.part_off = (uint32_t)kWaves * g.nslots * g.slot_bytes;
   g.prog_off = (uint32_t)(g.part_off + parts);
-  g.total = g.prog_off + kProgBytes;
+  g.sc_off = g.prog_off + kProgBytes;
+  g.total = g.sc_off + (uint32_t)g.nmine_max * kScaleBytes;
   return g.total <= kAxis1MaxLdsBytes;
 }
 
