@@ -355,10 +355,12 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
     }
   };
 
-  // the ring fills a little at a time (a burst of copies would stall the
-  // issuing wave): up to two tiles now, in slots the x slice does not use
+  // the ring fills a little at a time: one tile now, in a slot the x slice
+  // does not use, the second once the x slice is in registers (every
+  // workgroup's first tiles share HBM; a second tile in that first burst
+  // delays the first, most for k = 4)
   int next = 0;                                // next tile to copy; tiles go out in order
-  const int t0 = min(nmine, min(2, NS - g.xslots));
+  const int t0 = min(nmine, min(1, NS - g.xslots));
   for (; next < t0; ++next) issue_tile(next);
   wait_vmcnt(ncp * t0);                        // the x slice has landed
 
@@ -473,7 +475,7 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
   const int my_e = i == 0 ? e0 : i == 1 ? e1 : i == 2 ? e2 : e3;     // scale of column n = i
 
   __atomic_signal_fence(__ATOMIC_SEQ_CST);     // the x' reads above stay before any later copy
-  if (next == 0 && nmine > 0) issue_tile(next++);   // x filled all but one slot
+  for (; next < min(nmine, 2); ++next) issue_tile(next);   // the x slots are free now
 
   const uint32_t mul = kMul;
   const uint64_t add64 = kAdd;
