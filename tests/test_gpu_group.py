@@ -68,3 +68,24 @@ def test_group_of_one_and_bf16_out():
 def test_group_decoder_layer_projections_k4():
     # the decoder-layer set: 10240, 6144 and 64 rows over one x [4, 5120]
     _run((10240, 6144, 64), 5120, 4, 4, 313, torch.float32)
+
+
+def test_group_scales_at_odd_offset():
+    # one matrix's scales start 2 bytes into an allocation: the launch reads
+    # every scale from global memory instead of its LDS copy, and the outputs
+    # must not change
+    rng = np.random.default_rng(314)
+    Rs, C, k, M = (300, 77, 64), 1024, 3, 4
+    mats = [(ti.codes(rng, R, C, k), ti.scales(rng, R)) for R in Rs]
+    dx = _d(ti.activations(rng, M, C), torch.bfloat16)
+    dc = [_d(c, torch.int32) for c, _ in mats]
+    ds = [_d(s, torch.float16) for _, s in mats]
+    big = torch.empty(Rs[1] + 1, dtype=torch.float16, device=DEV)
+    odd = big[1:]
+    odd.copy_(ds[1])
+    assert odd.data_ptr() % 4 == 2
+    want = tq.matvec_axis1_group(dc, ds, dx, k, out_dtype=torch.float32)
+    got = tq.matvec_axis1_group(dc, [ds[0], odd, ds[2]], dx, k, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for R, a, b in zip(Rs, want, got):
+        np.testing.assert_array_equal(_bits(b), _bits(a), err_msg=f"R={R}: odd-offset scales changed the outputs")
