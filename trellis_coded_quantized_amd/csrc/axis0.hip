@@ -75,25 +75,26 @@ struct Axis0Geom {
   "ds_read2_b32 %" #O2 ", %" #A " offset0:" #S4 " offset1:" #S5 "\n\t"     \
   "ds_read2_b32 %" #O3 ", %" #A " offset0:" #S6 " offset1:" #S7 "\n\t"
 #define TRELLIS_A0_BLOCK(...)                                                \
-  TRELLIS_A0_ROWS(0, 1, 2, 3, 17, __VA_ARGS__)                               \
-  TRELLIS_A0_ROWS(4, 5, 6, 7, 18, __VA_ARGS__)                               \
-  TRELLIS_A0_ROWS(8, 9, 10, 11, 19, __VA_ARGS__)                             \
-  TRELLIS_A0_ROWS(12, 13, 14, 15, 20, __VA_ARGS__)                           \
-  "ds_read_b128 %16, %21\n\ts_waitcnt lgkmcnt(0)"
+  TRELLIS_A0_ROWS(0, 1, 2, 3, 18, __VA_ARGS__)                               \
+  TRELLIS_A0_ROWS(4, 5, 6, 7, 19, __VA_ARGS__)                               \
+  TRELLIS_A0_ROWS(8, 9, 10, 11, 20, __VA_ARGS__)                             \
+  TRELLIS_A0_ROWS(12, 13, 14, 15, 21, __VA_ARGS__)                           \
+  "ds_read_b128 %16, %22\n\tds_read_b32 %17, %23\n\ts_waitcnt lgkmcnt(0)"
 #define TRELLIS_A0_OPERANDS                                                  \
   : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]),  \
     "=&v"(o[7]), "=&v"(o[8]), "=&v"(o[9]), "=&v"(o[10]), "=&v"(o[11]), "=&v"(o[12]),           \
-    "=&v"(o[13]), "=&v"(o[14]), "=&v"(o[15]), "=&v"(bv)                                          \
-  : "v"(a0[0]), "v"(a1[0]), "v"(a0[1]), "v"(a1[1]), "v"(ab)                                    \
+    "=&v"(o[13]), "=&v"(o[14]), "=&v"(o[15]), "=&v"(bv), "=&v"(xv)                              \
+  : "v"(a0[0]), "v"(a1[0]), "v"(a0[1]), "v"(a1[1]), "v"(ab), "v"(ax)                           \
   : "memory"
 
 // The words of two 64-column chunks for the lane's eight tile rows, read from
 // the ring and waited for in one block: W[c][rr][0] at LDS byte address
 // a0[c] and W[c][rr][1] at a1[c], row rr lying rr * (2K + 1) * 4 dwords
-// further (one block plus one pad granule per row); also the 16 bytes at ab.
+// further (one block plus one pad granule per row); also the 16 bytes at ab
+// and the dword at ax (into xv).
 template <int K>
 __device__ __forceinline__ void lds_read_chunks2(const uint32_t (&a0)[2], const uint32_t (&a1)[2], uint32_t ab,
-                                                 uint32_t (&W)[2][8][2], lds_u32x4& bv) {
+                                                 uint32_t (&W)[2][8][2], lds_u32x4& bv, uint32_t ax, uint32_t& xv) {
   static_assert(words_per_block(K) / 4 + 1 == 2 * K + 1, "tile rows are one block plus one granule");
   lds_u32x2 o[16];
   if constexpr (K == 2) {
@@ -337,14 +338,6 @@ __global__ __launch_bounds__(kThreads) void axis0_kernel(const uint32_t* __restr
   const uint32_t mul = kMul;
   const uint64_t add64 = kAdd;
   for (int t = 0; t < nmy; ++t) {
-    // the two waves of a SIMD (w, w ^ 4) share its VALU: the one that has
-    // finished more blocks drops to the lower issue priority (on a tie the
-    // younger wave takes the higher one: the hardware favours the older)
-    {
-      const uint32_t other = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_read_b32(prog_other));
-      if ((uint32_t)t < other || ((uint32_t)t == other && wave >= 4)) __builtin_amdgcn_s_setprio(1);
-      else __builtin_amdgcn_s_setprio(0);
-    }
     wait_vmcnt(nwd * (next - 1 - t));          // tile t has landed
     const int blk = wave + kWaves * t;
     half8 Bv;
@@ -379,8 +372,20 @@ __global__ __launch_bounds__(kThreads) void axis0_kernel(const uint32_t* __restr
       const uint32_t a1[2] = {ta + (uint32_t)wna[ch] * 4u, ta + (uint32_t)wna[ch + 1] * 4u};
       uint32_t W[2][8][2];
       lds_u32x4 bv;
-      lds_read_chunks2<K>(a0, a1, ab, W, bv);
-      if (ch == 0) Bv = b_operand(bv);
+      uint32_t other_v;
+      lds_read_chunks2<K>(a0, a1, ab, W, bv, prog_other, other_v);
+      if (ch == 0) {
+        Bv = b_operand(bv);
+        // the two waves of a SIMD (w, w ^ 4) share its VALU: the one that has
+        // finished more blocks drops to the lower issue priority (on a tie
+        // the younger wave takes the higher one: the hardware favours the
+        // older); the partner's count comes with the first read block
+        const uint32_t other = (uint32_t)__builtin_amdgcn_readfirstlane((int)other_v);
+        if ((uint32_t)t < other || ((uint32_t)t == other && wave >= 4)) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
+      } else {
+        asm volatile("" : : "v"(other_v));     // (not needed for the second read block)
+      }
       decode_chunk(ch, W[0]);
       decode_chunk(ch + 1, W[1]);
     }

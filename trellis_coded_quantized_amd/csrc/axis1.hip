@@ -109,24 +109,26 @@ __device__ __forceinline__ uint16_t swiglu_bf16(float gate, float up) {
 
 // The code words of five run groups of one tile row, read from the ring and
 // waited for in one block: for group g the K words at LDS byte address aw[g]
-// and the spill word at as[g] (the word after the run, wrapped in its block).
+// and the spill word at as[g] (the word after the run, wrapped in its block);
+// the same block reads the dword at ax into xv.
 template <int K>
 __device__ __forceinline__ void lds_read_runs5(const uint32_t (&aw)[5], const uint32_t (&as)[5],
-                                               uint32_t (&W)[5][K + 1]) {
+                                               uint32_t (&W)[5][K + 1], uint32_t ax, uint32_t& xv) {
   if constexpr (K == 2) {
     lds_u32x2 p[5];
     uint32_t sp[5];
     asm volatile(
-        "ds_read_b64 %0, %10\n\tds_read_b32 %1, %11\n\t"
-        "ds_read_b64 %2, %12\n\tds_read_b32 %3, %13\n\t"
-        "ds_read_b64 %4, %14\n\tds_read_b32 %5, %15\n\t"
-        "ds_read_b64 %6, %16\n\tds_read_b32 %7, %17\n\t"
-        "ds_read_b64 %8, %18\n\tds_read_b32 %9, %19\n\t"
+        "ds_read_b64 %0, %11\n\tds_read_b32 %1, %12\n\t"
+        "ds_read_b64 %2, %13\n\tds_read_b32 %3, %14\n\t"
+        "ds_read_b64 %4, %15\n\tds_read_b32 %5, %16\n\t"
+        "ds_read_b64 %6, %17\n\tds_read_b32 %7, %18\n\t"
+        "ds_read_b64 %8, %19\n\tds_read_b32 %9, %20\n\t"
+        "ds_read_b32 %10, %21\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=&v"(p[0]), "=&v"(sp[0]), "=&v"(p[1]), "=&v"(sp[1]), "=&v"(p[2]), "=&v"(sp[2]), "=&v"(p[3]),
-          "=&v"(sp[3]), "=&v"(p[4]), "=&v"(sp[4])
-        : "v"(aw[0]), "v"(as[0]), "v"(aw[1]), "v"(as[1]), "v"(aw[2]), "v"(as[2]), "v"(aw[3]), "v"(as[3]),
-          "v"(aw[4]), "v"(as[4])
+        : "=&v"(p[0]), "=&v"(sp[0]), "=&v"(p[1]), "=&v"(sp[1]), "=&v"(p[2]), "=&v"(sp[2]), "=&v"(p[3]), "=&v"(sp[3]),
+          "=&v"(p[4]), "=&v"(sp[4]), "=&v"(xv)
+        : "v"(aw[0]), "v"(as[0]), "v"(aw[1]), "v"(as[1]), "v"(aw[2]), "v"(as[2]), "v"(aw[3]), "v"(as[3]), "v"(aw[4]),
+          "v"(as[4]), "v"(ax)
         : "memory");
 #pragma unroll
     for (int g = 0; g < 5; ++g) {
@@ -138,16 +140,17 @@ __device__ __forceinline__ void lds_read_runs5(const uint32_t (&aw)[5], const ui
     lds_u32x4 p[5];
     uint32_t sp[5];
     asm volatile(
-        "ds_read_b128 %0, %10\n\tds_read_b32 %1, %11\n\t"
-        "ds_read_b128 %2, %12\n\tds_read_b32 %3, %13\n\t"
-        "ds_read_b128 %4, %14\n\tds_read_b32 %5, %15\n\t"
-        "ds_read_b128 %6, %16\n\tds_read_b32 %7, %17\n\t"
-        "ds_read_b128 %8, %18\n\tds_read_b32 %9, %19\n\t"
+        "ds_read_b128 %0, %11\n\tds_read_b32 %1, %12\n\t"
+        "ds_read_b128 %2, %13\n\tds_read_b32 %3, %14\n\t"
+        "ds_read_b128 %4, %15\n\tds_read_b32 %5, %16\n\t"
+        "ds_read_b128 %6, %17\n\tds_read_b32 %7, %18\n\t"
+        "ds_read_b128 %8, %19\n\tds_read_b32 %9, %20\n\t"
+        "ds_read_b32 %10, %21\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=&v"(p[0]), "=&v"(sp[0]), "=&v"(p[1]), "=&v"(sp[1]), "=&v"(p[2]), "=&v"(sp[2]), "=&v"(p[3]),
-          "=&v"(sp[3]), "=&v"(p[4]), "=&v"(sp[4])
-        : "v"(aw[0]), "v"(as[0]), "v"(aw[1]), "v"(as[1]), "v"(aw[2]), "v"(as[2]), "v"(aw[3]), "v"(as[3]),
-          "v"(aw[4]), "v"(as[4])
+        : "=&v"(p[0]), "=&v"(sp[0]), "=&v"(p[1]), "=&v"(sp[1]), "=&v"(p[2]), "=&v"(sp[2]), "=&v"(p[3]), "=&v"(sp[3]),
+          "=&v"(p[4]), "=&v"(sp[4]), "=&v"(xv)
+        : "v"(aw[0]), "v"(as[0]), "v"(aw[1]), "v"(as[1]), "v"(aw[2]), "v"(as[2]), "v"(aw[3]), "v"(as[3]), "v"(aw[4]),
+          "v"(as[4]), "v"(ax)
         : "memory");
 #pragma unroll
     for (int g = 0; g < 5; ++g) {
@@ -159,17 +162,18 @@ __device__ __forceinline__ void lds_read_runs5(const uint32_t (&aw)[5], const ui
     lds_u32x2 p[5];
     uint32_t t3[5], sp[5];
     asm volatile(
-        "ds_read2_b32 %0, %15 offset1:1\n\tds_read_b32 %1, %15 offset:8\n\tds_read_b32 %2, %16\n\t"
-        "ds_read2_b32 %3, %17 offset1:1\n\tds_read_b32 %4, %17 offset:8\n\tds_read_b32 %5, %18\n\t"
-        "ds_read2_b32 %6, %19 offset1:1\n\tds_read_b32 %7, %19 offset:8\n\tds_read_b32 %8, %20\n\t"
-        "ds_read2_b32 %9, %21 offset1:1\n\tds_read_b32 %10, %21 offset:8\n\tds_read_b32 %11, %22\n\t"
-        "ds_read2_b32 %12, %23 offset1:1\n\tds_read_b32 %13, %23 offset:8\n\tds_read_b32 %14, %24\n\t"
+        "ds_read2_b32 %0, %16 offset1:1\n\tds_read_b32 %1, %16 offset:8\n\tds_read_b32 %2, %17\n\t"
+        "ds_read2_b32 %3, %18 offset1:1\n\tds_read_b32 %4, %18 offset:8\n\tds_read_b32 %5, %19\n\t"
+        "ds_read2_b32 %6, %20 offset1:1\n\tds_read_b32 %7, %20 offset:8\n\tds_read_b32 %8, %21\n\t"
+        "ds_read2_b32 %9, %22 offset1:1\n\tds_read_b32 %10, %22 offset:8\n\tds_read_b32 %11, %23\n\t"
+        "ds_read2_b32 %12, %24 offset1:1\n\tds_read_b32 %13, %24 offset:8\n\tds_read_b32 %14, %25\n\t"
+        "ds_read_b32 %15, %26\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(p[0]), "=&v"(t3[0]), "=&v"(sp[0]), "=&v"(p[1]), "=&v"(t3[1]), "=&v"(sp[1]), "=&v"(p[2]),
           "=&v"(t3[2]), "=&v"(sp[2]), "=&v"(p[3]), "=&v"(t3[3]), "=&v"(sp[3]), "=&v"(p[4]), "=&v"(t3[4]),
-          "=&v"(sp[4])
-        : "v"(aw[0]), "v"(as[0]), "v"(aw[1]), "v"(as[1]), "v"(aw[2]), "v"(as[2]), "v"(aw[3]), "v"(as[3]),
-          "v"(aw[4]), "v"(as[4])
+          "=&v"(sp[4]), "=&v"(xv)
+        : "v"(aw[0]), "v"(as[0]), "v"(aw[1]), "v"(as[1]), "v"(aw[2]), "v"(as[2]), "v"(aw[3]), "v"(as[3]), "v"(aw[4]),
+          "v"(as[4]), "v"(ax)
         : "memory");
 #pragma unroll
     for (int g = 0; g < 5; ++g) {
@@ -254,7 +258,8 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
   // up rows).  A pair that reaches past the matrix is not copied (a ragged
   // last row group; an odd R leaves its last row to the epilogue's global
   // read), nor are scales whose pointer is not 4-byte aligned.
-  bool sc_ok = ((reinterpret_cast<uintptr_t>(scales0) | (GATEUP ? reinterpret_cast<uintptr_t>(scales1) : 0u)) & 3u) == 0;
+  bool sc_ok =
+      ((reinterpret_cast<uintptr_t>(scales0) | (GATEUP ? reinterpret_cast<uintptr_t>(scales1) : 0u)) & 3u) == 0;
   if constexpr (GROUP) {
 #pragma unroll
     for (int j = 1; j < kMaxGroup; ++j)
@@ -480,15 +485,6 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
   const uint32_t mul = kMul;
   const uint64_t add64 = kAdd;
   for (int t = 0; t < nwhole; ++t) {
-    // the two waves of a SIMD (w, w ^ 4) share its VALU: the one that has
-    // finished more row groups drops to the lower issue priority, so neither
-    // runs ahead and leaves the other to finish alone (the hardware breaks
-    // ties by age, so on a tie the younger wave takes the higher priority)
-    {
-      const uint32_t other = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_read_b32(prog_other));
-      if ((uint32_t)t < other || ((uint32_t)t == other && wave >= 4)) __builtin_amdgcn_s_setprio(1);
-      else __builtin_amdgcn_s_setprio(0);
-    }
     wait_vmcnt(ncp * (next - 1 - t));          // tile t has landed (tiles after it may be in flight)
     const uint8_t* trow = ring + (size_t)(t % NS) * g.slot_bytes + (size_t)i * gsw * 16;
     f32x4 acc[4];
@@ -516,8 +512,19 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
       aw[gg] = tb + (uint32_t)wo[gg < NG ? gg : 0] * 4u;
       as[gg] = tb + (uint32_t)so[gg < NG ? gg : 0] * 4u;
     }
+    // the same read block fetches the partner wave's progress.  The two waves
+    // of a SIMD (w, w ^ 4) share its VALU: the one that has finished more row
+    // groups drops to the lower issue priority, so neither runs ahead and
+    // leaves the other to finish alone (the hardware breaks ties by age, so
+    // on a tie the younger wave takes the higher priority)
     uint32_t W[5][K + 1];
-    lds_read_runs5<K>(aw, as, W);
+    uint32_t other_v;
+    lds_read_runs5<K>(aw, as, W, prog_other, other_v);
+    {
+      const uint32_t other = (uint32_t)__builtin_amdgcn_readfirstlane((int)other_v);
+      if ((uint32_t)t < other || ((uint32_t)t == other && wave >= 4)) __builtin_amdgcn_s_setprio(1);
+      else __builtin_amdgcn_s_setprio(0);
+    }
 #pragma unroll
     for (int gg = 0; gg < NG; ++gg)
       if (gg < ngw) consume(W[gg], B[gg]);
@@ -555,7 +562,9 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
       as[gg] = tbh + (uint32_t)so[gg < NG ? gg : 0] * 4u;
     }
     uint32_t W[5][K + 1];
-    lds_read_runs5<K>(aw, as, W);
+    uint32_t other_v;
+    lds_read_runs5<K>(aw, as, W, prog_other, other_v);
+    asm volatile("" : : "v"(other_v));         // (the progress word is not needed here)
     f32x4 hacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int gg = 0; gg < NG; ++gg) {
