@@ -116,7 +116,7 @@ constexpr size_t kGemmWorkspace = (size_t)64 << 20;
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-constexpr int kGemmCandidates = 16;
+constexpr int kGemmCandidates = 64;
 
 struct GemmPlan {
   hipblasLtMatmulDesc_t desc = nullptr;
