@@ -296,10 +296,10 @@ __global__ __launch_bounds__(kThreads) void axis0_kernel(const uint32_t* __restr
 #pragma unroll
       for (int h = 0; h < 8; h += 2) {
         const float v0 = ldexpf(xv[n][h], ev[n]), v1 = ldexpf(xv[n][h + 1], ev[n]);
-        const _Float16 h0 = (_Float16)v0, h1 = (_Float16)v1;
-        const _Float16 l0 = (_Float16)(v0 - (float)h0), l1 = (_Float16)(v1 - (float)h1);
-        hw[h >> 1] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-        lw[h >> 1] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+        hw[h >> 1] = pack_f16x2(v0, v1);
+        const half2v hp = __builtin_bit_cast(half2v, hw[h >> 1]);
+        const _Float16 h0 = hp[0], h1 = hp[1];                 // by value
+        lw[h >> 1] = pack_f16x2(v0 - (float)h0, v1 - (float)h1);
       }
       lds_write_b128(lds_addr(xt + n * g.rps + rl), lds_u32x4{hw[0], hw[1], hw[2], hw[3]});
       lds_write_b128(lds_addr(xt + (4 + n) * g.rps + rl), lds_u32x4{lw[0], lw[1], lw[2], lw[3]});

@@ -441,9 +441,7 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
     uint32_t o[4];
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-      const _Float16 lo = (_Float16)ldexpf(bf16_bits_to_f32(u4[h] & 0xFFFFu), xe);
-      const _Float16 hi = (_Float16)ldexpf(bf16_bits_to_f32(u4[h] >> 16), xe);
-      o[h] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+      o[h] = pack_f16x2(ldexpf(bf16_bits_to_f32(u4[h] & 0xFFFFu), xe), ldexpf(bf16_bits_to_f32(u4[h] >> 16), xe));
     }
     if (xok[u]) lds_write_b128(xa[u], lds_u32x4{o[0], o[1], o[2], o[3]});
   }

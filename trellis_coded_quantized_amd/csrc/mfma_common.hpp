@@ -10,6 +10,13 @@ namespace trellis {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+
+// Two f32 values as a packed f16 pair (round to nearest even, a first in the
+// low half): one v_cvt_pk_f16_f32.
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{a, b}, half2v));
+}
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // 1MAD multiplier and addend in full (34038481, 76625530).
