@@ -85,11 +85,15 @@ struct Axis1Geom {
   void* gout[kMaxGroup];
 };
 
-__device__ __forceinline__ uint32_t max_abs8(const uint4& v) {
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// Largest |x| bit pattern of each half over the eight bf16 of a granule,
+// folded into r (packed unsigned 16-bit maxima: the bit patterns of
+// non-negative bf16 values order as their values).
+__device__ __forceinline__ u16x2 max_abs8(const uint4& v, u16x2 r) {
   const uint32_t u4[4] = {v.x, v.y, v.z, v.w};
-  uint32_t r = 0u;
 #pragma unroll
-  for (int h = 0; h < 4; ++h) r = max(r, max(u4[h] & 0x7FFFu, (u4[h] >> 16) & 0x7FFFu));
+  for (int h = 0; h < 4; ++h) r = __builtin_elementwise_max(r, __builtin_bit_cast(u16x2, u4[h] & 0x7FFF7FFFu));
   return r;
 }
 
@@ -396,12 +400,13 @@ __global__ __launch_bounds__(kThreads) void axis1_kernel(
     for (int u = 0; u < kXPer; ++u)
       xr[u] = xok[u] ? make_uint4(xv[u][0], xv[u][1], xv[u][2], xv[u][3]) : make_uint4(0u, 0u, 0u, 0u);
   }
-  uint32_t mx = 0u;
+  u16x2 mxp = {0, 0};
 #pragma unroll
   for (int u = 0; u < kXPer; ++u) {
     if (u >= nxu) break;                       // wave-uniform
-    mx = max(mx, max_abs8(xr[u]));             // zero past the slice
+    mxp = max_abs8(xr[u], mxp);                // zero past the slice
   }
+  uint32_t mx = max((uint32_t)mxp.x, (uint32_t)mxp.y);
   // maximum over the lane's group: within rows of 16 by rotation (every
   // lane of a row ends with the row's maximum), then across rows
   mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0x121, 0xF, 0xF, false));   // row_ror:1
