@@ -228,9 +228,14 @@ __global__ __launch_bounds__(kThreads) void axis0_kernel(const uint32_t* __restr
   // wave's partial sums are scaled back by 2^-e at the end.
   float xv[4][8];
   uint32_t mx0 = 0u, mx1 = 0u, mx2 = 0u, mx3 = 0u;
+  int next0 = 0;
   {
-    int next0 = 0;
-    for (; next0 < min(nmy, 1); ++next0) issue_tile(next0);   // tile 0 streams while x is prepared (more tiles would delay it)
+    // Tile 0 streams while x is prepared.  Only one wave of each SIMD pair
+    // (w < 4) puts its tile into the launch's first HBM burst, which every
+    // workgroup shares: the smaller burst lands sooner, and that wave keeps
+    // the SIMD busy while its partner's tile follows once x has landed.
+    // (More tiles in the burst would delay it further.)
+    for (; next0 < min(nmy, wave < 4 ? 1 : 0); ++next0) issue_tile(next0);
     uint4 xb[4];
     uint16_t sb[8];
     if (fast) {
@@ -259,6 +264,7 @@ __global__ __launch_bounds__(kThreads) void axis0_kernel(const uint32_t* __restr
 #pragma unroll
       for (int h = 0; h < 8; ++h) sb[h] = (hold && rl + h < nr) ? scales[r0 + rl + h] : (uint16_t)0;
     }
+    for (; next0 < min(nmy, 1); ++next0) issue_tile(next0);   // waves 4-7: tile 0 now
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
       const uint32_t w4[4] = {xb[n].x, xb[n].y, xb[n].z, xb[n].w};
@@ -307,7 +313,7 @@ __global__ __launch_bounds__(kThreads) void axis0_kernel(const uint32_t* __restr
   }
 
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  int next = min(nmy, 1);
+  int next = next0;
   for (; next < min(nmy, NS); ++next) issue_tile(next);
 
   // ---- 4. per-lane decode geometry for the four chunks: the 32-bit window
@@ -427,34 +433,26 @@ __global__ __launch_bounds__(kThreads) void axis0_kernel(const uint32_t* __restr
   }
 }
 
-__global__ __launch_bounds__(256) void axis0_fold_kernel(const float* __restrict__ partial,
+// The splits' partials [S][M][C] added in split order, one output per
+// thread, one wave per 64 outputs.  The fold is one memory round trip, and
+// single-wave workgroups spread its loads over more CUs than 256-thread
+// ones would, which shortens it.
+__global__ __launch_bounds__(64) void axis0_fold_kernel(const float* __restrict__ partial,
                                                          void* __restrict__ out, int out_f32,
                                                          int M, int64_t C, int S) {
-  const int64_t i4 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;   // four outputs of [M, C]
-  if (i4 >= (int64_t)M * C) return;
+  const int64_t i = (int64_t)blockIdx.x * 64 + threadIdx.x;
+  if (i >= (int64_t)M * C) return;
   const int64_t stride = (int64_t)M * C;
-  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+  float a = 0.f;
   for (int j0 = 0; j0 < S; j0 += 16) {         // up to sixteen splits' loads in flight at once
-    float4 v[16];
+    float v[16];
 #pragma unroll
-    for (int u = 0; u < 16; ++u)
-      v[u] = (j0 + u < S) ? *reinterpret_cast<const float4*>(partial + (j0 + u) * stride + i4)
-                          : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int u = 0; u < 16; ++u) v[u] = (j0 + u < S) ? partial[(j0 + u) * stride + i] : 0.f;
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {             // in split order
-      a.x += v[u].x;
-      a.y += v[u].y;
-      a.z += v[u].z;
-      a.w += v[u].w;
-    }
+    for (int u = 0; u < 16; ++u) a += v[u];
   }
-  if (out_f32) {
-    *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + i4) = a;
-  } else {
-    const uint32_t lo = (uint32_t)f32_to_bf16_bits(a.x) | ((uint32_t)f32_to_bf16_bits(a.y) << 16);
-    const uint32_t hi = (uint32_t)f32_to_bf16_bits(a.z) | ((uint32_t)f32_to_bf16_bits(a.w) << 16);
-    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + i4) = make_uint2(lo, hi);
-  }
+  if (out_f32) reinterpret_cast<float*>(out)[i] = a;
+  else reinterpret_cast<uint16_t*>(out)[i] = f32_to_bf16_bits(a);
 }
 
 
@@ -579,8 +577,8 @@ hipError_t launch_axis0(const uint32_t* codes, const uint16_t* scales, const uin
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
-  const int64_t n4 = (int64_t)M * C / 4;        // C is a multiple of 256
-  hipLaunchKernelGGL(axis0_fold_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream,
+  const int64_t nout = (int64_t)M * C;          // a multiple of 64 (C is a multiple of 256)
+  hipLaunchKernelGGL(axis0_fold_kernel, dim3((unsigned)((nout + 63) / 64)), dim3(64), 0, stream,
                      partial, out, out_f32, M, C, g.S);
   return hipGetLastError();
 }
