@@ -143,8 +143,8 @@ def _nrep(bytes_per_copy):
     return max(1, math.ceil(ROTATE_BYTES / bytes_per_copy))
 
 
-AXIS1_SOURCES = ("axis1.hip", "copy_ring.hpp", "mfma_common.hpp", "trellis_device.hpp")
-AXIS0_SOURCES = ("axis0.hip", "copy_ring.hpp", "mfma_common.hpp", "trellis_device.hpp")
+AXIS1_SOURCES = ("axis1.hip", "axis1_kernel.hpp", "copy_ring.hpp", "mfma_common.hpp", "trellis_device.hpp")
+AXIS0_SOURCES = ("axis0.hip", "axis0_kernel.hpp", "copy_ring.hpp", "mfma_common.hpp", "trellis_device.hpp")
 PREFILL_SOURCES = ("prefill.hip", "mfma_common.hpp", "trellis_device.hpp")
 
 
