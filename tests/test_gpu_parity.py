@@ -322,18 +322,34 @@ def test_prefill_fused_stream_pieces(k, R, M):
 
 
 @pytest.mark.parametrize("k", [2, 3, 4])
-@pytest.mark.parametrize("R,C,M", [(1000, 1024, 1), (1000, 1024, 32), (777, 512, 9), (40, 256, 17),
+@pytest.mark.parametrize("R,C,M", [(1000, 1024, 1), (1000, 1024, 32), (777, 512, 9), (777, 512, 16), (40, 256, 17),
                                    (4096, 5120, 32), (1000, 1024, 33), (777, 512, 48), (4096, 5120, 64)])
 def test_prefill_direct(k, R, C, M):
     # M <= 64 runs the register-direct kernel: 32-row weight tiles (a ragged last one when
-    # R % 32 != 0), column chunks split over workgroups and waves, one (M <= 32) or two x tiles;
-    # every output
+    # R % 32 != 0), column chunks split over workgroups and waves, one (M <= 32) or two x tiles,
+    # x read in place up to 16 rows; every output
     rng = np.random.default_rng(500 + R + C + M + k)
     codes, scales = rand_matrix(rng, R, C, k)
     x = ti.activations(rng, M, C)
     got = h_u16(tq.prefill(d_codes(codes), d_half(scales), d_bf16(x), k, algo=tq.PREFILL_FUSED))
     want, cond = oracle.prefill_sums(codes, scales, x, M, R, C, k, L, T, np.arange(M), np.arange(R), with_abs=True)
     tol.assert_bf16_close(got, want, cond, f"direct prefill R={R} C={C} M={M} k={k}")
+
+
+@pytest.mark.parametrize("k", [2, 3, 4])
+@pytest.mark.parametrize("R,C", [(1000, 1024), (4096, 5120)])
+def test_prefill_direct_x_in_place_matches_layout(k, R, C):
+    # up to 16 rows the register-direct kernel reads x in place (no layout pass); from 17 rows
+    # through the operand-order copy.  Same kernel arithmetic: the first M rows of a 17-row call
+    # must equal an M-row call bit for bit, at the in-place boundary and below it
+    rng = np.random.default_rng(700 + R + C + k)
+    codes, scales = rand_matrix(rng, R, C, k)
+    x = ti.activations(rng, 17, C)
+    dc, ds, dx = d_codes(codes), d_half(scales), d_bf16(x)
+    ref = tq.prefill(dc, ds, dx, k, algo=tq.PREFILL_FUSED)
+    for M in (1, 7, 16):
+        got = tq.prefill(dc, ds, dx[:M].contiguous(), k, algo=tq.PREFILL_FUSED)
+        assert torch.equal(got.view(torch.int16), ref[:M].view(torch.int16)), f"R={R} C={C} k={k} M={M}"
 
 
 @pytest.mark.parametrize("M", [32, 33, 64, 65, 128, 129, 256, 257])

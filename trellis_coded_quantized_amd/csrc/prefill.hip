@@ -587,14 +587,26 @@ __global__ __launch_bounds__(256) void prefill_fold_kernel(const float* __restri
 // machine stays evenly loaded.  FM x tiles of 32 rows (M <= 64); from 65
 // rows on, the tile kernel above shares each decoded weight among more rows.
 constexpr int kDirectMaxM = 64;
+// Up to this many rows the register-direct kernel reads x in place (no layout
+// pass): per eager call at 17408 x 5120, k = 2, 30.0 vs 32.8 us (M = 2), 31.5
+// vs 33.1 us (M = 8), 34.3 vs 34.7 us (M = 16), 43.0 vs 34.9 us (M = 32).
+constexpr int kDirectXMaxM = 16;
 
 // Two x tiles: registers capped for 4 waves per SIMD (a few spills outside
 // the step loop) ran 3-4 % faster than 3 waves per SIMD without spills.
-template <int K, int FM>
+//
+// XD: x is read in place (x [M, C] row-major) instead of from the operand-
+// order copy, and the layout pass is not launched.  A lane's 16 bytes of a
+// fragment are contiguous in its x row either way; in place, one load
+// touches a line per row of the tile instead of 8 lines, so it pays only
+// for few rows (M <= kDirectXMaxM): rows past M lie outside the buffer
+// range and read as zeros without a memory access.
+template <int K, int FM, bool XD = false>
 __global__ __launch_bounds__(256, FM == 2 ? 4 : 1) void prefill_direct_kernel(
     const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ xf, uint16_t* __restrict__ out, float* __restrict__ part, int R, int C,
     int M, int S) {
+  static_assert(!XD || FM == 1, "x read in place for one 32-row tile only");
   constexpr int WPB = words_per_block(K);
   constexpr int NL = Run16<K>::kLoad;
   __shared__ __attribute__((aligned(16))) float red[3][FM][16][64];   // waves 1..3's accumulators
@@ -614,11 +626,15 @@ __global__ __launch_bounds__(256, FM == 2 ? 4 : 1) void prefill_direct_kernel(
   const int cvo = row * row_bytes;
   const float sc = half_bits_to_f32(scales[row]);
   const int nblk = (M + 31) / 32;
-  const __amdgpu_buffer_rsrc_t xr =
-      __builtin_amdgcn_make_buffer_rsrc((void*)xf, (short)0, nblk * nsteps * 2 * kFrag, kRsrcWord3);
+  // fragment (tile i, step t, half h), lane u: x row 32 i + u % 32, columns
+  // 32 t + 16 (u / 32) + 8 h .. + 7
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)xf, (short)0, XD ? M * C * 2 : nblk * nsteps * 2 * kFrag, kRsrcWord3);
   uint32_t xvo[FM];
 #pragma unroll
-  for (int i = 0; i < FM; ++i) xvo[i] = (uint32_t)min(i, nblk - 1) * (uint32_t)(nsteps * 2 * kFrag) + lane * 16u;
+  for (int i = 0; i < FM; ++i)
+    xvo[i] = XD ? (uint32_t)(lane & 31) * (uint32_t)(C * 2) + (uint32_t)dh * 32u
+                : (uint32_t)min(i, nblk - 1) * (uint32_t)(nsteps * 2 * kFrag) + lane * 16u;
 
   auto load_x = [&](u32x4 (&dst)[2][FM], int t) {
     t = min(t, nsteps - 1);
@@ -626,7 +642,8 @@ __global__ __launch_bounds__(256, FM == 2 ? 4 : 1) void prefill_direct_kernel(
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int i = 0; i < FM; ++i)
-        dst[h][i] = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)xvo[i], (t * 2 + h) * kFrag, 0);
+        dst[h][i] = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)xvo[i], XD ? t * 64 + h * 16 : (t * 2 + h) * kFrag,
+                                                          0);
   };
 
   f32x16 acc[FM];
@@ -805,25 +822,31 @@ hipError_t launch_prefill_fused(const uint32_t* codes, const uint16_t* scales, c
   float* part = reinterpret_cast<float*>(ws + ((size_t)prefill_xf_bytes(C, M) + 255) / 256 * 256);
   const int r = (int)R, c = (int)C, m = (int)M;
   const int64_t nunits = prefill_xf_bytes(C, M) / 16;
-  hipLaunchKernelGGL(prefill_xlayout_kernel, dim3((unsigned)((nunits + 255) / 256)), dim3(256), 0, stream, x,
-                     reinterpret_cast<uint4*>(xf), m, c, nunits);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
+  const bool xd = !axis0 && M <= kDirectXMaxM;   // x read in place: no layout pass
+  if (!xd) {
+    hipLaunchKernelGGL(prefill_xlayout_kernel, dim3((unsigned)((nunits + 255) / 256)), dim3(256), 0, stream, x,
+                       reinterpret_cast<uint4*>(xf), m, c, nunits);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (!axis0 && M <= kDirectMaxM) {
     const int S = direct_splits(R, C);
     const dim3 dgrid((unsigned)(((R + 31) / 32) * S));
+#define TRELLIS_DIRECT_LAUNCH(KK)                                                                                  \
+  if (xd) hipLaunchKernelGGL((prefill_direct_kernel<KK, 1, true>), dgrid, dim3(256), 0, stream, codes, scales, x, out, \
+                             part, r, c, m, S);                                                                    \
+  else if (M > 32) hipLaunchKernelGGL((prefill_direct_kernel<KK, 2>), dgrid, dim3(256), 0, stream, codes, scales, xf,  \
+                                      out, part, r, c, m, S);                                                      \
+  else hipLaunchKernelGGL((prefill_direct_kernel<KK, 1>), dgrid, dim3(256), 0, stream, codes, scales, xf, out, part, r, \
+                          c, m, S)
     switch (k) {
-      case 2: if (M > 32) hipLaunchKernelGGL((prefill_direct_kernel<2, 2>), dgrid, dim3(256), 0, stream, codes, scales, xf, out, part, r, c, m, S);
-              else hipLaunchKernelGGL((prefill_direct_kernel<2, 1>), dgrid, dim3(256), 0, stream, codes, scales, xf, out, part, r, c, m, S);
-              break;
-      case 3: if (M > 32) hipLaunchKernelGGL((prefill_direct_kernel<3, 2>), dgrid, dim3(256), 0, stream, codes, scales, xf, out, part, r, c, m, S);
-              else hipLaunchKernelGGL((prefill_direct_kernel<3, 1>), dgrid, dim3(256), 0, stream, codes, scales, xf, out, part, r, c, m, S);
-              break;
-      case 4: if (M > 32) hipLaunchKernelGGL((prefill_direct_kernel<4, 2>), dgrid, dim3(256), 0, stream, codes, scales, xf, out, part, r, c, m, S);
-              else hipLaunchKernelGGL((prefill_direct_kernel<4, 1>), dgrid, dim3(256), 0, stream, codes, scales, xf, out, part, r, c, m, S);
-              break;
+      case 2: TRELLIS_DIRECT_LAUNCH(2); break;
+      case 3: TRELLIS_DIRECT_LAUNCH(3); break;
+      case 4: TRELLIS_DIRECT_LAUNCH(4); break;
       default: return hipErrorInvalidValue;
     }
+#undef TRELLIS_DIRECT_LAUNCH
     e = hipGetLastError();
     if (e != hipSuccess || S == 1) return e;
     const int64_t n = M * R;
