@@ -397,7 +397,7 @@ __device__ __forceinline__ void axis0_body(const uint32_t* __restrict__ codes, c
     }
     lds_write_b32(prog_mine, (uint32_t)t + 1u);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);   // this tile's reads stay before its slot is refilled
-    if (next < nmy && next <= t + NS) issue_tile(next++);
+    if (next < nmy && next <= t + 2) issue_tile(next++);   // one tile ahead once the first NS have gone out
   }
 
   // ---- 5. hi + lo into LDS; the waves' tiles are added in a
