@@ -392,12 +392,17 @@ __device__ __forceinline__ void axis0_body(const uint32_t* __restrict__ codes, c
       } else {
         asm volatile("" : : "v"(other_v));     // (not needed for the second read block)
       }
+      if (ch == kChunks - 2) {
+        // the tile's last words are in registers: its slot may be refilled
+        // now, ahead of the decode (one tile ahead once the first NS have
+        // gone out)
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (next < nmy && next <= t + 2) issue_tile(next++);
+      }
       decode_chunk(ch, W[0]);
       decode_chunk(ch + 1, W[1]);
     }
     lds_write_b32(prog_mine, (uint32_t)t + 1u);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);   // this tile's reads stay before its slot is refilled
-    if (next < nmy && next <= t + 2) issue_tile(next++);   // one tile ahead once the first NS have gone out
   }
 
   // ---- 5. hi + lo into LDS; the waves' tiles are added in a
