@@ -314,7 +314,7 @@ __device__ __forceinline__ void axis0_body(const uint32_t* __restrict__ codes, c
 
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   int next = next0;
-  for (; next < min(nmy, NS); ++next) issue_tile(next);
+  for (; next < min(nmy, 2); ++next) issue_tile(next);    // tile 1; then one tile ahead (below)
 
   // ---- 4. per-lane decode geometry for the four chunks: the 32-bit window
   // of columns 4i .. 4i+3 starts at bit (252 - t) k of the block (t = the
@@ -394,8 +394,8 @@ __device__ __forceinline__ void axis0_body(const uint32_t* __restrict__ codes, c
       }
       if (ch == kChunks - 2) {
         // the tile's last words are in registers: its slot may be refilled
-        // now, ahead of the decode (one tile ahead once the first NS have
-        // gone out)
+        // now, ahead of the decode (tile t + 2, one tile ahead of the next
+        // block)
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         if (next < nmy && next <= t + 2) issue_tile(next++);
       }
